@@ -1,0 +1,295 @@
+"""Plain CPU oracle (numpy) for the W4A16 / W4A8 group-quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` and by nothing else.  It shares no
+code, header, table or constant generator with the GPU library.
+
+Sources (web pages; cited by title and the part of the page):
+
+* [AWQ-vLLM]  "Implement AWQ quantization support for LLaMA" (vllm-project/vllm
+  PR 1032): the comment thread on the AWQ GEMM kernel, including the remark
+  that dequantization is the tricky part and the rest is plain FP16 work, and
+  the comment listing the Triton AWQ weight format (activations (M, K), packed
+  weights along K with ``pack_num`` codes per word, per-group scales and
+  zeros).
+* [QQQ-lmdeploy]  "[Feature] support qqq(w4a8) for lmdeploy" (InternLM/lmdeploy
+  issue 2274), section "Modification": a W4A8 GEMM, online (per-token)
+  activation quantization fused with RMSNorm, fused gate+up weights; section
+  "Benchmark": per-channel and g128 variants.
+* [AWQ-fixes]  "Some fixes for AWQ" (neuralmagic/compressed-tensors PR 269):
+  the opening comment (asymmetric quantization aligned with AutoAWQ's
+  pseudo-quantize rule), the reply defining W4A16 (fp16 in, int4 weights,
+  fp16 out, no activation quantization arguments) and the reply on 8-bit
+  matmuls that output int32 and are rescaled by weight and activation scales,
+  with activations quantized dynamically.
+
+Readings where the pages are silent (each one is listed in the design doc):
+
+* R1 asymmetric rule: per (row n, group g) ``s = (max - min) / 15`` computed in
+  fp32 (IEEE division), floored at 1e-5, stored as fp16 (RNE);
+  ``z = clamp(rint(-min / s16), 0, 15)``; ``q = clamp(rint(w / s16) + z, 0, 15)``
+  with the stored fp16 scale, in fp32.  Quantized codes are integers decided
+  in fp32, the precision the GPU kernel uses.
+* R2 rounding is round-half-to-even everywhere (``np.rint``).
+* R3 dequantization is ``(q - z) * s16`` (exact in fp64; a single fp16
+  rounding when exported as fp16).
+* R4 packing is the plain nibble order: element ``8*j + i`` of a packed axis
+  lives in bits ``4*i .. 4*i+3`` of word ``j``; pad nibbles are 0.
+  Layouts: ``qweight`` int32 [N, K/8] (packed along K), ``scales`` fp16
+  [K/G, N], ``qzeros`` int32 [K/G, ceil(N/8)] (packed along N).
+* R5 W4A8 weights (the pages print no constants): per-channel (group -1)
+  ``s_c = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s_c), -8, 7)``;
+  two-level g128: ``s_c = fp16(max(max|w| / 127, 1e-5))``,
+  ``w8 = clamp(rint(w / s_c), -127, 127)``, per group ``m = max|w8|``,
+  ``s_g = min(max(1, ceil(m / 7)), 18)`` (int8), ``q = clamp(rint(w8 / s_g), -7, 7)``.
+  Stored nibble is ``q + 8``.  ``|q * s_g| <= 126`` so the int4 x int8-scale
+  product always fits int8.  The constants are a reading; the implementation
+  is pinned by exhaustive invariants, the reading itself is "parity unpinned"
+  against the pages.
+* R6 W4A8 activations: RMSNorm ``y = x / sqrt(mean(x^2) + eps) * gamma`` in
+  fp64 with no fp16 round-trip of ``y``; the quantization decision is taken
+  in fp32 on ``y32 = fp32(y)``: ``M = max|y32|``, ``inv = fp32(127 / M)``,
+  ``xq = clamp(rint(fp32(y32 * inv)), -127, 127)``, ``s_a = fp32(M / 127)``;
+  a zero row gives ``s_a = 1``, ``xq = 0``.  Without gamma (no-norm mode)
+  ``y32 = x``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F16 = np.float16
+F32 = np.float32
+F64 = np.float64
+
+__all__ = [
+    "pack_nibbles", "unpack_nibbles",
+    "quantize_asym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
+    "linear_ref",
+    "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref",
+    "w4a8_acc_ref", "w4a8_linear_ref",
+]
+
+
+# --------------------------------------------------------------------------
+# Packing (R4).  [AWQ-vLLM], comment on the Triton AWQ weight format: codes are
+# packed ``pack_num`` = 8 per 32-bit word along one axis.
+# --------------------------------------------------------------------------
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes [R, C] (values 0..15) into int32 [R, ceil(C/8)].
+
+    Element ``8*j + i`` of a row goes to bits ``4*i .. 4*i+3`` of word ``j``.
+    Missing trailing elements are treated as code 0.
+    """
+    codes = np.asarray(codes)
+    if codes.ndim != 2:
+        raise ValueError("codes must be 2-D")
+    if codes.size and (codes.min() < 0 or codes.max() > 15):
+        raise ValueError("codes must lie in [0, 15]")
+    R, C = codes.shape
+    W = (C + 7) // 8
+    padded = np.zeros((R, W * 8), dtype=np.int64)
+    padded[:, :C] = codes
+    words = np.zeros((R, W), dtype=np.int64)
+    for i in range(8):
+        words += padded[:, i::8] << (4 * i)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def unpack_nibbles(words: np.ndarray, C: int) -> np.ndarray:
+    """Inverse of :func:`pack_nibbles`: int32 [R, W] -> uint8 codes [R, C]."""
+    words = np.asarray(words)
+    if words.dtype != np.int32:
+        raise ValueError("words must be int32")
+    u = words.view(np.uint32).astype(np.int64)
+    R, W = u.shape
+    if C > 8 * W:
+        raise ValueError("C larger than the packed capacity")
+    out = np.zeros((R, 8 * W), dtype=np.uint8)
+    for i in range(8):
+        out[:, i::8] = (u >> (4 * i)) & 0xF
+    return out[:, :C]
+
+
+# --------------------------------------------------------------------------
+# W4A16 asymmetric quantization (R1, R2).  [AWQ-fixes], opening comment.
+# --------------------------------------------------------------------------
+def quantize_asym(w16: np.ndarray, group_size: int = 128):
+    """Group-wise asymmetric uint4 quantization of fp16 weights [N, K].
+
+    Returns ``(codes uint8 [N, K], scales fp16 [N, K/G], zeros uint8 [N, K/G])``
+    in the natural (row, group) orientation.  All decisions in fp32.
+    """
+    w16 = np.asarray(w16)
+    if w16.dtype != F16 or w16.ndim != 2:
+        raise ValueError("w16 must be a 2-D float16 array")
+    N, K = w16.shape
+    G = int(group_size)
+    if G <= 0 or K % G:
+        raise ValueError("K must be a multiple of group_size")
+    w = w16.astype(F32).reshape(N, K // G, G)
+    mn = w.min(axis=2)
+    mx = w.max(axis=2)
+    s32 = (mx - mn) / F32(15.0)
+    s32 = np.maximum(s32, F32(1e-5))
+    s16 = s32.astype(F16)
+    s = s16.astype(F32)
+    z = np.clip(np.rint(-mn / s), F32(0), F32(15))
+    q = np.clip(np.rint(w / s[:, :, None]) + z[:, :, None], F32(0), F32(15))
+    return (q.reshape(N, K).astype(np.uint8), s16, z.astype(np.uint8))
+
+
+def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
+    """Natural-orientation quantized weights -> the packed layout of R4.
+
+    ``codes`` uint8 [N, K], ``scales`` fp16 [N, K/G], ``zeros`` uint8 [N, K/G]
+    -> ``(qweight int32 [N, K/8], scales fp16 [K/G, N], qzeros int32
+    [K/G, ceil(N/8)])``.
+    """
+    N, K = codes.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    qweight = pack_nibbles(codes)
+    scales_gn = np.ascontiguousarray(np.asarray(scales, dtype=F16).T)
+    qzeros = pack_nibbles(np.ascontiguousarray(np.asarray(zeros).T))
+    return qweight, scales_gn, qzeros
+
+
+def unpack_awq(qweight: np.ndarray, scales_gn: np.ndarray, qzeros: np.ndarray, K: int):
+    """Packed layout -> ``(codes [N, K], scales fp16 [N, K/G], zeros [N, K/G])``."""
+    N = qweight.shape[0]
+    codes = unpack_nibbles(qweight, K)
+    scales = np.ascontiguousarray(scales_gn.T)
+    zeros = np.ascontiguousarray(unpack_nibbles(qzeros, N).T)
+    return codes, scales, zeros
+
+
+def dequant_awq(qweight, scales_gn, qzeros, K: int, group_size: int = 128) -> np.ndarray:
+    """Dequantized weights ``(q - z) * s`` in fp64, [N, K] (R3).
+
+    [AWQ-vLLM], comment that dequantization is the tricky part; the product of
+    a small integer and an fp16 scale is exact in fp64.
+    """
+    codes, scales, zeros = unpack_awq(qweight, scales_gn, qzeros, K)
+    G = int(group_size)
+    N = codes.shape[0]
+    s = np.repeat(scales.astype(F64), G, axis=1)
+    z = np.repeat(zeros.astype(F64), G, axis=1)
+    assert s.shape == (N, K)
+    return (codes.astype(F64) - z) * s
+
+
+def linear_ref(x16: np.ndarray, w_deq: np.ndarray) -> np.ndarray:
+    """``Y = X @ w_deq^T`` in fp64 ([AWQ-fixes], reply defining W4A16: fp16
+    inputs multiplied by int4-quantized weights give fp16 outputs)."""
+    return np.asarray(x16, dtype=F64) @ np.asarray(w_deq, dtype=F64).T
+
+
+def awq_reference(w16: np.ndarray, x16: np.ndarray, group_size: int = 128):
+    """The whole W4A16 chain: quantize -> pack -> unpack -> dequant -> fp64 matmul.
+
+    Returns a dict with the packed tensors, the fp64 dequantized weights and
+    the fp64 outputs.
+    """
+    codes, scales, zeros = quantize_asym(w16, group_size)
+    qweight, scales_gn, qzeros = pack_awq(codes, scales, zeros)
+    w_deq = dequant_awq(qweight, scales_gn, qzeros, w16.shape[1], group_size)
+    y = linear_ref(x16, w_deq) if x16 is not None else None
+    return dict(qweight=qweight, scales=scales_gn, qzeros=qzeros, w_deq=w_deq, y=y)
+
+
+# --------------------------------------------------------------------------
+# W4A8 (R5, R6).  [QQQ-lmdeploy] "Modification" and "Benchmark";
+# [AWQ-fixes] reply on int32 matmul output rescaled by both scales.
+# --------------------------------------------------------------------------
+def quantize_w4a8(w16: np.ndarray, group_size: int = -1):
+    """Symmetric int4 weights for W4A8 (R5).
+
+    ``group_size == -1``: per-channel, returns ``(q int8 [N,K] in [-8,7],
+    cscale fp16 [N], None)``.  ``group_size == G > 0``: two-level, returns
+    ``(q int8 [N,K] in [-7,7], cscale fp16 [N], gscale int8 [N, K/G])``.
+    Decisions in fp32.
+    """
+    w16 = np.asarray(w16)
+    if w16.dtype != F16 or w16.ndim != 2:
+        raise ValueError("w16 must be a 2-D float16 array")
+    N, K = w16.shape
+    w = w16.astype(F32)
+    amax = np.abs(w).max(axis=1)
+    if group_size == -1:
+        s32 = np.maximum(amax / F32(7.0), F32(1e-5))
+        s16 = s32.astype(F16)
+        q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-8), F32(7))
+        return q.astype(np.int8), s16, None
+    G = int(group_size)
+    if G <= 0 or K % G:
+        raise ValueError("K must be a multiple of group_size")
+    s32 = np.maximum(amax / F32(127.0), F32(1e-5))
+    s16 = s32.astype(F16)
+    w8 = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-127), F32(127))
+    w8g = w8.reshape(N, K // G, G)
+    m = np.abs(w8g).max(axis=2)
+    sg = np.minimum(np.maximum(F32(1), np.ceil(m / F32(7))), F32(18))
+    q = np.clip(np.rint(w8g / sg[:, :, None]), F32(-7), F32(7))
+    return q.reshape(N, K).astype(np.int8), s16, sg.astype(np.int8)
+
+
+def pack_w4a8(q: np.ndarray, cscale: np.ndarray, gscale):
+    """-> ``(qweight int32 [N, K/8] of biased nibbles q+8, cscale fp16 [N],
+    gscale int8 [K/G, N] or None)``."""
+    qweight = pack_nibbles(np.asarray(q, dtype=np.int64) + 8)
+    gs = None if gscale is None else np.ascontiguousarray(np.asarray(gscale, dtype=np.int8).T)
+    return qweight, np.asarray(cscale, dtype=F16), gs
+
+
+def unpack_w4a8(qweight: np.ndarray, K: int) -> np.ndarray:
+    """Biased-nibble words -> signed int4 values [N, K] (int64)."""
+    return unpack_nibbles(qweight, K).astype(np.int64) - 8
+
+
+def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):
+    """Per-token symmetric int8 activation quantization, optionally fused with
+    RMSNorm (R6).  Returns ``(xq int8 [M,K], s_a fp32 [M], t fp64 [M,K])`` where
+    ``t`` is the fp32 value that was rounded to give ``xq`` (for near-tie
+    accounting in tests)."""
+    x = np.asarray(x16)
+    if x.dtype != F16 or x.ndim != 2:
+        raise ValueError("x16 must be a 2-D float16 array")
+    M, K = x.shape
+    if gamma16 is None:
+        y32 = x.astype(F32)
+    else:
+        x64 = x.astype(F64)
+        r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + float(eps))
+        y64 = x64 * r[:, None] * np.asarray(gamma16, dtype=F16).astype(F64)[None, :]
+        y32 = y64.astype(F32)
+    amax = np.abs(y32).max(axis=1) if K else np.zeros(M, F32)
+    xq = np.zeros((M, K), dtype=np.int8)
+    s_a = np.ones(M, dtype=F32)
+    t_all = np.zeros((M, K), dtype=F64)
+    for m in range(M):
+        if amax[m] == 0:
+            continue
+        inv = F32(127.0) / amax[m]
+        t = y32[m] * inv
+        xq[m] = np.clip(np.rint(t), -127, 127).astype(np.int8)
+        s_a[m] = amax[m] / F32(127.0)
+        t_all[m] = t
+    return xq, s_a, t_all
+
+
+def w4a8_acc_ref(xq: np.ndarray, q: np.ndarray, gscale_ng, group_size: int) -> np.ndarray:
+    """Exact integer accumulators ``acc[m,n] = sum_k xq[m,k] * q[n,k] * s_g[n, k//G]``
+    (int64).  ``gscale_ng`` is int8 [N, K/G] or None (per-channel)."""
+    xq = np.asarray(xq, dtype=np.int64)
+    q = np.asarray(q, dtype=np.int64)
+    if gscale_ng is not None:
+        G = int(group_size)
+        q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)
+    return xq @ q.T
+
+
+def w4a8_linear_ref(acc: np.ndarray, s_a: np.ndarray, cscale: np.ndarray) -> np.ndarray:
+    """fp64 outputs ``acc * s_a[m] * s_c[n]``."""
+    return (np.asarray(acc, dtype=F64) * np.asarray(s_a, dtype=F64)[:, None]
+            * np.asarray(cscale, dtype=F16).astype(F64)[None, :])
+

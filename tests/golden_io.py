@@ -1,0 +1,68 @@
+"""Readers for the hand-worked text fixtures under tests/golden/."""
+import os
+import struct
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def h16(hexstr: str) -> np.float16:
+    return np.frombuffer(struct.pack("<H", int(hexstr, 16)), dtype=np.float16)[0]
+
+
+def _values(tokens):
+    out = []
+    for t in tokens:
+        if "x" in t:
+            cnt, hx = t.split("x")
+            out += [h16(hx)] * int(cnt)
+        else:
+            out.append(h16(t))
+    return np.array(out, dtype=np.float16)
+
+
+def read_pack_words():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "pack_words.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        lhs, rhs = line.split("->")
+        rows.append(([int(v) for v in lhs.split()], int(rhs.strip(), 16)))
+    return rows
+
+
+def read_cases(name):
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tok = line.split()
+        if tok[0] == "case":
+            cur = {"name": tok[1], "code": {}, "deq": {}}
+            cases.append(cur)
+        elif tok[0] == "values":
+            cur["values"] = _values(tok[1:])
+        elif tok[0] == "scale":
+            cur["scale"] = h16(tok[1])
+            cur["zero"] = int(tok[3])
+        elif tok[0] == "code":
+            cur["code"][tok[1].upper()] = int(tok[2])
+        elif tok[0] == "deq":
+            cur["deq"][tok[1].upper()] = tok[2]
+        elif tok[0] == "group":
+            cur["group"] = int(tok[1])
+        elif tok[0] == "cscale":
+            cur["cscale"] = h16(tok[1])
+        elif tok[0] == "gscale":
+            cur["gscale"] = [int(v) for v in tok[1:]]
+        elif tok[0] == "q":
+            cur["q"] = [int(v) for v in tok[1:]]
+        elif tok[0] == "q_head":
+            parts = " ".join(tok[1:]).split("|")
+            cur["q_head"] = [[int(v) for v in p.split()] for p in parts]
+        else:
+            raise ValueError(f"unknown fixture key {tok[0]!r}")
+    return cases

@@ -1,0 +1,58 @@
+"""CPU: plant plausible mistakes in a copy of the oracle and check that at least
+one pin fails for each.  This shows the pins can catch a dropped term, a wrong
+sign, index or constant, or a transposed operand."""
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "ref.py")
+
+MUTANTS = [
+    ("scale divisor 16", "s32 = (mx - mn) / F32(15.0)", "s32 = (mx - mn) / F32(16.0)"),
+    ("scale from unrounded fp32", "s = s16.astype(F32)\n", "s = s32\n"),
+    ("zero sign flipped", "np.rint(-mn / s)", "np.rint(mn / s)"),
+    ("zero not added", "np.rint(w / s[:, :, None]) + z[:, :, None]", "np.rint(w / s[:, :, None])"),
+    ("code clamp 14", "+ z[:, :, None], F32(0), F32(15))", "+ z[:, :, None], F32(0), F32(14))"),
+    ("min/max swapped", "mn = w.min(axis=2)\n    mx = w.max(axis=2)", "mn = w.max(axis=2)\n    mx = w.min(axis=2)"),
+    ("dequant adds zero", "(codes.astype(F64) - z) * s", "(codes.astype(F64) + z) * s"),
+    ("dequant drops zero", "(codes.astype(F64) - z) * s", "codes.astype(F64) * s"),
+    ("pack nibble order reversed", "words += padded[:, i::8] << (4 * i)", "words += padded[:, i::8] << (4 * (7 - i))"),
+    ("unpack nibble order reversed", "out[:, i::8] = (u >> (4 * i)) & 0xF", "out[:, i::8] = (u >> (4 * (7 - i))) & 0xF"),
+    ("scales not transposed", "scales = np.ascontiguousarray(scales_gn.T)", "scales = np.ascontiguousarray(scales_gn).reshape(scales_gn.shape[::-1])"),
+    ("group index off by one", "s = np.repeat(scales.astype(F64), G, axis=1)", "s = np.roll(np.repeat(scales.astype(F64), G, axis=1), 1, axis=1)"),
+    ("matmul transposed operand", "np.asarray(w_deq, dtype=F64).T", "np.asarray(w_deq, dtype=F64).T[::-1]"),
+    ("w4a8 s_g cap 19", "np.ceil(m / F32(7))), F32(18))", "np.ceil(m / F32(7))), F32(19))"),
+    ("w4a8 s_g rint", "np.ceil(m / F32(7))", "np.rint(m / F32(7))"),
+    ("w4a8 first level /128", "amax / F32(127.0)", "amax / F32(128.0)"),
+    ("w4a8 bias 7", "np.asarray(q, dtype=np.int64) + 8)", "np.asarray(q, dtype=np.int64) + 7)"),
+    ("act eps dropped", "np.mean(x64 * x64, axis=1) + float(eps)", "np.mean(x64 * x64, axis=1)"),
+    ("act gamma dropped", "y64 = x64 * r[:, None] * np.asarray(gamma16, dtype=F16).astype(F64)[None, :]", "y64 = x64 * r[:, None]"),
+    ("act s_a over 128", "s_a[m] = amax[m] / F32(127.0)", "s_a[m] = amax[m] / F32(128.0)"),
+    ("act truncation", "xq[m] = np.clip(np.rint(t), -127, 127)", "xq[m] = np.clip(np.trunc(t), -127, 127)"),
+    ("act rounds half away from zero", "xq[m] = np.clip(np.rint(t), -127, 127)", "xq[m] = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -127, 127)"),
+    ("weight codes round half away from zero", "q = np.clip(np.rint(w / s[:, :, None])", "q = np.clip(np.sign(w) * np.floor(np.abs(w / s[:, :, None]) + 0.5)"),
+    ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
+]
+
+
+def _build(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mut = _build(old, new)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mut)
+        except Exception as e:  # AssertionError or a shape/type error the mistake causes
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutant {name!r}"
