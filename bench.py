@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A16-g128 linear layer on one MI355X.
+
+Default workload: the Llama-2-13B decode projection set -- fused QKV (K=5120,
+N=15360), O (5120, 5120), fused gate+up (5120, 27648) and down (13824, 5120) -- at
+M in {1, 4, 16} tokens.  One step = the 12 awq_gemm calls (every projection at every
+M).  Inputs are seeded synthetic tensors (weights ~N(0, 0.02) with 1% outlier input
+channels x10, activations ~N(0, 1)), quantized and packed on the GPU before timing;
+everything is resident in HBM when the timed region starts.  To keep the 256 MB
+Infinity Cache from serving weights, R copies of every packed weight set are rotated
+so that a weight set is re-read only after ~R x 165 MB of other weights.
+
+value = algorithmic bytes of all timed calls / wall time of the timed region (GB/s).
+Algorithmic bytes of one call: N*K/2 (codes) + 2*N*K/G (scales) + N*K/(2G) (zeros)
++ 2*M*K (X) + 2*M*N (Y).
+
+The JSON line also carries
+  roofline      the dominant kernel (the skinny M<=16 kernel: every decode call) from
+                per-launch HIP events recorded between the launches of the timed region
+  cpu_baseline  the CPU oracle (numpy dequant + fp64 matmul) on one decode step
+  detail        the other workloads (single M=8 GEMM, the batch crossover sweep, the
+                M=4096 prefill GEMMs in TFLOP/s, the W4A8 stage), timed separately
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+F16_PEAK_TFLOPS = 2516.6
+I8_PEAK_TOPS = 5033.2
+G = 128
+
+
+def awq_bytes(M, N, K):
+    return N * K / 2 + 2 * N * (K // G) + N * (K // G) / 2 + 2 * M * K + 2 * M * N
+
+
+def w4a8_bytes(M, N, K, two_level):
+    return N * K / 2 + 2 * N + (N * (K // G) if two_level else 0) + M * K + 4 * M + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="copies of each packed weight set")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--detail-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def rotated_awq(qw, sc, qz, r):
+    """Copy r of a packed W4A16 weight: the same matrix with its rows (output channels)
+    rolled by 56 r, a distinct buffer in HBM for cache rotation."""
+    import torch
+    sh = 56 * r
+    return (torch.roll(qw, sh, 0).contiguous(), torch.roll(sc, sh, 1).contiguous(),
+            torch.roll(qz, sh // 8, 1).contiguous())
+
+
+def rotated_w4a8(qw, gs, cs, r):
+    import torch
+    sh = 56 * r
+    return (torch.roll(qw, sh, 0).contiguous(), None if gs is None else torch.roll(gs, sh, 1).contiguous(),
+            torch.roll(cs, sh, 0).contiguous())
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
+                          "described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_gemm_amd as w4
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w4.load()
+
+    # ---------------------------------------------------------------- inputs
+    log("generating inputs")
+    host = {}
+    packed = {}
+    for name, (K, N) in synth.LLAMA2_13B.items():
+        inp = synth.make_linear(16, N, K, seed=0, outliers=True)
+        host[name] = inp
+        qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+        packed[name] = [rotated_awq(qw, sc, qz, r) for r in range(args.rotate)]
+        del qw, sc, qz
+    torch.cuda.synchronize()
+
+    Ms = (1, 4, 16)
+    names = list(synth.LLAMA2_13B)
+    xs = {(name, M): host[name].x[:M].contiguous().to(dev) for name in names for M in Ms}
+    ys = {(name, M): torch.empty((M, synth.LLAMA2_13B[name][1]), dtype=torch.float16, device=dev)
+          for name in names for M in Ms}
+    # calls[i] for round j: projections in order, M fixed per round, weight copy j % R
+    rounds = []
+    for j in range(len(Ms) * args.rotate):
+        M = Ms[j % len(Ms)]
+        r = j % args.rotate
+        rounds.append([(name, M, w4.bind_awq_gemm(xs[(name, M)], *packed[name][r], ys[(name, M)]))
+                       for name in names])
+    per_step = len(Ms) * len(names)
+    byts = {(name, M): awq_bytes(M, synth.LLAMA2_13B[name][1], synth.LLAMA2_13B[name][0])
+            for name in names for M in Ms}
+    step_bytes = sum(byts.values())
+
+    def calls_for_step(s):
+        out = []
+        for j in range(len(Ms)):
+            out += rounds[(s * len(Ms) + j) % len(rounds)]
+        return out
+
+    # --------------------------------------------------------------- warmup
+    log(f"warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        for (_, _, fn) in calls_for_step(s):
+            fn()
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed
+    stream = torch.cuda.current_stream(dev)
+    n_launch = per_step * args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)]
+    launch_bytes = []
+    plan = [calls_for_step(args.warmup + s) for s in range(args.steps)]
+    log(f"timed {args.steps} steps x {per_step} launches")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    i = 0
+    for s in range(args.steps):
+        for (name, M, fn) in plan[s]:
+            fn()
+            i += 1
+            evs[i].record(stream)
+            launch_bytes.append(byts[(name, M)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = evs[0].elapsed_time(evs[-1])
+    durs = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(n_launch)]) * 1e-3  # s
+    gbs = step_bytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = float(np.sum(launch_bytes) / np.sum(durs) / 1e9)
+    avg_us = float(np.mean(durs) * 1e6)
+    by_shape = {}
+    for k, (name, M, _) in enumerate([c for s in range(args.steps) for c in plan[s]]):
+        by_shape.setdefault(f"{name}_M{M}", []).append(durs[k])
+    shape_detail = {}
+    for key, v in by_shape.items():
+        name, M = key.rsplit("_M", 1)
+        b = byts[(name, int(M))]
+        t = float(np.mean(v))
+        shape_detail[key] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+                             "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3)}
+    log(f"timed region {total_ms:.3f} ms (host wall {wall * 1e3:.1f} ms): {gbs:.1f} GB/s")
+
+    result = {
+        "metric": "W4A16-g128 GEMM GB/s (M<=16) & TFLOP/s (M>=256) vs roofline, 13B shapes",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (int4 weights, fp32 accumulate)",
+        "data": "synthetic (seeded; W~N(0,0.02) with 1% outlier input channels x10, X~N(0,1))",
+        "config": {"workload": "Llama-2-13B decode projection set: QKV 5120x15360, O 5120x5120, "
+                               "gate+up 5120x27648, down 13824x5120 at M in {1,4,16}; g128 asymmetric uint4",
+                   "launches_per_step": per_step, "weight_copies_rotated": args.rotate,
+                   "bytes_per_step": int(step_bytes)},
+        "roofline": {"bound": "hbm", "kernel": "skinny_kernel<1> (awq_gemm, M<=16)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(avg_us, 3), "traffic": None},
+        "per_shape": shape_detail,
+    }
+
+    if not args.no_detail:
+        result["detail"] = detail(args, dev, torch, np, synth, w4, host, packed)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, synth, host)
+    print(json.dumps(result), flush=True)
+
+
+def _time_calls(torch, calls, iters):
+    """Average time per call of a list of bound calls run round robin (HIP events)."""
+    for fn in calls[: min(len(calls), 4)]:
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    n = 0
+    for it in range(iters):
+        calls[it % len(calls)]()
+        n += 1
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / n
+
+
+def detail(args, dev, torch, np, synth, w4, host, packed):
+    out = {}
+    it = args.detail_iters
+    # single M=8 GEMM (K=N=4096), rotated over 16 copies (8.9 MB each)
+    log("detail: single M=8 GEMM")
+    inp = synth.make_linear(8, 4096, 4096, seed=0, outliers=False)
+    qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+    x = inp.x.to(dev)
+    y = torch.empty((8, 4096), dtype=torch.float16, device=dev)
+    calls = [w4.bind_awq_gemm(x, *rotated_awq(qw, sc, qz, r), y) for r in range(64)]
+    t = _time_calls(torch, calls, max(it, 64) * 4)
+    b = awq_bytes(8, 4096, 4096)
+    out["single_m8_4096"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+                             "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3)}
+    del calls, qw, sc, qz
+    # batch crossover sweep K=5120, N=13824
+    log("detail: crossover sweep")
+    inp = synth.make_linear(256, 13824, 5120, seed=0, outliers=True)
+    qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+    copies = [rotated_awq(qw, sc, qz, r) for r in range(16)]
+    sweep = {}
+    for M in (1, 2, 8, 16, 32, 64, 128, 256):
+        x = inp.x[:M].contiguous().to(dev)
+        y = torch.empty((M, 13824), dtype=torch.float16, device=dev)
+        calls = [w4.bind_awq_gemm(x, *c, y) for c in copies]
+        t = _time_calls(torch, calls, max(it, 32))
+        b = awq_bytes(M, 13824, 5120)
+        fl = 2.0 * M * 13824 * 5120
+        sweep[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1), "TFLOPs": round(fl / t / 1e12, 2),
+                          "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3),
+                          "frac_f16": round(fl / t / 1e12 / F16_PEAK_TFLOPS, 4)}
+    out["crossover_5120x13824"] = sweep
+    del copies, qw, sc, qz
+    # prefill M=4096
+    log("detail: prefill")
+    pre = {}
+    for (K, N) in ((5120, 27648), (5120, 5120), (13824, 5120)):
+        name = {(5120, 27648): "gate_up", (5120, 5120): "o", (13824, 5120): "down"}[(K, N)]
+        x = synth.make_activations(4096, K, seed=4096, rms_spread=True).to(dev)
+        y = torch.empty((4096, N), dtype=torch.float16, device=dev)
+        calls = [w4.bind_awq_gemm(x, *packed[name][r], y) for r in range(len(packed[name]))]
+        t = _time_calls(torch, calls, max(4, it // 2))
+        fl = 2.0 * 4096 * N * K
+        pre[f"{K}x{N}"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                           "frac_f16": round(fl / t / 1e12 / F16_PEAK_TFLOPS, 4)}
+        del x, y, calls
+    out["prefill_13b_M4096"] = pre
+    # W4A8
+    log("detail: w4a8")
+    inp = synth.make_linear(4096, 13824, 5120, seed=0, outliers=True, rms_spread=True, with_gamma=True)
+    w8 = {}
+    wdev = inp.w.to(dev)
+    for group in (-1, 128):
+        qw, gs, cs = w4.w4a8_pack(wdev, group)
+        copies = [rotated_w4a8(qw, gs, cs, r) for r in range(16)]
+        for M in (1, 16, 256, 4096):
+            x = inp.x[:M].contiguous().to(dev)
+            xq = torch.empty((M, 5120), dtype=torch.int8, device=dev)
+            sa = torch.empty((M,), dtype=torch.float32, device=dev)
+            qa = w4.bind_w4a8_quant_act(x, inp.gamma.to(dev), xq, sa)
+            qa()
+            y = torch.empty((M, 13824), dtype=torch.float16, device=dev)
+            calls = [w4.bind_w4a8_gemm(xq, sa, c[0], c[1], c[2], y, group) for c in copies]
+            t = _time_calls(torch, calls, max(it, 16) if M < 4096 else max(4, it // 2))
+            tq = _time_calls(torch, [qa], 8)
+            b = w4a8_bytes(M, 13824, 5120, group > 0)
+            ops = 2.0 * M * 13824 * 5120
+            w8[f"{'g128' if group > 0 else 'pc'}_M{M}"] = {
+                "gemm_us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1), "TOPs": round(ops / t / 1e12, 2),
+                "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3), "frac_i8": round(ops / t / 1e12 / I8_PEAK_TOPS, 4),
+                "frac_f16": round(ops / t / 1e12 / F16_PEAK_TFLOPS, 4), "quant_act_us": round(tq * 1e6, 2)}
+        del copies, qw, gs, cs
+    out["w4a8_5120x13824"] = w8
+    return out
+
+
+def cpu_baseline(np, synth, host):
+    """The oracle (numpy dequant + fp64 matmul) on one decode step: the 4 projections at
+    M = 1, 4 and 16 (12 GEMMs), packed weights prepared untimed."""
+    import oracle.ref as ora
+    from threadpoolctl import threadpool_info
+
+    log("cpu baseline (oracle)")
+    tot_b = 0.0
+    tot_t = 0.0
+    for name, (K, N) in synth.LLAMA2_13B.items():
+        w = host[name].w.numpy()
+        c, s, z = ora.quantize_asym(w, G)
+        qw, sg, qz = ora.pack_awq(c, s, z)
+        for M in (1, 4, 16):
+            x = host[name].x[:M].numpy()
+            t0 = time.perf_counter()
+            wd = ora.dequant_awq(qw, sg, qz, K, G)
+            ora.linear_ref(x, wd)
+            tot_t += time.perf_counter() - t0
+            tot_b += awq_bytes(M, N, K)
+            del wd
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(tot_b / tot_t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one decode step: QKV/O/gate+up/down at M=1,4,16 (12 GEMMs), numpy fp64 dequant + BLAS matmul, "
+                      f"{tot_t:.1f} s", "host_cpu_count": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 / W4A8 group-quantized linear layer.
+ *
+ * The operation (W4A16):  Y[M,N] = X[M,K] . dequant(W)^T, with fp16 X and Y and
+ * 4-bit weights.  "Some fixes for AWQ" (neuralmagic/compressed-tensors PR 269), reply
+ * defining W4A16: fp16 input vectors multiplied by int4-quantized weights give fp16
+ * output vectors, with no activation-quantization argument.  Weights are quantized
+ * asymmetrically per (output row n, group of G consecutive k) as in the opening
+ * comment of that page (AutoAWQ's pseudo-quantize rule):
+ *     s = fp16(max(fp32(max - min) / 15, 1e-5)),  z = clamp(rint(-min / s), 0, 15),
+ *     q = clamp(rint(w / s) + z, 0, 15),  dequant(w) = (q - z) * s.
+ *
+ * The W4A8 stage ("[Feature] support qqq(w4a8) for lmdeploy", InternLM/lmdeploy issue
+ * 2274, section "Modification"): per-token int8 activations produced by an online
+ * quantization fused with RMSNorm, an int8 x int4 GEMM accumulating in int32, and an
+ * epilogue that rescales by the activation and weight scales ("Some fixes for AWQ",
+ * reply on 8-bit matmuls whose int32 output is rescaled by both scales).
+ *
+ * Memory layouts (row-major, contiguous; all pointers are DEVICE pointers owned by the
+ * caller; the library never allocates, frees, synchronizes or changes the current
+ * device; it only enqueues kernels on `stream`):
+ *   X        fp16  [M, K]
+ *   Y        fp16  [M, N]
+ *   W        fp16  [N, K]            (out, in)
+ *   qweight  int32 [N, K/8]          packed along K, plain nibble order: element k = 8j+i
+ *                                    of row n sits in bits 4i..4i+3 of word (n, j)
+ *   scales   fp16  [K/G, N]          per-group scales, group-major
+ *   qzeros   int32 [K/G, ceil(N/8)]  4-bit zero points packed along N, plain nibble
+ *                                    order, pad nibbles 0
+ *   (W4A8)   qweight int32 [N, K/8] of biased nibbles q + 8 (q in [-8, 7]),
+ *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
+ *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
+ *
+ * Sizes: M >= 0, N >= 0 (M == 0 or N == 0 is a no-op returning W4_OK), K a positive
+ * multiple of the group size.  group_size: 128 for W4A16; 128 or -1 (per-channel) for
+ * W4A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
+ *
+ * `stream` is a hipStream_t (NULL = the null stream).  All entry points are
+ * asynchronous: they return after validation and launch; a fault inside a kernel
+ * surfaces at the caller's next synchronization.  Argument checks happen before any
+ * HIP call, so an invalid call returns without touching the device.
+ *
+ * Return value: one of the W4_* codes below; w4_last_error() gives a thread-local
+ * message for the last failure on the calling thread.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  W4_OK = 0,
+  W4_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, K not a multiple of G, misalignment */
+  W4_ERR_UNSUPPORTED = 2,   /* group size or shape this build does not implement */
+  W4_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_bytes() */
+  W4_ERR_DEVICE = 4,        /* current device is not gfx950 */
+  W4_ERR_HIP = 5            /* a HIP runtime call failed (see w4_last_error) */
+};
+
+/*
+ * awq_pack -- quantize fp16 weights W [N, K] with the asymmetric group rule above and
+ * write qweight, scales and qzeros.  Quantization decisions are taken in fp32 (IEEE
+ * division, round-half-to-even), so the output is bit-exact and deterministic.
+ * M is unused (accepted for a uniform signature; must be >= 0).
+ */
+int awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros,
+             int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * awq_unpack_dequant -- write fp16 W_deq [N, K] = fp16((q - z) * s) with exactly one
+ * rounding per element (the dequantization step of the large-M GEMM).  Debug/export
+ * path; bit-exact.
+ */
+int awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros,
+                       void* w_out, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * awq_gemm_workspace_bytes -- bytes of workspace awq_gemm needs for this shape (0 when
+ * the chosen kernels do not split K).  The workspace holds split-K fp32 partial sums and
+ * per-tile arrival counters.  It must be zero-filled before its first use; every
+ * completed call leaves the counter region zeroed again, so a workspace can be reused
+ * by later calls on the same stream.  Calls that overlap in time (different streams)
+ * must not share a workspace.
+ */
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * awq_gemm -- Y [M, N] = X [M, K] . dequant(qweight, scales, qzeros)^T, fp32 accumulate,
+ * fp16 output (round to nearest even).  Dispatch: M <= 64 uses the bandwidth-bound
+ * skinny kernel (16x16x32 fp16 MFMA, split-K, per-group scaling in fp32); larger M uses
+ * the LDS-staged 32x32x16 fp16 MFMA GEMM with in-register dequantization.  Results are
+ * deterministic (split-K partials are summed in a fixed order).
+ */
+int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
+             void* y, void* workspace, size_t workspace_bytes,
+             int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * w4a8_pack -- quantize fp16 W [N, K] to symmetric int4 for W4A8 and pack it.
+ * group_size == -1: per-channel, cscale = fp16(max(max|w|/7, 1e-5)),
+ *   q = clamp(rint(w / cscale), -8, 7); gscale must be NULL.
+ * group_size == 128: two-level, cscale = fp16(max(max|w|/127, 1e-5)),
+ *   w8 = clamp(rint(w / cscale), -127, 127), per group s_g = min(max(1, ceil(max|w8|/7)), 18),
+ *   q = clamp(rint(w8 / s_g), -7, 7); gscale int8 [K/G, N] receives s_g.
+ * qweight receives q + 8 in the plain nibble order.  fp32 decisions; bit-exact.
+ */
+int w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale,
+              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * w4a8_quant_act -- per-token symmetric int8 quantization, optionally fused with RMSNorm
+ * ("[Feature] support qqq(w4a8) for lmdeploy", "Modification": online quantization fused
+ * with RMSNorm).  With gamma != NULL: y = x / sqrt(mean_k(x^2) + eps) * gamma (fp32, no
+ * fp16 round trip); with gamma == NULL: y = x.  Then amax = max|y|,
+ * xq = clamp(rint(y * fp32(127 / amax)), -127, 127), s_a = amax / 127; a zero row gives
+ * xq = 0, s_a = 1.  N and group_size are unused (must be >= 0 / any value).
+ */
+int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a,
+                   int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/* w4a8_gemm_workspace_bytes -- as awq_gemm_workspace_bytes, for w4a8_gemm / _i32. */
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * w4a8_gemm -- Y [M, N] = fp16(acc[m, n] * s_a[m] * cscale[n]) where
+ * acc[m, n] = sum_k xq[m, k] * q[n, k] * s_g[n, k / G] (s_g = 1 for group_size == -1) is
+ * computed exactly in int32 on the int8 MFMA units.  gscale is NULL iff group_size == -1.
+ */
+int w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
+              const void* cscale, void* y, void* workspace, size_t workspace_bytes,
+              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * w4a8_gemm_i32 -- the raw int32 accumulators acc [M, N] of w4a8_gemm (no rescaling).
+ * Bit-exact; for verification of the integer pipeline.
+ */
+int w4a8_gemm_i32(const int8_t* xq, const int32_t* qweight, const int8_t* gscale, int32_t* acc,
+                  void* workspace, size_t workspace_bytes,
+                  int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* w4_status_string(int status);
+/* Message for the last failure on the calling thread ("" if none). */
+const char* w4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

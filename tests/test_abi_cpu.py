@@ -1,0 +1,96 @@
+"""CPU: the C-ABI library loads, exports every symbol include/w4a16.h declares, and
+rejects invalid arguments before touching a device (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import w4a16_gemm_amd as w4
+    if not os.path.exists(w4.lib_path()):
+        pytest.fail("libw4a16.so is not built: run python -m w4a16_gemm_amd.build")
+    return w4.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
+              "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
+              "w4_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.w4_status_string(0) == b"W4_OK"
+    assert lib.w4_status_string(3) == b"W4_ERR_WORKSPACE"
+    assert lib.w4_status_string(99) == b"W4_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((None, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 128, None), 1, "x is NULL"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 200, 128, None), 1, "multiple of 128"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 0, 128, None), 1, "multiple of 128"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, -1, 64, 256, 128, None), 1, "negative"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 64, None), 2, "group_size"),
+    ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 128, None), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 1 << 31, 128, None), 2, "2^30"),
+    # a shape that splits K needs a workspace
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 16, 5120, 5120, 128, None), 3, "workspace"),
+])
+def test_awq_gemm_validation(lib, args, code, msg):
+    P = ctypes.c_void_p
+    conv = [P(a) if (i < 6 and a is not None) else a for i, a in enumerate(args)]
+    assert lib.awq_gemm(*conv) == code
+    assert msg in lib.w4_last_error().decode()
+
+
+def test_empty_shapes_are_noops(lib):
+    # M == 0 or N == 0 return OK before any pointer or device check
+    assert lib.awq_gemm(None, None, None, None, None, None, 0, 0, 64, 256, 128, None) == 0
+    assert lib.awq_gemm(None, None, None, None, None, None, 0, 4, 0, 256, 128, None) == 0
+    assert lib.w4a8_gemm(None, None, None, None, None, None, None, 0, 0, 64, 256, -1, None) == 0
+    assert lib.w4a8_quant_act(None, None, ctypes.c_float(1e-5), None, None, 0, 0, 256, 0, None) == 0
+
+
+def test_w4a8_validation(lib):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    # gscale must be NULL for per-channel and non-NULL for g128
+    assert lib.w4a8_gemm(f, f, f, f, f, f, None, 0, 4, 64, 256, -1, None) == 1
+    assert "gscale" in lib.w4_last_error().decode()
+    assert lib.w4a8_gemm(f, f, f, None, f, f, None, 0, 4, 64, 256, 128, None) == 1
+    assert lib.w4a8_gemm(f, f, f, None, f, f, None, 0, 4, 64, 256, 32, None) == 2
+    assert lib.w4a8_quant_act(f, None, ctypes.c_float(1e-5), f, f, 4, 0, 100, 0, None) == 1
+    assert lib.w4a8_quant_act(f, None, ctypes.c_float(-1.0), f, f, 4, 0, 128, 0, None) == 1
+    assert lib.w4a8_pack(f, f, None, f, 0, 64, 256, 128, None) == 1
+    assert lib.awq_pack(f, f, f, f, 0, 64, 256, 32, None) == 2
+
+
+def test_workspace_sizes(lib):
+    # decode shapes split K; prefill shapes do not; invalid shapes report 0
+    assert lib.awq_gemm_workspace_bytes(16, 5120, 5120, 128) > 0
+    assert lib.awq_gemm_workspace_bytes(4096, 27648, 5120, 128) == 0
+    assert lib.awq_gemm_workspace_bytes(16, 5120, 200, 128) == 0
+    assert lib.w4a8_gemm_workspace_bytes(1, 13824, 5120, -1) > 0
+    assert lib.w4a8_gemm_workspace_bytes(4096, 13824, 5120, 128) == 0

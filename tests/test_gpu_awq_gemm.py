@@ -1,0 +1,147 @@
+"""GPU parity of awq_gemm (W4A16) against the oracle.
+
+* small shapes spanning several tiles and ragged tails, oracle-packed weights fed to
+  the GPU GEMM (isolates the GEMM), both kernels (M <= 64 skinny, M > 64 MFMA GEMM),
+  with and without split-K, outputs pre-poisoned with NaN;
+* bit-exact identity probe and constructed-exact GEMMs;
+* determinism and workspace reuse;
+* every full-size workload shape, end to end (GPU quantize + pack + GEMM), on
+  sampled outputs the oracle computes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.ref as ora
+import synth
+import w4a16_gemm_amd as w4
+from gpu_util import TOL, announce, device, normalized_error, sample_idx, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_packed(w16, dev):
+    r = ora.awq_reference(w16, None, 128)
+    return r, [torch.from_numpy(np.ascontiguousarray(t)).to(dev) for t in (r["qweight"], r["scales"], r["qzeros"])]
+
+
+SMALL = [
+    (1, 64, 128), (3, 200, 384), (8, 1000, 1024), (16, 320, 2048), (16, 4096, 512), (17, 192, 512),
+    (32, 96, 1280), (33, 256, 768), (64, 64, 128), (64, 520, 4096), (65, 300, 640), (100, 8, 256),
+    (130, 520, 1024), (257, 1030, 2048), (300, 256, 384), (512, 512, 5120),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_awq_gemm_small_shapes(M, N, K):
+    dev = device()
+    announce(f"awq_gemm small M={M} N={N} K={K} ws={w4.awq_gemm_workspace_bytes(M, N, K)}")
+    inp = synth.make_linear(M, N, K, seed=M * 7 + N, outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    x = inp.x.to(dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = w4.awq_gemm(x, qw, sc, qz, out=out)
+    torch.cuda.synchronize()
+    yg = to_np(y).astype(np.float64)
+    assert np.all(np.isfinite(yg)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(yg, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M", [8, 64, 100])
+def test_awq_gemm_identity_probe_bit_exact(M):
+    """X rows are unit vectors e_k: Y[m, n] is the fp16 dequantized weight, bit for bit."""
+    dev = device()
+    N, K = 320, 1024
+    announce(f"identity probe M={M}")
+    w = synth.make_linear(0, N, K, seed=17, outliers=True).w.numpy()
+    ref, (qw, sc, qz) = _oracle_packed(w, dev)
+    ks = sample_idx(K, M, seed=M, must=(0, 127, 128, 1023))[:M]
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(len(ks)), ks] = 1
+    y = to_np(w4.awq_gemm(torch.from_numpy(x).to(dev), qw, sc, qz))
+    expect = ref["w_deq"][:, ks].T.astype(np.float16)
+    assert np.array_equal(y[:len(ks)].view(np.uint16), expect.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 256, 2048), (48, 192, 4096), (96, 256, 1024), (256, 512, 5120)])
+def test_awq_gemm_constructed_exact(M, N, K):
+    """Integer X in [-4, 4] and power-of-two scales: every partial sum is exact in fp32,
+    so the result is fp16_RNE of the exact integer product whatever the summation order."""
+    dev = device()
+    announce(f"constructed exact M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + K)
+    q = rng.integers(0, 16, size=(N, K))
+    q[:, ::128] = 0
+    q[:, 1::128] = 15
+    z = rng.integers(0, 16, size=(N, K // 128))
+    w = ((q - np.repeat(z, 128, axis=1)) * 0.125).astype(np.float16)
+    x = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    ref, (qw, sc, qz) = _oracle_packed(w, dev)
+    assert np.all(ref["scales"].astype(np.float64) == 0.125)
+    y = to_np(w4.awq_gemm(torch.from_numpy(x).to(dev), qw, sc, qz))
+    exact = (x.astype(np.int64) @ (q - np.repeat(z, 128, axis=1)).T) / 8.0
+    assert np.array_equal(y.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+
+
+def test_awq_gemm_deterministic_and_workspace_reuse():
+    dev = device()
+    announce("determinism / workspace reuse")
+    shapes = [(16, 5120, 5120), (4, 4096, 4096), (16, 5120, 5120), (128, 2048, 5120), (16, 5120, 5120)]
+    outs = {}
+    for (M, N, K) in shapes:
+        inp = synth.make_linear(M, N, K, seed=N, outliers=True)
+        qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+        y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz))
+        key = (M, N, K)
+        if key in outs:
+            assert np.array_equal(outs[key].view(np.uint16), y.view(np.uint16))
+        outs[key] = y
+
+
+def test_awq_gemm_empty():
+    dev = device()
+    qw, sc, qz = w4.awq_pack(torch.zeros((64, 256), dtype=torch.float16, device=dev))
+    y = w4.awq_gemm(torch.zeros((0, 256), dtype=torch.float16, device=dev), qw, sc, qz)
+    assert tuple(y.shape) == (0, 64)
+
+
+def _full_cases():
+    out = []
+    for name, cases in synth.workloads().items():
+        if name.startswith("w4a8"):
+            continue
+        for (M, N, K, kw) in cases:
+            out.append(pytest.param(M, N, K, kw, id=f"{name}-M{M}-N{N}-K{K}"))
+    return out
+
+
+_W_CACHE = {}
+
+
+def _packed_full(N, K, kw, dev):
+    key = (N, K, bool(kw.get("outliers")))
+    if key not in _W_CACHE:
+        _W_CACHE.clear()
+        w = synth.make_linear(0, N, K, seed=0, outliers=kw.get("outliers", False)).w
+        _W_CACHE[key] = (w, w4.awq_pack(w.to(dev)))
+    return _W_CACHE[key]
+
+
+@pytest.mark.parametrize("M,N,K,kw", _full_cases())
+def test_awq_gemm_full_size_sampled(M, N, K, kw):
+    dev = device()
+    announce(f"full size M={M} N={N} K={K}")
+    w, (qw, sc, qz) = _packed_full(N, K, kw, dev)
+    x = synth.make_activations(M, K, seed=1000 + M, rms_spread=kw.get("rms_spread", False))
+    y = w4.awq_gemm(x.to(dev), qw, sc, qz)
+    torch.cuda.synchronize()
+    ms = sample_idx(M, 48, seed=M)
+    ns = sample_idx(N, 384, seed=N + M, must=range(0, 64))
+    ref = ora.awq_reference(w.numpy()[ns], x.numpy()[ms], 128)
+    yg = to_np(y)[np.ix_(ms, ns)].astype(np.float64)
+    err = normalized_error(yg, ref["y"], np.linalg.norm(x.numpy()[ms].astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err

@@ -1,0 +1,123 @@
+"""GPU parity of the W4A8 stage against the oracle.
+
+* w4a8_quant_act: no-norm mode bit-exact (the fp32 decisions have one defined
+  sequence); RMSNorm mode equal except at near-ties, where the kernel's fp32 sum of
+  squares (a different summation order than the oracle's exact sum) may move the
+  value across a .5 boundary; there the code may differ by 1.
+* w4a8_gemm_i32: the int32 accumulators, bit-exact, fed the oracle's xq and packed
+  weights (per-channel and two-level g128), small ragged shapes and the full shapes.
+* w4a8_gemm: fp16 outputs within the normalized 2e-3 bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.ref as ora
+import synth
+import w4a16_gemm_amd as w4
+from gpu_util import TOL, announce, device, normalized_error, sample_idx, to_np
+
+pytestmark = pytest.mark.gpu
+
+# |t_gpu - t_oracle| bound for the RMSNorm-mode quantization argument t = y * 127 / max|y|:
+# fp32 sum of K squares (relative error <= ~log2(K) * 2^-24 after pairwise/tree
+# reduction, ~1e-6 bounded generously), two fp32 products and the division give a
+# relative error below ~2e-6, i.e. |dt| <= 127 * 2e-6 = 2.5e-4.
+NEAR_TIE = 2.5e-4
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 5120), (64, 13824), (300, 5120), (4096, 5120)])
+def test_quant_act_no_norm_bit_exact(M, K):
+    dev = device()
+    announce(f"quant_act no-norm M={M} K={K}")
+    x = synth.make_activations(M, K, seed=M, rms_spread=True)
+    x[0, :] = 0  # a zero row: s_a = 1, codes 0
+    xq, sa = w4.w4a8_quant_act(x.to(dev), None)
+    torch.cuda.synchronize()
+    rxq, rsa, _ = ora.w4a8_quant_act_ref(x.numpy(), None)
+    assert np.array_equal(to_np(xq), rxq)
+    assert np.array_equal(to_np(sa).view(np.uint32), rsa.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (16, 5120), (256, 5120), (4096, 5120), (33, 13824)])
+def test_quant_act_rmsnorm_near_ties_only(M, K):
+    dev = device()
+    announce(f"quant_act rmsnorm M={M} K={K}")
+    inp = synth.make_linear(M, 8, K, seed=M + 1, rms_spread=True, with_gamma=True)
+    x, gamma = inp.x, inp.gamma
+    if M > 1:
+        x[1, :] = 0
+    xq, sa = w4.w4a8_quant_act(x.to(dev), gamma.to(dev), 1e-5)
+    torch.cuda.synchronize()
+    rxq, rsa, t = ora.w4a8_quant_act_ref(x.numpy(), gamma.numpy(), 1e-5)
+    gq = to_np(xq).astype(np.int64)
+    diff = np.abs(gq - rxq.astype(np.int64))
+    assert diff.max() <= 1
+    frac = np.abs(np.abs(t - np.trunc(t)) - 0.5)
+    assert np.all(frac[diff == 1] < NEAR_TIE), float(frac[diff == 1].max())
+    assert (diff == 1).mean() < 1e-3
+    rel = np.abs(to_np(sa).astype(np.float64) / rsa.astype(np.float64) - 1)
+    assert rel.max() <= 2e-6
+    assert np.all(np.abs(gq).max(axis=1)[np.abs(x.numpy()).max(axis=1) > 0] == 127)
+
+
+def _oracle_w4a8(w16, group, dev):
+    q, cs, gs = ora.quantize_w4a8(w16, group)
+    qw, cs2, gs_gn = ora.pack_w4a8(q, cs, gs)
+    tens = [torch.from_numpy(np.ascontiguousarray(qw)).to(dev),
+            None if gs_gn is None else torch.from_numpy(gs_gn).to(dev),
+            torch.from_numpy(cs2).to(dev)]
+    return q, cs2, gs, tens
+
+
+@pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (5, 200, 384), (16, 1000, 1024), (33, 96, 2048), (64, 256, 640),
+                                   (100, 300, 1280), (257, 520, 2048), (512, 512, 5120)])
+def test_w4a8_gemm_small(group, M, N, K):
+    dev = device()
+    announce(f"w4a8 small M={M} N={N} K={K} group={group}")
+    inp = synth.make_linear(M, N, K, seed=M * 3 + N, outliers=True, rms_spread=True, with_gamma=True)
+    q, cs, gs, (qw, gsd, csd) = _oracle_w4a8(inp.w.numpy(), group, dev)
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    xqd, sad = torch.from_numpy(xq).to(dev), torch.from_numpy(sa).to(dev)
+    acc = to_np(w4.w4a8_gemm_i32(xqd, qw, gsd, group))
+    racc = ora.w4a8_acc_ref(xq, q, gs, 128)
+    assert np.abs(racc).max() < 2**31
+    assert np.array_equal(acc.astype(np.int64), racc)
+    out = w4.w4a8_gemm(xqd, sad, qw, gsd, csd, group)
+    torch.cuda.synchronize()
+    y = to_np(out).astype(np.float64)
+    yr = ora.w4a8_linear_ref(racc, sa, cs)
+    qs = q.astype(np.float64) * (1 if gs is None else np.repeat(gs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * cs.astype(np.float64)
+    xn = np.linalg.norm(xq.astype(np.float64), axis=1) * sa.astype(np.float64)
+    assert normalized_error(y, yr, xn, wn) <= TOL
+
+
+@pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_w4a8_full_size_sampled(group, M):
+    """C5 shapes (K = 5120, N = 13824) end to end on the GPU: pack, quant_act (RMSNorm),
+    GEMM; accumulators bit-exact on the oracle's xq; fp16 outputs within 2e-3."""
+    dev = device()
+    N, K = 13824, 5120
+    announce(f"w4a8 full M={M} group={group}")
+    inp = synth.make_linear(M, N, K, seed=0, outliers=True, rms_spread=True, with_gamma=True)
+    qw, gs, cs = w4.w4a8_pack(inp.w.to(dev), group)
+    xq, sa = w4.w4a8_quant_act(inp.x.to(dev), inp.gamma.to(dev))
+    y = w4.w4a8_gemm(xq, sa, qw, gs, cs, group)
+    rxq, rsa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    acc = w4.w4a8_gemm_i32(torch.from_numpy(rxq).to(dev), qw, gs, group)
+    torch.cuda.synchronize()
+    ms = sample_idx(M, 48, seed=M)
+    ns = sample_idx(N, 256, seed=7, must=range(0, 32))
+    q, rcs, rgs = ora.quantize_w4a8(inp.w.numpy()[ns], group)
+    racc = ora.w4a8_acc_ref(rxq[ms], q, rgs, 128)
+    assert np.array_equal(to_np(acc)[np.ix_(ms, ns)].astype(np.int64), racc)
+    # fp16 outputs of the all-GPU chain against the oracle chain
+    yr = ora.w4a8_linear_ref(racc, rsa[ms], rcs)
+    qs = q.astype(np.float64) * (1 if rgs is None else np.repeat(rgs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * rcs.astype(np.float64)
+    xn = np.linalg.norm(rxq[ms].astype(np.float64), axis=1) * rsa[ms].astype(np.float64)
+    err = normalized_error(to_np(y)[np.ix_(ms, ns)].astype(np.float64), yr, xn, wn)
+    assert err <= TOL, err

@@ -1,0 +1,22 @@
+"""MI355X (gfx950) W4A16 / W4A8 group-quantized linear layer.
+
+Python binding of the C ABI in ``include/w4a16.h`` (``libw4a16.so``); the
+functions carry the names of the C entry points.
+"""
+from ._lib import (  # noqa: F401
+    W4Error,
+    awq_gemm,
+    awq_gemm_workspace_bytes,
+    awq_pack,
+    awq_unpack_dequant,
+    bind_awq_gemm,
+    bind_w4a8_gemm,
+    bind_w4a8_quant_act,
+    lib_path,
+    load,
+    w4a8_gemm,
+    w4a8_gemm_i32,
+    w4a8_gemm_workspace_bytes,
+    w4a8_pack,
+    w4a8_quant_act,
+)

@@ -1,0 +1,330 @@
+"""ctypes binding of ``libw4a16.so`` (the C ABI declared in ``include/w4a16.h``).
+
+Argument marshalling only: every function checks dtypes, devices, shapes and
+contiguity, allocates its outputs (and, where a kernel splits K, a cached
+zero-filled workspace) with torch on the input's device, and calls the C entry
+point of the same name on torch's current stream.  All computation happens in the
+HIP kernels; there is no CPU or PyTorch fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+W4_OK = 0
+_lib = None
+_lock = threading.Lock()
+
+
+class W4Error(RuntimeError):
+    """A non-zero status returned by the C library."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load (once) and return the ctypes handle of libw4a16.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m w4a16_gemm_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        sig = {
+            "awq_pack": [P, P, P, P, I64, I64, I64, I32, P],
+            "awq_unpack_dequant": [P, P, P, P, I64, I64, I32, P],
+            "awq_gemm": [P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
+            "w4a8_pack": [P, P, P, P, I64, I64, I64, I32, P],
+            "w4a8_quant_act": [P, P, F, P, P, I64, I64, I64, I32, P],
+            "w4a8_gemm": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
+            "w4a8_gemm_i32": [P, P, P, P, P, SZ, I64, I64, I64, I32, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        for name in ("awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes"):
+            fn = getattr(lib, name)
+            fn.argtypes = [I64, I64, I64, I32]
+            fn.restype = ctypes.c_size_t
+        lib.w4_status_string.argtypes = [ctypes.c_int]
+        lib.w4_status_string.restype = ctypes.c_char_p
+        lib.w4_last_error.argtypes = []
+        lib.w4_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, status: int):
+    if status != W4_OK:
+        lib = load()
+        raise W4Error(fn, status, f"{lib.w4_status_string(status).decode()}: {lib.w4_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# Workspaces: one zero-filled buffer per (device, stream), grown on demand.  The
+# kernels leave its counter region zeroed after every completed call, so it can be
+# reused by later calls on the same stream.
+_ws_cache: dict = {}
+
+
+def _workspace(dev, nbytes: int):
+    if nbytes == 0:
+        return None, 0
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf, buf.numel()
+
+
+# ------------------------------------------------------------------ W4A16
+def awq_pack(w: torch.Tensor, group_size: int = 128):
+    """fp16 W [N, K] -> (qweight int32 [N, K/8], scales fp16 [K/G, N], qzeros int32 [K/G, ceil(N/8)])."""
+    _need(w, "w", torch.float16, 2)
+    N, K = w.shape
+    dev = w.device
+    G = group_size if group_size > 0 else K
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
+    qzeros = torch.empty((K // G, (N + 7) // 8), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check("awq_pack", load().awq_pack(_ptr(w), _ptr(qweight), _ptr(scales), _ptr(qzeros), 0, N, K,
+                                           group_size, _stream(dev)))
+    return qweight, scales, qzeros
+
+
+def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):
+    """Packed weights -> fp16 W_deq [N, K] = fp16((q - z) * s)."""
+    _need(qweight, "qweight", torch.int32, 2)
+    dev = qweight.device
+    _need(scales, "scales", torch.float16, 2, dev)
+    _need(qzeros, "qzeros", torch.int32, 2, dev)
+    N, K = qweight.shape[0], qweight.shape[1] * 8
+    out = torch.empty((N, K), dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        _check("awq_unpack_dequant", load().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out),
+                                                               N, K, group_size, _stream(dev)))
+    return out
+
+
+def awq_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = 128) -> int:
+    return int(load().awq_gemm_workspace_bytes(M, N, K, group_size))
+
+
+def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, workspace=None):
+    """Y [M, N] = X [M, K] . dequant(W)^T  (fp16 in, fp16 out, fp32 accumulate)."""
+    _need(x, "x", torch.float16, 2)
+    dev = x.device
+    _need(qweight, "qweight", torch.int32, 2, dev)
+    _need(scales, "scales", torch.float16, 2, dev)
+    _need(qzeros, "qzeros", torch.int32, 2, dev)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    else:
+        _need(out, "out", torch.float16, 2, dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    lib = load()
+    with torch.cuda.device(dev):
+        if workspace is None:
+            ws, nb = _workspace(dev, lib.awq_gemm_workspace_bytes(M, N, K, group_size))
+        else:
+            ws, nb = workspace, workspace.numel() * workspace.element_size()
+        _check("awq_gemm", lib.awq_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), _ptr(ws),
+                                        nb, M, N, K, group_size, _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------------- W4A8
+def w4a8_pack(w: torch.Tensor, group_size: int = -1):
+    """fp16 W [N, K] -> (qweight int32 [N, K/8] biased nibbles, gscale int8 [K/G, N] or None, cscale fp16 [N])."""
+    _need(w, "w", torch.float16, 2)
+    N, K = w.shape
+    dev = w.device
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    cscale = torch.empty((N,), dtype=torch.float16, device=dev)
+    gscale = torch.empty((K // group_size, N), dtype=torch.int8, device=dev) if group_size > 0 else None
+    with torch.cuda.device(dev):
+        _check("w4a8_pack", load().w4a8_pack(_ptr(w), _ptr(qweight), _ptr(gscale), _ptr(cscale), 0, N, K,
+                                             group_size, _stream(dev)))
+    return qweight, gscale, cscale
+
+
+def w4a8_quant_act(x: torch.Tensor, gamma=None, eps: float = 1e-5):
+    """fp16 X [M, K] (and optional RMSNorm gamma [K]) -> (xq int8 [M, K], s_a fp32 [M])."""
+    _need(x, "x", torch.float16, 2)
+    dev = x.device
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float16, 1, dev)
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_a = torch.empty((M,), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("w4a8_quant_act", load().w4a8_quant_act(_ptr(x), _ptr(gamma), float(eps), _ptr(xq), _ptr(s_a), M, 0,
+                                                       K, 0, _stream(dev)))
+    return xq, s_a
+
+
+def w4a8_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = -1) -> int:
+    return int(load().w4a8_gemm_workspace_bytes(M, N, K, group_size))
+
+
+def _w4a8_args(xq, qweight, gscale, group_size):
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(qweight, "qweight", torch.int32, 2, dev)
+    if gscale is not None:
+        _need(gscale, "gscale", torch.int8, 2, dev)
+    M, K = xq.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
+    return dev, M, N, K
+
+
+def w4a8_gemm(xq, s_a, qweight, gscale, cscale, group_size: int = -1, out=None):
+    """Y [M, N] = fp16(acc * s_a[m] * cscale[n]), acc the exact int32 sum of xq * q * s_g."""
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(cscale, "cscale", torch.float16, 1, dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w4a8_gemm_workspace_bytes(M, N, K, group_size))
+        _check("w4a8_gemm", lib.w4a8_gemm(_ptr(xq), _ptr(s_a), _ptr(qweight), _ptr(gscale), _ptr(cscale), _ptr(out),
+                                          _ptr(ws), nb, M, N, K, group_size, _stream(dev)))
+    return out
+
+
+def w4a8_gemm_i32(xq, qweight, gscale, group_size: int = -1):
+    """Raw int32 accumulators acc [M, N] of w4a8_gemm."""
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w4a8_gemm_workspace_bytes(M, N, K, group_size))
+        _check("w4a8_gemm_i32", lib.w4a8_gemm_i32(_ptr(xq), _ptr(qweight), _ptr(gscale), _ptr(acc), _ptr(ws), nb, M,
+                                                  N, K, group_size, _stream(dev)))
+    return acc
+
+
+def bind_awq_gemm(x, qweight, scales, qzeros, out, group_size: int = 128):
+    """Validate once and return a zero-argument callable that enqueues awq_gemm on the
+    current stream with pre-marshalled arguments (for tight launch loops: benchmarks,
+    stream capture).  The workspace is allocated here, not at call time."""
+    _need(x, "x", torch.float16, 2)
+    dev = x.device
+    _need(qweight, "qweight", torch.int32, 2, dev)
+    _need(scales, "scales", torch.float16, 2, dev)
+    _need(qzeros, "qzeros", torch.int32, 2, dev)
+    _need(out, "out", torch.float16, 2, dev)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K or tuple(out.shape) != (M, N):
+        raise ValueError("inconsistent shapes")
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.awq_gemm_workspace_bytes(M, N, K, group_size))
+        stream = _stream(dev)
+    args = (_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), _ptr(ws), nb, M, N, K, group_size, stream)
+    fn = lib.awq_gemm
+    keep = (x, qweight, scales, qzeros, out, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("awq_gemm", rc)
+        return keep
+    return call
+
+
+def bind_w4a8_gemm(xq, s_a, qweight, gscale, cscale, out, group_size: int = -1):
+    """As bind_awq_gemm, for w4a8_gemm."""
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(cscale, "cscale", torch.float16, 1, dev)
+    _need(out, "out", torch.float16, 2, dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w4a8_gemm_workspace_bytes(M, N, K, group_size))
+        stream = _stream(dev)
+    args = (_ptr(xq), _ptr(s_a), _ptr(qweight), _ptr(gscale), _ptr(cscale), _ptr(out), _ptr(ws), nb, M, N, K,
+            group_size, stream)
+    fn = lib.w4a8_gemm
+    keep = (xq, s_a, qweight, gscale, cscale, out, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w4a8_gemm", rc)
+        return keep
+    return call
+
+
+def bind_w4a8_quant_act(x, gamma, xq, s_a, eps: float = 1e-5):
+    """As bind_awq_gemm, for w4a8_quant_act."""
+    _need(x, "x", torch.float16, 2)
+    dev = x.device
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float16, 1, dev)
+    _need(xq, "xq", torch.int8, 2, dev)
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    M, K = x.shape
+    lib = load()
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+    args = (_ptr(x), _ptr(gamma), ctypes.c_float(eps), _ptr(xq), _ptr(s_a), M, 0, K, 0, stream)
+    fn = lib.w4a8_quant_act
+    keep = (x, gamma, xq, s_a)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w4a8_quant_act", rc)
+        return keep
+    return call

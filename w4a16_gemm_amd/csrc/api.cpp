@@ -1,0 +1,244 @@
+// C ABI of the W4A16 / W4A8 linear layer library (declarations and the contract of
+// every entry point are in include/w4a16.h).  This file only validates arguments,
+// checks the device, picks a kernel and enqueues it on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/w4a16.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// Shape rules shared by the entry points.  K must be a positive multiple of 128 (the
+// group size of the packed layout); M and N may be zero (no-op).
+int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(W4_ERR_INVALID_ARG, "%s: negative size (M=%lld N=%lld K=%lld)", fn,
+                                           (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(W4_ERR_UNSUPPORTED, "%s: size above 2^30 (M=%lld N=%lld K=%lld)", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (K == 0 || K % 128 != 0)
+    return fail(W4_ERR_INVALID_ARG, "%s: K=%lld must be a positive multiple of 128", fn, (long long)K);
+  if (N * (K / 8) > (int64_t(1) << 40))
+    return fail(W4_ERR_UNSUPPORTED, "%s: N*K too large", fn);
+  return W4_OK;
+}
+
+int check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (auto& p : ptrs) {
+    if (p.second == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: %s is NULL", fn, p.first);
+    if (!aligned16(p.second)) return fail(W4_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, p.first);
+  }
+  return W4_OK;
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_dev_ok[64];
+
+int check_device(const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(W4_ERR_DEVICE, "%s: device index %d out of range", fn, dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: hipGetDeviceProperties: %s", fn, hipGetErrorString(e));
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    if (st == 2) return fail(W4_ERR_DEVICE, "%s: device %d is %s, this library is built for gfx950 only", fn, dev,
+                             prop.gcnArchName);
+  }
+  if (st == 2) return fail(W4_ERR_DEVICE, "%s: device %d is not gfx950", fn, dev);
+  return W4_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return W4_OK;
+}
+
+size_t awq_ws(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  return M <= 64 ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K) : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+#define W4_TRY(expr)          \
+  do {                        \
+    const int rc_ = (expr);   \
+    if (rc_ != W4_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int64_t M, int64_t N, int64_t K,
+             int32_t group_size, void* stream) {
+  const char* fn = "awq_pack";
+  g_last_error.clear();
+  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"w", w}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_awq_pack(w, qweight, scales, qzeros, (int)N, (int)K, (hipStream_t)stream));
+}
+
+int awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros, void* w_out, int64_t N,
+                       int64_t K, int32_t group_size, void* stream) {
+  const char* fn = "awq_unpack_dequant";
+  g_last_error.clear();
+  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_mnk(fn, 0, N, K));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"w_out", w_out}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_awq_unpack_dequant(qweight, scales, qzeros, w_out, (int)N, (int)K,
+                                                    (hipStream_t)stream));
+}
+
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (group_size != 128 || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return awq_ws(M, N, K);
+}
+
+int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros, void* y,
+             void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size,
+             void* stream) {
+  const char* fn = "awq_gemm";
+  g_last_error.clear();
+  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (M == 0 || N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"x", x}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"y", y}}));
+  const size_t need = awq_ws(M, N, K);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  }
+  W4_TRY(check_device(fn));
+  hipError_t e;
+  if (M <= 64) e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, (hipStream_t)stream);
+  else e = w4::launch_gemm(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, (hipStream_t)stream);
+  return launched(fn, e);
+}
+
+int w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int64_t M, int64_t N, int64_t K,
+              int32_t group_size, void* stream) {
+  const char* fn = "w4a8_pack";
+  g_last_error.clear();
+  if (group_size != 128 && group_size != -1)
+    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"w", w}, {"qweight", qweight}, {"cscale", cscale}}));
+  if (group_size == -1 && gscale != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale must be NULL for group_size=-1", fn);
+  if (group_size == 128 && gscale == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale is NULL", fn);
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w4a8_pack(w, qweight, gscale, cscale, (int)N, (int)K, group_size == 128 ? 1 : 0,
+                                           (hipStream_t)stream));
+}
+
+int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int64_t M, int64_t N,
+                   int64_t K, int32_t group_size, void* stream) {
+  const char* fn = "w4a8_quant_act";
+  (void)group_size;
+  g_last_error.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(W4_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (K == 0 || K % 8 != 0) return fail(W4_ERR_INVALID_ARG, "%s: K=%lld must be a positive multiple of 8", fn, (long long)K);
+  if (M > kMaxDim || K > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: size above 2^30", fn);
+  if (!(eps >= 0.0f)) return fail(W4_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (M == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"x", x}, {"xq", xq}, {"s_a", s_a}}));
+  if (gamma != nullptr && !aligned16(gamma)) return fail(W4_ERR_INVALID_ARG, "%s: gamma is not 16-byte aligned", fn);
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w4a8_quant_act(x, gamma, eps, xq, s_a, (int)M, (int)K, (hipStream_t)stream));
+}
+
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if ((group_size != 128 && group_size != -1) || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim ||
+      N > kMaxDim || K > kMaxDim)
+    return 0;
+  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, group_size);
+}
+
+static int w4a8_common(const char* fn, const int8_t* xq, const float* s_a, const int32_t* qweight,
+                       const int8_t* gscale, const void* cscale, void* y, int32_t* acc, void* workspace,
+                       size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
+  g_last_error.clear();
+  if (group_size != 128 && group_size != -1)
+    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (M == 0 || N == 0) return W4_OK;
+  if (acc) {
+    W4_TRY(check_ptrs(fn, {{"xq", xq}, {"qweight", qweight}, {"acc", acc}}));
+  } else {
+    W4_TRY(check_ptrs(fn, {{"xq", xq}, {"s_a", s_a}, {"qweight", qweight}, {"cscale", cscale}, {"y", y}}));
+  }
+  if (group_size == 128 && gscale == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale is NULL", fn);
+  if (group_size == -1 && gscale != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale must be NULL for group_size=-1", fn);
+  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, group_size);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  }
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w4a8_gemm(xq, s_a, qweight, gscale, cscale, y, acc, workspace, (int)M, (int)N,
+                                           (int)K, group_size, (hipStream_t)stream));
+}
+
+int w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale, const void* cscale,
+              void* y, void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size,
+              void* stream) {
+  return w4a8_common("w4a8_gemm", xq, s_a, qweight, gscale, cscale, y, nullptr, workspace, workspace_bytes, M, N, K,
+                     group_size, stream);
+}
+
+int w4a8_gemm_i32(const int8_t* xq, const int32_t* qweight, const int8_t* gscale, int32_t* acc, void* workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
+  return w4a8_common("w4a8_gemm_i32", xq, nullptr, qweight, gscale, nullptr, nullptr, acc, workspace,
+                     workspace_bytes, M, N, K, group_size, stream);
+}
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_ERR_INVALID_ARG: return "W4_ERR_INVALID_ARG";
+    case W4_ERR_UNSUPPORTED: return "W4_ERR_UNSUPPORTED";
+    case W4_ERR_WORKSPACE: return "W4_ERR_WORKSPACE";
+    case W4_ERR_DEVICE: return "W4_ERR_DEVICE";
+    case W4_ERR_HIP: return "W4_ERR_HIP";
+    default: return "W4_ERR_UNKNOWN";
+  }
+}
+
+const char* w4_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// nibble unpacking and the exact int4 -> fp16 dequantization.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int16_t_ __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_f16: D[16x16] += A[16x32] * B[32x16].  Lane l holds A row
+// (l % 16), B column (l % 16), and 8 K-elements (a K-slot) each; the same K-slot
+// assignment is used for A and B, so any consistent mapping of real k indices to
+// (lane / 16, element) gives the same product.  D: lane l holds column l % 16,
+// rows 4 * (l / 16) + r, r = 0..3.
+__device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_f16: D[32x32] += A[32x16] * B[16x32].  Lane l holds A row
+// (l % 32), B column (l % 32), 8 K-elements each.  D: lane l holds column l % 32,
+// rows 8 * (r / 4) + 4 * (l / 32) + (r % 4), r = 0..15.
+__device__ __forceinline__ float16_t mfma32(half8_t a, half8_t b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// int8: v_mfma_i32_16x16x64_i8 (16 K-bytes per lane) and v_mfma_i32_32x32x32_i8.
+__device__ __forceinline__ int4_t mfma16_i8(int4_t a, int4_t b, int4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int16_t_ mfma32_i8(int4_t a, int4_t b, int16_t_ c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------ nibble unpacking
+// One packed word holds 8 consecutive elements e_0..e_7 (e_i in bits 4i..4i+3).
+// unpack_1024: four registers of packed fp16 pairs (1024 + e_{2p}, 1024 + e_{2p+1}),
+// p = 0..3, i.e. the 8 elements in natural order as half8, each exactly 1024 + code.
+// 0x6400 is fp16 1024.0; a code c in the low mantissa bits gives 1024 + c exactly.
+// v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7 of the
+// first, 0x0c gives 0.
+__device__ __forceinline__ half8_t unpack_1024(uint32_t w) {
+  const uint32_t s = w >> 4;
+  u32x4 r;
+  r[0] = (__builtin_amdgcn_perm(s, w, 0x0c040c00u) & 0x000f000fu) | 0x64006400u;
+  r[1] = (__builtin_amdgcn_perm(s, w, 0x0c050c01u) & 0x000f000fu) | 0x64006400u;
+  r[2] = (__builtin_amdgcn_perm(s, w, 0x0c060c02u) & 0x000f000fu) | 0x64006400u;
+  r[3] = (__builtin_amdgcn_perm(s, w, 0x0c070c03u) & 0x000f000fu) | 0x64006400u;
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// Exact dequantization of one word: ((1024 + q) - (1024 + z)) is the exact integer
+// q - z in fp16, then one multiply by the fp16 scale: a single rounding per element.
+// negz2 = -(1024 + z) in both halves, s2 = scale in both halves.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t negz2, half2_t s2) {
+  half8_t v = unpack_1024(w);
+  half2_t p0 = {v[0], v[1]}, p1 = {v[2], v[3]}, p2 = {v[4], v[5]}, p3 = {v[6], v[7]};
+  p0 = (p0 + negz2) * s2;
+  p1 = (p1 + negz2) * s2;
+  p2 = (p2 + negz2) * s2;
+  p3 = (p3 + negz2) * s2;
+  half8_t o = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return o;
+}
+
+__device__ __forceinline__ half2_t splat2(half_t h) { return half2_t{h, h}; }
+
+// Biased int4 (stored nibble b = q + 8) -> 16 * q as int8 bytes, natural order.
+// b ^ 8 is the 4-bit two's complement of q; placing it in the high nibble of a byte
+// gives the int8 value 16 * q exactly.  Returns the 8 elements as two words
+// (elements 0..3, 4..7).
+__device__ __forceinline__ void unpack_i4x16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t t = w ^ 0x88888888u;
+  const uint32_t ev = (t << 4) & 0xf0f0f0f0u;  // bytes: 16*q0, 16*q2, 16*q4, 16*q6
+  const uint32_t od = t & 0xf0f0f0f0u;         // bytes: 16*q1, 16*q3, 16*q5, 16*q7
+  lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // q0 q1 q2 q3
+  hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // q4 q5 q6 q7
+}
+
+// Biased int4 (b = q + 8) times a per-group int8 scale s -> int8 bytes q * s (|q s| <= 127
+// is guaranteed by the weight rule), natural order, as two words (elements 0..3, 4..7).
+// The products are formed in 16-bit lanes: (b * s + (-8 s)) mod 2^16 is q * s as int16,
+// whose low byte is the int8 value.  sp = (s, s), cp = (-8 s, -8 s) as u16 pairs.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack_i4_scaled(uint32_t w, u16x2 sp, u16x2 cp, uint32_t& lo, uint32_t& hi) {
+  const u16x2 e0 = __builtin_bit_cast(u16x2, w & 0x000f000fu);          // b0, b4
+  const u16x2 e1 = __builtin_bit_cast(u16x2, (w >> 4) & 0x000f000fu);   // b1, b5
+  const u16x2 e2 = __builtin_bit_cast(u16x2, (w >> 8) & 0x000f000fu);   // b2, b6
+  const u16x2 e3 = __builtin_bit_cast(u16x2, (w >> 12) & 0x000f000fu);  // b3, b7
+  const uint32_t r0 = __builtin_bit_cast(uint32_t, (u16x2)(e0 * sp + cp));
+  const uint32_t r1 = __builtin_bit_cast(uint32_t, (u16x2)(e1 * sp + cp));
+  const uint32_t r2 = __builtin_bit_cast(uint32_t, (u16x2)(e2 * sp + cp));
+  const uint32_t r3 = __builtin_bit_cast(uint32_t, (u16x2)(e3 * sp + cp));
+  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x06020400u);  // p0 p1 p4 p5
+  const uint32_t t1 = __builtin_amdgcn_perm(r3, r2, 0x06020400u);  // p2 p3 p6 p7
+  lo = __builtin_amdgcn_perm(t1, t0, 0x05040100u);                 // p0 p1 p2 p3
+  hi = __builtin_amdgcn_perm(t1, t0, 0x07060302u);                 // p4 p5 p6 p7
+}
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Workgroup -> tile remapping for 8 XCDs.  Workgroups are handed to the XCDs round
+// robin (id % 8); this returns a logical id such that the workgroups one XCD runs are
+// consecutive logical ids, so neighbouring tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int per = total / 8;
+  if (per == 0 || id >= per * 8) return id;
+  return (id % 8) * per + id / 8;
+}
+
+}  // namespace w4

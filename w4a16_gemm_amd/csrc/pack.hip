@@ -1,0 +1,191 @@
+// Weight quantization and packing kernels (offline-style, one pass over W).
+//
+//  * awq_pack: asymmetric 4-bit group quantization ("Some fixes for AWQ",
+//    neuralmagic/compressed-tensors PR 269, opening comment: the asymmetric rule of
+//    AutoAWQ's pseudo-quantize) and packing into the plain nibble order (packed
+//    weight format of the Triton AWQ kernels in "Implement AWQ quantization support
+//    for LLaMA", vllm-project/vllm PR 1032: pack_num = 8 codes per 32-bit word).
+//  * awq_unpack_dequant: fp16((q - z) * s), the GEMM's dequantization, exported.
+//  * w4a8_pack: symmetric int4 weights for the W4A8 GEMM, per-channel or two-level
+//    with int8 group scales ("[Feature] support qqq(w4a8) for lmdeploy", section
+//    "Benchmark": QQQ per-channel and QQQ-g128 variants).
+//
+// Every quantization decision is made in fp32 with IEEE division and
+// round-half-to-even (rintf), and there is no a*b+c in these expressions, so the
+// codes are bit-reproducible.
+#include "kernels.hpp"
+
+namespace w4 {
+
+// One thread per (group g, row n); n is the fastest index so that the 8 threads of a
+// zero-point word are 8 consecutive lanes.  npad = N rounded up to a multiple of 8.
+__global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict__ w,
+                                                        int32_t* __restrict__ qweight,
+                                                        half_t* __restrict__ scales,
+                                                        int32_t* __restrict__ qzeros,
+                                                        int N, int K, int npad) {
+  const int ng = K / 128;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = tid < (int64_t)npad * ng;
+  const int g = live ? (int)(tid / npad) : 0;
+  const int n = live ? (int)(tid % npad) : 0;
+  const bool valid = live && n < N;
+  uint32_t zbits = 0;
+  if (valid) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(w + (int64_t)n * K + (int64_t)g * 128);
+    u32x4 raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw[i] = src[i];
+    const half_t* h = reinterpret_cast<const half_t*>(raw);
+    float mn = (float)h[0], mx = (float)h[0];
+#pragma unroll
+    for (int i = 1; i < 128; ++i) {
+      const float v = (float)h[i];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    float s32 = (mx - mn) / 15.0f;
+    s32 = fmaxf(s32, 1e-5f);
+    const half_t s16 = (half_t)s32;
+    const float s = (float)s16;
+    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f);
+    u32x4 out[4];
+    uint32_t* ow = reinterpret_cast<uint32_t*>(out);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(rintf((float)h[8 * j + i] / s) + z, 0.0f), 15.0f);
+        word |= ((uint32_t)q) << (4 * i);
+      }
+      ow[j] = word;
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(qweight + (int64_t)n * (K / 8) + (int64_t)g * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = out[i];
+    scales[(int64_t)g * N + n] = s16;
+    zbits = ((uint32_t)z) << (4 * (n & 7));
+  }
+  // OR the 8 nibbles of the zero-point word across the 8 consecutive lanes.
+  zbits |= __shfl_xor(zbits, 1, kWave);
+  zbits |= __shfl_xor(zbits, 2, kWave);
+  zbits |= __shfl_xor(zbits, 4, kWave);
+  if (live && (n & 7) == 0 && n < N) qzeros[(int64_t)g * (npad / 8) + n / 8] = (int32_t)zbits;
+}
+
+// One thread per packed word (n, j): eight fp16 outputs.
+__global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t* __restrict__ qweight,
+                                                                  const half_t* __restrict__ scales,
+                                                                  const uint32_t* __restrict__ qzeros,
+                                                                  half_t* __restrict__ out, int N, int K) {
+  const int wpr = K / 8;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= (int64_t)N * wpr) return;
+  const int n = (int)(tid / wpr);
+  const int j = (int)(tid % wpr);
+  const int g = j / 16;
+  const int nzw = (N + 7) / 8;
+  const uint32_t z = (qzeros[(int64_t)g * nzw + n / 8] >> (4 * (n & 7))) & 15u;
+  const half_t s = scales[(int64_t)g * N + n];
+  const half2_t negz2 = splat2(-(half_t)(1024 + z));
+  const half8_t v = dequant8(qweight[tid], negz2, splat2(s));
+  *reinterpret_cast<half8_t*>(out + (int64_t)n * K + (int64_t)j * 8) = v;
+}
+
+// One workgroup (256 threads) per row n.  Pass 1: amax over the row.  Pass 2: codes.
+// Two-level mode: a group of 128 k is 16 words handled by 16 consecutive lanes.
+__global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict__ w,
+                                                         uint32_t* __restrict__ qweight,
+                                                         int8_t* __restrict__ gscale,
+                                                         half_t* __restrict__ cscale,
+                                                         int N, int K, int two_level) {
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  const half_t* row = w + (int64_t)n * K;
+  const int wpr = K / 8;
+  float amax = 0.0f;
+  for (int j = threadIdx.x; j < wpr; j += 256) {
+    const half8_t v = *reinterpret_cast<const half8_t*>(row + 8 * j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s32 = fmaxf(amax / (two_level ? 127.0f : 7.0f), 1e-5f);
+  const half_t s16 = (half_t)s32;
+  const float s = (float)s16;
+  if (threadIdx.x == 0) cscale[n] = s16;
+  // wpr is a multiple of 16 (K multiple of 128) in two-level mode, and 256 is a multiple
+  // of 16, so every 16-lane segment holds exactly one group.
+  const int jmax = (wpr + 255) / 256 * 256;
+  for (int j = threadIdx.x; j < jmax; j += 256) {
+    const bool ok = j < wpr;
+    float e[8];
+    if (ok) {
+      const half8_t v = *reinterpret_cast<const half8_t*>(row + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = (float)v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = 0.0f;
+    }
+    uint32_t word = 0;
+    if (!two_level) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(rintf(e[i] / s), -8.0f), 7.0f);
+        word |= ((uint32_t)((int)q + 8)) << (4 * i);
+      }
+    } else {
+      float w8[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w8[i] = fminf(fmaxf(rintf(e[i] / s), -127.0f), 127.0f);
+        m = fmaxf(m, fabsf(w8[i]));
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      const float sg = fminf(fmaxf(1.0f, ceilf(m / 7.0f)), 18.0f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(rintf(w8[i] / sg), -7.0f), 7.0f);
+        word |= ((uint32_t)((int)q + 8)) << (4 * i);
+      }
+      if (ok && (j & 15) == 0) gscale[(int64_t)(j / 16) * N + n] = (int8_t)(int)sg;
+    }
+    if (ok) qweight[(int64_t)n * wpr + j] = word;
+  }
+}
+
+hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
+                           hipStream_t stream) {
+  const int npad = (N + 7) / 8 * 8;
+  const int64_t total = (int64_t)npad * (K / 128);
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(awq_pack_kernel, dim3(blocks), dim3(256), 0, stream, (const half_t*)w, qweight,
+                     (half_t*)scales, qzeros, N, K, npad);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros,
+                                     void* out, int N, int K, hipStream_t stream) {
+  const int64_t total = (int64_t)N * (K / 8);
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(awq_unpack_dequant_kernel, dim3(blocks), dim3(256), 0, stream,
+                     (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros,
+                     (half_t*)out, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
+                            int two_level, hipStream_t stream) {
+  hipLaunchKernelGGL(w4a8_pack_kernel, dim3(N), dim3(256), 0, stream, (const half_t*)w,
+                     (uint32_t*)qweight, gscale, (half_t*)cscale, N, K, two_level);
+  return hipGetLastError();
+}
+
+}  // namespace w4

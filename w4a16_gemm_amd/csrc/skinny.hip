@@ -1,0 +1,247 @@
+// Skinny W4A16 GEMM for M <= 64 (decode): bandwidth-bound, every packed weight byte
+// is read once.
+//
+// The pages single out the small-batch regime ("Implement AWQ quantization support
+// for LLaMA", vllm-project/vllm PR 1032: the AWQ GEMM is fastest below batch 8 and
+// on par with FP16 at batch 16) and say that dequantization is the tricky part.
+// Here the dequantization is folded into per-group fp32 arithmetic:
+//
+//   Y[m,n] = sum_g s[n,g] * ( T_g[m,n] - (1024 + z[n,g]) * S_g[m] ),
+//   T_g[m,n] = sum_{k in g} X[m,k] * (1024 + q[n,k]),   S_g[m] = sum_{k in g} X[m,k],
+//
+// which equals sum_k X[m,k] * (q - z) * s exactly in real arithmetic.  The MFMA
+// consumes the raw fp16 values 1024 + q (nine VALU ops per 8 codes, no per-element
+// subtract or multiply); S_g comes from one extra MFMA against a B operand of ones.
+// fp16 x (1024 + q) products are exact in fp32; only the fp32 sums round.
+//
+// Work split: a workgroup (4 waves) owns 64 output columns n (4 tiles of 16) and a
+// contiguous range of K groups (split-K across workgroups); its waves take the groups
+// of that range round robin.  Per group, lane l of a wave loads one 16-byte chunk
+// (32 codes) of row n0 + 16t + (l % 16) for each of the 4 tiles t, and the 64 bytes
+// of X it needs; the four MFMAs of a group use word j of every lane's chunk, and A
+// is loaded with the same K-slot assignment.  Partial sums are reduced across the
+// waves in LDS, then across split-K workgroups through the workspace by the last
+// arriving workgroup, in a fixed order.
+#include "kernels.hpp"
+
+namespace w4 {
+
+namespace {
+
+constexpr int kRows = 64;      // output columns (weight rows) per workgroup
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kTargetBlocks = 1024;
+
+template <int MT>
+struct GroupRegs {
+  u32x4 b[4];         // packed codes: 4 words (32 k) for each of the 4 n-tiles
+  half8_t a[MT][4];   // X fragments: MT m-tiles x 4 MFMAs
+  float s[4];         // scale of this lane's row in each n-tile
+  float c[4];         // 1024 + zero of this lane's row in each n-tile
+};
+
+template <int MT>
+__device__ __forceinline__ void load_group(GroupRegs<MT>& r, const half_t* __restrict__ x,
+                                           const uint32_t* __restrict__ qweight,
+                                           const half_t* __restrict__ scales,
+                                           const uint32_t* __restrict__ qzeros, int g, int n0, int lane,
+                                           int M, int N, int K) {
+  const int wpr = K / 8;
+  const int nzw = (N + 7) / 8;
+  const int slot = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = n0 + 16 * t + (lane & 15);
+    if (n < N) {
+      r.b[t] = *reinterpret_cast<const u32x4*>(qweight + (int64_t)n * wpr + g * 16 + slot * 4);
+      r.s[t] = (float)scales[(int64_t)g * N + n];
+      const uint32_t zw = qzeros[(int64_t)g * nzw + (n >> 3)];
+      r.c[t] = (float)(1024u + ((zw >> (4 * (n & 7))) & 15u));
+    } else {
+      r.b[t] = u32x4{0u, 0u, 0u, 0u};
+      r.s[t] = 0.0f;
+      r.c[t] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + (lane & 15);
+    const half8_t* src = reinterpret_cast<const half8_t*>(x + (int64_t)m * K + g * 128 + slot * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (m < M) r.a[mt][j] = src[j];
+      else r.a[mt][j] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void compute_group(const GroupRegs<MT>& r, float4_t (&yacc)[MT][4]) {
+  const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  float4_t ssum[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    ssum[mt] = float4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ssum[mt] = mfma16(r.a[mt][j], ones, ssum[mt]);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    half8_t bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = unpack_1024(r.b[t][j]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float4_t tacc = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tacc = mfma16(r.a[mt][j], bv[j], tacc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = fmaf(-r.c[t], ssum[mt][i], tacc[i]);
+        yacc[mt][t][i] = fmaf(r.s[t], d, yacc[mt][t][i]);
+      }
+    }
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void skinny_kernel(const half_t* __restrict__ x,
+                                                          const uint32_t* __restrict__ qweight,
+                                                          const half_t* __restrict__ scales,
+                                                          const uint32_t* __restrict__ qzeros,
+                                                          half_t* __restrict__ y, unsigned* __restrict__ counters,
+                                                          float* __restrict__ partials, int M, int N, int K,
+                                                          int splits, int gps) {
+  __shared__ float red[4][MT * 16 * kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rb = blockIdx.x;
+  const int split = blockIdx.y;
+  const int n0 = rb * kRows;
+  const int ng = K / 128;
+  const int gbeg = split * gps;
+  const int gend = min(ng, gbeg + gps);
+
+  float4_t yacc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) yacc[mt][t] = float4_t{0, 0, 0, 0};
+
+  GroupRegs<MT> cur, nxt;
+  int g = gbeg + wave;
+  if (g < gend) load_group<MT>(cur, x, qweight, scales, qzeros, g, n0, lane, M, N, K);
+  for (; g < gend; g += 4) {
+    const bool more = g + 4 < gend;
+    if (more) load_group<MT>(nxt, x, qweight, scales, qzeros, g + 4, n0, lane, M, N, K);
+    compute_group<MT>(cur, yacc);
+    if (more) cur = nxt;
+  }
+
+  // Cross-wave reduction.  Element (mt, t, i) of lane l is output row
+  // m = 16 mt + 4 (l / 16) + i, column n = n0 + 16 t + (l % 16).
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][((mt * 4 + t) * 4 + i) * kWave + lane] = yacc[mt][t][i];
+  __syncthreads();
+
+  const int rows = min(M, MT * 16);
+  // Walk the outputs with n fastest for coalesced stores.
+  float vals[MT * 16 * kRows / kThreads];
+#pragma unroll
+  for (int it = 0; it < MT * 16 * kRows / kThreads; ++it) {
+    const int o = it * kThreads + threadIdx.x;
+    const int m = o / kRows, nl = o % kRows;
+    const int t = nl >> 4, ln = nl & 15;
+    const int mt = m >> 4, i = m & 3, lq = (m & 15) >> 2;
+    const int idx = ((mt * 4 + t) * 4 + i) * kWave + lq * 16 + ln;
+    vals[it] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+  }
+
+  if (splits == 1) {
+#pragma unroll
+    for (int it = 0; it < MT * 16 * kRows / kThreads; ++it) {
+      const int o = it * kThreads + threadIdx.x;
+      const int m = o / kRows, n = n0 + o % kRows;
+      if (m < rows && n < N) y[(int64_t)m * N + n] = (half_t)vals[it];
+    }
+    return;
+  }
+
+  // Split-K: publish fp32 partials, the last workgroup of this column block sums them.
+#pragma unroll
+  for (int it = 0; it < MT * 16 * kRows / kThreads; ++it) {
+    const int o = it * kThreads + threadIdx.x;
+    const int m = o / kRows, n = n0 + o % kRows;
+    if (m < rows && n < N) partials[((int64_t)split * M + m) * N + n] = vals[it];
+  }
+  if (!splitk_arrive(counters + rb, splits)) return;
+#pragma unroll
+  for (int it = 0; it < MT * 16 * kRows / kThreads; ++it) {
+    const int o = it * kThreads + threadIdx.x;
+    const int m = o / kRows, n = n0 + o % kRows;
+    if (m < rows && n < N) {
+      float s = 0.0f;
+      for (int sp = 0; sp < splits; ++sp) s += partials[((int64_t)sp * M + m) * N + n];
+      y[(int64_t)m * N + n] = (half_t)s;
+    }
+  }
+}
+
+}  // namespace
+
+SkinnyPlan skinny_plan(int M, int N, int K) {
+  SkinnyPlan p;
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.row_blocks = (N + kRows - 1) / kRows;
+  const int ng = K / 128;
+  int splits = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
+  splits = max(1, min(splits, ng / 4));  // at least one group per wave
+  p.gps = (ng + splits - 1) / splits;
+  p.splits = (ng + p.gps - 1) / p.gps;
+  return p;
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t skinny_workspace_bytes(int M, int N, int K) {
+  const SkinnyPlan p = skinny_plan(M, N, K);
+  if (p.splits == 1) return 0;
+  return align_up((size_t)p.row_blocks * sizeof(unsigned), kCounterBytesAlign) +
+         (size_t)p.splits * M * N * sizeof(float);
+}
+
+hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
+                         void* y, void* ws, int M, int N, int K, hipStream_t stream) {
+  const SkinnyPlan p = skinny_plan(M, N, K);
+  unsigned* counters = (unsigned*)ws;
+  float* partials = ws ? (float*)((char*)ws + align_up((size_t)p.row_blocks * sizeof(unsigned),
+                                                         kCounterBytesAlign))
+                       : nullptr;
+  const dim3 grid(p.row_blocks, p.splits), block(kThreads);
+  const half_t* xh = (const half_t*)x;
+  const uint32_t* qw = (const uint32_t*)qweight;
+  const half_t* sc = (const half_t*)scales;
+  const uint32_t* qz = (const uint32_t*)qzeros;
+  half_t* yh = (half_t*)y;
+  switch (p.mt) {
+    case 1:
+      hipLaunchKernelGGL(skinny_kernel<1>, grid, block, 0, stream, xh, qw, sc, qz, yh, counters, partials, M, N,
+                         K, p.splits, p.gps);
+      break;
+    case 2:
+      hipLaunchKernelGGL(skinny_kernel<2>, grid, block, 0, stream, xh, qw, sc, qz, yh, counters, partials, M, N,
+                         K, p.splits, p.gps);
+      break;
+    default:
+      hipLaunchKernelGGL(skinny_kernel<4>, grid, block, 0, stream, xh, qw, sc, qz, yh, counters, partials, M, N,
+                         K, p.splits, p.gps);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4

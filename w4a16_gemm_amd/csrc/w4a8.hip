@@ -1,0 +1,379 @@
+// W4A8 stage: online per-token int8 activation quantization fused with RMSNorm, and
+// the int8 x int4 GEMM on the int8 MFMA units with exact int32 accumulation.
+//
+// "[Feature] support qqq(w4a8) for lmdeploy" (InternLM/lmdeploy issue 2274), section
+// "Modification": a W4A8 GEMM kernel; online activation quantization fused with
+// element-wise ops such as RMSNorm; section "Benchmark": per-channel and g128 weight
+// variants.  "Some fixes for AWQ" (neuralmagic/compressed-tensors PR 269), reply on
+// 8-bit matmuls: the int8 product accumulates to int32 and is rescaled by the weight
+// and activation scales; activations are quantized dynamically per token.
+//
+// Weight codes are stored as biased nibbles b = q + 8.
+//   per-channel:  b ^ 8 is the 4-bit two's complement of q; shifted into the high
+//                 nibble of a byte it is the int8 value 16 q, so the MFMA accumulates
+//                 16 * sum(xq * q) exactly and an exact arithmetic shift by 4 (every
+//                 term is a multiple of 16) gives acc = sum_k xq * q.
+//   two-level:    each code is expanded per group to the int8 value q * s_g (formed in
+//                 16-bit lanes, |q s_g| <= 126), so the MFMA accumulates
+//                 acc = sum_k xq * q * s_g directly.
+// Both are the exact integer sum_k xq[m,k] * q[n,k] * s_g[n,k/G] (s_g = 1 per-channel).
+#include "kernels.hpp"
+
+namespace w4 {
+
+namespace {
+
+// ------------------------------------------------------------ quant_act
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One workgroup per token row.  Three passes over the row (it stays in L2/L1):
+// sum of squares, max |y|, codes.  y = (x * r) * gamma in fp32.
+__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const half_t* __restrict__ x,
+                                                               const half_t* __restrict__ gamma, float eps,
+                                                               int8_t* __restrict__ xq, float* __restrict__ s_a,
+                                                               int K) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const half8_t* xr = reinterpret_cast<const half8_t*>(x + row * K);
+  const half8_t* gr = reinterpret_cast<const half8_t*>(gamma);
+  const int nv = K / 8;
+  float r = 1.0f;
+  if (gamma) {
+    float ss = 0.0f;
+    for (int j = threadIdx.x; j < nv; j += kQThreads) {
+      const half8_t v = xr[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
+    }
+    ss = block_sum(ss, red);
+    r = 1.0f / sqrtf(ss / (float)K + eps);
+  }
+  float amax = 0.0f;
+  for (int j = threadIdx.x; j < nv; j += kQThreads) {
+    const half8_t v = xr[j];
+    if (gamma) {
+      const half8_t g = gr[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(((float)v[i] * r) * (float)g[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+    }
+  }
+  amax = block_max(amax, red);
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+  uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * K);
+  for (int j = threadIdx.x; j < nv; j += kQThreads) {
+    const half8_t v = xr[j];
+    uint64_t packed = 0;
+    if (gamma) {
+      const half8_t g = gr[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float yv = ((float)v[i] * r) * (float)g[i];
+        const float q = fminf(fmaxf(rintf(yv * inv), -127.0f), 127.0f);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(rintf((float)v[i] * inv), -127.0f), 127.0f);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+      }
+    }
+    dst[j] = packed;
+  }
+}
+
+// ------------------------------------------------------------- the GEMM
+// Tile BM x 256 x 128 (one group of 128 k per step), 256 threads; the 4 waves split N
+// (64 columns each = two 32-column fragments) and share all BM = 32 * MI rows (MI
+// 32-row fragments).  A (xq) tiles go through LDS as 128-byte rows of 8 16-byte
+// chunks (chunk c of row r at c ^ (r % 8)).  B: lane l (column l % 32, K-slot h = l / 32)
+// loads words 8h..8h+7 of its row for this step (two 16-byte chunks); k32-step s uses
+// words 8h + 2s, 8h + 2s + 1 (16 codes, k = 8 (8h + 2s) .. + 15), and A is read from
+// LDS with the same slot assignment.
+//
+// Per-channel weights enter the MFMA as 16 q (exact shift at the end); two-level
+// weights enter as q * s_g, expanded per group in registers (|q s_g| <= 126 fits int8),
+// so both variants accumulate the exact integer sum in one int32 accumulator set.
+constexpr int WBN = 256, WBK = 128;
+constexpr int kWThreads = 256;
+
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { return cs ? cs[n] : (half_t)1; }
+
+template <int MI, bool TWO>
+__global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
+    const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
+    int K, int tiles_m, int tiles_n, int splits, int gps) {
+  constexpr int BM = 32 * MI;
+  __shared__ u32x4 lds[2][BM * 8];
+
+  const int total = tiles_m * tiles_n * splits;
+  const int id = xcd_remap(blockIdx.x, total);
+  const int tile = id / splits;
+  const int split = id % splits;
+  const int tm = tile % tiles_m;
+  const int tn = tile / tiles_m;
+  const int m0 = tm * BM, n0 = tn * WBN;
+  const int ng = K / WBK;
+  const int gbeg = split * gps;
+  const int gend = min(ng, gbeg + gps);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const int wpr = K / 8;
+
+  int nrow[2];
+  bool nok[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    nrow[f] = n0 + wave * 64 + f * 32 + col;
+    nok[f] = nrow[f] < N;
+  }
+
+  int16_t_ acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
+
+  constexpr int kChunks = BM * 8;  // 16-byte chunks per A tile
+  constexpr int kPer = (kChunks + kWThreads - 1) / kWThreads;
+  u32x4 areg[kPer];
+  auto load_a = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int cid = threadIdx.x + i * kWThreads;
+      const int r = cid >> 3, c = cid & 7;
+      const int m = m0 + r;
+      if (cid < kChunks && m < M) areg[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)m * K + g * WBK + c * 16);
+      else areg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int cid = threadIdx.x + i * kWThreads;
+      if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = areg[i];
+    }
+  };
+  u32x4 breg[2][2];
+  auto load_b = [&](int g, u32x4 (&dst)[2][2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      if (nok[f]) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(qweight + (int64_t)nrow[f] * wpr + g * 16 + h * 8);
+        dst[f][0] = p[0];
+        dst[f][1] = p[1];
+      } else {
+        dst[f][0] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        dst[f][1] = dst[f][0];
+      }
+    }
+  };
+
+  if (gbeg < gend) {
+    load_a(gbeg);
+    load_b(gbeg, breg);
+    store_a(0);
+  }
+  __syncthreads();
+
+  for (int g = gbeg; g < gend; ++g) {
+    const int buf = (g - gbeg) & 1;
+    const bool more = g + 1 < gend;
+    u32x4 bnext[2][2];
+    if (more) {
+      load_a(g + 1);
+      load_b(g + 1, bnext);
+    }
+    u16x2 sp[2], cp[2];
+    if (TWO) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int sg = nok[f] ? (int)gscale[(int64_t)g * N + nrow[f]] : 0;
+        sp[f] = u16x2{(unsigned short)sg, (unsigned short)sg};
+        cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int4_t bf[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const uint32_t w0 = breg[f][s >> 1][(s & 1) * 2];
+        const uint32_t w1 = breg[f][s >> 1][(s & 1) * 2 + 1];
+        uint32_t a0, a1, a2, a3;
+        if (TWO) {
+          unpack_i4_scaled(w0, sp[f], cp[f], a0, a1);
+          unpack_i4_scaled(w1, sp[f], cp[f], a2, a3);
+        } else {
+          unpack_i4x16(w0, a0, a1);
+          unpack_i4x16(w1, a2, a3);
+        }
+        bf[f] = int4_t{(int)a0, (int)a1, (int)a2, (int)a3};
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const u32x4 av = lds[buf][swz8(i * 32 + col, h * 4 + s)];
+        const int4_t a = __builtin_bit_cast(int4_t, av);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[i][f] = mfma32_i8(a, bf[f], acc[i][f]);
+      }
+    }
+    if (more) {
+      store_a(buf ^ 1);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        breg[f][0] = bnext[f][0];
+        breg[f][1] = bnext[f][1];
+      }
+    }
+    __syncthreads();
+  }
+  if (!TWO) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][f][r] >>= 4;
+  }
+
+  // element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f]
+  if (splits > 1) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (!nok[f]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M) partials[((int64_t)split * M + m) * N + nrow[f]] = acc[i][f][r];
+        }
+      }
+    if (!splitk_arrive(counters + tile, splits)) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (!nok[f]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M) {
+            int32_t v = 0;
+            for (int sp_ = 0; sp_ < splits; ++sp_) v += partials[((int64_t)sp_ * M + m) * N + nrow[f]];
+            acc[i][f][r] = v;
+          }
+        }
+      }
+  }
+  const float cs0 = nok[0] ? (float)cscale_or_one(cscale, nrow[0]) : 0.0f;
+  const float cs1 = nok[1] ? (float)cscale_or_one(cscale, nrow[1]) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      if (!nok[f]) continue;
+      const float cs = f == 0 ? cs0 : cs1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M) {
+          if (acc_out) acc_out[(int64_t)m * N + nrow[f]] = acc[i][f][r];
+          else y[(int64_t)m * N + nrow[f]] = (half_t)(((float)acc[i][f][r] * s_a[m]) * cs);
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
+                                 int K, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_act_kernel, dim3(M), dim3(kQThreads), 0, stream, (const half_t*)x,
+                     (const half_t*)gamma, eps, xq, s_a, K);
+  return hipGetLastError();
+}
+
+W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
+  (void)group_size;
+  W4A8Plan p;
+  p.bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+  p.tiles_m = (M + p.bm - 1) / p.bm;
+  p.tiles_n = (N + WBN - 1) / WBN;
+  const int ng = K / WBK;
+  const int tiles = p.tiles_m * p.tiles_n;
+  int splits = 1;
+  while (tiles * splits < 512 && ng / (splits * 2) >= 2) splits *= 2;
+  p.kt_per_split = (ng + splits - 1) / splits;
+  p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
+  return p;
+}
+
+size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
+  const W4A8Plan p = w4a8_plan(M, N, K, group_size);
+  if (p.splits == 1) return 0;
+  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
+                     kCounterBytesAlign * kCounterBytesAlign;
+  return cnt + (size_t)p.splits * M * N * sizeof(int32_t);
+}
+
+hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
+                            const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
+                            int group_size, hipStream_t stream) {
+  const W4A8Plan p = w4a8_plan(M, N, K, group_size);
+  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
+                     kCounterBytesAlign * kCounterBytesAlign;
+  unsigned* counters = (unsigned*)ws;
+  int32_t* partials = ws ? (int32_t*)((char*)ws + cnt) : nullptr;
+  const int blocks = p.tiles_m * p.tiles_n * p.splits;
+  const dim3 grid(blocks), block(kWThreads);
+  const uint32_t* qw = (const uint32_t*)qweight;
+  const half_t* cs = (const half_t*)cscale;
+  half_t* yh = (half_t*)y;
+  const int8_t* gs = group_size == -1 ? nullptr : gscale;
+#define W4A8_LAUNCH(MI, TWO)                                                                                  \
+  hipLaunchKernelGGL((w4a8_gemm_kernel<MI, TWO>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
+  const int mi = p.bm / 32;
+  if (gs) {
+    if (mi == 1) W4A8_LAUNCH(1, true);
+    else if (mi == 2) W4A8_LAUNCH(2, true);
+    else W4A8_LAUNCH(4, true);
+  } else {
+    if (mi == 1) W4A8_LAUNCH(1, false);
+    else if (mi == 2) W4A8_LAUNCH(2, false);
+    else W4A8_LAUNCH(4, false);
+  }
+#undef W4A8_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace w4
