@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--detail-iters", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w4a8", "copy"],
+                    help="decode (default, the reported metric); prefill / w4a8 / copy run one kernel family "
+                         "alone (for profiling); copy is a plain device copy of known size that calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -94,6 +98,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w4.load()
+    if args.workload != "decode":
+        print(json.dumps(single_workload(args, dev, torch, np, synth, w4)), flush=True)
+        return
 
     # ---------------------------------------------------------------- inputs
     log("generating inputs")
@@ -201,6 +208,52 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, synth, host)
     print(json.dumps(result), flush=True)
+
+
+def single_workload(args, dev, torch, np, synth, w4):
+    """One kernel family alone, for profiling: K timed iterations after W warmups."""
+    res = {"workload": args.workload, "steps": args.steps, "warmup": args.warmup}
+    if args.workload == "copy":
+        n = 512 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        calls = [lambda: b.copy_(a)]
+        res["bytes_read_per_call"] = n
+        res["bytes_written_per_call"] = n
+    elif args.workload == "prefill":
+        calls = []
+        for (K, N) in ((5120, 27648), (5120, 5120), (13824, 5120)):
+            inp = synth.make_linear(0, N, K, seed=0, outliers=True)
+            qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+            x = synth.make_activations(4096, K, seed=4096, rms_spread=True).to(dev)
+            y = torch.empty((4096, N), dtype=torch.float16, device=dev)
+            calls.append(w4.bind_awq_gemm(x, qw, sc, qz, y))
+        res["flops_per_round"] = sum(2.0 * 4096 * N * K for (K, N) in ((5120, 27648), (5120, 5120), (13824, 5120)))
+    else:  # w4a8 at M = 4096, both weight variants
+        inp = synth.make_linear(4096, 13824, 5120, seed=0, outliers=True, rms_spread=True, with_gamma=True)
+        x = inp.x.to(dev)
+        g = inp.gamma.to(dev)
+        xq = torch.empty((4096, 5120), dtype=torch.int8, device=dev)
+        sa = torch.empty((4096,), dtype=torch.float32, device=dev)
+        calls = [w4.bind_w4a8_quant_act(x, g, xq, sa)]
+        for group in (-1, 128):
+            qw, gs, cs = w4.w4a8_pack(inp.w.to(dev), group)
+            y = torch.empty((4096, 13824), dtype=torch.float16, device=dev)
+            calls.append(w4.bind_w4a8_gemm(xq, sa, qw, gs, cs, y, group))
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(args.steps):
+        for c in calls:
+            c()
+    a1.record()
+    torch.cuda.synchronize()
+    res["ms_per_round"] = a0.elapsed_time(a1) / args.steps
+    return res
 
 
 def _time_calls(torch, calls, iters):

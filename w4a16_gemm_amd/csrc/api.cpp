@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -92,6 +93,16 @@ size_t awq_ws(int64_t M, int64_t N, int64_t K) {
   } while (0)
 
 }  // namespace
+
+namespace w4 {
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (v == nullptr || *v == 0) return dflt;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+}
+}  // namespace w4
 
 extern "C" {
 

@@ -86,16 +86,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  // global -> register staging of one X tile: 1024 chunks, 4 per thread
+  // global -> register staging of one X tile: 1024 chunks, 4 per thread.  Loads are
+  // branch-free (rows past M read a clamped valid row, zeroed before the LDS store) so
+  // they issue back to back.
   u32x4 areg[4];
   auto load_a = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int cid = threadIdx.x + i * kThreads;
       const int r = cid >> 3, c = cid & 7;
-      const int m = m0 + r;
-      if (m < M) areg[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + kt * BK + c * 8);
-      else areg[i] = u32x4{0u, 0u, 0u, 0u};
+      const int m = min(m0 + r, M - 1);
+      areg[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + kt * BK + c * 8);
     }
   };
   auto store_a = [&](int buf) {
@@ -103,49 +104,60 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
     for (int i = 0; i < 4; ++i) {
       const int cid = threadIdx.x + i * kThreads;
       const int r = cid >> 3, c = cid & 7;
-      lds[buf][swz(r, c)] = areg[i];
+      lds[buf][swz(r, c)] = (m0 + r < M) ? areg[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // Columns past N read a clamped valid row; their outputs are never stored.
+  int nclamp[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) nclamp[f] = min(nrow[f], N - 1);
   u32x4 breg[2];
   auto load_b = [&](int kt, u32x4 (&dst)[2]) {
 #pragma unroll
+    for (int f = 0; f < 2; ++f)
+      dst[f] = *reinterpret_cast<const u32x4*>(qweight + (int64_t)nclamp[f] * wpr + kt * 8 + h * 4);
+  };
+  // Scale and zero point of this lane's rows for one 128-group: the raw words are
+  // prefetched one BK step ahead together with the codes, then converted to the packed
+  // fp16 pairs -(1024 + z) and s used by dequant8.
+  uint32_t zraw[2];
+  half_t sraw[2];
+  auto load_sz = [&](int g, uint32_t (&zr)[2], half_t (&sr)[2]) {
+#pragma unroll
     for (int f = 0; f < 2; ++f) {
-      if (nok[f]) dst[f] = *reinterpret_cast<const u32x4*>(qweight + (int64_t)nrow[f] * wpr + kt * 8 + h * 4);
-      else dst[f] = u32x4{0u, 0u, 0u, 0u};
+      zr[f] = qzeros[(int64_t)g * nzw + (nclamp[f] >> 3)];
+      sr[f] = scales[(int64_t)g * N + nclamp[f]];
     }
   };
   half2_t negz2[2], s2[2];
-  auto load_sz = [&](int g) {
+  auto set_sz = [&](const uint32_t (&zr)[2], const half_t (&sr)[2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      if (nok[f]) {
-        const uint32_t zw = qzeros[(int64_t)g * nzw + (nrow[f] >> 3)];
-        const uint32_t z = (zw >> (4 * (nrow[f] & 7))) & 15u;
-        negz2[f] = splat2(-(half_t)(1024u + z));
-        s2[f] = splat2(scales[(int64_t)g * N + nrow[f]]);
-      } else {
-        negz2[f] = splat2((half_t)0);
-        s2[f] = splat2((half_t)0);
-      }
+      const uint32_t z = (zr[f] >> (4 * (nclamp[f] & 7))) & 15u;
+      negz2[f] = splat2(-(half_t)(1024u + z));
+      s2[f] = splat2(sr[f]);
     }
   };
 
   if (kbeg < kend) {
     load_a(kbeg);
     load_b(kbeg, breg);
+    load_sz(kbeg >> 1, zraw, sraw);  // 2 BK steps per 128-group
     store_a(0);
+    set_sz(zraw, sraw);
   }
   __syncthreads();
 
   for (int kt = kbeg; kt < kend; ++kt) {
     const int buf = (kt - kbeg) & 1;
     const bool more = kt + 1 < kend;
+    const bool new_group = ((kt + 1) & 1) == 0;
     u32x4 bnext[2];
     if (more) {
       load_a(kt + 1);
       load_b(kt + 1, bnext);
+      if (new_group) load_sz((kt + 1) >> 1, zraw, sraw);
     }
-    if (kt == kbeg || (kt & 1) == 0) load_sz(kt >> 1);  // 2 BK steps per 128-group
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8_t bf[2];
@@ -163,6 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
       store_a(buf ^ 1);
       breg[0] = bnext[0];
       breg[1] = bnext[1];
+      if (new_group) set_sz(zraw, sraw);
     }
     __syncthreads();
   }
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) partials[((int64_t)split * M + m) * N + nrow[f]] = acc[i][f][r];
+        if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
       }
     }
   if (!splitk_arrive(counters + tile, splits)) return;
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
         const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M) {
           float s = 0.0f;
-          for (int sp = 0; sp < splits; ++sp) s += partials[((int64_t)sp * M + m) * N + nrow[f]];
+          for (int sp = 0; sp < splits; ++sp) s += ld_coherent(partials + ((int64_t)sp * M + m) * N + nrow[f]);
           y[(int64_t)m * N + nrow[f]] = (half_t)s;
         }
       }
@@ -220,9 +233,11 @@ GemmPlan gemm_plan(int M, int N, int K) {
   p.tiles_n = (N + BN - 1) / BN;
   const int ktiles = K / BK;
   const int tiles = p.tiles_m * p.tiles_n;
+  const int target = env_int("W4_GEMM_SPLIT_TARGET", 256);
   int splits = 1;
-  // fill at least ~one workgroup per CU; keep >= 8 BK steps per split
-  while (tiles * splits < 256 && ktiles / (splits * 2) >= 8) splits *= 2;
+  // fill the CUs when there are few tiles; keep >= 8 BK steps per split
+  while (tiles * splits < target && ktiles / (splits * 2) >= 8) splits *= 2;
+  if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ktiles + splits - 1) / splits;
   p.splits = (ktiles + p.kt_per_split - 1) / p.kt_per_split;
   return p;
@@ -231,18 +246,14 @@ GemmPlan gemm_plan(int M, int N, int K) {
 size_t gemm_workspace_bytes(int M, int N, int K) {
   const GemmPlan p = gemm_plan(M, N, K);
   if (p.splits == 1) return 0;
-  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
-                     kCounterBytesAlign * kCounterBytesAlign;
-  return cnt + (size_t)p.splits * M * N * sizeof(float);
+  return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(float);
 }
 
 hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
                        void* y, void* ws, int M, int N, int K, hipStream_t stream) {
   const GemmPlan p = gemm_plan(M, N, K);
   unsigned* counters = (unsigned*)ws;
-  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
-                     kCounterBytesAlign * kCounterBytesAlign;
-  float* partials = ws ? (float*)((char*)ws + cnt) : nullptr;
+  float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int blocks = p.tiles_m * p.tiles_n * p.splits;
   hipLaunchKernelGGL(gemm_kernel, dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y, counters,

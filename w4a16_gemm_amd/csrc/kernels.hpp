@@ -5,24 +5,49 @@
 
 namespace w4 {
 
-// Split-K arrival.  Every block of a tile stores its fp32 partial sums, then calls
-// this; it returns true in exactly one block (the last to arrive), which then sums
-// the partials in split order (deterministic) and writes the result.  The last block
-// resets the counter to 0, so a zero-filled counter region stays zero across calls.
+// Split-K across workgroups.  Every block of a tile writes its partial sums with
+// agent-scope relaxed atomic stores, waits for them to complete, and bumps the tile's
+// arrival counter; the block that arrives last reads all partials (agent-scope loads)
+// in split order -- deterministic -- and writes the result.  Agent-scope stores and
+// loads are coherent across the XCDs' L2 caches on their own (the compiler marks them
+// for the coherence point), so no whole-cache writeback or invalidate is needed; the
+// counter RMW is performed at the coherence point.  The last block resets the counter
+// to 0, so a zero-filled counter region stays zero across calls.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool splitk_arrive(unsigned* counter, int splits) {
   __shared__ int is_last;
-  __threadfence();  // release: this thread's partial stores are visible device-wide
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = atomicAdd(counter, 1u);
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (old == (unsigned)(splits - 1));
-    if (is_last) atomicExch(counter, 0u);
+    if (is_last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  const bool last = is_last != 0;
-  if (last) __threadfence();  // acquire: see the other blocks' partials
-  return last;
+  return is_last != 0;
 }
+
+// Workspace layout: a fixed region of kMaxCounters uint32 arrival counters at offset 0
+// (zero-filled by the caller once; never used for anything else, so reusing one
+// workspace for different shapes is safe), then the partial sums.  Plans only split K
+// when the number of tiles is below kMaxCounters.
+constexpr int kMaxCounters = 4096;
+constexpr size_t kCounterRegionBytes = kMaxCounters * sizeof(unsigned);
+
+// Host-side tuning knob: integer environment variable, or `dflt` when unset.
+int env_int(const char* name, int dflt);
 
 // Tile plan of the skinny (M <= 64) W4A16 kernel.
 struct SkinnyPlan {
@@ -43,8 +68,6 @@ struct W4A8Plan {
   int tiles_m, tiles_n, splits, kt_per_split, bm;
 };
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
-
-constexpr size_t kCounterBytesAlign = 256;
 
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
                            hipStream_t stream);

@@ -169,36 +169,44 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     for (int i = 0; i < kPer; ++i) {
       const int cid = threadIdx.x + i * kWThreads;
       const int r = cid >> 3, c = cid & 7;
-      const int m = m0 + r;
-      if (cid < kChunks && m < M) areg[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)m * K + g * WBK + c * 16);
-      else areg[i] = u32x4{0u, 0u, 0u, 0u};
+      const int m = min(m0 + r, M - 1);  // branch-free: clamped row, zeroed at the LDS store
+      areg[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)m * K + g * WBK + c * 16);
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int cid = threadIdx.x + i * kWThreads;
-      if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = areg[i];
+      if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = (m0 + (cid >> 3) < M) ? areg[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // Columns past N read a clamped valid row; their outputs are never stored.
+  int nclamp[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) nclamp[f] = min(nrow[f], N - 1);
   u32x4 breg[2][2];
   auto load_b = [&](int g, u32x4 (&dst)[2][2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      if (nok[f]) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(qweight + (int64_t)nrow[f] * wpr + g * 16 + h * 8);
-        dst[f][0] = p[0];
-        dst[f][1] = p[1];
-      } else {
-        dst[f][0] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        dst[f][1] = dst[f][0];
-      }
+      const u32x4* p = reinterpret_cast<const u32x4*>(qweight + (int64_t)nclamp[f] * wpr + g * 16 + h * 8);
+      dst[f][0] = p[0];
+      dst[f][1] = p[1];
+    }
+  };
+
+  // Group scales of this lane's rows, prefetched one step ahead with the codes.
+  int sgraw[2] = {1, 1};
+  auto load_sg = [&](int g, int (&dst)[2]) {
+    if (TWO) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) dst[f] = (int)gscale[(int64_t)g * N + nclamp[f]];
     }
   };
 
   if (gbeg < gend) {
     load_a(gbeg);
     load_b(gbeg, breg);
+    load_sg(gbeg, sgraw);
     store_a(0);
   }
   __syncthreads();
@@ -206,19 +214,20 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   for (int g = gbeg; g < gend; ++g) {
     const int buf = (g - gbeg) & 1;
     const bool more = g + 1 < gend;
-    u32x4 bnext[2][2];
-    if (more) {
-      load_a(g + 1);
-      load_b(g + 1, bnext);
-    }
     u16x2 sp[2], cp[2];
     if (TWO) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const int sg = nok[f] ? (int)gscale[(int64_t)g * N + nrow[f]] : 0;
+        const int sg = sgraw[f];
         sp[f] = u16x2{(unsigned short)sg, (unsigned short)sg};
         cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
       }
+    }
+    u32x4 bnext[2][2];
+    if (more) {
+      load_a(g + 1);
+      load_b(g + 1, bnext);
+      load_sg(g + 1, sgraw);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -274,7 +283,7 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) partials[((int64_t)split * M + m) * N + nrow[f]] = acc[i][f][r];
+          if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
         }
       }
     if (!splitk_arrive(counters + tile, splits)) return;
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
           const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (m < M) {
             int32_t v = 0;
-            for (int sp_ = 0; sp_ < splits; ++sp_) v += partials[((int64_t)sp_ * M + m) * N + nrow[f]];
+            for (int sp_ = 0; sp_ < splits; ++sp_) v += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + nrow[f]);
             acc[i][f][r] = v;
           }
         }
@@ -330,8 +339,10 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   p.tiles_n = (N + WBN - 1) / WBN;
   const int ng = K / WBK;
   const int tiles = p.tiles_m * p.tiles_n;
+  const int target = env_int("W4_W4A8_SPLIT_TARGET", 512);
   int splits = 1;
-  while (tiles * splits < 512 && ng / (splits * 2) >= 2) splits *= 2;
+  while (tiles * splits < target && ng / (splits * 2) >= 2) splits *= 2;
+  if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ng + splits - 1) / splits;
   p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
   return p;
@@ -340,19 +351,15 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
 size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
   const W4A8Plan p = w4a8_plan(M, N, K, group_size);
   if (p.splits == 1) return 0;
-  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
-                     kCounterBytesAlign * kCounterBytesAlign;
-  return cnt + (size_t)p.splits * M * N * sizeof(int32_t);
+  return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(int32_t);
 }
 
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
                             const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
                             int group_size, hipStream_t stream) {
   const W4A8Plan p = w4a8_plan(M, N, K, group_size);
-  const size_t cnt = ((size_t)p.tiles_m * p.tiles_n * sizeof(unsigned) + kCounterBytesAlign - 1) /
-                     kCounterBytesAlign * kCounterBytesAlign;
   unsigned* counters = (unsigned*)ws;
-  int32_t* partials = ws ? (int32_t*)((char*)ws + cnt) : nullptr;
+  int32_t* partials = ws ? (int32_t*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int blocks = p.tiles_m * p.tiles_n * p.splits;
   const dim3 grid(blocks), block(kWThreads);
   const uint32_t* qw = (const uint32_t*)qweight;
