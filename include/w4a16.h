@@ -22,12 +22,17 @@
  *   X        fp16  [M, K]
  *   Y        fp16  [M, N]
  *   W        fp16  [N, K]            (out, in)
- *   qweight  int32 [N, K/8]          packed along K, plain nibble order: element k = 8j+i
- *                                    of row n sits in bits 4i..4i+3 of word (n, j)
+ *   qweight  int32 [ceil(N/16), K/128, 4, 16, 4]
+ *                                    codes packed along K in plain nibble order (element
+ *                                    k = 8j+i of row n in bits 4i..4i+3 of that row's word j),
+ *                                    words stored tiled: word j of row n sits at
+ *                                    [n/16][j/16][(j%16)/4][n%16][j%4], i.e. 1 KB blocks of
+ *                                    16 rows x 128 k; rows past N are padding (code 0)
  *   scales   fp16  [K/G, N]          per-group scales, group-major
  *   qzeros   int32 [K/G, ceil(N/8)]  4-bit zero points packed along N, plain nibble
  *                                    order, pad nibbles 0
- *   (W4A8)   qweight int32 [N, K/8] of biased nibbles q + 8 (q in [-8, 7]),
+ *   (W4A8)   qweight int32 [ceil(N/16), K/128, 4, 16, 4] (same tiling) of biased nibbles
+ *            q + 8 (q in [-8, 7]; padding rows q = 0),
  *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
  *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
  *
@@ -107,7 +112,8 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
  * group_size == 128: two-level, cscale = fp16(max(max|w|/127, 1e-5)),
  *   w8 = clamp(rint(w / cscale), -127, 127), per group s_g = min(max(1, ceil(max|w8|/7)), 18),
  *   q = clamp(rint(w8 / s_g), -7, 7); gscale int8 [K/G, N] receives s_g.
- * qweight receives q + 8 in the plain nibble order.  fp32 decisions; bit-exact.
+ * qweight receives q + 8 (plain nibble order, tiled word layout above).  fp32 decisions;
+ * bit-exact.
  */
 int w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale,
               int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);

@@ -35,8 +35,12 @@ Readings where the pages are silent (each one is listed in the design doc):
   rounding when exported as fp16).
 * R4 packing is the plain nibble order: element ``8*j + i`` of a packed axis
   lives in bits ``4*i .. 4*i+3`` of word ``j``; pad nibbles are 0.
-  Layouts: ``qweight`` int32 [N, K/8] (packed along K), ``scales`` fp16
-  [K/G, N], ``qzeros`` int32 [K/G, ceil(N/8)] (packed along N).
+  Layouts: the codes of row n form words ``j = 0 .. K/8-1`` (packed along K);
+  ``qweight`` stores these words tiled as int32 [ceil(N/16), K/128, 4, 16, 4]:
+  word j of row n sits at ``[n // 16, j // 16, (j % 16) // 4, n % 16, j % 4]``
+  (one 1 KB block holds 16 rows x 128 k; rows past N are padding with code 0,
+  or q = 0 for W4A8).  ``scales`` fp16 [K/G, N]; ``qzeros`` int32
+  [K/G, ceil(N/8)] (zero points packed along N).
 * R5 W4A8 weights (the pages print no constants): per-channel (group -1)
   ``s_c = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s_c), -8, 7)``;
   two-level g128: ``s_c = fp16(max(max|w| / 127, 1e-5))``,
@@ -62,7 +66,7 @@ F32 = np.float32
 F64 = np.float64
 
 __all__ = [
-    "pack_nibbles", "unpack_nibbles",
+    "pack_nibbles", "unpack_nibbles", "tile_words", "untile_words",
     "quantize_asym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref",
@@ -110,6 +114,43 @@ def unpack_nibbles(words: np.ndarray, C: int) -> np.ndarray:
     return out[:, :C]
 
 
+def tile_words(words: np.ndarray, pad_word: int = 0) -> np.ndarray:
+    """Row-major code words [N, K/8] -> the tiled qweight [ceil(N/16), K/128, 4, 16, 4]
+    (R4): word j of row n goes to ``[n // 16, j // 16, (j % 16) // 4, n % 16, j % 4]``.
+    Rows past N are filled with ``pad_word``."""
+    words = np.asarray(words)
+    if words.dtype != np.int32 or words.ndim != 2:
+        raise ValueError("words must be 2-D int32")
+    N, W = words.shape
+    if W % 16:
+        raise ValueError("K must be a multiple of 128")
+    Np = -(-N // 16) * 16
+    full = np.full((Np, W), np.uint32(pad_word & 0xFFFFFFFF).view(np.int32), dtype=np.int32)
+    full[:N] = words
+    out = np.empty((Np // 16, W // 16, 4, 16, 4), dtype=np.int32)
+    for n in range(16):
+        for slot in range(4):
+            for w in range(4):
+                out[:, :, slot, n, w] = full[n::16, slot * 4 + w::16]
+    return out
+
+
+def untile_words(tiled: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of :func:`tile_words`: tiled qweight -> row-major words [N, K/8]."""
+    tiled = np.asarray(tiled)
+    if tiled.dtype != np.int32 or tiled.ndim != 5 or tiled.shape[2:] != (4, 16, 4):
+        raise ValueError("tiled qweight must be int32 [N/16, K/128, 4, 16, 4]")
+    T, G = tiled.shape[:2]
+    if N > 16 * T:
+        raise ValueError("N larger than the tiled capacity")
+    full = np.empty((16 * T, 16 * G), dtype=np.int32)
+    for n in range(16):
+        for slot in range(4):
+            for w in range(4):
+                full[n::16, slot * 4 + w::16] = tiled[:, :, slot, n, w]
+    return full[:N]
+
+
 # --------------------------------------------------------------------------
 # W4A16 asymmetric quantization (R1, R2).  [AWQ-fixes], opening comment.
 # --------------------------------------------------------------------------
@@ -142,13 +183,13 @@ def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
     """Natural-orientation quantized weights -> the packed layout of R4.
 
     ``codes`` uint8 [N, K], ``scales`` fp16 [N, K/G], ``zeros`` uint8 [N, K/G]
-    -> ``(qweight int32 [N, K/8], scales fp16 [K/G, N], qzeros int32
-    [K/G, ceil(N/8)])``.
+    -> ``(qweight int32 [ceil(N/16), K/128, 4, 16, 4], scales fp16 [K/G, N],
+    qzeros int32 [K/G, ceil(N/8)])``.
     """
     N, K = codes.shape
-    if K % 8:
-        raise ValueError("K must be a multiple of 8")
-    qweight = pack_nibbles(codes)
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    qweight = tile_words(pack_nibbles(codes))
     scales_gn = np.ascontiguousarray(np.asarray(scales, dtype=F16).T)
     qzeros = pack_nibbles(np.ascontiguousarray(np.asarray(zeros).T))
     return qweight, scales_gn, qzeros
@@ -156,8 +197,8 @@ def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
 
 def unpack_awq(qweight: np.ndarray, scales_gn: np.ndarray, qzeros: np.ndarray, K: int):
     """Packed layout -> ``(codes [N, K], scales fp16 [N, K/G], zeros [N, K/G])``."""
-    N = qweight.shape[0]
-    codes = unpack_nibbles(qweight, K)
+    N = scales_gn.shape[1]
+    codes = unpack_nibbles(untile_words(qweight, N), K)
     scales = np.ascontiguousarray(scales_gn.T)
     zeros = np.ascontiguousarray(unpack_nibbles(qzeros, N).T)
     return codes, scales, zeros
@@ -171,7 +212,7 @@ def dequant_awq(qweight, scales_gn, qzeros, K: int, group_size: int = 128) -> np
     """
     codes, scales, zeros = unpack_awq(qweight, scales_gn, qzeros, K)
     G = int(group_size)
-    N = codes.shape[0]
+    N = codes.shape[0]  # the number of real rows (scales_gn.shape[1])
     s = np.repeat(scales.astype(F64), G, axis=1)
     z = np.repeat(zeros.astype(F64), G, axis=1)
     assert s.shape == (N, K)
@@ -234,16 +275,16 @@ def quantize_w4a8(w16: np.ndarray, group_size: int = -1):
 
 
 def pack_w4a8(q: np.ndarray, cscale: np.ndarray, gscale):
-    """-> ``(qweight int32 [N, K/8] of biased nibbles q+8, cscale fp16 [N],
-    gscale int8 [K/G, N] or None)``."""
-    qweight = pack_nibbles(np.asarray(q, dtype=np.int64) + 8)
+    """-> ``(qweight int32 [ceil(N/16), K/128, 4, 16, 4] of biased nibbles q+8 (pad
+    rows q = 0), cscale fp16 [N], gscale int8 [K/G, N] or None)``."""
+    qweight = tile_words(pack_nibbles(np.asarray(q, dtype=np.int64) + 8), pad_word=0x88888888)
     gs = None if gscale is None else np.ascontiguousarray(np.asarray(gscale, dtype=np.int8).T)
     return qweight, np.asarray(cscale, dtype=F16), gs
 
 
-def unpack_w4a8(qweight: np.ndarray, K: int) -> np.ndarray:
-    """Biased-nibble words -> signed int4 values [N, K] (int64)."""
-    return unpack_nibbles(qweight, K).astype(np.int64) - 8
+def unpack_w4a8(qweight: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Tiled biased-nibble words -> signed int4 values [N, K] (int64)."""
+    return unpack_nibbles(untile_words(qweight, N), K).astype(np.int64) - 8
 
 
 def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):

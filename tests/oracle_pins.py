@@ -60,6 +60,28 @@ def pin_pack_bijection(ora):
     assert np.all((w2.view(np.uint32)[:, 2] >> 20) == 0)  # 3 pad nibbles are zero
 
 
+def pin_tile_layout(ora):
+    """Tiled word order: a single code placed at (n, k) lands in exactly one word of
+    the flat qweight, at the offset computed by hand from the layout rule
+    ((n/16 * K/128 + k/128) * 4 + (k % 128)/32) * 64 + (n % 16) * 4 + (k % 32)/8,
+    nibble k % 8; tile/untile are inverse bijections; pad rows carry the pad word."""
+    N, K = 37, 256
+    for (n, k, c) in ((17, 200, 9), (0, 0, 15), (36, 255, 1), (15, 127, 6), (16, 128, 3)):
+        codes = np.zeros((N, K), np.uint8)
+        codes[n, k] = c
+        flat = ora.tile_words(ora.pack_nibbles(codes)).reshape(-1).view(np.uint32)
+        off = ((n // 16 * (K // 128) + k // 128) * 4 + (k % 128) // 32) * 64 + (n % 16) * 4 + (k % 32) // 8
+        assert flat.size == 48 * K // 8
+        assert int(flat[off]) == c << (4 * (k % 8)), (n, k)
+        assert np.count_nonzero(flat) == 1
+    rng = _rng(5)
+    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    t = ora.tile_words(words, pad_word=0x88888888)
+    assert t.shape == (3, 2, 4, 16, 4)
+    assert np.array_equal(ora.untile_words(t, N), words)
+    assert np.all(ora.untile_words(t, 48)[N:].view(np.uint32) == 0x88888888)
+
+
 # ------------------------------------------------------- asymmetric rule
 def pin_asym_worked(ora):
     """Hand-worked groups (tests/golden/asym_g128_worked.txt)."""
@@ -289,7 +311,7 @@ def pin_w4a8_acc_bruteforce(ora):
         w = synth.make_linear(0, N, K, seed=13, outliers=True).w.numpy()
         q, cs, gs = ora.quantize_w4a8(w, group)
         qw, cs2, gs_gn = ora.pack_w4a8(q, cs, gs)
-        qq = ora.unpack_w4a8(qw, K)
+        qq = ora.unpack_w4a8(qw, N, K)
         assert np.array_equal(qq, q.astype(np.int64))
         acc = ora.w4a8_acc_ref(xq.astype(np.int8), qq, gs, G)
         for m in range(M):
@@ -307,7 +329,7 @@ def pin_w4a8_acc_bruteforce(ora):
 
 
 ALL_PINS = [
-    pin_pack_words, pin_pack_bijection,
+    pin_pack_words, pin_pack_bijection, pin_tile_layout,
     pin_asym_worked, pin_asym_constructed, pin_asym_roundtrip_bound,
     pin_fraction_bruteforce, pin_identity_probe, pin_per_channel_special_case,
     pin_constructed_exact_gemm,

@@ -55,8 +55,8 @@ FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 64, None), 2, "group_size"),
     ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 128, None), 1, "aligned"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 1 << 31, 128, None), 2, "2^30"),
-    # a shape that splits K needs a workspace
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 16, 5120, 5120, 128, None), 3, "workspace"),
+    # a narrow-N shape splits K and needs a workspace
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, 256, 5120, 128, None), 3, "workspace"),
 ])
 def test_awq_gemm_validation(lib, args, code, msg):
     P = ctypes.c_void_p
@@ -89,7 +89,7 @@ def test_w4a8_validation(lib):
 
 def test_workspace_sizes(lib):
     # decode shapes split K; prefill shapes do not; invalid shapes report 0
-    assert lib.awq_gemm_workspace_bytes(16, 5120, 5120, 128) > 0
+    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 128) > 0
     assert lib.awq_gemm_workspace_bytes(4096, 27648, 5120, 128) == 0
     assert lib.awq_gemm_workspace_bytes(16, 5120, 200, 128) == 0
     assert lib.w4a8_gemm_workspace_bytes(1, 13824, 5120, -1) > 0

@@ -145,3 +145,37 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
     err = normalized_error(yg, ref["y"], np.linalg.norm(x.numpy()[ms].astype(np.float64), axis=1),
                            np.linalg.norm(ref["w_deq"], axis=1))
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("tiles", ["1", "2", "4"])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (33, 96, 768), (64, 300, 640)])
+def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
+    """Each tile width / prefetch-depth variant of the M <= 64 kernel (forced through its
+    tuning variable), against the oracle."""
+    dev = device()
+    monkeypatch.setenv("W4_SKINNY_TILES", tiles)
+    announce(f"skinny tiles={tiles} M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N + int(tiles), outliers=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz)).astype(np.float64)
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("shape", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048)])
+def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
+    """Each tile shape of the M > 64 MFMA GEMM (forced through its tuning variable;
+    128x256, 128x128, 64x256, 64x128), with ragged M and N, against the oracle."""
+    dev = device()
+    monkeypatch.setenv("W4_GEMM_SHAPE", shape)
+    announce(f"gemm shape={shape} M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N + int(shape), outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz)).astype(np.float64)
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err

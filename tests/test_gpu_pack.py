@@ -64,7 +64,7 @@ def test_awq_pack_bit_exact_full_shapes(shape):
     rows = sample_idx(N, 192, seed=N, must=range(0, 16))
     codes, scales, zeros = ora.quantize_asym(w.numpy()[rows], 128)
     rqw, _, _ = ora.pack_awq(codes, scales, zeros)
-    assert np.array_equal(to_np(qw)[rows], rqw)
+    assert np.array_equal(ora.untile_words(to_np(qw), N)[rows], ora.untile_words(rqw, len(rows)))
     assert np.array_equal(to_np(sc)[:, rows].view(np.uint16), np.ascontiguousarray(scales.T).view(np.uint16))
     g_codes, _, g_zeros = ora.unpack_awq(to_np(qw), to_np(sc), to_np(qz), K)
     assert np.array_equal(g_zeros[rows], zeros)
@@ -81,7 +81,9 @@ def test_w4a8_pack_bit_exact(group, N, K):
     rows = sample_idx(N, 256, seed=1) if N > 256 else np.arange(N)
     q, rcs, rgs = ora.quantize_w4a8(w.numpy()[rows], group)
     rqw, rcs2, rgs_gn = ora.pack_w4a8(q, rcs, rgs)
-    assert np.array_equal(to_np(qw)[rows], rqw)
+    assert np.array_equal(ora.untile_words(to_np(qw), N)[rows], ora.untile_words(rqw, len(rows)))
+    if N <= 256:
+        assert np.array_equal(to_np(qw), rqw)  # whole tiled array, padding rows included
     assert np.array_equal(to_np(cs)[rows].view(np.uint16), rcs2.view(np.uint16))
     if group == -1:
         assert gs is None
@@ -99,7 +101,7 @@ def test_w4a8_pack_golden_rows():
         w = np.tile(row[None, :], (8, 1))
         qw, gs, cs = w4.w4a8_pack(torch.from_numpy(w).to(dev), c["group"])
         torch.cuda.synchronize()
-        q = ora.unpack_w4a8(to_np(qw), K)
+        q = ora.unpack_w4a8(to_np(qw), 8, K)
         assert to_np(cs)[0].view(np.uint16) == c["cscale"].view(np.uint16)
         if c["group"] == -1:
             assert q[0, :len(c["q"])].tolist() == c["q"]

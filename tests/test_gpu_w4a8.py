@@ -80,7 +80,7 @@ def test_w4a8_gemm_small(group, M, N, K):
     q, cs, gs, (qw, gsd, csd) = _oracle_w4a8(inp.w.numpy(), group, dev)
     xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
     xqd, sad = torch.from_numpy(xq).to(dev), torch.from_numpy(sa).to(dev)
-    acc = to_np(w4.w4a8_gemm_i32(xqd, qw, gsd, group))
+    acc = to_np(w4.w4a8_gemm_i32(xqd, qw, gsd, group, N=N))
     racc = ora.w4a8_acc_ref(xq, q, gs, 128)
     assert np.abs(racc).max() < 2**31
     assert np.array_equal(acc.astype(np.int64), racc)
@@ -107,7 +107,7 @@ def test_w4a8_full_size_sampled(group, M):
     xq, sa = w4.w4a8_quant_act(inp.x.to(dev), inp.gamma.to(dev))
     y = w4.w4a8_gemm(xq, sa, qw, gs, cs, group)
     rxq, rsa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
-    acc = w4.w4a8_gemm_i32(torch.from_numpy(rxq).to(dev), qw, gs, group)
+    acc = w4.w4a8_gemm_i32(torch.from_numpy(rxq).to(dev), qw, gs, group, N=N)
     torch.cuda.synchronize()
     ms = sample_idx(M, 48, seed=M)
     ns = sample_idx(N, 256, seed=7, must=range(0, 32))

@@ -21,6 +21,8 @@ MUTANTS = [
     ("dequant drops zero", "(codes.astype(F64) - z) * s", "codes.astype(F64) * s"),
     ("pack nibble order reversed", "words += padded[:, i::8] << (4 * i)", "words += padded[:, i::8] << (4 * (7 - i))"),
     ("unpack nibble order reversed", "out[:, i::8] = (u >> (4 * i)) & 0xF", "out[:, i::8] = (u >> (4 * (7 - i))) & 0xF"),
+    ("tile rows and slots swapped", "out[:, :, slot, n, w] = full[n::16, slot * 4 + w::16]", "out[:, :, slot, n, w] = full[n::16, (w * 4 + slot)::16]"),
+    ("untile rows and slots swapped", "full[n::16, slot * 4 + w::16] = tiled[:, :, slot, n, w]", "full[n::16, (w * 4 + slot)::16] = tiled[:, :, slot, n, w]"),
     ("scales not transposed", "scales = np.ascontiguousarray(scales_gn.T)", "scales = np.ascontiguousarray(scales_gn).reshape(scales_gn.shape[::-1])"),
     ("group index off by one", "s = np.repeat(scales.astype(F64), G, axis=1)", "s = np.roll(np.repeat(scales.astype(F64), G, axis=1), 1, axis=1)"),
     ("matmul transposed operand", "np.asarray(w_deq, dtype=F64).T", "np.asarray(w_deq, dtype=F64).T[::-1]"),

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     bind_w4a8_gemm,
     bind_w4a8_quant_act,
     lib_path,
+    qweight_shape,
     load,
     w4a8_gemm,
     w4a8_gemm_i32,

@@ -117,14 +117,27 @@ def _workspace(dev, nbytes: int):
     return buf, buf.numel()
 
 
+def qweight_shape(N: int, K: int):
+    """Shape of the tiled packed weights: int32 [ceil(N/16), K/128, 4, 16, 4] -- 1 KB
+    blocks of 16 rows x 128 k; word j of row n at [n//16, j//16, (j%16)//4, n%16, j%4]."""
+    return ((N + 15) // 16, K // 128, 4, 16, 4)
+
+
+def _need_qweight(qweight, N, K, dev):
+    _need(qweight, "qweight", torch.int32, 5, dev)
+    if tuple(qweight.shape) != qweight_shape(N, K):
+        raise ValueError(f"qweight shape {tuple(qweight.shape)} != {qweight_shape(N, K)} for N={N}, K={K}")
+
+
 # ------------------------------------------------------------------ W4A16
 def awq_pack(w: torch.Tensor, group_size: int = 128):
-    """fp16 W [N, K] -> (qweight int32 [N, K/8], scales fp16 [K/G, N], qzeros int32 [K/G, ceil(N/8)])."""
+    """fp16 W [N, K] -> (qweight int32 [ceil(N/16), K/128, 4, 16, 4], scales fp16 [K/G, N],
+    qzeros int32 [K/G, ceil(N/8)])."""
     _need(w, "w", torch.float16, 2)
     N, K = w.shape
     dev = w.device
     G = group_size if group_size > 0 else K
-    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
     scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
     qzeros = torch.empty((K // G, (N + 7) // 8), dtype=torch.int32, device=dev)
     with torch.cuda.device(dev):
@@ -135,11 +148,11 @@ def awq_pack(w: torch.Tensor, group_size: int = 128):
 
 def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):
     """Packed weights -> fp16 W_deq [N, K] = fp16((q - z) * s)."""
-    _need(qweight, "qweight", torch.int32, 2)
-    dev = qweight.device
-    _need(scales, "scales", torch.float16, 2, dev)
+    _need(scales, "scales", torch.float16, 2)
+    dev = scales.device
     _need(qzeros, "qzeros", torch.int32, 2, dev)
-    N, K = qweight.shape[0], qweight.shape[1] * 8
+    N, K = scales.shape[1], scales.shape[0] * group_size
+    _need_qweight(qweight, N, K, dev)
     out = torch.empty((N, K), dtype=torch.float16, device=dev)
     with torch.cuda.device(dev):
         _check("awq_unpack_dequant", load().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out),
@@ -155,13 +168,11 @@ def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, worksp
     """Y [M, N] = X [M, K] . dequant(W)^T  (fp16 in, fp16 out, fp32 accumulate)."""
     _need(x, "x", torch.float16, 2)
     dev = x.device
-    _need(qweight, "qweight", torch.int32, 2, dev)
     _need(scales, "scales", torch.float16, 2, dev)
     _need(qzeros, "qzeros", torch.int32, 2, dev)
     M, K = x.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 8 != K:
-        raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
+    N = scales.shape[1]
+    _need_qweight(qweight, N, K, dev)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
     else:
@@ -181,11 +192,12 @@ def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, worksp
 
 # ------------------------------------------------------------------- W4A8
 def w4a8_pack(w: torch.Tensor, group_size: int = -1):
-    """fp16 W [N, K] -> (qweight int32 [N, K/8] biased nibbles, gscale int8 [K/G, N] or None, cscale fp16 [N])."""
+    """fp16 W [N, K] -> (qweight int32 [ceil(N/16), K/128, 4, 16, 4] of biased nibbles,
+    gscale int8 [K/G, N] or None, cscale fp16 [N])."""
     _need(w, "w", torch.float16, 2)
     N, K = w.shape
     dev = w.device
-    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
     cscale = torch.empty((N,), dtype=torch.float16, device=dev)
     gscale = torch.empty((K // group_size, N), dtype=torch.int8, device=dev) if group_size > 0 else None
     with torch.cuda.device(dev):
@@ -213,24 +225,21 @@ def w4a8_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = -1) -> i
     return int(load().w4a8_gemm_workspace_bytes(M, N, K, group_size))
 
 
-def _w4a8_args(xq, qweight, gscale, group_size):
+def _w4a8_args(xq, qweight, gscale, group_size, N):
     _need(xq, "xq", torch.int8, 2)
     dev = xq.device
-    _need(qweight, "qweight", torch.int32, 2, dev)
     if gscale is not None:
         _need(gscale, "gscale", torch.int8, 2, dev)
     M, K = xq.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 8 != K:
-        raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
+    _need_qweight(qweight, N, K, dev)
     return dev, M, N, K
 
 
 def w4a8_gemm(xq, s_a, qweight, gscale, cscale, group_size: int = -1, out=None):
     """Y [M, N] = fp16(acc * s_a[m] * cscale[n]), acc the exact int32 sum of xq * q * s_g."""
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+    _need(cscale, "cscale", torch.float16, 1)
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
     _need(s_a, "s_a", torch.float32, 1, dev)
-    _need(cscale, "cscale", torch.float16, 1, dev)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
     lib = load()
@@ -241,9 +250,12 @@ def w4a8_gemm(xq, s_a, qweight, gscale, cscale, group_size: int = -1, out=None):
     return out
 
 
-def w4a8_gemm_i32(xq, qweight, gscale, group_size: int = -1):
-    """Raw int32 accumulators acc [M, N] of w4a8_gemm."""
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+def w4a8_gemm_i32(xq, qweight, gscale, group_size: int = -1, N: int | None = None):
+    """Raw int32 accumulators acc [M, N] of w4a8_gemm (N defaults to 16 * qweight.shape[0];
+    give it when N is not a multiple of 16)."""
+    if N is None:
+        N = 16 * qweight.shape[0]
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, N)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev)
     lib = load()
     with torch.cuda.device(dev):
@@ -259,13 +271,13 @@ def bind_awq_gemm(x, qweight, scales, qzeros, out, group_size: int = 128):
     stream capture).  The workspace is allocated here, not at call time."""
     _need(x, "x", torch.float16, 2)
     dev = x.device
-    _need(qweight, "qweight", torch.int32, 2, dev)
     _need(scales, "scales", torch.float16, 2, dev)
     _need(qzeros, "qzeros", torch.int32, 2, dev)
     _need(out, "out", torch.float16, 2, dev)
     M, K = x.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 8 != K or tuple(out.shape) != (M, N):
+    N = scales.shape[1]
+    _need_qweight(qweight, N, K, dev)
+    if tuple(out.shape) != (M, N):
         raise ValueError("inconsistent shapes")
     lib = load()
     with torch.cuda.device(dev):
@@ -285,9 +297,9 @@ def bind_awq_gemm(x, qweight, scales, qzeros, out, group_size: int = 128):
 
 def bind_w4a8_gemm(xq, s_a, qweight, gscale, cscale, out, group_size: int = -1):
     """As bind_awq_gemm, for w4a8_gemm."""
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size)
+    _need(cscale, "cscale", torch.float16, 1)
+    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
     _need(s_a, "s_a", torch.float32, 1, dev)
-    _need(cscale, "cscale", torch.float16, 1, dev)
     _need(out, "out", torch.float16, 2, dev)
     lib = load()
     with torch.cuda.device(dev):

@@ -41,6 +41,17 @@ __device__ __forceinline__ int16_t_ mfma32_i8(int4_t a, int4_t b, int16_t_ c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// ----------------------------------------------------- tiled weight layout
+// Packed weights are stored in 1 KB blocks of 16 rows x 128 k (one group): block
+// (n / 16, g) holds, for slot = 0..3 (32 k each) and row r = n % 16, the four words
+// 4 slot .. 4 slot + 3 of that row's group at word offset 64 slot + 4 r.  The array is
+// int32 [ceil(N/16), K/128, 4, 16, 4]; one wave reading lane l -> chunk l reads a
+// contiguous 1 KB block (rows l % 16, slot l / 16).  Returns the word offset of the
+// 16-byte chunk (row n, group g, slot); ng = K / 128.
+__device__ __forceinline__ int64_t tiled_chunk(int n, int g, int slot, int ng) {
+  return ((int64_t)((n >> 4) * ng + g) * 4 + slot) * 64 + (n & 15) * 4;
+}
+
 // ------------------------------------------------------ nibble unpacking
 // One packed word holds 8 consecutive elements e_0..e_7 (e_i in bits 4i..4i+3).
 // unpack_1024: four registers of packed fp16 pairs (1024 + e_{2p}, 1024 + e_{2p+1}),
@@ -48,13 +59,23 @@ __device__ __forceinline__ int16_t_ mfma32_i8(int4_t a, int4_t b, int16_t_ c) {
 // 0x6400 is fp16 1024.0; a code c in the low mantissa bits gives 1024 + c exactly.
 // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7 of the
 // first, 0x0c gives 0.
+// (x & mask) | bits in one v_and_or_b32.  VOP3 encodings on gfx9 take no literal
+// constants, so the two constants are passed in registers (the plain C expression
+// compiles to a separate v_and_b32 and v_or_b32, each with a literal).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
+  return r;
+}
+
 __device__ __forceinline__ half8_t unpack_1024(uint32_t w) {
   const uint32_t s = w >> 4;
+  const uint32_t mask = 0x000f000fu, magic = 0x64006400u;
   u32x4 r;
-  r[0] = (__builtin_amdgcn_perm(s, w, 0x0c040c00u) & 0x000f000fu) | 0x64006400u;
-  r[1] = (__builtin_amdgcn_perm(s, w, 0x0c050c01u) & 0x000f000fu) | 0x64006400u;
-  r[2] = (__builtin_amdgcn_perm(s, w, 0x0c060c02u) & 0x000f000fu) | 0x64006400u;
-  r[3] = (__builtin_amdgcn_perm(s, w, 0x0c070c03u) & 0x000f000fu) | 0x64006400u;
+  r[0] = and_or(__builtin_amdgcn_perm(s, w, 0x0c040c00u), mask, magic);
+  r[1] = and_or(__builtin_amdgcn_perm(s, w, 0x0c050c01u), mask, magic);
+  r[2] = and_or(__builtin_amdgcn_perm(s, w, 0x0c060c02u), mask, magic);
+  r[3] = and_or(__builtin_amdgcn_perm(s, w, 0x0c070c03u), mask, magic);
   return __builtin_bit_cast(half8_t, r);
 }
 

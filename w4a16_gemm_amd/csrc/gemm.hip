@@ -9,33 +9,37 @@
 // MFMA does the FP16 work; the dequantization (9 VALU ops to expand a word, 8 packed
 // fp16 ops for (q - z) * s) is amortized over the 128 rows of a wave tile.
 //
-// Tile: BM x BN x BK = 128 x 256 x 64, 256 threads.  The 4 waves split N: wave w owns
-// columns [64 w, 64 w + 64) as two 32-column MFMA fragments, and all 128 rows as four
-// 32-row fragments (acc = 4 x 2 x 16 fp32 per lane).  Each weight code is therefore
-// dequantized exactly once per workgroup.  Per BK step a lane loads one 16-byte chunk
+// Tile: BM x BN x BK = (32 MI) x (128 NF) x 64, 256 threads, (MI, NF) in {4, 2} x {2, 1}.
+// The 4 waves split N: wave w owns 32 NF columns as NF 32-column MFMA fragments, and
+// all BM rows as MI 32-row fragments (acc = MI x NF x 16 fp32 per lane).  Each weight
+// code is therefore dequantized exactly once per workgroup.  Per BK step a lane loads one 16-byte chunk
 // (4 words = 32 codes) per fragment: lane l (column l % 32, K-slot h = l / 32) takes
-// words 4h..4h+3 of the 8 words of its row in this BK step, and k16-step s uses word
-// s.  The X fragment for k16-step s is read from LDS with the same K-slot assignment
+// words 4h..4h+3 of the 8 words of its row in this BK step (slot 2 (kt % 2) + h of the
+// tiled layout: 16 lanes read 256 contiguous bytes), and k16-step s uses word s.  The X fragment for k16-step s is read from LDS with the same K-slot assignment
 // (row l % 32, elements k = 8 (4h + s) .. + 7).  X rows live in LDS as 128-byte rows
 // of 8 16-byte chunks, chunk c of row r stored at position c ^ (r % 8) so that the
 // 32 rows read by one instruction hit distinct banks.
 //
 // Workgroups are remapped so that the tiles one XCD runs at a time form compact
-// groups of 8 M-tiles (they share weight columns in that XCD's L2).  Split-K over BK
-// steps is used when there are too few tiles to fill the 256 CUs; partials are summed
-// by the last arriving workgroup in split order (deterministic).
+// groups of 8 M-tiles (they share weight columns in that XCD's L2).  Smaller tiles are
+// chosen before split-K when M or N is small; split-K over BK steps remains for grids
+// that are still too small, with partials summed by the last arriving workgroup in
+// split order (deterministic).
 #include "kernels.hpp"
 
 namespace w4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+// Tile BM x BN = (32 MI) x (128 NF): wave w owns columns [32 NF w, 32 NF (w + 1)) as NF
+// 32-column fragments and all BM rows as MI 32-row fragments.
+template <int MI, int NF>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restrict__ x,
                                                             const uint32_t* __restrict__ qweight,
                                                             const half_t* __restrict__ scales,
@@ -43,7 +47,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
                                                             half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                             float* __restrict__ partials, int M, int N, int K,
                                                             int tiles_m, int tiles_n, int splits, int kps) {
-  __shared__ u32x4 lds[2][BM * 8];  // 2 x 16 KB
+  constexpr int BM = 32 * MI, BN = 128 * NF;
+  constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
+  __shared__ u32x4 lds[2][BM * 8];
 
   const int total = tiles_m * tiles_n * splits;
   const int id = xcd_remap(blockIdx.x, total);
@@ -64,35 +70,37 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   const int kend = min(ktiles, kbeg + kps);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int wpr = K / 8;
   const int nzw = (N + 7) / 8;
+  const int ng = K / 128;
 
-  int nrow[2];
-  bool nok[2];
+  int nrow[NF], nclamp[NF];
+  bool nok[NF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    nrow[f] = n0 + wave * 64 + f * 32 + col;
+  for (int f = 0; f < NF; ++f) {
+    nrow[f] = n0 + wave * 32 * NF + f * 32 + col;
     nok[f] = nrow[f] < N;
+    // columns past N read a clamped valid row; their outputs are never stored
+    nclamp[f] = min(nrow[f], N - 1);
   }
 
-  float16_t acc[4][2];
+  float16_t acc[MI][NF];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  // global -> register staging of one X tile: 1024 chunks, 4 per thread.  Loads are
-  // branch-free (rows past M read a clamped valid row, zeroed before the LDS store) so
-  // they issue back to back.
-  u32x4 areg[4];
+  // global -> register staging of one X tile (BM x 64 halves).  Loads are branch-free
+  // so they issue back to back: rows past M read a clamped valid row (it only reaches
+  // output rows that are never stored).
+  u32x4 areg[kAPer];
   auto load_a = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAPer; ++i) {
       const int cid = threadIdx.x + i * kThreads;
       const int r = cid >> 3, c = cid & 7;
       const int m = min(m0 + r, M - 1);
@@ -101,142 +109,162 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAPer; ++i) {
       const int cid = threadIdx.x + i * kThreads;
-      const int r = cid >> 3, c = cid & 7;
-      lds[buf][swz(r, c)] = (m0 + r < M) ? areg[i] : u32x4{0u, 0u, 0u, 0u};
+      lds[buf][swz(cid >> 3, cid & 7)] = areg[i];
     }
   };
-  // Columns past N read a clamped valid row; their outputs are never stored.
-  int nclamp[2];
+  u32x4 breg[NF];
+  auto load_b = [&](int kt, u32x4 (&dst)[NF]) {
+    // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
 #pragma unroll
-  for (int f = 0; f < 2; ++f) nclamp[f] = min(nrow[f], N - 1);
-  u32x4 breg[2];
-  auto load_b = [&](int kt, u32x4 (&dst)[2]) {
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-      dst[f] = *reinterpret_cast<const u32x4*>(qweight + (int64_t)nclamp[f] * wpr + kt * 8 + h * 4);
+    for (int f = 0; f < NF; ++f)
+      dst[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
   };
   // Scale and zero point of this lane's rows for one 128-group: the raw words are
   // prefetched one BK step ahead together with the codes, then converted to the packed
   // fp16 pairs -(1024 + z) and s used by dequant8.
-  uint32_t zraw[2];
-  half_t sraw[2];
-  auto load_sz = [&](int g, uint32_t (&zr)[2], half_t (&sr)[2]) {
+  uint32_t zraw[NF];
+  half_t sraw[NF];
+  auto load_sz = [&](int g) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      zr[f] = qzeros[(int64_t)g * nzw + (nclamp[f] >> 3)];
-      sr[f] = scales[(int64_t)g * N + nclamp[f]];
+    for (int f = 0; f < NF; ++f) {
+      zraw[f] = qzeros[(int64_t)g * nzw + (nclamp[f] >> 3)];
+      sraw[f] = scales[(int64_t)g * N + nclamp[f]];
     }
   };
-  half2_t negz2[2], s2[2];
-  auto set_sz = [&](const uint32_t (&zr)[2], const half_t (&sr)[2]) {
+  half2_t negz2[NF], s2[NF];
+  auto set_sz = [&]() {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const uint32_t z = (zr[f] >> (4 * (nclamp[f] & 7))) & 15u;
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t z = (zraw[f] >> (4 * (nclamp[f] & 7))) & 15u;
       negz2[f] = splat2(-(half_t)(1024u + z));
-      s2[f] = splat2(sr[f]);
+      s2[f] = splat2(sraw[f]);
     }
   };
 
   if (kbeg < kend) {
     load_a(kbeg);
     load_b(kbeg, breg);
-    load_sz(kbeg >> 1, zraw, sraw);  // 2 BK steps per 128-group
+    load_sz(kbeg >> 1);  // 2 BK steps per 128-group
     store_a(0);
-    set_sz(zraw, sraw);
+    set_sz();
   }
   __syncthreads();
 
+  // The next step's loads are issued unconditionally (clamped to the last step on the
+  // final iteration) so that no load sits in a conditional block and the waits before
+  // the MFMAs cover only what they consume.
   for (int kt = kbeg; kt < kend; ++kt) {
     const int buf = (kt - kbeg) & 1;
-    const bool more = kt + 1 < kend;
+    const int kn = min(kt + 1, kend - 1);
     const bool new_group = ((kt + 1) & 1) == 0;
-    u32x4 bnext[2];
-    if (more) {
-      load_a(kt + 1);
-      load_b(kt + 1, bnext);
-      if (new_group) load_sz((kt + 1) >> 1, zraw, sraw);
-    }
+    u32x4 bnext[NF];
+    load_a(kn);
+    load_b(kn, bnext);
+    load_sz(kn >> 1);
+    // keep these loads here, ahead of the MFMAs (the scheduler would otherwise sink them
+    // next to their use at the end of the step and expose the full memory latency)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8_t bf[2];
+      half8_t bf[NF];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) bf[f] = dequant8(breg[f][s], negz2[f], s2[f]);
+      for (int f = 0; f < NF; ++f) bf[f] = dequant8(breg[f][s], negz2[f], s2[f]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
         const half8_t a = __builtin_bit_cast(half8_t, av);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) acc[i][f] = mfma32(a, bf[f], acc[i][f]);
+        for (int f = 0; f < NF; ++f) acc[i][f] = mfma32(a, bf[f], acc[i][f]);
       }
     }
-    if (more) {
-      store_a(buf ^ 1);
-      breg[0] = bnext[0];
-      breg[1] = bnext[1];
-      if (new_group) set_sz(zraw, sraw);
-    }
+    store_a(buf ^ 1);  // the other buffer was last read before the previous barrier
+#pragma unroll
+    for (int f = 0; f < NF; ++f) breg[f] = bnext[f];
+    if (new_group) set_sz();
     __syncthreads();
   }
 
   // Output element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f].
-  if (splits == 1) {
+  if (splits > 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < NF; ++f) {
         if (!nok[f]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) y[(int64_t)m * N + nrow[f]] = (half_t)acc[i][f][r];
+          if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
         }
       }
-    return;
+    if (!splitk_arrive(counters + tile, splits)) return;
+    // Last workgroup: re-read every partial (its own included) and sum in split order,
+    // one 16-value fragment at a time (its 16 loads in flight together).
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        float16_t sum;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+        for (int sp = 0; sp < splits; ++sp) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), M - 1);
+            sum[r] += ld_coherent(partials + ((int64_t)sp * M + m) * N + nclamp[f]);
+          }
+        }
+        acc[i][f] = sum;
+      }
   }
-
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < NF; ++f) {
       if (!nok[f]) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
-      }
-    }
-  if (!splitk_arrive(counters + tile, splits)) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      if (!nok[f]) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) {
-          float s = 0.0f;
-          for (int sp = 0; sp < splits; ++sp) s += ld_coherent(partials + ((int64_t)sp * M + m) * N + nrow[f]);
-          y[(int64_t)m * N + nrow[f]] = (half_t)s;
-        }
+        if (m < M) y[(int64_t)m * N + nrow[f]] = (half_t)acc[i][f][r];
       }
     }
 }
 
 }  // namespace
 
+// Tile shapes, largest first: (MI, NF) = (4, 2) 128 x 256, (4, 1) 128 x 128, (2, 2) 64 x 256,
+// (2, 1) 64 x 128.  The plan takes the first shape that gives at least kMinTiles tiles
+// (a full wave of workgroups); split-K only when even the smallest does not.
+static const int kShapes[4][2] = {{4, 2}, {4, 1}, {2, 2}, {2, 1}};
+
 GemmPlan gemm_plan(int M, int N, int K) {
   GemmPlan p;
-  p.tiles_m = (M + BM - 1) / BM;
-  p.tiles_n = (N + BN - 1) / BN;
+  const int min_tiles = env_int("W4_GEMM_MIN_TILES", 256);
+  const int forced = env_int("W4_GEMM_SHAPE", 0);  // 1..4 selects kShapes[forced - 1]
+  int pick = 3;
+  if (forced >= 1 && forced <= 4) {
+    pick = forced - 1;
+  } else {
+    for (int i = 0; i < 4; ++i) {
+      const int tm = (M + 32 * kShapes[i][0] - 1) / (32 * kShapes[i][0]);
+      const int tn = (N + 128 * kShapes[i][1] - 1) / (128 * kShapes[i][1]);
+      if (tm * tn >= min_tiles) {
+        pick = i;
+        break;
+      }
+    }
+  }
+  p.mi = kShapes[pick][0];
+  p.nf = kShapes[pick][1];
+  p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
+  p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
   const int ktiles = K / BK;
   const int tiles = p.tiles_m * p.tiles_n;
-  const int target = env_int("W4_GEMM_SPLIT_TARGET", 256);
   int splits = 1;
   // fill the CUs when there are few tiles; keep >= 8 BK steps per split
-  while (tiles * splits < target && ktiles / (splits * 2) >= 8) splits *= 2;
+  while (tiles * splits < min_tiles / 2 && ktiles / (splits * 2) >= 8) splits *= 2;
   if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ktiles + splits - 1) / splits;
   p.splits = (ktiles + p.kt_per_split - 1) / p.kt_per_split;
@@ -255,9 +283,15 @@ hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int blocks = p.tiles_m * p.tiles_n * p.splits;
-  hipLaunchKernelGGL(gemm_kernel, dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,
-                     (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y, counters,
-                     partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split);
+#define GEMM_LAUNCH(MI, NF)                                                                                   \
+  hipLaunchKernelGGL((gemm_kernel<MI, NF>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,          \
+                     (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,     \
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
+  if (p.mi == 4 && p.nf == 2) GEMM_LAUNCH(4, 2);
+  else if (p.mi == 4) GEMM_LAUNCH(4, 1);
+  else if (p.nf == 2) GEMM_LAUNCH(2, 2);
+  else GEMM_LAUNCH(2, 1);
+#undef GEMM_LAUNCH
   return hipGetLastError();
 }
 

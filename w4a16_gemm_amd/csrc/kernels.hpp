@@ -52,7 +52,9 @@ int env_int(const char* name, int dflt);
 // Tile plan of the skinny (M <= 64) W4A16 kernel.
 struct SkinnyPlan {
   int mt;          // 16-row M tiles (1, 2 or 4)
-  int row_blocks;  // ceil(N / 64)
+  int tiles;       // 16-column tiles per workgroup (1, 2 or 4)
+  int depth;       // groups in flight per wave (register sets)
+  int row_blocks;  // ceil(N / (16 tiles))
   int splits;      // split-K factor over groups
   int gps;         // groups per split
 };
@@ -60,6 +62,7 @@ SkinnyPlan skinny_plan(int M, int N, int K);
 
 // Tile plan of the large-M W4A16 GEMM.
 struct GemmPlan {
+  int mi, nf;  // tile = (32 mi) x (128 nf)
   int tiles_m, tiles_n, splits, kt_per_split;
 };
 GemmPlan gemm_plan(int M, int N, int K);

@@ -17,10 +17,11 @@
 
 namespace w4 {
 
-// One thread per (group g, row n); n is the fastest index so that the 8 threads of a
-// zero-point word are 8 consecutive lanes.  npad = N rounded up to a multiple of 8.
+// One thread per (group g, row n), n fastest, over npad = N rounded up to 16 rows:
+// the 8 threads of a zero-point word are 8 consecutive lanes, and padding rows
+// (n >= N) write code 0 so that the whole tiled array is defined.
 __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict__ w,
-                                                        int32_t* __restrict__ qweight,
+                                                        uint32_t* __restrict__ qweight,
                                                         half_t* __restrict__ scales,
                                                         int32_t* __restrict__ qzeros,
                                                         int N, int K, int npad) {
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
   const int n = live ? (int)(tid % npad) : 0;
   const bool valid = live && n < N;
   uint32_t zbits = 0;
+  u32x4 out[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   if (valid) {
     const u32x4* src = reinterpret_cast<const u32x4*>(w + (int64_t)n * K + (int64_t)g * 128);
     u32x4 raw[16];
@@ -49,7 +51,6 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
     const half_t s16 = (half_t)s32;
     const float s = (float)s16;
     const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f);
-    u32x4 out[4];
     uint32_t* ow = reinterpret_cast<uint32_t*>(out);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -61,17 +62,18 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
       }
       ow[j] = word;
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(qweight + (int64_t)n * (K / 8) + (int64_t)g * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = out[i];
     scales[(int64_t)g * N + n] = s16;
     zbits = ((uint32_t)z) << (4 * (n & 7));
+  }
+  if (live) {
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) *reinterpret_cast<u32x4*>(qweight + tiled_chunk(n, g, slot, ng)) = out[slot];
   }
   // OR the 8 nibbles of the zero-point word across the 8 consecutive lanes.
   zbits |= __shfl_xor(zbits, 1, kWave);
   zbits |= __shfl_xor(zbits, 2, kWave);
   zbits |= __shfl_xor(zbits, 4, kWave);
-  if (live && (n & 7) == 0 && n < N) qzeros[(int64_t)g * (npad / 8) + n / 8] = (int32_t)zbits;
+  if (valid && (n & 7) == 0) qzeros[(int64_t)g * ((N + 7) / 8) + n / 8] = (int32_t)zbits;
 }
 
 // One thread per packed word (n, j): eight fp16 outputs.
@@ -89,12 +91,14 @@ __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t*
   const uint32_t z = (qzeros[(int64_t)g * nzw + n / 8] >> (4 * (n & 7))) & 15u;
   const half_t s = scales[(int64_t)g * N + n];
   const half2_t negz2 = splat2(-(half_t)(1024 + z));
-  const half8_t v = dequant8(qweight[tid], negz2, splat2(s));
+  const uint32_t word = qweight[tiled_chunk(n, g, (j & 15) >> 2, K / 128) + (j & 3)];
+  const half8_t v = dequant8(word, negz2, splat2(s));
   *reinterpret_cast<half8_t*>(out + (int64_t)n * K + (int64_t)j * 8) = v;
 }
 
 // One workgroup (256 threads) per row n.  Pass 1: amax over the row.  Pass 2: codes.
 // Two-level mode: a group of 128 k is 16 words handled by 16 consecutive lanes.
+// Workgroups past N (up to N rounded to 16) write padding rows of q = 0 (word 0x88888888).
 __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict__ w,
                                                          uint32_t* __restrict__ qweight,
                                                          int8_t* __restrict__ gscale,
@@ -102,6 +106,12 @@ __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict
                                                          int N, int K, int two_level) {
   __shared__ float red[4];
   const int n = blockIdx.x;
+  const int ng = K / 128;
+  if (n >= N) {
+    for (int j = threadIdx.x; j < K / 8; j += 256)
+      qweight[tiled_chunk(n, j / 16, (j & 15) >> 2, ng) + (j & 3)] = 0x88888888u;
+    return;
+  }
   const half_t* row = w + (int64_t)n * K;
   const int wpr = K / 8;
   float amax = 0.0f;
@@ -157,16 +167,16 @@ __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict
       }
       if (ok && (j & 15) == 0) gscale[(int64_t)(j / 16) * N + n] = (int8_t)(int)sg;
     }
-    if (ok) qweight[(int64_t)n * wpr + j] = word;
+    if (ok) qweight[tiled_chunk(n, j / 16, (j & 15) >> 2, ng) + (j & 3)] = word;
   }
 }
 
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
                            hipStream_t stream) {
-  const int npad = (N + 7) / 8 * 8;
+  const int npad = (N + 15) / 16 * 16;
   const int64_t total = (int64_t)npad * (K / 128);
   const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(awq_pack_kernel, dim3(blocks), dim3(256), 0, stream, (const half_t*)w, qweight,
+  hipLaunchKernelGGL(awq_pack_kernel, dim3(blocks), dim3(256), 0, stream, (const half_t*)w, (uint32_t*)qweight,
                      (half_t*)scales, qzeros, N, K, npad);
   return hipGetLastError();
 }
@@ -183,7 +193,7 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
 
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
                             int two_level, hipStream_t stream) {
-  hipLaunchKernelGGL(w4a8_pack_kernel, dim3(N), dim3(256), 0, stream, (const half_t*)w,
+  hipLaunchKernelGGL(w4a8_pack_kernel, dim3((N + 15) / 16 * 16), dim3(256), 0, stream, (const half_t*)w,
                      (uint32_t*)qweight, gscale, (half_t*)cscale, N, K, two_level);
   return hipGetLastError();
 }

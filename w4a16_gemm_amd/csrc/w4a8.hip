@@ -140,10 +140,9 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   const int gend = min(ng, gbeg + gps);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int wpr = K / 8;
 
   int nrow[2];
   bool nok[2];
@@ -169,7 +168,7 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     for (int i = 0; i < kPer; ++i) {
       const int cid = threadIdx.x + i * kWThreads;
       const int r = cid >> 3, c = cid & 7;
-      const int m = min(m0 + r, M - 1);  // branch-free: clamped row, zeroed at the LDS store
+      const int m = min(m0 + r, M - 1);  // branch-free: a clamped row only reaches unstored outputs
       areg[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)m * K + g * WBK + c * 16);
     }
   };
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int cid = threadIdx.x + i * kWThreads;
-      if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = (m0 + (cid >> 3) < M) ? areg[i] : u32x4{0u, 0u, 0u, 0u};
+      if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = areg[i];
     }
   };
   // Columns past N read a clamped valid row; their outputs are never stored.
@@ -186,11 +185,11 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   for (int f = 0; f < 2; ++f) nclamp[f] = min(nrow[f], N - 1);
   u32x4 breg[2][2];
   auto load_b = [&](int g, u32x4 (&dst)[2][2]) {
+    // words 8h .. 8h + 7 of the group = slots 2h and 2h + 1 of the tiled layout
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(qweight + (int64_t)nclamp[f] * wpr + g * 16 + h * 8);
-      dst[f][0] = p[0];
-      dst[f][1] = p[1];
+      dst[f][0] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h, ng));
+      dst[f][1] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h + 1, ng));
     }
   };
 
@@ -213,7 +212,6 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
 
   for (int g = gbeg; g < gend; ++g) {
     const int buf = (g - gbeg) & 1;
-    const bool more = g + 1 < gend;
     u16x2 sp[2], cp[2];
     if (TWO) {
 #pragma unroll
@@ -223,12 +221,13 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
         cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
       }
     }
+    // next group's loads, unconditional (clamped on the last iteration; see the W4A16 GEMM)
+    const int gn = min(g + 1, gend - 1);
     u32x4 bnext[2][2];
-    if (more) {
-      load_a(g + 1);
-      load_b(g + 1, bnext);
-      load_sg(g + 1, sgraw);
-    }
+    load_a(gn);
+    load_b(gn, bnext);
+    load_sg(gn, sgraw);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       int4_t bf[2];
@@ -254,13 +253,11 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
         for (int f = 0; f < 2; ++f) acc[i][f] = mfma32_i8(a, bf[f], acc[i][f]);
       }
     }
-    if (more) {
-      store_a(buf ^ 1);
+    store_a(buf ^ 1);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        breg[f][0] = bnext[f][0];
-        breg[f][1] = bnext[f][1];
-      }
+    for (int f = 0; f < 2; ++f) {
+      breg[f][0] = bnext[f][0];
+      breg[f][1] = bnext[f][1];
     }
     __syncthreads();
   }
@@ -287,21 +284,20 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
         }
       }
     if (!splitk_arrive(counters + tile, splits)) return;
+    // Last workgroup: add the other splits' partials to its own (integer sums are exact
+    // in any order), one 16-value fragment at a time (its loads in flight together).
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        if (!nok[f]) continue;
+      for (int f = 0; f < 2; ++f)
+        for (int sp_ = 0; sp_ < splits; ++sp_) {
+          if (sp_ == split) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) {
-            int32_t v = 0;
-            for (int sp_ = 0; sp_ < splits; ++sp_) v += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + nrow[f]);
-            acc[i][f][r] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), M - 1);
+            acc[i][f][r] += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + nclamp[f]);
           }
         }
-      }
   }
   const float cs0 = nok[0] ? (float)cscale_or_one(cscale, nrow[0]) : 0.0f;
   const float cs1 = nok[1] ? (float)cscale_or_one(cscale, nrow[1]) : 0.0f;
