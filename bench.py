@@ -46,6 +46,25 @@ def w4a8_bytes(M, N, K, two_level):
     return N * K / 2 + 2 * N + (N * (K // G) if two_level else 0) + M * K + 4 * M + 2 * M * N
 
 
+def profiled_traffic(key):
+    """HBM bytes per launch of a kernel as measured by the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy), or None when the kernel's
+    sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec["source_hash"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,7 +215,9 @@ def main():
                    "bytes_per_step": int(step_bytes)},
         "roofline": {"bound": "hbm", "kernel": "skinny_kernel (awq_gemm, M<=16)", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "avg_launch_us": round(avg_us, 3), "traffic": None},
+                     "avg_launch_us": round(avg_us, 3),
+                     "algorithmic_bytes_per_launch": int(step_bytes / per_step),
+                     "traffic": profiled_traffic("skinny_decode_13b")},
         "per_shape": shape_detail,
     }
 
