@@ -150,14 +150,44 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
 @pytest.mark.parametrize("tiles", ["1", "2", "4"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (33, 96, 768), (64, 300, 640)])
 def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
-    """Each tile width / prefetch-depth variant of the M <= 64 kernel (forced through its
-    tuning variable), against the oracle."""
+    """Each tile width / prefetch-depth variant of the register-X M <= 64 kernel (forced
+    through its tuning variables), against the oracle."""
     dev = device()
     monkeypatch.setenv("W4_SKINNY_TILES", tiles)
+    monkeypatch.setenv("W4_SKINNY_LDS", "0")
     announce(f"skinny tiles={tiles} M={M} N={N} K={K}")
     inp = synth.make_linear(M, N, K, seed=M + N + int(tiles), outliers=True)
     ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
     y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz)).astype(np.float64)
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("variant", ["1,4,1,4,0", "1,8,1,8,0", "2,4,2,4,0", "2,4,1,2,5", "4,2,1,4,0", "4,2,2,2,2",
+                                     "1,4,2,2,3",
+                                     "lds-off"])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 5120), (7, 130, 13824)])
+def test_skinny_lds_variants(variant, M, N, K, monkeypatch):
+    """The M <= 16 kernel with X staged in LDS, every compiled (tiles, depth) pair, M = 1
+    and M > 1 epilogues, and
+    several workgroup shapes (column groups x K-waves) and forced split counts, forced
+    through its tuning variables; K = 5120 at M = 16 and K = 13824 at M = 7 exceed one
+    LDS slice and must split.  'lds-off' forces the register-X kernel at M <= 16."""
+    dev = device()
+    if variant == "lds-off":
+        monkeypatch.setenv("W4_SKINNY_LDS", "0")
+    else:
+        t, d, wn, wk, sp = variant.split(",")
+        for k, v in (("LDS", "1"), ("TILES", t), ("DEPTH", d), ("WN", wn), ("WK", wk), ("SPLITS", sp)):
+            monkeypatch.setenv("W4_SKINNY_" + k, v)
+    announce(f"skinny lds variant={variant} M={M} N={N} K={K} ws={w4.awq_gemm_workspace_bytes(M, N, K)}")
+    inp = synth.make_linear(M, N, K, seed=M + N, outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
     yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
     err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
                            np.linalg.norm(ref["w_deq"], axis=1))

@@ -100,7 +100,7 @@ int env_int(const char* name, int dflt) {
   if (v == nullptr || *v == 0) return dflt;
   char* end = nullptr;
   const long x = std::strtol(v, &end, 10);
-  return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+  return (end && *end == 0 && x >= 0 && x < (1L << 30)) ? (int)x : dflt;
 }
 }  // namespace w4
 

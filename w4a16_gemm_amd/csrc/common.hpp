@@ -60,17 +60,23 @@ __device__ __forceinline__ int64_t tiled_chunk(int n, int g, int slot, int ng) {
 // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7 of the
 // first, 0x0c gives 0.
 // (x & mask) | bits in one v_and_or_b32.  VOP3 encodings on gfx9 take no literal
-// constants, so the two constants are passed in registers (the plain C expression
-// compiles to a separate v_and_b32 and v_or_b32, each with a literal).
+// constants, so with literal operands the expression compiles to a separate v_and_b32
+// and v_or_b32.  The constants are therefore passed through vreg(), an empty asm that
+// hides their value: the compiler then keeps them in registers (hoisted out of loops)
+// and selects v_and_or_b32 itself.  The instruction stays compiler-generated, so the
+// hazard checks around in-flight MFMAs (a VALU write to an MFMA source needs wait
+// states) apply to it; hand-written VALU asm would escape them.
+__device__ __forceinline__ uint32_t vreg(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
-  return r;
+  return (x & mask) | bits;
 }
 
 __device__ __forceinline__ half8_t unpack_1024(uint32_t w) {
   const uint32_t s = w >> 4;
-  const uint32_t mask = 0x000f000fu, magic = 0x64006400u;
+  const uint32_t mask = vreg(0x000f000fu), magic = vreg(0x64006400u);
   u32x4 r;
   r[0] = and_or(__builtin_amdgcn_perm(s, w, 0x0c040c00u), mask, magic);
   r[1] = and_or(__builtin_amdgcn_perm(s, w, 0x0c050c01u), mask, magic);

@@ -14,7 +14,8 @@
 // subtract or multiply); S_g comes from one extra MFMA against a B operand of ones.
 // fp16 x (1024 + q) products are exact in fp32; only the fp32 sums round.
 //
-// Work split: a workgroup (4 waves) owns 16 T output columns n (T = 1, 2 or 4 tiles of 16)
+// Work split (register-X kernel, 16 < M <= 64; the M <= 16 kernel further below stages X
+// in LDS): a workgroup (4 waves) owns 16 T output columns n (T = 1, 2 or 4 tiles of 16)
 // and a contiguous range of K groups (split-K across workgroups only for narrow N); its
 // waves take the groups of that range round robin.  Per group, lane l of a wave loads
 // one 16-byte chunk (32 codes) of row n0 + 16t + (l % 16) for each tile t -- with the tiled
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
                                                                half_t* __restrict__ y,
                                                                unsigned* __restrict__ counters,
                                                                float* __restrict__ partials, int M, int N, int K,
-                                                               int splits, int gps) {
+                                                               int splits, int gps, int drain) {
   constexpr int kT = WAVES * kWave;
   constexpr int kCols = 16 * T;           // output columns of one workgroup
   constexpr int kOut = MT * 16 * kCols;   // outputs of one workgroup
@@ -146,24 +147,25 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   // loop, the waits before each compute only cover the group being computed.
   GroupRegs<MT, T> r[D];
   const int glast = gend - 1;
-  int g = gbeg + wave;
-  if (g < gend) {
+  const int g = gbeg + wave;
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-      load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K);
-  }
-  for (; g < gend; g += D * WAVES) {
-    bool done = false;
+  for (int d = 0; d < D; ++d)
+    load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K);
+  // Steady state without conditions (the wait before each compute then covers only its
+  // own register set), then the remaining < D groups; all counts are wave-uniform.
+  const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
+  int it = 0;
+  for (; it + D <= mine; it += D) {
+    if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (!done) {
-        compute_group<MT, T>(r[d], yacc, n0, lane, N);
-        load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + (d + D) * WAVES, glast), n0, lane, M, N, K);
-        done = g + (d + 1) * WAVES >= gend;  // wave-uniform
-      }
+      compute_group<MT, T>(r[d], yacc, n0, lane, N);
+      load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
     }
-    if (done) break;
   }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (it + d < mine) compute_group<MT, T>(r[d], yacc, n0, lane, N);
 
   // Cross-wave reduction.  Element (mt, t, i) of lane l is output row
   // m = 16 mt + 4 (l / 16) + i, column n = n0 + 16 t + (l % 16).
@@ -230,6 +232,282 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   }
 }
 
+
+// ---------------------------------------------------------------------------------
+// M <= 16: X staged in LDS, codes unpacked in five VALU operations per word.
+//
+// The workgroup copies its slice of X (M rows x its K range) into LDS once; the
+// per-group register sets that are prefetched D deep then carry only what comes from
+// HBM: T x 16 bytes of codes, T scales and T zero-point words per lane.
+//
+// B operand: for the 8 codes of a word, v_and_or_b32 with mask 0x000f000f and fp16
+// 1024 in both halves gives (1024 + q_0, 1024 + q_4) -- a code in the low mantissa bits
+// under exponent 2^10 -- and with mask 0x00f000f0 and fp16 64 gives (64 + q_1, 64 + q_5)
+// -- a code in mantissa bits 4..7 under exponent 2^6 is worth q exactly.  The same on
+// the word shifted right by 8 gives k = 2, 6 and 3, 7: four v_and_or_b32 and one shift
+// per word, the k order within every 8 being 0,4,1,5,2,6,3,7.  X is stored in LDS in
+// that order, so one MFMA chain forms, exactly up to its fp32 sums,
+//   T_g[m,n] = sum_k X[m,k] q[n,k] + P_g[m],   P_g[m] = 1024 sum_{k even} X[m,k] + 64 sum_{k odd} X[m,k],
+// and the group's contribution to Y is s (T_g - P_g - z S_g), S_g[m] = sum_{k in g} X[m,k].
+// P_g and S_g depend on X only: they are summed in fp32 while X is staged, reduced over
+// the 16 chunks of a group with DPP moves (fixed order, deterministic) and kept in LDS.
+// LDS rows of X are padded by 16 bytes, so the 16 rows of an A fragment fall in
+// distinct banks.
+//
+// A workgroup is WN x WK waves: WN column groups of 16 T columns each, and WK waves that
+// take the groups of the K range round robin; partial sums are reduced across the WK
+// waves in LDS (reusing the X region), then across split-K workgroups as above.
+template <int T>
+struct WStage {
+  u32x4 b[T];      // packed codes: chunk of this lane's row / K-slot in each n-tile
+  half_t s[T];     // scale of this lane's row in each n-tile (raw fp16)
+  uint32_t zw[T];  // packed zero-point word holding this lane's row in each n-tile
+};
+
+template <int T>
+__device__ __forceinline__ void load_wstage(WStage<T>& r, const uint32_t* __restrict__ qweight,
+                                            const half_t* __restrict__ scales,
+                                            const uint32_t* __restrict__ qzeros, int g, int tile0, int lane,
+                                            int N, int ng, int nzw) {
+  const int last_tile = (N - 1) >> 4;
+  const half_t* srow = scales + (int64_t)g * N;
+  const uint32_t* zrow = qzeros + (int64_t)g * nzw;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int tile = min(tile0 + t, last_tile);
+    const int nc = min(16 * (tile0 + t) + (lane & 15), N - 1);
+    r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+    r.s[t] = srow[nc];
+    r.zw[t] = zrow[nc >> 3];
+  }
+}
+
+__device__ __forceinline__ half8_t unpack_mixed(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t e1024,
+                                                uint32_t e64) {
+  const uint32_t w8 = w >> 8;
+  u32x4 r;
+  r[0] = and_or(w, mlo, e1024);   // 1024 + q0, 1024 + q4
+  r[1] = and_or(w, mhi, e64);     //   64 + q1,   64 + q5
+  r[2] = and_or(w8, mlo, e1024);  // 1024 + q2, 1024 + q6
+  r[3] = and_or(w8, mhi, e64);    //   64 + q3,   64 + q7
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// DPP row moves (16-lane rows): quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror,
+// row_mirror; the four partial sums below make every lane of a row hold the row total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// cc / cpr for 0 <= cc < 16 cpr, cpr < 2^16: (cc + 0.5) / cpr lies at least 0.5 / cpr
+// away from an integer, far more than the fp32 rounding of the product.
+__device__ __forceinline__ int chunk_row(int cc, int cpr) {
+  return (int)(((float)cc + 0.5f) * (1.0f / (float)cpr));
+}
+
+// Stage one 16-byte chunk (8 halves of X) of chunk index cc (clamped into the slice) to
+// LDS in the k order 0,4,1,5,2,6,3,7, and add its even / odd sums to the group's S, P
+// (written by the first lane of the 16 lanes that hold the group's 16 chunks; `live`
+// is false for the clamped copies past the slice, which are rewritten, not summed).
+__device__ __forceinline__ void stage_chunk(u32x4 v, int cc, bool live, int cpr, int rs, half_t* xs, float* sp) {
+  const int row = chunk_row(cc, cpr), col = cc - row * cpr;
+  u32x4 o;
+  o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // x0, x4
+  o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // x1, x5
+  o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // x2, x6
+  o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // x3, x7
+  *reinterpret_cast<u32x4*>(xs + row * rs + col * 8) = o;
+  // (vector elements are copied to scalars before __builtin_bit_cast: applied directly
+  // to an element of an ext_vector this hipcc reads element 0)
+  const uint32_t o0 = o[0], o1 = o[1], o2 = o[2], o3 = o[3];
+  const half2_t one2 = {1, 1};
+  float e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o0), one2, 0.0f, false);
+  e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o2), one2, e, false);
+  float od = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o1), one2, 0.0f, false);
+  od = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o3), one2, od, false);
+  e = row16_sum(e);
+  od = row16_sum(od);
+  if (live && (col & 15) == 0) {
+    float* g = sp + (col >> 4) * 32;
+    g[row] = e + od;
+    g[16 + row] = 1024.0f * e + 64.0f * od;
+  }
+}
+
+// One group: A fragments and S, P from LDS, then per n-tile T_g and the fold into the
+// accumulators.  ONE_ROW: M == 1, only accumulator element 0 of lanes 0..15 is an output.
+template <int T, bool ONE_ROW>
+__device__ __forceinline__ void compute_wstage(const WStage<T>& r, const half_t* xrow, const float* spg,
+                                               float4_t (&yacc)[T], const int (&zsh)[T], int lane) {
+  half8_t a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const half8_t*>(xrow + 8 * j);
+  const float4_t S = *reinterpret_cast<const float4_t*>(spg + 4 * (lane >> 4));
+  const float4_t P = *reinterpret_cast<const float4_t*>(spg + 16 + 4 * (lane >> 4));
+  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    half8_t bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mlo, mhi, e1024, e64);
+    float4_t tacc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tacc = mfma16(a[j], bv[j], tacc);
+    const float z = (float)((r.zw[t] >> zsh[t]) & 15u);
+    const float sc = (float)r.s[t];
+#pragma unroll
+    for (int i = 0; i < (ONE_ROW ? 1 : 4); ++i) {
+      const float d = fmaf(-z, S[i], tacc[i] - P[i]);
+      yacc[t][i] = fmaf(sc, d, yacc[t][i]);
+    }
+  }
+}
+
+constexpr int kXChunksPerPass = 8;  // 16-byte chunks of X each thread stages per pass
+
+template <int T, int D, bool ONE_ROW>
+__global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restrict__ x,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const half_t* __restrict__ scales,
+                                                         const uint32_t* __restrict__ qzeros,
+                                                         half_t* __restrict__ y, unsigned* __restrict__ counters,
+                                                         float* __restrict__ partials, int M, int N, int K,
+                                                         int splits, int gps, int wn_count, int drain) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WN = wn_count;
+  const int WK = (nthreads >> 6) / WN;
+  const int wn = wave % WN, wk = wave / WN;
+  const int cols = 16 * T * WN;
+  const int n0 = blockIdx.x * cols;
+  const int tile0 = (n0 >> 4) + wn * T;
+  const int split = blockIdx.y;
+  const int ng = K / 128;
+  const int nzw = (N + 7) / 8;
+  const int gbeg = split * gps;
+  const int gend = min(ng, gbeg + gps);
+  const int kb = (gend - gbeg) * 128;
+  const int rs = kb + 8;  // padded LDS row stride in halves
+  half_t* xs = reinterpret_cast<half_t*>(smem);
+  float* sp = reinterpret_cast<float*>(smem + M * rs * 2);  // [group][S rows 0..15, P rows 0..15]
+
+  // The first pass of the X slice is issued before the weight prefetch, so that it
+  // arrives first and the first compute waits only for it and its own weights.  Every
+  // load and LDS store is unconditional: chunk indices past the slice are clamped to its
+  // last chunk (rewritten with the same value), group indices past the range to the
+  // last group.
+  const int cpr = kb >> 3;  // 16-byte chunks per row (a multiple of 16)
+  const int total = M * cpr;
+  const int64_t xoff = (int64_t)gbeg * 128;
+  u32x4 xv[kXChunksPerPass];
+#pragma unroll
+  for (int i = 0; i < kXChunksPerPass; ++i) {
+    const int cc = min((int)threadIdx.x + i * nthreads, total - 1);
+    const int row = chunk_row(cc, cpr), col = cc - row * cpr;
+    xv[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)row * K + xoff + col * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the X loads ahead of the weight loads
+  WStage<T> r[D];
+  const int glast = gend - 1;
+  const int g = gbeg + wk;
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_wstage<T>(r[d], qweight, scales, qzeros, min(g + d * WK, glast), tile0, lane, N, ng, nzw);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kXChunksPerPass; ++i) {
+    const int c = threadIdx.x + i * nthreads;
+    stage_chunk(xv[i], min(c, total - 1), c < total, cpr, rs, xs, sp);
+  }
+  // further passes (M * K-range larger than one pass of the workgroup)
+  for (int c0 = threadIdx.x + kXChunksPerPass * nthreads; c0 < total; c0 += kXChunksPerPass * nthreads) {
+#pragma unroll
+    for (int i = 0; i < kXChunksPerPass; ++i) {
+      const int cc = min(c0 + i * nthreads, total - 1);
+      const int row = chunk_row(cc, cpr), col = cc - row * cpr;
+      xv[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)row * K + xoff + col * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kXChunksPerPass; ++i) {
+      const int c = c0 + i * nthreads;
+      stage_chunk(xv[i], min(c, total - 1), c < total, cpr, rs, xs, sp);
+    }
+  }
+  __syncthreads();
+
+  float4_t yacc[T];
+  int zsh[T];  // bit offset of this lane's zero point in its packed word
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    yacc[t] = float4_t{0, 0, 0, 0};
+    zsh[t] = 4 * (min(16 * (tile0 + t) + (lane & 15), N - 1) & 7);
+  }
+  // this lane's A row (rows past M read row M - 1; those outputs are never stored)
+  const half_t* xrow = xs + min(lane & 15, M - 1) * rs + (lane >> 4) * 32;
+  // Steady state without conditions (so that the wait before each compute covers only
+  // its own register set), then the remaining < D groups; all counts are wave-uniform.
+  const int mine = g < gend ? (gend - g + WK - 1) / WK : 0;
+  int it = 0;
+  for (; it + D <= mine; it += D) {
+    if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int gl = g + (it + d) * WK - gbeg;
+      compute_wstage<T, ONE_ROW>(r[d], xrow + gl * 128, sp + gl * 32, yacc, zsh, lane);
+      load_wstage<T>(r[d], qweight, scales, qzeros, min(gbeg + gl + D * WK, glast), tile0, lane, N, ng, nzw);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (it + d < mine) {
+      const int gl = g + (it + d) * WK - gbeg;
+      compute_wstage<T, ONE_ROW>(r[d], xrow + gl * 128, sp + gl * 32, yacc, zsh, lane);
+    }
+  }
+
+  // Cross-wave reduction in LDS (the X slice is dead after this barrier).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * T + t) * 256 + i * 64 + lane] = yacc[t][i];
+  __syncthreads();
+
+  // Outputs (m < M, n fastest).  Element (t, i) of lane l of wave (wn, wk) is row
+  // 4 (l / 16) + i, column 16 (wn T + t) + l % 16 of the workgroup.
+  const int outs = M * cols;
+  for (int o = threadIdx.x; o < outs; o += nthreads) {
+    const int m = o / cols, nl = o - m * cols;
+    const int wn_ = nl / (16 * T), t = (nl >> 4) % T;
+    const int idx = t * 256 + (m & 3) * 64 + (m >> 2) * 16 + (nl & 15);
+    float v = 0.0f;
+    for (int k = 0; k < WK; ++k) v += red[(k * WN + wn_) * T * 256 + idx];
+    const int n = n0 + nl;
+    if (n >= N) continue;
+    if (splits == 1) y[(int64_t)m * N + n] = (half_t)v;
+    else st_coherent(partials + ((int64_t)split * M + m) * N + n, v);
+  }
+  if (splits == 1) return;
+  if (!splitk_arrive(counters + blockIdx.x, splits)) return;
+  for (int o = threadIdx.x; o < outs; o += nthreads) {
+    const int m = o / cols, n = n0 + o - m * cols;
+    if (n >= N) continue;
+    float v = 0.0f;
+    for (int sp_ = 0; sp_ < splits; ++sp_) v += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + n);
+    y[(int64_t)m * N + n] = (half_t)v;
+  }
+}
+
 }  // namespace
 
 // Waves per workgroup: 4.  At ~190 VGPRs two 4-wave workgroups fit per CU, so grids of
@@ -242,13 +520,68 @@ static int skinny_waves(int) { return 4; }
 // kMinBlocks workgroups; only when even T = 1 does not (N < 16 kMinBlocks) is K split.
 SkinnyPlan skinny_plan(int M, int N, int K) {
   SkinnyPlan p;
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int ng = K / 128;
+  p.lds = 0;
+  p.wn = 1;
+  p.wk = 4;
+  p.smem = 0;
+  p.drain = env_int("W4_SKINNY_DRAIN", 0);
+  // (Very wide N with a K too long for one LDS slice would need more arrival counters
+  // than the workspace holds; such shapes take the register-X kernel below.)
+  constexpr int kLdsBudget = 65536 - 256;  // dynamic LDS; the split-K flag is static
+  // X slice M (128 gps + 8) halves plus S, P (32 floats per group) within the budget
+  const int lds_gmax = max(1, (kLdsBudget - 16 * M) / (256 * M + 128));
+  const bool lds_ok = M <= 16 && !(ng > lds_gmax && (N + 15) / 16 >= kMaxCounters);
+  // Default kernel and shape, from sweeps on the MI355X over the Llama-2-13B projection
+  // shapes at M = 1, 4, 16: the LDS kernel wins for M <= 4 except on narrow, short
+  // matrices (N and K <= 8192), where its X staging is not repaid; above M = 4 the
+  // register-X kernel wins (the LDS slice then limits the K range per workgroup).
+  int use_lds = lds_ok && M <= 4 && !(N <= 8192 && K <= 8192);
+  int t = 1, d = 4, wn = 1, wk = 4, target = 256;
+  if (N > 16384) { t = 4; d = 2; }
+  else if (N > 8192) { wn = 2; }
+  else { wn = 2; wk = 2; target = 512; }
+  use_lds = env_int("W4_SKINNY_LDS", use_lds) && lds_ok;
+  if (use_lds) {
+    // X slice in LDS: under 64 KB per workgroup (two resident per CU), which bounds
+    // the groups per split.
+    p.lds = 1;
+    p.mt = 1;
+    const int te = env_int("W4_SKINNY_TILES", 0);
+    if (te == 1 || te == 2 || te == 4) t = te;
+    p.tiles = t;
+    // compiled (tiles, depth) pairs: (1, 4), (1, 8), (2, 4), (4, 2)
+    d = env_int("W4_SKINNY_DEPTH", d);
+    if (t == 4) d = 2;
+    else if (t == 2 || d != 8) d = 4;
+    p.depth = d;
+    p.wn = max(1, env_int("W4_SKINNY_WN", wn));
+    p.wk = max(1, env_int("W4_SKINNY_WK", wk));
+    if (p.wn * p.wk > 8) { p.wn = 1; p.wk = 4; }
+    p.row_blocks = (N + 16 * t * p.wn - 1) / (16 * t * p.wn);
+    const int min_splits = (ng + lds_gmax - 1) / lds_gmax;
+    target = env_int("W4_SKINNY_BLOCKS", target);
+    int splits = (target + p.row_blocks - 1) / p.row_blocks;
+    splits = min(splits, max(1, ng / p.wk));
+    const int pct = env_int("W4_SKINNY_PARTIAL_PCT", 10);
+    splits = min(splits, max(1, (int)((int64_t)K * pct / (1600LL * M))));
+    const int forced = env_int("W4_SKINNY_SPLITS", 0);
+    if (forced > 0) splits = forced;
+    splits = max(max(1, splits), min_splits);
+    if (p.row_blocks >= kMaxCounters) splits = 1;  // then min_splits == 1 (lds_ok)
+    p.gps = (ng + splits - 1) / splits;
+    p.splits = (ng + p.gps - 1) / p.gps;
+    const int xbytes = M * (p.gps * 128 + 8) * 2 + p.gps * 128;  // X slice + per-group S, P
+    const int rbytes = p.wn * p.wk * t * 1024;
+    p.smem = max(xbytes, rbytes);
+    return p;
+  }
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int waves = skinny_waves(p.mt);
   // Tiles per workgroup.  With few rows of X (M <= 4) the narrowest tiles that still
   // give enough workgroups avoid split-K; with more rows each X fragment should serve
   // several tiles (X traffic is 4 M / T bytes per weight byte), so T >= 2.
-  int t = env_int("W4_SKINNY_TILES", 0);
+  t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4) {
     if (M <= 4) t = (N <= 16 * 320) ? 1 : ((N <= 32 * 480) ? 2 : 4);
     else t = ((N + 63) / 64 >= 128) ? 4 : 2;
@@ -256,7 +589,7 @@ SkinnyPlan skinny_plan(int M, int N, int K) {
   p.tiles = t;
   p.depth = t == 1 ? 4 : 2;
   p.row_blocks = (N + 16 * t - 1) / (16 * t);
-  const int target = env_int("W4_SKINNY_BLOCKS", 320);
+  target = env_int("W4_SKINNY_BLOCKS", 320);
   int splits = (target + p.row_blocks - 1) / p.row_blocks;
   splits = min(splits, ng / waves);  // at least one group per wave
   // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the codes
@@ -287,9 +620,23 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
   const half_t* sc = (const half_t*)scales;
   const uint32_t* qz = (const uint32_t*)qzeros;
   half_t* yh = (half_t*)y;
+  if (p.lds) {
+    const dim3 block(64 * p.wn * p.wk);
+#define LDS_LAUNCH1(T, D, ONE)                                                                                \
+  hipLaunchKernelGGL((skinny_lds_kernel<T, D, ONE>), grid, block, p.smem, stream, xh, qw, sc, qz, yh, counters, \
+                     partials, M, N, K, p.splits, p.gps, p.wn, p.drain)
+#define LDS_LAUNCH(T, D) \
+  if (M == 1) LDS_LAUNCH1(T, D, true); else LDS_LAUNCH1(T, D, false)
+    if (p.tiles == 1) { if (p.depth == 4) LDS_LAUNCH(1, 4); else LDS_LAUNCH(1, 8); }
+    else if (p.tiles == 2) { LDS_LAUNCH(2, 4); }
+    else { LDS_LAUNCH(4, 2); }
+#undef LDS_LAUNCH
+#undef LDS_LAUNCH1
+    return hipGetLastError();
+  }
 #define SKINNY_LAUNCH(MT, T, D)                                                                          \
   hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, counters, \
-                     partials, M, N, K, p.splits, p.gps)
+                     partials, M, N, K, p.splits, p.gps, p.drain)
 #define SKINNY_LAUNCH_T(MT)                    \
   if (p.tiles == 4) SKINNY_LAUNCH(MT, 4, 2);   \
   else if (p.tiles == 2) SKINNY_LAUNCH(MT, 2, 2); \
