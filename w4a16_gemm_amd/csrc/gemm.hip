@@ -17,8 +17,9 @@
 // words 4h..4h+3 of the 8 words of its row in this BK step (slot 2 (kt % 2) + h of the
 // tiled layout: 16 lanes read 256 contiguous bytes), and k16-step s uses word s.  The X fragment for k16-step s is read from LDS with the same K-slot assignment
 // (row l % 32, elements k = 8 (4h + s) .. + 7).  X rows live in LDS as 128-byte rows
-// of 8 16-byte chunks, chunk c of row r stored at position c ^ (r % 8) so that the
-// 32 rows read by one instruction hit distinct banks.
+// of 8 16-byte chunks, chunk c of row r stored at position c ^ ((r / 2) % 8): two
+// consecutive rows fill one 256-byte bank window, so any 16 consecutive rows read at
+// the same chunk hit 16 distinct 16-byte bank groups.
 //
 // Workgroups are remapped so that the tiles one XCD runs at a time form compact
 // groups of 8 M-tiles (they share weight columns in that XCD's L2).  Smaller tiles are
@@ -35,7 +36,7 @@ constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // Tile BM x BN = (32 MI) x (128 NF): wave w owns columns [32 NF w, 32 NF (w + 1)) as NF
 // 32-column fragments and all BM rows as MI 32-row fragments.
