@@ -149,6 +149,18 @@ int w4a8_gemm_i32(const int8_t* xq, const int32_t* qweight, const int8_t* gscale
                   void* workspace, size_t workspace_bytes,
                   int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
 
+/*
+ * w4_pack_codes -- pack 4-bit codes [R, C] (uint8, one code per byte, values 0..15; only the
+ * low 4 bits of each byte are used) into int32 [R, ceil(C / 8)], row-major, plain nibble
+ * order: element 8j + i of a row goes to bits 4i..4i+3 of word j, missing trailing
+ * elements are 0.  The packing rule the pages fix for the AWQ weight format ("Implement
+ * AWQ quantization support for LLaMA", vllm-project/vllm PR 1032: pack_num = 8 codes per
+ * 32-bit word), without the tiling of qweight; for exporting codes or zero points in the
+ * plain layout.  R, C >= 0 (R == 0 or C == 0 is a no-op); codes needs no alignment, out must
+ * be 16-byte aligned.  Bit-exact.
+ */
+int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* w4_status_string(int status);
 /* Message for the last failure on the calling thread ("" if none). */

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
               "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
-              "w4_last_error"):
+              "w4_last_error", "w4_pack_codes"):
         assert n in names
 
 
@@ -71,6 +71,17 @@ def test_empty_shapes_are_noops(lib):
     assert lib.awq_gemm(None, None, None, None, None, None, 0, 4, 0, 256, 128, None) == 0
     assert lib.w4a8_gemm(None, None, None, None, None, None, None, 0, 0, 64, 256, -1, None) == 0
     assert lib.w4a8_quant_act(None, None, ctypes.c_float(1e-5), None, None, 0, 0, 256, 0, None) == 0
+
+
+def test_pack_codes_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.w4_pack_codes(None, None, 0, 5, None) == 0  # empty: no pointer or device check
+    assert lib.w4_pack_codes(P(FAKE), P(FAKE), -1, 8, None) == 1
+    assert "negative" in lib.w4_last_error().decode()
+    assert lib.w4_pack_codes(None, P(FAKE), 3, 8, None) == 1
+    assert "codes is NULL" in lib.w4_last_error().decode()
+    assert lib.w4_pack_codes(P(FAKE), P(FAKE + 4), 3, 8, None) == 1
+    assert "aligned" in lib.w4_last_error().decode()
 
 
 def test_w4a8_validation(lib):

@@ -109,3 +109,16 @@ def test_w4a8_pack_golden_rows():
             assert to_np(gs)[:, 0].tolist() == c["gscale"]
             for g, head in enumerate(c["q_head"]):
                 assert q[0, g * 128:g * 128 + len(head)].tolist() == head
+
+
+@pytest.mark.parametrize("R,C", [(1, 8), (37, 131), (300, 1000), (5, 3), (64, 640)])
+def test_pack_codes_bit_exact(R, C):
+    """w4_pack_codes: plain row-major nibble packing, against the oracle's packer (ragged
+    C: trailing nibbles 0), codes spanning 0..15."""
+    dev = device()
+    announce(f"w4_pack_codes R={R} C={C}")
+    codes = synth.uniform_ints((R, C), 0, 15, seed=R * 31 + C).numpy().astype(np.uint8)
+    codes[0, 0] = 15
+    out = w4.w4_pack_codes(torch.from_numpy(codes).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), ora.pack_nibbles(codes))

@@ -20,4 +20,5 @@ from ._lib import (  # noqa: F401
     w4a8_gemm_workspace_bytes,
     w4a8_pack,
     w4a8_quant_act,
+    w4_pack_codes,
 )

@@ -54,6 +54,7 @@ def load():
             "w4a8_quant_act": [P, P, F, P, P, I64, I64, I64, I32, P],
             "w4a8_gemm": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4a8_gemm_i32": [P, P, P, P, P, SZ, I64, I64, I64, I32, P],
+            "w4_pack_codes": [P, P, I64, I64, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -144,6 +145,17 @@ def awq_pack(w: torch.Tensor, group_size: int = 128):
         _check("awq_pack", load().awq_pack(_ptr(w), _ptr(qweight), _ptr(scales), _ptr(qzeros), 0, N, K,
                                            group_size, _stream(dev)))
     return qweight, scales, qzeros
+
+
+def w4_pack_codes(codes):
+    """uint8 codes [R, C] (values 0..15) -> int32 [R, ceil(C/8)], plain nibble order."""
+    _need(codes, "codes", torch.uint8, 2)
+    dev = codes.device
+    R, C = codes.shape
+    out = torch.empty((R, (C + 7) // 8), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check("w4_pack_codes", load().w4_pack_codes(_ptr(codes), _ptr(out), R, C, _stream(dev)))
+    return out
 
 
 def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):

@@ -131,6 +131,19 @@ int awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t
                                                     (hipStream_t)stream));
 }
 
+int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void* stream) {
+  const char* fn = "w4_pack_codes";
+  g_last_error.clear();
+  if (R < 0 || C < 0) return fail(W4_ERR_INVALID_ARG, "%s: negative size (R=%lld C=%lld)", fn, (long long)R, (long long)C);
+  if (R > kMaxDim || C > kMaxDim || R * ((C + 7) / 8) > (int64_t(1) << 40))
+    return fail(W4_ERR_UNSUPPORTED, "%s: size too large (R=%lld C=%lld)", fn, (long long)R, (long long)C);
+  if (R == 0 || C == 0) return W4_OK;
+  if (codes == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: codes is NULL", fn);
+  W4_TRY(check_ptrs(fn, {{"out", out}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_pack_codes(codes, out, R, C, (hipStream_t)stream));
+}
+
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (group_size != 128 || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   return awq_ws(M, N, K);

@@ -78,6 +78,7 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
                            hipStream_t stream);
+hipError_t launch_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, hipStream_t stream);
 hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros,
                                      void* out, int N, int K, hipStream_t stream);
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,

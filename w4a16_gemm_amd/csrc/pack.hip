@@ -171,6 +171,27 @@ __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict
   }
 }
 
+// One thread per output word (row r, word j): eight bytes of codes -> one word.
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ out,
+                                                          int64_t R, int64_t C) {
+  const int64_t W = (C + 7) / 8;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= R * W) return;
+  const int64_t r = tid / W, j = tid - r * W;
+  const uint8_t* src = codes + r * C + j * 8;
+  const int n = (int)min<int64_t>(8, C - j * 8);
+  uint32_t word = 0;
+  for (int i = 0; i < n; ++i) word |= ((uint32_t)src[i] & 15u) << (4 * i);
+  out[tid] = word;
+}
+
+hipError_t launch_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, hipStream_t stream) {
+  const int64_t total = R * ((C + 7) / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, (uint32_t*)out, R, C);
+  return hipGetLastError();
+}
+
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
                            hipStream_t stream) {
   const int npad = (N + 15) / 16 * 16;
