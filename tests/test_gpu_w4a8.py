@@ -121,3 +121,30 @@ def test_w4a8_full_size_sampled(group, M):
     xn = np.linalg.norm(rxq[ms].astype(np.float64), axis=1) * rsa[ms].astype(np.float64)
     err = normalized_error(to_np(y)[np.ix_(ms, ns)].astype(np.float64), yr, xn, wn)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("tiles", ["1", "2", "4", "off"])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (7, 1000, 2048), (16, 130, 13824), (3, 64, 128)])
+def test_w4a8_skinny_variants(group, tiles, M, N, K, monkeypatch):
+    """The M <= 16 W4A8 kernel at each tile width (forced through its tuning variable),
+    ragged N, one group (K = 128) and split K; 'off' forces the tiled GEMM.  int32
+    accumulators bit-exact on the oracle's xq."""
+    dev = device()
+    if tiles == "off":
+        monkeypatch.setenv("W4_W4A8_SKINNY", "0")
+    else:
+        monkeypatch.setenv("W4_W4A8_TILES", tiles)
+    announce(f"w4a8 skinny tiles={tiles} M={M} N={N} K={K} group={group}")
+    inp = synth.make_linear(M, N, K, seed=M * 11 + N, outliers=True, rms_spread=True, with_gamma=True)
+    q, cs, gs, (qw, gsd, csd) = _oracle_w4a8(inp.w.numpy(), group, dev)
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    xqd = torch.from_numpy(xq).to(dev)
+    acc = to_np(w4.w4a8_gemm_i32(xqd, qw, gsd, group, N=N))
+    assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, gs, 128))
+    out = to_np(w4.w4a8_gemm(xqd, torch.from_numpy(sa).to(dev), qw, gsd, csd, group)).astype(np.float64)
+    yr = ora.w4a8_linear_ref(ora.w4a8_acc_ref(xq, q, gs, 128), sa, cs)
+    qs = q.astype(np.float64) * (1 if gs is None else np.repeat(gs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * cs.astype(np.float64)
+    xn = np.linalg.norm(xq.astype(np.float64), axis=1) * sa.astype(np.float64)
+    assert normalized_error(out, yr, xn, wn) <= TOL

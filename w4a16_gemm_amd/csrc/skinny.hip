@@ -579,20 +579,21 @@ SkinnyPlan skinny_plan(int M, int N, int K) {
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int waves = skinny_waves(p.mt);
   // Tiles per workgroup: with more rows each X fragment should serve more tiles (X
-  // traffic is 4 M / T bytes per weight byte).  Split-K target: 320 workgroups for
-  // M <= 8; for 8 < M <= 16, 512 unless the columns alone give 320 (sweeps on the
-  // projection shapes).
+  // traffic is 4 M / T bytes per weight byte).  Split-K target: 320 workgroups, or 512
+  // for 8 < M <= 16 (and 4 < M <= 8 with long K) unless the columns alone give 320
+  // (sweeps on the projection shapes).
   t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4) {
     if (M <= 4) t = (N <= 16 * 320) ? 1 : ((N <= 32 * 480) ? 2 : 4);
-    else if (M <= 8) t = 2;
+    else if (M <= 8) t = N > 16384 ? 4 : 2;
     else if (M <= 16) t = 4;
     else t = ((N + 63) / 64 >= 128) ? 4 : 2;
   }
   p.tiles = t;
   p.depth = t == 1 ? 4 : 2;
   p.row_blocks = (N + 16 * t - 1) / (16 * t);
-  target = env_int("W4_SKINNY_BLOCKS", (M > 8 && M <= 16 && p.row_blocks < 320) ? 512 : 320);
+  target = env_int("W4_SKINNY_BLOCKS",
+                   (M > 4 && M <= 16 && p.row_blocks < 320 && (M > 8 || K > 8192)) ? 512 : 320);
   int splits = (target + p.row_blocks - 1) / p.row_blocks;
   splits = min(splits, ng / waves);  // at least one group per wave
   // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the codes

@@ -318,6 +318,142 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Skinny W4A8 (M <= 16): bandwidth-bound, every packed byte read once, on
+// v_mfma_i32_16x16x64_i8.  Work split as in the register-X W4A16 skinny kernel: a
+// workgroup (4 waves) owns 16 T columns and a range of groups, its waves take the groups
+// round robin with D register sets prefetched.  Per group a lane loads its 16-byte code
+// chunk (row l % 16, k-slot l / 16 = 32 k) of each tile -- one contiguous 1 KB block per
+// wave -- and the two 16-byte xq pieces of the same k range; MFMA j uses words 2j, 2j + 1
+// of the chunk (16 k) expanded to int8 (16 q per-channel, q s_g two-level).  The int32
+// accumulators need no per-group work: the sum is exact, so the cross-wave (LDS) and
+// split-K reductions are exact in any order.
+template <int T, bool TWO>
+struct W8Regs {
+  u32x4 b[T];      // code chunk of this lane's row in each n-tile
+  int4_t a[2];     // xq: k = 32 slot + 16 j .. + 15, j = 0, 1
+  int32_t gsv[T];  // group scale of this lane's row in each n-tile (two-level)
+};
+
+template <int T, bool TWO>
+__device__ __forceinline__ void w8_load(W8Regs<T, TWO>& r, const int8_t* __restrict__ xq,
+                                        const uint32_t* __restrict__ qweight, const int8_t* __restrict__ gscale,
+                                        int g, int n0, int lane, int M, int N, int K) {
+  const int ng = K / 128;
+  const int last_tile = (N - 1) >> 4;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int tile = min((n0 >> 4) + t, last_tile);
+    r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+    if (TWO) r.gsv[t] = gscale[(int64_t)g * N + min(n0 + 16 * t + (lane & 15), N - 1)];
+  }
+  const int m = min(lane & 15, M - 1);
+  const int4_t* src = reinterpret_cast<const int4_t*>(xq + (int64_t)m * K + g * 128 + (lane >> 4) * 32);
+  r.a[0] = src[0];
+  r.a[1] = src[1];
+}
+
+template <int T, bool TWO>
+__device__ __forceinline__ void w8_compute(const W8Regs<T, TWO>& r, int4_t (&acc)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    u16x2 sp = {1, 1}, cp = {0, 0};
+    if (TWO) {
+      const unsigned short g16 = (unsigned short)r.gsv[t];
+      sp = u16x2{g16, g16};
+      const unsigned short c16 = (unsigned short)(-8 * r.gsv[t]);
+      cp = u16x2{c16, c16};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t e[4];
+      const uint32_t w0 = r.b[t][2 * j], w1 = r.b[t][2 * j + 1];
+      if (TWO) {
+        unpack_i4_scaled(w0, sp, cp, e[0], e[1]);
+        unpack_i4_scaled(w1, sp, cp, e[2], e[3]);
+      } else {
+        unpack_i4x16(w0, e[0], e[1]);
+        unpack_i4x16(w1, e[2], e[3]);
+      }
+      const int4_t bv = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
+      acc[t] = mfma16_i8(r.a[j], bv, acc[t]);
+    }
+  }
+}
+
+template <int T, int D, bool TWO>
+__global__ __launch_bounds__(256) void w4a8_skinny_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
+    const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
+    int K, int splits, int gps) {
+  constexpr int WAVES = 4, kT = WAVES * kWave, kCols = 16 * T;
+  __shared__ int32_t red[WAVES][T * 4 * kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = blockIdx.x, split = blockIdx.y;
+  const int n0 = rb * kCols;
+  const int ng = K / 128;
+  const int gbeg = split * gps, gend = min(ng, gbeg + gps);
+
+  int4_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = int4_t{0, 0, 0, 0};
+  W8Regs<T, TWO> r[D];
+  const int glast = gend - 1;
+  const int g = gbeg + wave;
+#pragma unroll
+  for (int d = 0; d < D; ++d) w8_load<T, TWO>(r[d], xq, qweight, gscale, min(g + d * WAVES, glast), n0, lane, M, N, K);
+  // steady state without conditions, then the remaining < D groups (wave-uniform counts)
+  const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
+  int it = 0;
+  for (; it + D <= mine; it += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      w8_compute<T, TWO>(r[d], acc);
+      w8_load<T, TWO>(r[d], xq, qweight, gscale, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (it + d < mine) w8_compute<T, TWO>(r[d], acc);
+
+  // Cross-wave reduction: element (t, i) of lane l is row 4 (l / 16) + i, column
+  // n0 + 16 t + l % 16.
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][(t * 4 + i) * kWave + lane] = acc[t][i];
+  __syncthreads();
+  const int outs = M * kCols;
+  for (int o = threadIdx.x; o < outs; o += kT) {
+    const int m = o / kCols, nl = o - m * kCols, n = n0 + nl;
+    const int idx = ((nl >> 4) * 4 + (m & 3)) * kWave + (m >> 2) * 16 + (nl & 15);
+    int32_t v = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w][idx];
+    if (n >= N) continue;
+    if (splits == 1) {
+      if (!TWO) v >>= 4;  // exact: every term was 16 q
+      if (acc_out) acc_out[(int64_t)m * N + n] = v;
+      else y[(int64_t)m * N + n] = (half_t)(((float)v * s_a[m]) * (float)cscale[n]);
+    } else {
+      st_coherent(partials + ((int64_t)split * M + m) * N + n, v);
+    }
+  }
+  if (splits == 1) return;
+  if (!splitk_arrive(counters + rb, splits)) return;
+  for (int o = threadIdx.x; o < outs; o += kT) {
+    const int m = o / kCols, n = n0 + o - m * kCols;
+    if (n >= N) continue;
+    int32_t v = 0;
+    for (int sp_ = 0; sp_ < splits; ++sp_) v += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + n);
+    if (!TWO) v >>= 4;
+    if (acc_out) acc_out[(int64_t)m * N + n] = v;
+    else y[(int64_t)m * N + n] = (half_t)(((float)v * s_a[m]) * (float)cscale[n]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
@@ -327,9 +463,29 @@ hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, in
   return hipGetLastError();
 }
 
+// M <= 16 takes the skinny kernel (tiles of 16 columns per workgroup, split-K towards
+// 320 workgroups while each wave keeps a group); larger M the tiled MFMA GEMM.
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   (void)group_size;
   W4A8Plan p;
+  p.skinny = 0;
+  if (M <= 16 && env_int("W4_W4A8_SKINNY", 1)) {
+    const int ng = K / 128;
+    int t = env_int("W4_W4A8_TILES", 0);
+    if (t != 1 && t != 2 && t != 4) t = M <= 4 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : 4;
+    p.skinny = 1;
+    p.bm = 16;
+    p.tiles_m = 1;
+    p.tiles_n = (N + 16 * t - 1) / (16 * t);
+    p.tiles = t;
+    const int target = env_int("W4_W4A8_SKINNY_BLOCKS", 320);
+    int splits = (target + p.tiles_n - 1) / p.tiles_n;
+    splits = max(1, min(splits, ng / 4));
+    if (p.tiles_n >= kMaxCounters) splits = 1;
+    p.kt_per_split = (ng + splits - 1) / splits;
+    p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
+    return p;
+  }
   p.bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + WBN - 1) / WBN;
@@ -362,6 +518,23 @@ hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* q
   const half_t* cs = (const half_t*)cscale;
   half_t* yh = (half_t*)y;
   const int8_t* gs = group_size == -1 ? nullptr : gscale;
+  if (p.skinny) {
+    const dim3 sgrid(p.tiles_n, p.splits), sblock(256);
+#define W4A8_SKINNY(T, D, TWO)                                                                                  \
+  hipLaunchKernelGGL((w4a8_skinny_kernel<T, D, TWO>), sgrid, sblock, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out, \
+                     counters, partials, M, N, K, p.splits, p.kt_per_split)
+    if (gs) {
+      if (p.tiles == 4) W4A8_SKINNY(4, 2, true);
+      else if (p.tiles == 2) W4A8_SKINNY(2, 2, true);
+      else W4A8_SKINNY(1, 4, true);
+    } else {
+      if (p.tiles == 4) W4A8_SKINNY(4, 2, false);
+      else if (p.tiles == 2) W4A8_SKINNY(2, 2, false);
+      else W4A8_SKINNY(1, 4, false);
+    }
+#undef W4A8_SKINNY
+    return hipGetLastError();
+  }
 #define W4A8_LAUNCH(MI, TWO)                                                                                  \
   hipLaunchKernelGGL((w4a8_gemm_kernel<MI, TWO>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
                      counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
