@@ -245,8 +245,13 @@ GemmPlan gemm_plan(int M, int N, int K) {
   const int min_tiles = env_int("W4_GEMM_MIN_TILES", 256);
   const int forced = env_int("W4_GEMM_SHAPE", 0);  // 1..4 selects kShapes[forced - 1]
   int pick = 3;
+  // 64 < M <= 512: narrow (128-column) tiles and split-K to at least 320 workgroups
+  // (sweeps on K = 5120, N in {5120, 13824}, M = 96 .. 512).
+  const bool mid = M <= 512 && forced == 0;
   if (forced >= 1 && forced <= 4) {
     pick = forced - 1;
+  } else if (mid) {
+    pick = (M >= 96 && (N >= 8192 || M >= 256)) ? 1 : 3;
   } else {
     for (int i = 0; i < 4; ++i) {
       const int tm = (M + 32 * kShapes[i][0] - 1) / (32 * kShapes[i][0]);
@@ -265,7 +270,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
   const int tiles = p.tiles_m * p.tiles_n;
   int splits = 1;
   // fill the CUs when there are few tiles; keep >= 8 BK steps per split
-  while (tiles * splits < min_tiles / 2 && ktiles / (splits * 2) >= 8) splits *= 2;
+  const int want = mid ? 320 : min_tiles / 2;
+  while (tiles * splits < want && ktiles / (splits * 2) >= 8) splits *= 2;
+  const int forced_splits = env_int("W4_GEMM_SPLITS", 0);
+  if (forced_splits > 0) splits = min(forced_splits, ktiles);
   if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ktiles + splits - 1) / splits;
   p.splits = (ktiles + p.kt_per_split - 1) / p.kt_per_split;
