@@ -491,7 +491,7 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   p.tiles_n = (N + WBN - 1) / WBN;
   const int ng = K / WBK;
   const int tiles = p.tiles_m * p.tiles_n;
-  const int target = env_int("W4_W4A8_SPLIT_TARGET", 512);
+  const int target = env_int("W4_W4A8_SPLIT_TARGET", 128);  // int32 partials are M N 4 bytes per split
   int splits = 1;
   while (tiles * splits < target && ng / (splits * 2) >= 2) splits *= 2;
   if (tiles >= kMaxCounters) splits = 1;
