@@ -96,10 +96,11 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
 
 /*
  * awq_gemm -- Y [M, N] = X [M, K] . dequant(qweight, scales, qzeros)^T, fp32 accumulate,
- * fp16 output (round to nearest even).  Dispatch: M <= 64 uses the bandwidth-bound
- * skinny kernel (16x16x32 fp16 MFMA, split-K, per-group scaling in fp32); larger M uses
- * the LDS-staged 32x32x16 fp16 MFMA GEMM with in-register dequantization.  Results are
- * deterministic (split-K partials are summed in a fixed order).
+ * fp16 output (round to nearest even).  Dispatch: M <= 64 uses a bandwidth-bound skinny
+ * kernel (16x16x32 fp16 MFMA on exact fp16 encodings of the codes, per-group scaling in
+ * fp32; for M <= 4 with X staged in LDS); larger M uses the LDS-staged 32x32x16 fp16
+ * MFMA GEMM with in-register dequantization.  Results are deterministic (split-K
+ * partials are summed in a fixed order).
  */
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
              void* y, void* workspace, size_t workspace_bytes,
@@ -135,7 +136,9 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_
 /*
  * w4a8_gemm -- Y [M, N] = fp16(acc[m, n] * s_a[m] * cscale[n]) where
  * acc[m, n] = sum_k xq[m, k] * q[n, k] * s_g[n, k / G] (s_g = 1 for group_size == -1) is
- * computed exactly in int32 on the int8 MFMA units.  gscale is NULL iff group_size == -1.
+ * computed exactly in int32 on the int8 MFMA units (M <= 16: bandwidth-bound kernel on
+ * 16x16x64 int8 MFMA; larger M: LDS-staged 32x32x32 int8 MFMA GEMM).  gscale is NULL iff
+ * group_size == -1.
  */
 int w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
               const void* cscale, void* y, void* workspace, size_t workspace_bytes,

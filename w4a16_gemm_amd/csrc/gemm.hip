@@ -6,8 +6,12 @@
 // "Implement AWQ quantization support for LLaMA" (vllm-project/vllm PR 1032): the AWQ
 // GEMM runs dequantized fp16 weights through the tensor cores; dequantization is the
 // tricky part and the rest is normal FP16 work.  On gfx950 the same split holds: the
-// MFMA does the FP16 work; the dequantization (9 VALU ops to expand a word, 8 packed
-// fp16 ops for (q - z) * s) is amortized over the 128 rows of a wave tile.
+// MFMA does the FP16 work; the dequantization is amortized over the 128 rows of a wave
+// tile.  A word is expanded in 5 VALU ops to fp16 (1024 + q) at even k (code in the low
+// mantissa bits under exponent 2^10) and (64 + q) at odd k (code in mantissa bits 4..7
+// under exponent 2^6), in the k order 0,4,1,5,2,6,3,7; subtracting 1024 + z or 64 + z is
+// exact, and the multiply by s is the element's single fp16 rounding (4 packed adds, 4
+// packed multiplies).  X chunks are permuted to the same k order when staged in LDS.
 //
 // Tile: BM x BN x BK = (32 MI) x (128 NF) x 64, 256 threads, (MI, NF) in {4, 2} x {2, 1}.
 // The 4 waves split N: wave w owns 32 NF columns as NF 32-column MFMA fragments, and
@@ -112,7 +116,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int cid = threadIdx.x + i * kThreads;
-      lds[buf][swz(cid >> 3, cid & 7)] = areg[i];
+      const u32x4 v = areg[i];
+      u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching dequant_mixed
+      o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+      o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+      o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+      o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+      lds[buf][swz(cid >> 3, cid & 7)] = o;
     }
   };
   u32x4 breg[NF];
@@ -134,15 +144,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
       sraw[f] = scales[(int64_t)g * N + nclamp[f]];
     }
   };
-  half2_t negz2[NF], s2[NF];
+  half2_t c1024[NF], c64[NF], s2[NF];
   auto set_sz = [&]() {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const uint32_t z = (zraw[f] >> (4 * (nclamp[f] & 7))) & 15u;
-      negz2[f] = splat2(-(half_t)(1024u + z));
+      c1024[f] = splat2(-(half_t)(1024u + z));
+      c64[f] = splat2(-(half_t)(64u + z));
       s2[f] = splat2(sraw[f]);
     }
   };
+  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
 
   if (kbeg < kend) {
     load_a(kbeg);
@@ -171,7 +183,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
     for (int s = 0; s < 4; ++s) {
       half8_t bf[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) bf[f] = dequant8(breg[f][s], negz2[f], s2[f]);
+      for (int f = 0; f < NF; ++f) {
+        const uint32_t w = breg[f][s];
+        const uint32_t w8 = w >> 8;
+        half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
+        half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
+        half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
+        half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
+        p0 = (p0 + c1024[f]) * s2[f];
+        p1 = (p1 + c64[f]) * s2[f];
+        p2 = (p2 + c1024[f]) * s2[f];
+        p3 = (p3 + c64[f]) * s2[f];
+        bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
