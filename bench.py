@@ -367,31 +367,37 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
     return out
 
 
-def cpu_baseline(np, synth, host):
-    """The oracle (numpy dequant + fp64 matmul) on one decode step: the 4 projections at
-    M = 1, 4 and 16 (12 GEMMs), packed weights prepared untimed."""
+def cpu_baseline(np, synth, host, min_seconds=10.0, max_steps=8):
+    """The oracle (numpy dequant + fp64 matmul) on whole decode steps -- the 4 projections
+    at M = 1, 4 and 16 (12 GEMMs), packed weights prepared untimed -- repeated until about
+    min_seconds of CPU work (at most max_steps steps)."""
     import oracle.ref as ora
     from threadpoolctl import threadpool_info
 
     log("cpu baseline (oracle)")
+    packed = {}
+    for name, (K, N) in synth.LLAMA2_13B.items():
+        c, s, z = ora.quantize_asym(host[name].w.numpy(), G)
+        packed[name] = ora.pack_awq(c, s, z)
     tot_b = 0.0
     tot_t = 0.0
-    for name, (K, N) in synth.LLAMA2_13B.items():
-        w = host[name].w.numpy()
-        c, s, z = ora.quantize_asym(w, G)
-        qw, sg, qz = ora.pack_awq(c, s, z)
-        for M in (1, 4, 16):
-            x = host[name].x[:M].numpy()
-            t0 = time.perf_counter()
-            wd = ora.dequant_awq(qw, sg, qz, K, G)
-            ora.linear_ref(x, wd)
-            tot_t += time.perf_counter() - t0
-            tot_b += awq_bytes(M, N, K)
-            del wd
+    steps = 0
+    while steps < max_steps and (steps == 0 or tot_t < min_seconds):
+        for name, (K, N) in synth.LLAMA2_13B.items():
+            qw, sg, qz = packed[name]
+            for M in (1, 4, 16):
+                x = host[name].x[:M].numpy()
+                t0 = time.perf_counter()
+                wd = ora.dequant_awq(qw, sg, qz, K, G)
+                ora.linear_ref(x, wd)
+                tot_t += time.perf_counter() - t0
+                tot_b += awq_bytes(M, N, K)
+                del wd
+        steps += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(tot_b / tot_t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "one decode step: QKV/O/gate+up/down at M=1,4,16 (12 GEMMs), numpy fp64 dequant + BLAS matmul, "
-                      f"{tot_t:.1f} s", "host_cpu_count": os.cpu_count()}
+            "sample": f"{steps} decode steps: QKV/O/gate+up/down at M=1,4,16 (12 GEMMs each), numpy fp64 dequant "
+                      f"+ BLAS matmul, {tot_t:.1f} s", "host_cpu_count": os.cpu_count()}
 
 
 if __name__ == "__main__":
