@@ -102,8 +102,8 @@ def rotated_w4a8(qw, gs, cs, r):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
-                          "described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (sharding the layer over "
+                          "several GPUs is not implemented)"}))
         sys.exit(2)
 
     import numpy as np

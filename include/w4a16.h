@@ -61,7 +61,7 @@ extern "C" {
 enum {
   W4_OK = 0,
   W4_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, K not a multiple of G, misalignment */
-  W4_ERR_UNSUPPORTED = 2,   /* group size or shape this build does not implement */
+  W4_ERR_UNSUPPORTED = 2,   /* group size or shape not implemented */
   W4_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_bytes() */
   W4_ERR_DEVICE = 4,        /* current device is not gfx950 */
   W4_ERR_HIP = 5            /* a HIP runtime call failed (see w4_last_error) */

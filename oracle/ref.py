@@ -23,7 +23,7 @@ Sources (web pages; cited by title and the part of the page):
   matmuls that output int32 and are rescaled by weight and activation scales,
   with activations quantized dynamically.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * R1 asymmetric rule: per (row n, group g) ``s = (max - min) / 15`` computed in
   fp32 (IEEE division), floored at 1e-5, stored as fp16 (RNE);
