@@ -209,3 +209,32 @@ def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
     err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
                            np.linalg.norm(ref["w_deq"], axis=1))
     assert err <= TOL, err
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 48, 64, 65, 96, 127, 129, 200, 300]))
+        N = int(rng.integers(1, 700))
+        K = 128 * int(rng.integers(1, 41))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(40, seed=2026))
+def test_awq_gemm_random_shapes(M, N, K):
+    """Seeded random shapes across every dispatch boundary (M = 1..300, any N, K up to
+    5120): both skinny kernels, every GEMM tile shape the plan picks, split and unsplit,
+    ragged N; outputs pre-poisoned with NaN."""
+    dev = device()
+    announce(f"awq_gemm random M={M} N={N} K={K} ws={w4.awq_gemm_workspace_bytes(M, N, K)}")
+    inp = synth.make_linear(M, N, K, seed=M * 131 + N * 7 + K, outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err

@@ -148,3 +148,23 @@ def test_w4a8_skinny_variants(group, tiles, M, N, K, monkeypatch):
     wn = np.linalg.norm(qs, axis=1) * cs.astype(np.float64)
     xn = np.linalg.norm(xq.astype(np.float64), axis=1) * sa.astype(np.float64)
     assert normalized_error(out, yr, xn, wn) <= TOL
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([1, 2, 5, 16, 17, 33, 64, 100, 257])), int(rng.integers(1, 600)),
+             128 * int(rng.integers(1, 33))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("M,N,K", _random_shapes(16, seed=2027))
+def test_w4a8_random_shapes(group, M, N, K):
+    """Seeded random shapes across the skinny / GEMM boundary and split-K choices: int32
+    accumulators bit-exact on the oracle's xq."""
+    dev = device()
+    announce(f"w4a8 random M={M} N={N} K={K} group={group}")
+    inp = synth.make_linear(M, N, K, seed=M * 17 + N + K, outliers=True, rms_spread=True, with_gamma=True)
+    q, cs, gs, (qw, gsd, csd) = _oracle_w4a8(inp.w.numpy(), group, dev)
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    acc = to_np(w4.w4a8_gemm_i32(torch.from_numpy(xq).to(dev), qw, gsd, group, N=N))
+    assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, gs, 128))
