@@ -56,6 +56,12 @@ Readings where the pages are silent:
   ``xq = clamp(rint(fp32(y32 * inv)), -127, 127)``, ``s_a = fp32(M / 127)``;
   a zero row gives ``s_a = 1``, ``xq = 0``.  Without gamma (no-norm mode)
   ``y32 = x``.
+* R12 SiLU-gated activations ([QQQ-lmdeploy], "Modification": online
+  quantization fused with element-wise operations such as SiLU; gate and up
+  weights fused into one weight): the fused gate+up output ``[M, 2I]`` holds gate
+  in columns ``0..I-1`` and up in ``I..2I-1``; ``y = silu(gate) * up`` with
+  ``silu(g) = g / (1 + exp(-g))``, in fp64 with no fp16 round trip, then the R6
+  quantization decision on ``fp32(y)``.
 """
 from __future__ import annotations
 
@@ -70,7 +76,7 @@ __all__ = [
     "quantize_asym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref",
-    "w4a8_acc_ref", "w4a8_linear_ref",
+    "w4a8_acc_ref", "w4a8_linear_ref", "silu_ref", "silu_mul_quant_ref",
 ]
 
 
@@ -303,6 +309,15 @@ def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):
         r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + float(eps))
         y64 = x64 * r[:, None] * np.asarray(gamma16, dtype=F16).astype(F64)[None, :]
         y32 = y64.astype(F32)
+    return _quant_rows_int8(y32)
+
+
+def _quant_rows_int8(y32: np.ndarray):
+    """Per-row symmetric int8 quantization of fp32 values (R6): ``amax = max|y|``,
+    ``xq = clamp(rint(y * fp32(127 / amax)), -127, 127)``, ``s_a = amax / 127``; a zero
+    row gives ``xq = 0, s_a = 1``.  Returns ``(xq, s_a, t)`` with ``t`` the fp32 values
+    that were rounded."""
+    M, K = y32.shape
     amax = np.abs(y32).max(axis=1) if K else np.zeros(M, F32)
     xq = np.zeros((M, K), dtype=np.int8)
     s_a = np.ones(M, dtype=F32)
@@ -316,6 +331,30 @@ def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):
         s_a[m] = amax[m] / F32(127.0)
         t_all[m] = t
     return xq, s_a, t_all
+
+
+def silu_ref(g: np.ndarray) -> np.ndarray:
+    """SiLU in fp64: ``g / (1 + exp(-g))`` (written as ``g * sigmoid(g)`` with the
+    overflow-safe branch for negative g)."""
+    g = np.asarray(g, dtype=F64)
+    e = np.exp(-np.abs(g))
+    sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return g * sig
+
+
+def silu_mul_quant_ref(gate_up16: np.ndarray):
+    """The SiLU-gated input of the down projection quantized per token (R12): the fused
+    gate+up output ``[M, 2I]`` holds gate in columns ``0..I-1`` and up in ``I..2I-1``;
+    ``y = silu(gate) * up`` in fp64 (no fp16 round trip), then the per-token int8 rule
+    of :func:`_quant_rows_int8` on ``fp32(y)``.  Returns ``(xq int8 [M, I], s_a fp32 [M],
+    t fp64 [M, I])``."""
+    gu = np.asarray(gate_up16)
+    if gu.dtype != F16 or gu.ndim != 2 or gu.shape[1] % 2:
+        raise ValueError("gate_up16 must be a 2-D float16 array with an even number of columns")
+    I = gu.shape[1] // 2
+    g = gu[:, :I].astype(F64)
+    u = gu[:, I:].astype(F64)
+    return _quant_rows_int8((silu_ref(g) * u).astype(F32))
 
 
 def w4a8_acc_ref(xq: np.ndarray, q: np.ndarray, gscale_ng, group_size: int) -> np.ndarray:

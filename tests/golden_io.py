@@ -66,3 +66,24 @@ def read_cases(name):
         else:
             raise ValueError(f"unknown fixture key {tok[0]!r}")
     return cases
+
+
+def read_silu_cases():
+    """Cases of golden/silu_mul_quant_worked.txt: ``gate_up`` (fp16 hex), ``s_a``
+    (decimal) and ``xq`` (ints)."""
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, "silu_mul_quant_worked.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *rest = line.split()
+        if key == "case":
+            cur = {"name": rest[0]}
+            cases.append(cur)
+        elif key == "gate_up":
+            cur["gate_up"] = _values(rest)
+        elif key == "s_a":
+            cur["s_a"] = float(rest[0])
+        elif key == "xq":
+            cur["xq"] = [int(v) for v in rest]
+    return cases

@@ -19,7 +19,7 @@ from fractions import Fraction
 import numpy as np
 
 import synth
-from golden_io import read_cases, read_pack_words
+from golden_io import read_cases, read_pack_words, read_silu_cases
 
 F16, F32, F64 = np.float16, np.float32, np.float64
 
@@ -302,6 +302,57 @@ def pin_quant_act_closed_forms(ora):
     assert float(sz[0]) == 1.0 and not xz.any()
 
 
+def pin_silu_worked(ora):
+    """Hand-worked SiLU-gated row (tests/golden/silu_mul_quant_worked.txt)."""
+    for case in read_silu_cases():
+        xq, sa, _ = ora.silu_mul_quant_ref(case["gate_up"][None, :])
+        assert xq[0].tolist() == case["xq"], case["name"]
+        assert abs(float(sa[0]) - case["s_a"]) <= 1e-7 * case["s_a"], case["name"]
+
+
+def pin_silu_closed_forms(ora):
+    """silu(0) = 0; silu(g) - silu(-g) = g; silu(ln 3) = 0.75 ln 3; silu(g) -> g for
+    large g and -> 0 for very negative g (no overflow at the fp16 extremes)."""
+    g = np.concatenate([np.linspace(-30, 30, 601), [0.0, 1e-3, -1e-3, 65504.0, -65504.0]])
+    s = ora.silu_ref(g)
+    assert s[-5] == 0.0
+    assert np.all(np.abs((s - ora.silu_ref(-g)) - g) <= 1e-14 * np.maximum(1, np.abs(g)))
+    assert abs(ora.silu_ref(np.log(3.0)) - 0.75 * np.log(3.0)) <= 1e-15
+    assert s[-2] == 65504.0 and s[-1] == 0.0 and np.all(np.isfinite(s))
+    # the minimum of silu is about -0.2785 at g = -1.2785 (root of 1 + g (1 - sigmoid(g)) = 0)
+    assert abs(s.min() - (-0.27846454)) < 1e-3
+
+
+def pin_silu_special_cases(ora):
+    """Gate values >= 40 make silu(g) = g exactly in fp64 (exp(-40) < 2^-53), so with
+    up = 1 the SiLU-gated quantization equals the plain per-token rule on the gate,
+    and with up = -1 its codes are negated; a zero gate row gives s_a = 1, codes 0."""
+    rng = _rng(31)
+    M, I = 6, 384
+    gate = rng.uniform(40, 2000, size=(M, I)).astype(F16)
+    gate[:, ::7] = rng.uniform(40, 60000, size=(M, (I + 6) // 7)).astype(F16)
+    ones = np.ones((M, I), F16)
+    xq, sa, _ = ora.silu_mul_quant_ref(np.concatenate([gate, ones], axis=1))
+    rq, rsa, _ = ora.w4a8_quant_act_ref(gate, None)
+    assert np.array_equal(xq, rq) and np.array_equal(sa, rsa)
+    xn, san, _ = ora.silu_mul_quant_ref(np.concatenate([gate, -ones], axis=1))
+    assert np.array_equal(xn, -rq) and np.array_equal(san, rsa)
+    z = np.zeros((1, 2 * I), F16)
+    z[0, I:] = 5.0
+    xz, sz, _ = ora.silu_mul_quant_ref(z)
+    assert float(sz[0]) == 1.0 and not xz.any()
+    # a row with up = 0 except one element: only that element is non-zero, code +-127
+    r = np.zeros((1, 2 * I), F16)
+    r[0, :I] = rng.uniform(-4, 4, size=I).astype(F16)
+    r[0, I + 17] = 2.0
+    xo, so, _ = ora.silu_mul_quant_ref(r)
+    expect = np.zeros(I, np.int64)
+    sv = ora.silu_ref(float(r[0, 17]))
+    expect[17] = 127 if sv > 0 else -127
+    assert np.array_equal(xo[0].astype(np.int64), expect)
+    assert abs(float(so[0]) - abs(2.0 * sv) / 127) <= 1e-7 * abs(2.0 * sv) / 127
+
+
 def pin_w4a8_acc_bruteforce(ora):
     """Integer accumulators against Python-int loops, both weight variants."""
     rng = _rng(31)
@@ -334,4 +385,5 @@ ALL_PINS = [
     pin_fraction_bruteforce, pin_identity_probe, pin_per_channel_special_case,
     pin_constructed_exact_gemm,
     pin_w4a8_worked, pin_w4a8_exhaustive, pin_quant_act_closed_forms, pin_w4a8_acc_bruteforce,
+    pin_silu_worked, pin_silu_closed_forms, pin_silu_special_cases,
 ]

@@ -36,6 +36,10 @@ MUTANTS = [
     ("act truncation", "xq[m] = np.clip(np.rint(t), -127, 127)", "xq[m] = np.clip(np.trunc(t), -127, 127)"),
     ("act rounds half away from zero", "xq[m] = np.clip(np.rint(t), -127, 127)", "xq[m] = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -127, 127)"),
     ("weight codes round half away from zero", "q = np.clip(np.rint(w / s[:, :, None])", "q = np.clip(np.sign(w) * np.floor(np.abs(w / s[:, :, None]) + 0.5)"),
+    ("silu returns the sigmoid", "    return g * sig\n", "    return sig\n"),
+    ("silu sigmoid of -g", "sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))", "sig = np.where(g >= 0, e / (1.0 + e), 1.0 / (1.0 + e))"),
+    ("silu gate and up swapped", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "u = gu[:, :I].astype(F64)\n    g = gu[:, I:].astype(F64)"),
+    ("silu gate and up interleaved", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "g = gu[:, 0::2].astype(F64)\n    u = gu[:, 1::2].astype(F64)"),
     ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
 ]
 
