@@ -364,6 +364,22 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
                 "frac_f16": round(ops / t / 1e12 / F16_PEAK_TFLOPS, 4), "quant_act_us": round(tq * 1e6, 2)}
         del copies, qw, gs, cs
     out["w4a8_5120x13824"] = w8
+    # SiLU-gated quantization of the down projection's input (I = 13824), 4 rotated inputs
+    log("detail: silu_mul_quant")
+    smq = {}
+    I = 13824
+    for M in (1, 16, 256, 4096):
+        nbuf = 4 if M < 4096 else 1
+        gus = [synth.make_activations(M, 2 * I, seed=M + r, rms_spread=True).to(dev) for r in range(nbuf)]
+        xq = torch.empty((M, I), dtype=torch.int8, device=dev)
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+        calls = [w4.bind_w4a8_silu_mul_quant(g, xq, sa) for g in gus]
+        t = _time_calls(torch, calls, max(it, 16))
+        b = M * (2 * I * 2 + I + 4)
+        smq[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+                        "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del gus
+    out["silu_mul_quant_I13824"] = smq
     return out
 
 

@@ -130,6 +130,22 @@ int w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale,
 int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a,
                    int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
 
+/*
+ * w4a8_silu_mul_quant -- the SiLU-gated input of the down projection, quantized per token
+ * ("[Feature] support qqq(w4a8) for lmdeploy", "Modification": online quantization fused
+ * with element-wise operations such as SiLU; gate and up weights fused into one weight).
+ * gate_up: fp16 [M, 2K] row-major, the fused gate+up projection output, gate in columns
+ * 0..K-1 and up in K..2K-1.  y = silu(gate) * up with silu(g) = g / (1 + exp(-g)), in
+ * fp32 with no fp16 round trip; then the rule of w4a8_quant_act on y: xq int8 [M, K],
+ * s_a fp32 [M] (a zero row gives xq = 0, s_a = 1).  K must be a positive multiple of 8
+ * (at most 2^29); N and group_size are unused.  The caller owns every buffer; all
+ * pointers are device pointers, 16-byte aligned; the call is asynchronous on `stream`.
+ * Codes equal those of the exact y except where y * 127 / max|y| lies within the fp32
+ * error of exp and the three roundings of a half-integer (a difference of 1 there).
+ */
+int w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a,
+                        int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
 /* w4a8_gemm_workspace_bytes -- as awq_gemm_workspace_bytes, for w4a8_gemm / _i32. */
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
 

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
               "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
-              "w4_last_error", "w4_pack_codes"):
+              "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant"):
         assert n in names
 
 
@@ -71,6 +71,7 @@ def test_empty_shapes_are_noops(lib):
     assert lib.awq_gemm(None, None, None, None, None, None, 0, 4, 0, 256, 128, None) == 0
     assert lib.w4a8_gemm(None, None, None, None, None, None, None, 0, 0, 64, 256, -1, None) == 0
     assert lib.w4a8_quant_act(None, None, ctypes.c_float(1e-5), None, None, 0, 0, 256, 0, None) == 0
+    assert lib.w4a8_silu_mul_quant(None, None, None, 0, 0, 256, 0, None) == 0
 
 
 def test_pack_codes_validation(lib):
@@ -94,6 +95,12 @@ def test_w4a8_validation(lib):
     assert lib.w4a8_gemm(f, f, f, None, f, f, None, 0, 4, 64, 256, 32, None) == 2
     assert lib.w4a8_quant_act(f, None, ctypes.c_float(1e-5), f, f, 4, 0, 100, 0, None) == 1
     assert lib.w4a8_quant_act(f, None, ctypes.c_float(-1.0), f, f, 4, 0, 128, 0, None) == 1
+    assert lib.w4a8_silu_mul_quant(f, f, f, 4, 0, 100, 0, None) == 1
+    assert "multiple of 8" in lib.w4_last_error().decode()
+    assert lib.w4a8_silu_mul_quant(f, f, f, -1, 0, 128, 0, None) == 1
+    assert lib.w4a8_silu_mul_quant(f, None, f, 4, 0, 128, 0, None) == 1
+    assert "xq is NULL" in lib.w4_last_error().decode()
+    assert lib.w4a8_silu_mul_quant(f, f, f, 4, 0, 1 << 30, 0, None) == 2
     assert lib.w4a8_pack(f, f, None, f, 0, 64, 256, 128, None) == 1
     assert lib.awq_pack(f, f, f, f, 0, 64, 256, 32, None) == 2
 

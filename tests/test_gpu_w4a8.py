@@ -7,6 +7,8 @@
 * w4a8_gemm_i32: the int32 accumulators, bit-exact, fed the oracle's xq and packed
   weights (per-channel and two-level g128), small ragged shapes and the full shapes.
 * w4a8_gemm: fp16 outputs within the normalized 2e-3 bound.
+* w4a8_silu_mul_quant: codes equal except at near-ties (the kernel's y is fp32, the
+  oracle's fp64), where they may differ by 1; s_a within 1e-6 relative.
 """
 import numpy as np
 import pytest
@@ -59,6 +61,65 @@ def test_quant_act_rmsnorm_near_ties_only(M, K):
     rel = np.abs(to_np(sa).astype(np.float64) / rsa.astype(np.float64) - 1)
     assert rel.max() <= 2e-6
     assert np.all(np.abs(gq).max(axis=1)[np.abs(x.numpy()).max(axis=1) > 0] == 127)
+
+
+# |t_gpu - t_oracle| bound for the SiLU-gated quantization argument t = y * 127 / max|y|:
+# the kernel's fp32 y = silu(g) * u carries exp (about 1 ulp), the add, the correctly
+# rounded division and the product, a relative error below ~3.5 ulp = 2.1e-7 against
+# fp32 of the exact y; t = y * fp32(127 / amax) adds the same for amax and two roundings,
+# about 5.5e-7 relative, i.e. |dt| <= 127 * 5.5e-7 = 7e-5; doubled for margin.
+NEAR_TIE_SILU = 1.5e-4
+
+
+# widths cover every launch variant: 256 threads with 1, 2, 4 and 8 vectors per thread,
+# 1024 threads with 4 and 8, and the streaming variant; I = 8 leaves 255 threads idle
+@pytest.mark.parametrize("M,I", [(1, 8), (2, 1000), (3, 2056), (64, 5120), (1, 13824), (16, 13824),
+                                 (257, 13824), (5, 20000), (4, 40000), (3, 70008), (4096, 13824)])
+def test_silu_mul_quant_near_ties_only(M, I):
+    dev = device()
+    announce(f"silu_mul_quant M={M} I={I}")
+    gu = synth.make_activations(M, 2 * I, seed=M + I, rms_spread=True)
+    gu[0, :I] = 0  # zero gate row: y = 0, s_a = 1, codes 0
+    if M > 2:
+        gu[1, :I] = -65504.0  # silu -> -0: a zero row from the exp overflow side
+        gu[2, : I // 2] = 65504.0  # silu(g) = g: the largest |y| in the test
+    xq, sa = w4.w4a8_silu_mul_quant(gu.to(dev))
+    torch.cuda.synchronize()
+    rxq, rsa, t = ora.silu_mul_quant_ref(gu.numpy())
+    gq = to_np(xq).astype(np.int64)
+    diff = np.abs(gq - rxq.astype(np.int64))
+    assert diff.max() <= 1
+    frac = np.abs(np.abs(t - np.trunc(t)) - 0.5)
+    assert np.all(frac[diff == 1] < NEAR_TIE_SILU), float(frac[diff == 1].max())
+    assert (diff == 1).mean() < 1e-3
+    rel = np.abs(to_np(sa).astype(np.float64) / rsa.astype(np.float64) - 1)
+    assert rel.max() <= 1e-6
+    assert float(to_np(sa)[0]) == 1.0 and not gq[0].any()
+    if M > 2:
+        assert float(to_np(sa)[1]) == 1.0 and not gq[1].any()
+    live = np.abs(t).max(axis=1) > 0
+    assert np.all(np.abs(gq).max(axis=1)[live] == 127)
+
+
+def test_silu_mul_quant_bound_call_repeats():
+    dev = device()
+    announce("silu_mul_quant bound call")
+    M, I = 16, 13824
+    gu = synth.make_activations(M, 2 * I, seed=5, rms_spread=True).to(dev)
+    xq = torch.empty((M, I), dtype=torch.int8, device=dev)
+    sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    call = w4.bind_w4a8_silu_mul_quant(gu, xq, sa)
+    call()
+    torch.cuda.synchronize()
+    first = (to_np(xq).copy(), to_np(sa).copy())
+    xq.fill_(0)
+    sa.fill_(0)
+    call()
+    torch.cuda.synchronize()
+    rq, rs = w4.w4a8_silu_mul_quant(gu)
+    torch.cuda.synchronize()
+    for a in (first, (to_np(xq), to_np(sa))):
+        assert np.array_equal(a[0], to_np(rq)) and np.array_equal(a[1].view(np.uint32), to_np(rs).view(np.uint32))
 
 
 def _oracle_w4a8(w16, group, dev):

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     bind_awq_gemm,
     bind_w4a8_gemm,
     bind_w4a8_quant_act,
+    bind_w4a8_silu_mul_quant,
     lib_path,
     qweight_shape,
     load,
@@ -20,5 +21,6 @@ from ._lib import (  # noqa: F401
     w4a8_gemm_workspace_bytes,
     w4a8_pack,
     w4a8_quant_act,
+    w4a8_silu_mul_quant,
     w4_pack_codes,
 )

@@ -52,6 +52,7 @@ def load():
             "awq_gemm": [P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4a8_pack": [P, P, P, P, I64, I64, I64, I32, P],
             "w4a8_quant_act": [P, P, F, P, P, I64, I64, I64, I32, P],
+            "w4a8_silu_mul_quant": [P, P, P, I64, I64, I64, I32, P],
             "w4a8_gemm": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4a8_gemm_i32": [P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4_pack_codes": [P, P, I64, I64, P],
@@ -233,6 +234,22 @@ def w4a8_quant_act(x: torch.Tensor, gamma=None, eps: float = 1e-5):
     return xq, s_a
 
 
+def w4a8_silu_mul_quant(gate_up: torch.Tensor):
+    """fp16 fused gate+up output [M, 2I] (gate columns first) -> (xq int8 [M, I] of
+    silu(gate) * up, s_a fp32 [M])."""
+    _need(gate_up, "gate_up", torch.float16, 2)
+    dev = gate_up.device
+    M, K2 = gate_up.shape
+    if K2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    xq = torch.empty((M, K2 // 2), dtype=torch.int8, device=dev)
+    s_a = torch.empty((M,), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("w4a8_silu_mul_quant", load().w4a8_silu_mul_quant(_ptr(gate_up), _ptr(xq), _ptr(s_a), M, 0,
+                                                                 K2 // 2, 0, _stream(dev)))
+    return xq, s_a
+
+
 def w4a8_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = -1) -> int:
     return int(load().w4a8_gemm_workspace_bytes(M, N, K, group_size))
 
@@ -350,5 +367,29 @@ def bind_w4a8_quant_act(x, gamma, xq, s_a, eps: float = 1e-5):
         rc = fn(*args)
         if rc != W4_OK:
             _check("w4a8_quant_act", rc)
+        return keep
+    return call
+
+
+def bind_w4a8_silu_mul_quant(gate_up, xq, s_a):
+    """As bind_awq_gemm, for w4a8_silu_mul_quant."""
+    _need(gate_up, "gate_up", torch.float16, 2)
+    dev = gate_up.device
+    _need(xq, "xq", torch.int8, 2, dev)
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    M, K2 = gate_up.shape
+    if K2 % 2 or tuple(xq.shape) != (M, K2 // 2) or tuple(s_a.shape) != (M,):
+        raise ValueError("shapes: gate_up [M, 2I], xq [M, I], s_a [M]")
+    lib = load()
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+    args = (_ptr(gate_up), _ptr(xq), _ptr(s_a), M, 0, K2 // 2, 0, stream)
+    fn = lib.w4a8_silu_mul_quant
+    keep = (gate_up, xq, s_a)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w4a8_silu_mul_quant", rc)
         return keep
     return call

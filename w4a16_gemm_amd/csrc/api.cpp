@@ -204,6 +204,20 @@ int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, floa
   return launched(fn, w4::launch_w4a8_quant_act(x, gamma, eps, xq, s_a, (int)M, (int)K, (hipStream_t)stream));
 }
 
+int w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int64_t M, int64_t N, int64_t K,
+                        int32_t group_size, void* stream) {
+  const char* fn = "w4a8_silu_mul_quant";
+  (void)group_size;
+  g_last_error.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(W4_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (K == 0 || K % 8 != 0) return fail(W4_ERR_INVALID_ARG, "%s: K=%lld must be a positive multiple of 8", fn, (long long)K);
+  if (M > kMaxDim || K > kMaxDim / 2) return fail(W4_ERR_UNSUPPORTED, "%s: size above the limit (M <= 2^30, K <= 2^29)", fn);
+  if (M == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"gate_up", gate_up}, {"xq", xq}, {"s_a", s_a}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w4a8_silu_mul_quant(gate_up, xq, s_a, (int)M, (int)K, (hipStream_t)stream));
+}
+
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if ((group_size != 128 && group_size != -1) || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim ||
       N > kMaxDim || K > kMaxDim)

@@ -95,6 +95,8 @@ hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
                                  int K, hipStream_t stream);
+hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int M, int I,
+                                      hipStream_t stream);
 
 size_t w4a8_workspace_bytes(int M, int N, int K, int group_size);
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,

@@ -26,6 +26,9 @@ namespace {
 // ------------------------------------------------------------ quant_act
 constexpr int kQThreads = 256;
 
+// Row kernels loop over rows; at most 2^20 workgroups are launched.
+inline unsigned row_grid(int M) { return (unsigned)(M < (1 << 20) ? M : (1 << 20)); }
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   __syncthreads();
@@ -46,58 +49,150 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const half_t* __restrict__ x,
                                                                const half_t* __restrict__ gamma, float eps,
                                                                int8_t* __restrict__ xq, float* __restrict__ s_a,
-                                                               int K) {
+                                                               int M, int K) {
   __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const half8_t* xr = reinterpret_cast<const half8_t*>(x + row * K);
-  const half8_t* gr = reinterpret_cast<const half8_t*>(gamma);
-  const int nv = K / 8;
-  float r = 1.0f;
-  if (gamma) {
-    float ss = 0.0f;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const half8_t* xr = reinterpret_cast<const half8_t*>(x + row * K);
+    const half8_t* gr = reinterpret_cast<const half8_t*>(gamma);
+    const int nv = K / 8;
+    float r = 1.0f;
+    if (gamma) {
+      float ss = 0.0f;
+      for (int j = threadIdx.x; j < nv; j += kQThreads) {
+        const half8_t v = xr[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
+      }
+      ss = block_sum(ss, red);
+      r = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    float amax = 0.0f;
     for (int j = threadIdx.x; j < nv; j += kQThreads) {
       const half8_t v = xr[j];
+      if (gamma) {
+        const half8_t g = gr[j];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
-    }
-    ss = block_sum(ss, red);
-    r = 1.0f / sqrtf(ss / (float)K + eps);
-  }
-  float amax = 0.0f;
-  for (int j = threadIdx.x; j < nv; j += kQThreads) {
-    const half8_t v = xr[j];
-    if (gamma) {
-      const half8_t g = gr[j];
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(((float)v[i] * r) * (float)g[i]));
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(((float)v[i] * r) * (float)g[i]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
-    }
-  }
-  amax = block_max(amax, red);
-  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
-  uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * K);
-  for (int j = threadIdx.x; j < nv; j += kQThreads) {
-    const half8_t v = xr[j];
-    uint64_t packed = 0;
-    if (gamma) {
-      const half8_t g = gr[j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float yv = ((float)v[i] * r) * (float)g[i];
-        const float q = fminf(fmaxf(rintf(yv * inv), -127.0f), 127.0f);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float q = fminf(fmaxf(rintf((float)v[i] * inv), -127.0f), 127.0f);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
       }
     }
-    dst[j] = packed;
+    amax = block_max(amax, red);
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+    uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * K);
+    for (int j = threadIdx.x; j < nv; j += kQThreads) {
+      const half8_t v = xr[j];
+      uint64_t packed = 0;
+      if (gamma) {
+        const half8_t g = gr[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float yv = ((float)v[i] * r) * (float)g[i];
+          const float q = fminf(fmaxf(rintf(yv * inv), -127.0f), 127.0f);
+          packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float q = fminf(fmaxf(rintf((float)v[i] * inv), -127.0f), 127.0f);
+          packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+        }
+      }
+      dst[j] = packed;
+    }
+  }
+}
+
+// ------------------------------------------------------- silu_mul_quant
+// The SiLU-gated input of the down projection, quantized per token: row m of the fused
+// gate+up output [M, 2I] holds gate in columns 0..I-1 and up in I..2I-1;
+// y = silu(g) * u in fp32 with silu(g) = g / (1 + exp(-g)) (exp(-g) = inf for very
+// negative g gives -0), then the per-token int8 rule of quant_act.
+//
+// One workgroup of T threads per row.  With R > 0 the row fits in registers (R vectors
+// of 8 per thread, T * R * 8 >= I): every load is issued up front (clamped indexes, so
+// all are in bounds and none waits on a branch), y is formed once and kept for the code
+// pass, and each input byte is read once.  R = 0 streams longer rows twice (max pass,
+// then the code pass recomputes y).
+template <int T>
+__device__ __forceinline__ float block_max_t(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ uint64_t pack_codes8(const float* y, float inv) {
+  uint64_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = fminf(fmaxf(rintf(y[i] * inv), -127.0f), 127.0f);
+    packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+  }
+  return packed;
+}
+
+template <int T, int R>
+__global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restrict__ gu, int8_t* __restrict__ xq,
+                                                            float* __restrict__ s_a, int M, int I) {
+  __shared__ float red[T / 64];
+  const int nv = I / 8;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const half8_t* g8 = reinterpret_cast<const half8_t*>(gu + row * 2 * I);
+    const half8_t* u8 = g8 + nv;
+    uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * I);
+    float amax = 0.0f;
+    if constexpr (R > 0) {
+      half8_t gv[R], uv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int j = min((int)threadIdx.x + r * T, nv - 1);
+        gv[r] = g8[j];
+        uv[r] = u8[j];
+      }
+      float y[R][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool live = (int)threadIdx.x + r * T < nv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          y[r][i] = live ? silu_f32((float)gv[r][i]) * (float)uv[r][i] : 0.0f;
+          amax = fmaxf(amax, fabsf(y[r][i]));
+        }
+      }
+      amax = block_max_t<T>(amax, red);
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int j = (int)threadIdx.x + r * T;
+        if (j < nv) dst[j] = pack_codes8(y[r], inv);
+      }
+    } else {
+      for (int j = threadIdx.x; j < nv; j += T) {
+        const half8_t g = g8[j], u = u8[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(silu_f32((float)g[i]) * (float)u[i]));
+      }
+      amax = block_max_t<T>(amax, red);
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+      for (int j = threadIdx.x; j < nv; j += T) {
+        const half8_t g = g8[j], u = u8[j];
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = silu_f32((float)g[i]) * (float)u[i];
+        dst[j] = pack_codes8(y, inv);
+      }
+    }
   }
 }
 
@@ -458,8 +553,25 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
                                  int K, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_act_kernel, dim3(M), dim3(kQThreads), 0, stream, (const half_t*)x,
-                     (const half_t*)gamma, eps, xq, s_a, K);
+  hipLaunchKernelGGL(quant_act_kernel, dim3(row_grid(M)), dim3(kQThreads), 0, stream, (const half_t*)x,
+                     (const half_t*)gamma, eps, xq, s_a, M, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int M, int I,
+                                      hipStream_t stream) {
+  const int nv = I / 8;
+  const half_t* gu = (const half_t*)gate_up;
+  const dim3 grid(row_grid(M));
+#define W4_SMQ(T, R) hipLaunchKernelGGL((silu_mul_quant_kernel<T, R>), grid, dim3(T), 0, stream, gu, xq, s_a, M, I)
+  if (nv <= 256) W4_SMQ(256, 1);
+  else if (nv <= 512) W4_SMQ(256, 2);
+  else if (nv <= 1024) W4_SMQ(256, 4);
+  else if (nv <= 2048) W4_SMQ(256, 8);
+  else if (nv <= 4096) W4_SMQ(1024, 4);
+  else if (nv <= 8192) W4_SMQ(1024, 8);
+  else W4_SMQ(1024, 0);
+#undef W4_SMQ
   return hipGetLastError();
 }
 
