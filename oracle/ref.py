@@ -61,7 +61,10 @@ Readings where the pages are silent:
   weights fused into one weight): the fused gate+up output ``[M, 2I]`` holds gate
   in columns ``0..I-1`` and up in ``I..2I-1``; ``y = silu(gate) * up`` with
   ``silu(g) = g / (1 + exp(-g))``, in fp64 with no fp16 round trip, then the R6
-  quantization decision on ``fp32(y)``.
+  quantization decision on ``fp32(y)``.  A row whose largest ``|y|`` is below
+  ``2^-64`` counts as a zero row (``xq = 0``, ``s_a = 1``): silu of a very negative
+  gate reaches the fp32 subnormal range, where ``127 / max|y|`` overflows and the
+  products lose their precision, so the rule is not meaningful there.
 """
 from __future__ import annotations
 
@@ -312,18 +315,18 @@ def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):
     return _quant_rows_int8(y32)
 
 
-def _quant_rows_int8(y32: np.ndarray):
+def _quant_rows_int8(y32: np.ndarray, zero_below: float = 0.0):
     """Per-row symmetric int8 quantization of fp32 values (R6): ``amax = max|y|``,
     ``xq = clamp(rint(y * fp32(127 / amax)), -127, 127)``, ``s_a = amax / 127``; a zero
-    row gives ``xq = 0, s_a = 1``.  Returns ``(xq, s_a, t)`` with ``t`` the fp32 values
-    that were rounded."""
+    row (or one with ``amax < zero_below``, R12) gives ``xq = 0, s_a = 1``.  Returns
+    ``(xq, s_a, t)`` with ``t`` the fp32 values that were rounded."""
     M, K = y32.shape
     amax = np.abs(y32).max(axis=1) if K else np.zeros(M, F32)
     xq = np.zeros((M, K), dtype=np.int8)
     s_a = np.ones(M, dtype=F32)
     t_all = np.zeros((M, K), dtype=F64)
     for m in range(M):
-        if amax[m] == 0:
+        if amax[m] == 0 or amax[m] < zero_below:
             continue
         inv = F32(127.0) / amax[m]
         t = y32[m] * inv
@@ -331,6 +334,10 @@ def _quant_rows_int8(y32: np.ndarray):
         s_a[m] = amax[m] / F32(127.0)
         t_all[m] = t
     return xq, s_a, t_all
+
+
+# R12: rows whose largest |silu(g) * u| is below 2^-64 count as zero rows.
+SILU_ZERO_BELOW = 2.0 ** -64
 
 
 def silu_ref(g: np.ndarray) -> np.ndarray:
@@ -346,15 +353,15 @@ def silu_mul_quant_ref(gate_up16: np.ndarray):
     """The SiLU-gated input of the down projection quantized per token (R12): the fused
     gate+up output ``[M, 2I]`` holds gate in columns ``0..I-1`` and up in ``I..2I-1``;
     ``y = silu(gate) * up`` in fp64 (no fp16 round trip), then the per-token int8 rule
-    of :func:`_quant_rows_int8` on ``fp32(y)``.  Returns ``(xq int8 [M, I], s_a fp32 [M],
-    t fp64 [M, I])``."""
+    of :func:`_quant_rows_int8` on ``fp32(y)``; a row with ``max|y| < 2^-64`` counts as
+    a zero row.  Returns ``(xq int8 [M, I], s_a fp32 [M], t fp64 [M, I])``."""
     gu = np.asarray(gate_up16)
     if gu.dtype != F16 or gu.ndim != 2 or gu.shape[1] % 2:
         raise ValueError("gate_up16 must be a 2-D float16 array with an even number of columns")
     I = gu.shape[1] // 2
     g = gu[:, :I].astype(F64)
     u = gu[:, I:].astype(F64)
-    return _quant_rows_int8((silu_ref(g) * u).astype(F32))
+    return _quant_rows_int8((silu_ref(g) * u).astype(F32), SILU_ZERO_BELOW)
 
 
 def w4a8_acc_ref(xq: np.ndarray, q: np.ndarray, gscale_ng, group_size: int) -> np.ndarray:

@@ -351,6 +351,17 @@ def pin_silu_special_cases(ora):
     expect[17] = 127 if sv > 0 else -127
     assert np.array_equal(xo[0].astype(np.int64), expect)
     assert abs(float(so[0]) - abs(2.0 * sv) / 127) <= 1e-7 * abs(2.0 * sv) / 127
+    # |y| <= 50 e^-50 = 9.6e-21 < 2^-64 = 5.4e-20: a zero row; |y| = 45 e^-45 u, up to 1.3e-18,
+    # is above it: a live row, every code negative and the largest magnitude 127
+    lo = np.zeros((2, 2 * I), F16)
+    lo[0, :I] = -50.0
+    lo[1, :I] = -45.0
+    lo[:, I:] = rng.uniform(0.5, 1.0, size=(2, I)).astype(F16)
+    lo[:, I + 3] = 1.0
+    xl, sl, _ = ora.silu_mul_quant_ref(lo)
+    assert float(sl[0]) == 1.0 and not xl[0].any()
+    assert xl[1].max() < 0 and xl[1].min() == -127
+    assert abs(float(sl[1]) - 45 * np.exp(-45.0) / 127) <= 1e-6 * 45 * np.exp(-45.0) / 127
 
 
 def pin_w4a8_acc_bruteforce(ora):

@@ -40,6 +40,7 @@ MUTANTS = [
     ("silu sigmoid of -g", "sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))", "sig = np.where(g >= 0, e / (1.0 + e), 1.0 / (1.0 + e))"),
     ("silu gate and up swapped", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "u = gu[:, :I].astype(F64)\n    g = gu[:, I:].astype(F64)"),
     ("silu gate and up interleaved", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "g = gu[:, 0::2].astype(F64)\n    u = gu[:, 1::2].astype(F64)"),
+    ("silu tiny rows quantized", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32), SILU_ZERO_BELOW)", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32))"),
     ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
 ]
 
