@@ -137,11 +137,13 @@ int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, floa
  * gate_up: fp16 [M, 2K] row-major, the fused gate+up projection output, gate in columns
  * 0..K-1 and up in K..2K-1.  y = silu(gate) * up with silu(g) = g / (1 + exp(-g)), in
  * fp32 with no fp16 round trip; then the rule of w4a8_quant_act on y: xq int8 [M, K],
- * s_a fp32 [M] (a zero row gives xq = 0, s_a = 1).  K must be a positive multiple of 8
- * (at most 2^29); N and group_size are unused.  The caller owns every buffer; all
- * pointers are device pointers, 16-byte aligned; the call is asynchronous on `stream`.
- * Codes equal those of the exact y except where y * 127 / max|y| lies within the fp32
- * error of exp and the three roundings of a half-integer (a difference of 1 there).
+ * s_a fp32 [M]; a row with max|y| < 2^-64 (zero rows included) gives xq = 0, s_a = 1.
+ * K must be a positive multiple of 8 (at most 2^29); N and group_size are unused.  The
+ * caller owns every buffer; all pointers are device pointers, 16-byte aligned; the call
+ * is asynchronous on `stream`.  y carries about 9 units of fp32 rounding (exp and the
+ * reciprocal are the 1-ulp hardware approximations), so codes equal those of the exact
+ * y except where y * 127 / max|y| lies within 2e-4 of a half-integer (a difference of 1
+ * there).
  */
 int w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a,
                         int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);

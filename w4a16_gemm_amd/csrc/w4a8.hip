@@ -108,14 +108,26 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const half_t* __re
 // ------------------------------------------------------- silu_mul_quant
 // The SiLU-gated input of the down projection, quantized per token: row m of the fused
 // gate+up output [M, 2I] holds gate in columns 0..I-1 and up in I..2I-1;
-// y = silu(g) * u in fp32 with silu(g) = g / (1 + exp(-g)) (exp(-g) = inf for very
-// negative g gives -0), then the per-token int8 rule of quant_act.
+// y = silu(g) * u = g u / (1 + exp(-g)) in fp32, then the per-token int8 rule of
+// quant_act; a row whose max|y| is below 2^-64 is a zero row (127 / max|y| would
+// overflow, and y there comes from subnormal products).
+//
+// The kernel is arithmetic-bound unless y is cheap: per element it spends about 16 VALU
+// operations.  exp(-g) = 2^xh * 2^xl with xh = fp32(-g log2 e) and xl the rounding
+// residual of that product (exact by fma, plus the residual of the fp32 constant), and
+// 2^xl = 1 + xl ln 2 to first order (|xl| < 2^-16 wherever 2^xh is neither 0 nor inf);
+// 2^xh and the reciprocal are the 1-ulp hardware approximations.  exp(-g) = inf for very
+// negative g gives y = +-0.  Codes: t = y * fp32(127 / amax) is rounded to the nearest
+// integer (ties to even) by adding 1.5 * 2^23, whose low byte is then the two's
+// complement code; |t| <= 127 (1 + 2^-23) < 127.5, so no clamp is needed.
 //
 // One workgroup of T threads per row.  With R > 0 the row fits in registers (R vectors
 // of 8 per thread, T * R * 8 >= I): every load is issued up front (clamped indexes, so
 // all are in bounds and none waits on a branch), y is formed once and kept for the code
 // pass, and each input byte is read once.  R = 0 streams longer rows twice (max pass,
 // then the code pass recomputes y).
+constexpr float kSiluZeroBelow = 0x1p-64f;
+
 template <int T>
 __device__ __forceinline__ float block_max_t(float v, float* red) {
   v = wave_max(v);
@@ -128,17 +140,35 @@ __device__ __forceinline__ float block_max_t(float v, float* red) {
   return m;
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
-
-__device__ __forceinline__ uint64_t pack_codes8(const float* y, float inv) {
-  uint64_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q = fminf(fmaxf(rintf(y[i] * inv), -127.0f), 127.0f);
-    packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
-  }
-  return packed;
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  constexpr float kL = 1.44269502162933349609375f;   // fp32(log2 e)
+  constexpr float kLlo = 1.925963e-08f;              // log2 e - kL
+  constexpr float kLn2 = 0.693147182f;
+  const float xh = g * -kL;
+  const float xl = fmaf(g, -kLlo, fmaf(g, -kL, -xh));
+  const float e = __builtin_amdgcn_exp2f(xh) * fmaf(xl, kLn2, 1.0f);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
 }
+
+__device__ __forceinline__ void silu_mul8(const half8_t& g, const half8_t& u, float* y) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = silu_mul((float)g[i], (float)u[i]);
+}
+
+// Low byte of rint(t) + 1.5 * 2^23 for four values, packed into one word.
+__device__ __forceinline__ uint32_t pack_codes4(const float* y, float inv) {
+  uint32_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(y[i] * inv + 12582912.0f);
+  return __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+}
+
+__device__ __forceinline__ uint2 pack_codes8(const float* y, float inv) {
+  return make_uint2(pack_codes4(y, inv), pack_codes4(y + 4, inv));
+}
+
+__device__ __forceinline__ float row_inv(float amax) { return amax >= kSiluZeroBelow ? 127.0f / amax : 0.0f; }
+__device__ __forceinline__ float row_scale(float amax) { return amax >= kSiluZeroBelow ? amax / 127.0f : 1.0f; }
 
 template <int T, int R>
 __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restrict__ gu, int8_t* __restrict__ xq,
@@ -148,7 +178,7 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const half8_t* g8 = reinterpret_cast<const half8_t*>(gu + row * 2 * I);
     const half8_t* u8 = g8 + nv;
-    uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * I);
+    uint2* dst = reinterpret_cast<uint2*>(xq + row * I);
     float amax = 0.0f;
     if constexpr (R > 0) {
       half8_t gv[R], uv[R];
@@ -161,16 +191,15 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
       float y[R][8];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const bool live = (int)threadIdx.x + r * T < nv;
+        silu_mul8(gv[r], uv[r], y[r]);
+        if ((int)threadIdx.x + r * T < nv) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          y[r][i] = live ? silu_f32((float)gv[r][i]) * (float)uv[r][i] : 0.0f;
-          amax = fmaxf(amax, fabsf(y[r][i]));
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[r][i]));
         }
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+      const float inv = row_inv(amax);
+      if (threadIdx.x == 0) s_a[row] = row_scale(amax);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int j = (int)threadIdx.x + r * T;
@@ -178,18 +207,17 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
       }
     } else {
       for (int j = threadIdx.x; j < nv; j += T) {
-        const half8_t g = g8[j], u = u8[j];
+        float y[8];
+        silu_mul8(g8[j], u8[j], y);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(silu_f32((float)g[i]) * (float)u[i]));
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+      const float inv = row_inv(amax);
+      if (threadIdx.x == 0) s_a[row] = row_scale(amax);
       for (int j = threadIdx.x; j < nv; j += T) {
-        const half8_t g = g8[j], u = u8[j];
         float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = silu_f32((float)g[i]) * (float)u[i];
+        silu_mul8(g8[j], u8[j], y);
         dst[j] = pack_codes8(y, inv);
       }
     }
