@@ -28,7 +28,10 @@ pytestmark = pytest.mark.gpu
 NEAR_TIE = 2.5e-4
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (7, 5120), (64, 13824), (300, 5120), (4096, 5120)])
+# widths cover every launch variant: 256 threads with 1, 2, 4 and 8 vectors of 8 per
+# thread, 1024 threads with 4, and the streaming variant
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (7, 5120), (64, 13824), (300, 5120), (5, 20096), (2, 40064),
+                                 (4096, 5120), (4096, 13824)])
 def test_quant_act_no_norm_bit_exact(M, K):
     dev = device()
     announce(f"quant_act no-norm M={M} K={K}")
@@ -41,7 +44,8 @@ def test_quant_act_no_norm_bit_exact(M, K):
     assert np.array_equal(to_np(sa).view(np.uint32), rsa.view(np.uint32))
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (16, 5120), (256, 5120), (4096, 5120), (33, 13824)])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (16, 5120), (256, 5120), (4096, 5120), (33, 13824), (5, 20096),
+                                 (2, 40064)])
 def test_quant_act_rmsnorm_near_ties_only(M, K):
     dev = device()
     announce(f"quant_act rmsnorm M={M} K={K}")

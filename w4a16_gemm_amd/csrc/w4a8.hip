@@ -23,84 +23,168 @@ namespace w4 {
 
 namespace {
 
-// ------------------------------------------------------------ quant_act
-constexpr int kQThreads = 256;
+// ------------------------------------------------------------ row kernels
+// quant_act and silu_mul_quant: one workgroup of T threads per token row.  With R > 0
+// the row fits in registers (R vectors of 8 per thread, T * R * 8 >= K): every load is
+// issued up front (clamped indexes, so all are in bounds and none waits on a branch), y
+// is formed once and kept for the code pass, and each input byte is read once.  R = 0
+// streams longer rows through L2 again for each pass.
+//
+// Codes: t = y * fp32(127 / amax) is rounded to the nearest integer (ties to even) by
+// adding 1.5 * 2^23, whose low byte is then the two's complement code; |y| <= amax gives
+// |t| <= 127 (1 + 2^-23) < 127.5, so no clamp is needed.
 
 // Row kernels loop over rows; at most 2^20 workgroups are launched.
 inline unsigned row_grid(int M) { return (unsigned)(M < (1 << 20) ? M : (1 << 20)); }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
+template <int T>
+__device__ __forceinline__ float block_sum_t(float v, float* red) {
   v = wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  float s = red[0];
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) s += red[w];
+  return s;
 }
-__device__ __forceinline__ float block_max(float v, float* red) {
+
+template <int T>
+__device__ __forceinline__ float block_max_t(float v, float* red) {
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
 }
 
-// One workgroup per token row.  Three passes over the row (it stays in L2/L1):
-// sum of squares, max |y|, codes.  y = (x * r) * gamma in fp32.
-__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const half_t* __restrict__ x,
-                                                               const half_t* __restrict__ gamma, float eps,
-                                                               int8_t* __restrict__ xq, float* __restrict__ s_a,
-                                                               int M, int K) {
-  __shared__ float red[4];
+// Low byte of rint(t) + 1.5 * 2^23 for four values, packed into one word.  t = y * inv
+// is rounded to fp32 before the add (no fma contraction: a single rounding of
+// y * inv + 1.5 * 2^23 would differ from rint(fp32(t)) next to half-integers).
+__device__ __forceinline__ uint32_t pack_codes4(const float* y, float inv) {
+#pragma clang fp contract(off)
+  uint32_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(y[i] * inv + 12582912.0f);
+  return __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+}
+
+__device__ __forceinline__ uint2 pack_codes8(const float* y, float inv) {
+  return make_uint2(pack_codes4(y, inv), pack_codes4(y + 4, inv));
+}
+
+// Launch a row kernel template K<T, R> for rows of nv vectors of 8 (R8_1024: whether
+// K<1024, 8> fits the 128 VGPRs of a 1024-thread workgroup; else such rows stream).
+#define W4_ROW_DISPATCH(KERNEL, R8_1024, nv, grid, stream, ...)                                      \
+  do {                                                                                               \
+    if ((nv) <= 256) hipLaunchKernelGGL((KERNEL<256, 1>), grid, dim3(256), 0, stream, __VA_ARGS__);   \
+    else if ((nv) <= 512) hipLaunchKernelGGL((KERNEL<256, 2>), grid, dim3(256), 0, stream, __VA_ARGS__); \
+    else if ((nv) <= 1024) hipLaunchKernelGGL((KERNEL<256, 4>), grid, dim3(256), 0, stream, __VA_ARGS__); \
+    else if ((nv) <= 2048) hipLaunchKernelGGL((KERNEL<256, 8>), grid, dim3(256), 0, stream, __VA_ARGS__); \
+    else if ((nv) <= 4096) hipLaunchKernelGGL((KERNEL<1024, 4>), grid, dim3(1024), 0, stream, __VA_ARGS__); \
+    else if ((R8_1024) && (nv) <= 8192)                                                            \
+      hipLaunchKernelGGL((KERNEL<1024, R8_1024 ? 8 : 0>), grid, dim3(1024), 0, stream, __VA_ARGS__);  \
+    else hipLaunchKernelGGL((KERNEL<1024, 0>), grid, dim3(1024), 0, stream, __VA_ARGS__);            \
+  } while (0)
+
+// ------------------------------------------------------------ quant_act
+// y = (x * r) * gamma in fp32 with r = 1 / sqrt(sum(x^2) / K + eps) (RMSNorm), or y = x
+// without gamma; then amax = max|y|, codes as above, s_a = amax / 127; a zero row gives
+// codes 0 and s_a = 1.  Without gamma every step is exact or one fp32 rounding in the
+// order of the definition, so the codes are bit-exact.
+template <int T, int R>
+__global__ __launch_bounds__(T) void quant_act_kernel(const half_t* __restrict__ x, const half_t* __restrict__ gamma,
+                                                       float eps, int8_t* __restrict__ xq, float* __restrict__ s_a,
+                                                       int M, int K) {
+  __shared__ float red[T / 64];
+  const int nv = K / 8;
+  const half8_t* gr = reinterpret_cast<const half8_t*>(gamma);
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const half8_t* xr = reinterpret_cast<const half8_t*>(x + row * K);
-    const half8_t* gr = reinterpret_cast<const half8_t*>(gamma);
-    const int nv = K / 8;
-    float r = 1.0f;
-    if (gamma) {
-      float ss = 0.0f;
-      for (int j = threadIdx.x; j < nv; j += kQThreads) {
-        const half8_t v = xr[j];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
-      }
-      ss = block_sum(ss, red);
-      r = 1.0f / sqrtf(ss / (float)K + eps);
-    }
+    uint2* dst = reinterpret_cast<uint2*>(xq + row * K);
     float amax = 0.0f;
-    for (int j = threadIdx.x; j < nv; j += kQThreads) {
-      const half8_t v = xr[j];
-      if (gamma) {
-        const half8_t g = gr[j];
+    if constexpr (R > 0) {
+      half8_t xv[R];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(((float)v[i] * r) * (float)g[i]));
+      for (int r = 0; r < R; ++r) xv[r] = xr[min((int)threadIdx.x + r * T, nv - 1)];
+      float y[R][8];
+      if (gamma) {
+        half8_t gv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) gv[r] = gr[min((int)threadIdx.x + r * T, nv - 1)];
+        float ss = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if ((int)threadIdx.x + r * T < nv) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf((float)xv[r][i], (float)xv[r][i], ss);
+          }
+        }
+        ss = block_sum_t<T>(ss, red);
+        const float rs = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[r][i] = ((float)xv[r][i] * rs) * (float)gv[r][i];
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[r][i] = (float)xv[r][i];
       }
-    }
-    amax = block_max(amax, red);
-    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-    if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
-    uint64_t* dst = reinterpret_cast<uint64_t*>(xq + row * K);
-    for (int j = threadIdx.x; j < nv; j += kQThreads) {
-      const half8_t v = xr[j];
-      uint64_t packed = 0;
+      // clamped duplicates repeat an element of the row: harmless for the max
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[r][i]));
+      amax = block_max_t<T>(amax, red);
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int j = (int)threadIdx.x + r * T;
+        if (j < nv) dst[j] = pack_codes8(y[r], inv);
+      }
+    } else {
+      float rs = 1.0f;
       if (gamma) {
-        const half8_t g = gr[j];
+        float ss = 0.0f;
+        for (int j = threadIdx.x; j < nv; j += T) {
+          const half8_t v = xr[j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float yv = ((float)v[i] * r) * (float)g[i];
-          const float q = fminf(fmaxf(rintf(yv * inv), -127.0f), 127.0f);
-          packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+          for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float q = fminf(fmaxf(rintf((float)v[i] * inv), -127.0f), 127.0f);
-          packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
-        }
+        ss = block_sum_t<T>(ss, red);
+        rs = 1.0f / sqrtf(ss / (float)K + eps);
       }
-      dst[j] = packed;
+      auto row_y = [&](int j, float* y) {
+        const half8_t v = xr[j];
+        if (gamma) {
+          const half8_t g = gr[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = ((float)v[i] * rs) * (float)g[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = (float)v[i];
+        }
+      };
+      for (int j = threadIdx.x; j < nv; j += T) {
+        float y[8];
+        row_y(j, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+      }
+      amax = block_max_t<T>(amax, red);
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      if (threadIdx.x == 0) s_a[row] = amax > 0.0f ? amax / 127.0f : 1.0f;
+      for (int j = threadIdx.x; j < nv; j += T) {
+        float y[8];
+        row_y(j, y);
+        dst[j] = pack_codes8(y, inv);
+      }
     }
   }
 }
@@ -117,28 +201,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const half_t* __re
 // residual of that product (exact by fma, plus the residual of the fp32 constant), and
 // 2^xl = 1 + xl ln 2 to first order (|xl| < 2^-16 wherever 2^xh is neither 0 nor inf);
 // 2^xh and the reciprocal are the 1-ulp hardware approximations.  exp(-g) = inf for very
-// negative g gives y = +-0.  Codes: t = y * fp32(127 / amax) is rounded to the nearest
-// integer (ties to even) by adding 1.5 * 2^23, whose low byte is then the two's
-// complement code; |t| <= 127 (1 + 2^-23) < 127.5, so no clamp is needed.
-//
-// One workgroup of T threads per row.  With R > 0 the row fits in registers (R vectors
-// of 8 per thread, T * R * 8 >= I): every load is issued up front (clamped indexes, so
-// all are in bounds and none waits on a branch), y is formed once and kept for the code
-// pass, and each input byte is read once.  R = 0 streams longer rows twice (max pass,
-// then the code pass recomputes y).
+// negative g gives y = +-0.
 constexpr float kSiluZeroBelow = 0x1p-64f;
-
-template <int T>
-__device__ __forceinline__ float block_max_t(float v, float* red) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int w = 1; w < T / 64; ++w) m = fmaxf(m, red[w]);
-  return m;
-}
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   constexpr float kL = 1.44269502162933349609375f;   // fp32(log2 e)
@@ -155,20 +219,8 @@ __device__ __forceinline__ void silu_mul8(const half8_t& g, const half8_t& u, fl
   for (int i = 0; i < 8; ++i) y[i] = silu_mul((float)g[i], (float)u[i]);
 }
 
-// Low byte of rint(t) + 1.5 * 2^23 for four values, packed into one word.
-__device__ __forceinline__ uint32_t pack_codes4(const float* y, float inv) {
-  uint32_t b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(y[i] * inv + 12582912.0f);
-  return __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-}
-
-__device__ __forceinline__ uint2 pack_codes8(const float* y, float inv) {
-  return make_uint2(pack_codes4(y, inv), pack_codes4(y + 4, inv));
-}
-
-__device__ __forceinline__ float row_inv(float amax) { return amax >= kSiluZeroBelow ? 127.0f / amax : 0.0f; }
-__device__ __forceinline__ float row_scale(float amax) { return amax >= kSiluZeroBelow ? amax / 127.0f : 1.0f; }
+__device__ __forceinline__ float silu_inv(float amax) { return amax >= kSiluZeroBelow ? 127.0f / amax : 0.0f; }
+__device__ __forceinline__ float silu_scale(float amax) { return amax >= kSiluZeroBelow ? amax / 127.0f : 1.0f; }
 
 template <int T, int R>
 __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restrict__ gu, int8_t* __restrict__ xq,
@@ -191,15 +243,13 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
       float y[R][8];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        silu_mul8(gv[r], uv[r], y[r]);
-        if ((int)threadIdx.x + r * T < nv) {
+        silu_mul8(gv[r], uv[r], y[r]);  // clamped duplicates: harmless for the max
 #pragma unroll
-          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[r][i]));
-        }
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[r][i]));
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = row_inv(amax);
-      if (threadIdx.x == 0) s_a[row] = row_scale(amax);
+      const float inv = silu_inv(amax);
+      if (threadIdx.x == 0) s_a[row] = silu_scale(amax);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int j = (int)threadIdx.x + r * T;
@@ -213,8 +263,8 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = row_inv(amax);
-      if (threadIdx.x == 0) s_a[row] = row_scale(amax);
+      const float inv = silu_inv(amax);
+      if (threadIdx.x == 0) s_a[row] = silu_scale(amax);
       for (int j = threadIdx.x; j < nv; j += T) {
         float y[8];
         silu_mul8(g8[j], u8[j], y);
@@ -581,25 +631,14 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
                                  int K, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_act_kernel, dim3(row_grid(M)), dim3(kQThreads), 0, stream, (const half_t*)x,
-                     (const half_t*)gamma, eps, xq, s_a, M, K);
+  W4_ROW_DISPATCH(quant_act_kernel, false, K / 8, dim3(row_grid(M)), stream, (const half_t*)x, (const half_t*)gamma, eps,
+                  xq, s_a, M, K);
   return hipGetLastError();
 }
 
 hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int M, int I,
                                       hipStream_t stream) {
-  const int nv = I / 8;
-  const half_t* gu = (const half_t*)gate_up;
-  const dim3 grid(row_grid(M));
-#define W4_SMQ(T, R) hipLaunchKernelGGL((silu_mul_quant_kernel<T, R>), grid, dim3(T), 0, stream, gu, xq, s_a, M, I)
-  if (nv <= 256) W4_SMQ(256, 1);
-  else if (nv <= 512) W4_SMQ(256, 2);
-  else if (nv <= 1024) W4_SMQ(256, 4);
-  else if (nv <= 2048) W4_SMQ(256, 8);
-  else if (nv <= 4096) W4_SMQ(1024, 4);
-  else if (nv <= 8192) W4_SMQ(1024, 8);
-  else W4_SMQ(1024, 0);
-#undef W4_SMQ
+  W4_ROW_DISPATCH(silu_mul_quant_kernel, true, I / 8, dim3(row_grid(M)), stream, (const half_t*)gate_up, xq, s_a, M, I);
   return hipGetLastError();
 }
 
