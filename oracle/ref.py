@@ -56,6 +56,15 @@ Readings where the pages are silent:
   ``xq = clamp(rint(fp32(y32 * inv)), -127, 127)``, ``s_a = fp32(M / 127)``;
   a zero row gives ``s_a = 1``, ``xq = 0``.  Without gamma (no-norm mode)
   ``y32 = x``.
+* R13 W4A16 per-channel ([QQQ-lmdeploy] "Benchmark" and a reply in its thread
+  name per-channel quantization, group_size = -1, beside g128): group_size -1
+  means one group spanning all of K; the R1 rule then applies per row; scales
+  are fp16 [1, N] and zero points int32 [1, ceil(N/8)].
+* R14 W4A16 symmetric ([AWQ-fixes], reply on preset schemes: a W4A16_ASYM preset
+  beside W4A16, which is therefore the symmetric one): per (row, group)
+  ``s = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s), -8, 7)`` (the R5
+  per-channel constants), stored as the code ``q + 8`` with zero point 8, so
+  ``(code - 8) * s = q * s`` dequantizes it with the asymmetric formula.
 * R12 SiLU-gated activations ([QQQ-lmdeploy], "Modification": online
   quantization fused with element-wise operations such as SiLU; gate and up
   weights fused into one weight): the fused gate+up output ``[M, 2I]`` holds gate
@@ -76,7 +85,7 @@ F64 = np.float64
 
 __all__ = [
     "pack_nibbles", "unpack_nibbles", "tile_words", "untile_words",
-    "quantize_asym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
+    "quantize_asym", "quantize_sym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref",
     "w4a8_acc_ref", "w4a8_linear_ref", "silu_ref", "silu_mul_quant_ref",
@@ -163,20 +172,26 @@ def untile_words(tiled: np.ndarray, N: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # W4A16 asymmetric quantization (R1, R2).  [AWQ-fixes], opening comment.
 # --------------------------------------------------------------------------
-def quantize_asym(w16: np.ndarray, group_size: int = 128):
-    """Group-wise asymmetric uint4 quantization of fp16 weights [N, K].
-
-    Returns ``(codes uint8 [N, K], scales fp16 [N, K/G], zeros uint8 [N, K/G])``
-    in the natural (row, group) orientation.  All decisions in fp32.
-    """
+def _groups(w16: np.ndarray, group_size: int):
+    """fp16 [N, K] -> fp32 [N, K/G, G]; group_size -1 is one group over K (R13)."""
     w16 = np.asarray(w16)
     if w16.dtype != F16 or w16.ndim != 2:
         raise ValueError("w16 must be a 2-D float16 array")
     N, K = w16.shape
-    G = int(group_size)
+    G = K if int(group_size) == -1 else int(group_size)
     if G <= 0 or K % G:
         raise ValueError("K must be a multiple of group_size")
-    w = w16.astype(F32).reshape(N, K // G, G)
+    return w16.astype(F32).reshape(N, K // G, G), N, K
+
+
+def quantize_asym(w16: np.ndarray, group_size: int = 128):
+    """Group-wise asymmetric uint4 quantization of fp16 weights [N, K] (R1;
+    group_size -1: per row, R13).
+
+    Returns ``(codes uint8 [N, K], scales fp16 [N, K/G], zeros uint8 [N, K/G])``
+    in the natural (row, group) orientation.  All decisions in fp32.
+    """
+    w, N, K = _groups(w16, group_size)
     mn = w.min(axis=2)
     mx = w.max(axis=2)
     s32 = (mx - mn) / F32(15.0)
@@ -186,6 +201,20 @@ def quantize_asym(w16: np.ndarray, group_size: int = 128):
     z = np.clip(np.rint(-mn / s), F32(0), F32(15))
     q = np.clip(np.rint(w / s[:, :, None]) + z[:, :, None], F32(0), F32(15))
     return (q.reshape(N, K).astype(np.uint8), s16, z.astype(np.uint8))
+
+
+def quantize_sym(w16: np.ndarray, group_size: int = 128):
+    """Group-wise symmetric int4 quantization for W4A16 (R14): per (row, group)
+    ``s = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s), -8, 7)`` with the
+    stored scale, in fp32.  Returns ``(codes uint8 [N, K] = q + 8, scales fp16
+    [N, K/G], zeros uint8 [N, K/G] = 8)``, the orientation of :func:`quantize_asym`."""
+    w, N, K = _groups(w16, group_size)
+    amax = np.abs(w).max(axis=2)
+    s16 = np.maximum(amax / F32(7.0), F32(1e-5)).astype(F16)
+    s = s16.astype(F32)
+    q = np.clip(np.rint(w / s[:, :, None]), F32(-8), F32(7))
+    codes = (q + F32(8)).reshape(N, K).astype(np.uint8)
+    return codes, s16, np.full(s16.shape, 8, dtype=np.uint8)
 
 
 def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
@@ -220,7 +249,7 @@ def dequant_awq(qweight, scales_gn, qzeros, K: int, group_size: int = 128) -> np
     a small integer and an fp16 scale is exact in fp64.
     """
     codes, scales, zeros = unpack_awq(qweight, scales_gn, qzeros, K)
-    G = int(group_size)
+    G = K if int(group_size) == -1 else int(group_size)
     N = codes.shape[0]  # the number of real rows (scales_gn.shape[1])
     s = np.repeat(scales.astype(F64), G, axis=1)
     z = np.repeat(zeros.astype(F64), G, axis=1)
@@ -234,13 +263,14 @@ def linear_ref(x16: np.ndarray, w_deq: np.ndarray) -> np.ndarray:
     return np.asarray(x16, dtype=F64) @ np.asarray(w_deq, dtype=F64).T
 
 
-def awq_reference(w16: np.ndarray, x16: np.ndarray, group_size: int = 128):
-    """The whole W4A16 chain: quantize -> pack -> unpack -> dequant -> fp64 matmul.
+def awq_reference(w16: np.ndarray, x16: np.ndarray, group_size: int = 128, symmetric: bool = False):
+    """The whole W4A16 chain: quantize (R1, or R14 when symmetric) -> pack -> unpack
+    -> dequant -> fp64 matmul.
 
     Returns a dict with the packed tensors, the fp64 dequantized weights and
     the fp64 outputs.
     """
-    codes, scales, zeros = quantize_asym(w16, group_size)
+    codes, scales, zeros = (quantize_sym if symmetric else quantize_asym)(w16, group_size)
     qweight, scales_gn, qzeros = pack_awq(codes, scales, zeros)
     w_deq = dequant_awq(qweight, scales_gn, qzeros, w16.shape[1], group_size)
     y = linear_ref(x16, w_deq) if x16 is not None else None

@@ -87,3 +87,28 @@ def read_silu_cases():
         elif key == "xq":
             cur["xq"] = [int(v) for v in rest]
     return cases
+
+
+def read_variant_cases():
+    """Cases of golden/w4a16_variants_worked.txt: ``rule``, ``group``, ``values`` (fp16),
+    ``scales`` (fp16 per group), ``zeros`` and ``codes_head`` (per group: leading codes)."""
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, "w4a16_variants_worked.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *rest = line.split()
+        if key == "case":
+            cur = {"name": rest[0]}
+            cases.append(cur)
+        elif key == "rule":
+            cur["rule"] = rest[0]
+        elif key == "group":
+            cur["group"] = int(rest[0])
+        elif key in ("values", "scales"):
+            cur[key] = _values(rest)
+        elif key == "zeros":
+            cur["zeros"] = [int(v) for v in rest]
+        elif key == "codes_head":
+            cur["codes_head"] = [[int(v) for v in part.split()] for part in " ".join(rest).split("|")]
+    return cases

@@ -19,7 +19,7 @@ from fractions import Fraction
 import numpy as np
 
 import synth
-from golden_io import read_cases, read_pack_words, read_silu_cases
+from golden_io import read_cases, read_pack_words, read_silu_cases, read_variant_cases
 
 F16, F32, F64 = np.float16, np.float32, np.float64
 
@@ -364,6 +364,62 @@ def pin_silu_special_cases(ora):
     assert abs(float(sl[1]) - 45 * np.exp(-45.0) / 127) <= 1e-6 * 45 * np.exp(-45.0) / 127
 
 
+# ------------------------------------------------------- W4A16 variants
+def pin_variants_worked(ora):
+    """Hand-worked per-channel and symmetric rows (tests/golden/w4a16_variants_worked.txt)."""
+    for case in read_variant_cases():
+        quant = ora.quantize_sym if case["rule"] == "sym" else ora.quantize_asym
+        codes, sc, z = quant(case["values"][None, :], case["group"])
+        assert sc[0].view(np.uint16).tolist() == case["scales"].view(np.uint16).tolist(), case["name"]
+        assert z[0].tolist() == case["zeros"], case["name"]
+        for b, head in enumerate(case["codes_head"]):
+            assert codes[0, 128 * b:128 * b + len(head)].tolist() == head, (case["name"], b)
+
+
+def pin_sym_properties(ora):
+    """Symmetric rule: codes in [1, 15] (|w| / s <= 7 (1 + 2^-11) never rounds past 7),
+    |w - (code - 8) s| <= s / 2, negating W maps every code c to 16 - c with the same
+    scales (rint is odd), and zeros are 8; per-channel is one scale per row."""
+    rng = _rng(41)
+    w = (rng.standard_normal((24, 512)) * 0.02).astype(F16)
+    w[3, 17] = 0.3
+    for G in (128, -1):
+        c, sc, z = ora.quantize_sym(w, G)
+        assert c.min() >= 1 and c.max() <= 15 and np.all(z == 8)
+        Gk = 512 if G == -1 else G
+        sv = np.repeat(sc.astype(F64), Gk, axis=1)
+        assert np.all(np.abs(w.astype(F64) - (c.astype(F64) - 8) * sv) <= sv / 2 + 1e-12)
+        cn, scn, _ = ora.quantize_sym(-w, G)
+        assert np.array_equal(cn.astype(np.int64), 16 - c.astype(np.int64)) and np.array_equal(scn, sc)
+        assert sc.shape == (24, 512 // Gk)
+
+
+def pin_variants_constructed_exact(ora):
+    """Weights q * 2^-6 with q in [-7, 7] and each group (or row) holding +-7 come back
+    exactly from the symmetric rule (s = fp16(7 * 2^-6 / 7) = 2^-6), and asymmetric
+    per-channel weights (c - z) * 2^-4 with each row spanning codes 0..15 come back
+    exactly; X of small integers then gives exact outputs through the whole chain."""
+    rng = _rng(43)
+    M, N, K = 3, 16, 384
+    x = rng.integers(-4, 5, size=(M, K)).astype(F16)
+    q = rng.integers(-7, 8, size=(N, K))
+    q[:, ::128] = 7
+    w = (q * 2.0**-6).astype(F16)
+    for G in (128, -1):
+        ref = ora.awq_reference(w, x, G, symmetric=True)
+        exact = x.astype(np.int64) @ q.T
+        assert np.array_equal(ref["y"] * 64, exact.astype(F64)), G
+    z = rng.integers(0, 16, size=N)
+    c = rng.integers(0, 16, size=(N, K))
+    c[:, 0] = 0
+    c[:, 1] = 15
+    c = np.minimum(np.maximum(c, 0), 15)
+    w2 = ((c - z[:, None]) * 2.0**-4).astype(F16)
+    ref2 = ora.awq_reference(w2, x, -1)
+    assert np.array_equal(ref2["y"] * 16, (x.astype(np.int64) @ (c - z[:, None]).T).astype(F64))
+    assert ref2["scales"].shape == (1, N) and ref2["qzeros"].shape == (1, 2)
+
+
 def pin_w4a8_acc_bruteforce(ora):
     """Integer accumulators against Python-int loops, both weight variants."""
     rng = _rng(31)
@@ -397,4 +453,5 @@ ALL_PINS = [
     pin_constructed_exact_gemm,
     pin_w4a8_worked, pin_w4a8_exhaustive, pin_quant_act_closed_forms, pin_w4a8_acc_bruteforce,
     pin_silu_worked, pin_silu_closed_forms, pin_silu_special_cases,
+    pin_variants_worked, pin_sym_properties, pin_variants_constructed_exact,
 ]

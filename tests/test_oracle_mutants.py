@@ -41,6 +41,10 @@ MUTANTS = [
     ("silu gate and up swapped", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "u = gu[:, :I].astype(F64)\n    g = gu[:, I:].astype(F64)"),
     ("silu gate and up interleaved", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "g = gu[:, 0::2].astype(F64)\n    u = gu[:, 1::2].astype(F64)"),
     ("silu tiny rows quantized", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32), SILU_ZERO_BELOW)", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32))"),
+    ("sym divisor 8", "s16 = np.maximum(amax / F32(7.0), F32(1e-5)).astype(F16)", "s16 = np.maximum(amax / F32(8.0), F32(1e-5)).astype(F16)"),
+    ("sym max without abs", "amax = np.abs(w).max(axis=2)", "amax = w.max(axis=2)"),
+    ("sym zero point 7", "codes = (q + F32(8)).reshape(N, K).astype(np.uint8)", "codes = (q + F32(7)).reshape(N, K).astype(np.uint8)"),
+    ("per-channel as g128", "G = K if int(group_size) == -1 else int(group_size)\n    if G <= 0", "G = 128 if int(group_size) == -1 else int(group_size)\n    if G <= 0"),
     ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
 ]
 
