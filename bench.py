@@ -380,6 +380,27 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3)}
         del gus
     out["silu_mul_quant_I13824"] = smq
+    # W4A16 variants: per-channel and symmetric weights on the same kernels
+    log("detail: w4a16 variants")
+    var = {}
+    for (K, N) in ((5120, 27648), (5120, 5120)):
+        w = synth.make_linear(0, N, K, seed=0, outliers=True).w.to(dev)
+        for group, sym in ((128, False), (-1, False), (128, True), (-1, True)):
+            pack = w4.awq_pack_sym if sym else w4.awq_pack
+            qw, sc, qz = pack(w, group)
+            copies = [rotated_awq(qw, sc, qz, r) for r in range(4)]
+            for M in ((1, 16) if N > 8192 else (4096,)):
+                x = synth.make_activations(M, K, seed=M, rms_spread=True).to(dev)
+                y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                calls = [w4.bind_awq_gemm(x, *c, y, group) for c in copies]
+                t = _time_calls(torch, calls, max(it, 16) if M < 4096 else max(4, it // 2))
+                b = awq_bytes(M, N, K) if group > 0 else awq_bytes(M, N, K) - (2 * N * K // 128 + N * K // 256) + 2 * N + N // 2
+                key = f"{'pc' if group < 0 else 'g128'}_{'sym' if sym else 'asym'}_{K}x{N}_M{M}"
+                var[key] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+                            "TFLOPs": round(2.0 * M * N * K / t / 1e12, 1)}
+            del copies, qw, sc, qz
+        del w
+    out["w4a16_variants"] = var
     return out
 
 

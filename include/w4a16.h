@@ -9,6 +9,12 @@
  * comment of that page (AutoAWQ's pseudo-quantize rule):
  *     s = fp16(max(fp32(max - min) / 15, 1e-5)),  z = clamp(rint(-min / s), 0, 15),
  *     q = clamp(rint(w / s) + z, 0, 15),  dequant(w) = (q - z) * s.
+ * Per-channel weights (group_size -1) form one group over K per row (a reading of the
+ * per-channel variant named on the lmdeploy QQQ page below).  Symmetric weights
+ * (awq_pack_sym; the W4A16 preset named beside W4A16_ASYM on the compressed-tensors
+ * page, read with the W4A8 per-channel constants) use s = fp16(max(max|w| / 7, 1e-5)),
+ * q = clamp(rint(w / s), -8, 7), stored as the code q + 8 with zero point 8, so every
+ * W4A16 entry point below serves them unchanged.
  *
  * The W4A8 stage ("[Feature] support qqq(w4a8) for lmdeploy", InternLM/lmdeploy issue
  * 2274, section "Modification"): per-token int8 activations produced by an online
@@ -28,17 +34,16 @@
  *                                    words stored tiled: word j of row n sits at
  *                                    [n/16][j/16][(j%16)/4][n%16][j%4], i.e. 1 KB blocks of
  *                                    16 rows x 128 k; rows past N are padding (code 0)
- *   scales   fp16  [K/G, N]          per-group scales, group-major
+ *   scales   fp16  [K/G, N]          per-group scales, group-major ([1, N] per-channel)
  *   qzeros   int32 [K/G, ceil(N/8)]  4-bit zero points packed along N, plain nibble
- *                                    order, pad nibbles 0
+ *                                    order, pad nibbles 0 ([1, ceil(N/8)] per-channel)
  *   (W4A8)   qweight int32 [ceil(N/16), K/128, 4, 16, 4] (same tiling) of biased nibbles
  *            q + 8 (q in [-8, 7]; padding rows q = 0),
  *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
  *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
  *
  * Sizes: M >= 0, N >= 0 (M == 0 or N == 0 is a no-op returning W4_OK), K a positive
- * multiple of the group size.  group_size: 128 for W4A16; 128 or -1 (per-channel) for
- * W4A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
+ * multiple of 128.  group_size: 128 or -1 (per-channel), for W4A16 and W4A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
  *
  * `stream` is a hipStream_t (NULL = the null stream).  All entry points are
  * asynchronous: they return after validation and launch; a fault inside a kernel
@@ -71,10 +76,19 @@ enum {
  * awq_pack -- quantize fp16 weights W [N, K] with the asymmetric group rule above and
  * write qweight, scales and qzeros.  Quantization decisions are taken in fp32 (IEEE
  * division, round-half-to-even), so the output is bit-exact and deterministic.
- * M is unused (accepted for a uniform signature; must be >= 0).
+ * M is unused (accepted for a uniform signature; must be >= 0).  group_size -1 runs a
+ * per-row statistics kernel first (two launches on `stream`).
  */
 int awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros,
              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
+ * awq_pack_sym -- as awq_pack with the symmetric rule: s = fp16(max(max|w| / 7, 1e-5))
+ * per (row, group), code q + 8 with q = clamp(rint(w / s), -8, 7), every zero point 8
+ * (the nibble of every real row is 8).  Same layouts, arguments and errors.
+ */
+int awq_pack_sym(const void* w, int32_t* qweight, void* scales, int32_t* qzeros,
+                 int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
 
 /*
  * awq_unpack_dequant -- write fp16 W_deq [N, K] = fp16((q - z) * s) with exactly one

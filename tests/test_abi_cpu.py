@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
               "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
-              "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant"):
+              "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant", "awq_pack_sym"):
         assert n in names
 
 
@@ -55,8 +55,10 @@ FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 64, None), 2, "group_size"),
     ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 128, None), 1, "aligned"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 1 << 31, 128, None), 2, "2^30"),
-    # a narrow-N shape splits K and needs a workspace
+    # a narrow-N shape splits K and needs a workspace (per-channel alike)
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, 256, 5120, 128, None), 3, "workspace"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, 256, 5120, -1, None), 3, "workspace"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 0, None), 2, "group_size"),
 ])
 def test_awq_gemm_validation(lib, args, code, msg):
     P = ctypes.c_void_p
@@ -103,6 +105,12 @@ def test_w4a8_validation(lib):
     assert lib.w4a8_silu_mul_quant(f, f, f, 4, 0, 1 << 30, 0, None) == 2
     assert lib.w4a8_pack(f, f, None, f, 0, 64, 256, 128, None) == 1
     assert lib.awq_pack(f, f, f, f, 0, 64, 256, 32, None) == 2
+    assert lib.awq_pack_sym(f, f, f, f, 0, 64, 256, 64, None) == 2
+    assert "group_size" in lib.w4_last_error().decode()
+    assert lib.awq_pack_sym(f, None, f, f, 0, 64, 256, -1, None) == 1
+    assert "qweight is NULL" in lib.w4_last_error().decode()
+    assert lib.awq_pack_sym(None, None, None, None, 0, 0, 256, -1, None) == 0
+    assert lib.awq_unpack_dequant(f, f, f, f, 64, 200, -1, None) == 1
 
 
 def test_workspace_sizes(lib):
@@ -110,5 +118,7 @@ def test_workspace_sizes(lib):
     assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 128) > 0
     assert lib.awq_gemm_workspace_bytes(4096, 27648, 5120, 128) == 0
     assert lib.awq_gemm_workspace_bytes(16, 5120, 200, 128) == 0
+    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, -1) == lib.awq_gemm_workspace_bytes(1, 256, 5120, 128)
+    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 64) == 0
     assert lib.w4a8_gemm_workspace_bytes(1, 256, 5120, -1) > 0  # narrow N splits K
     assert lib.w4a8_gemm_workspace_bytes(4096, 13824, 5120, 128) == 0

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     awq_gemm,
     awq_gemm_workspace_bytes,
     awq_pack,
+    awq_pack_sym,
     awq_unpack_dequant,
     bind_awq_gemm,
     bind_w4a8_gemm,

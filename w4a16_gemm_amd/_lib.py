@@ -48,6 +48,7 @@ def load():
         P, I64, I32, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         sig = {
             "awq_pack": [P, P, P, P, I64, I64, I64, I32, P],
+            "awq_pack_sym": [P, P, P, P, I64, I64, I64, I32, P],
             "awq_unpack_dequant": [P, P, P, P, I64, I64, I32, P],
             "awq_gemm": [P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4a8_pack": [P, P, P, P, I64, I64, I64, I32, P],
@@ -134,7 +135,16 @@ def _need_qweight(qweight, N, K, dev):
 # ------------------------------------------------------------------ W4A16
 def awq_pack(w: torch.Tensor, group_size: int = 128):
     """fp16 W [N, K] -> (qweight int32 [ceil(N/16), K/128, 4, 16, 4], scales fp16 [K/G, N],
-    qzeros int32 [K/G, ceil(N/8)])."""
+    qzeros int32 [K/G, ceil(N/8)]); group_size -1: per-channel (scales [1, N])."""
+    return _pack_w4a16("awq_pack", w, group_size)
+
+
+def awq_pack_sym(w: torch.Tensor, group_size: int = 128):
+    """As awq_pack with the symmetric rule (codes q + 8, zero points 8)."""
+    return _pack_w4a16("awq_pack_sym", w, group_size)
+
+
+def _pack_w4a16(name, w, group_size):
     _need(w, "w", torch.float16, 2)
     N, K = w.shape
     dev = w.device
@@ -143,7 +153,7 @@ def awq_pack(w: torch.Tensor, group_size: int = 128):
     scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
     qzeros = torch.empty((K // G, (N + 7) // 8), dtype=torch.int32, device=dev)
     with torch.cuda.device(dev):
-        _check("awq_pack", load().awq_pack(_ptr(w), _ptr(qweight), _ptr(scales), _ptr(qzeros), 0, N, K,
+        _check(name, getattr(load(), name)(_ptr(w), _ptr(qweight), _ptr(scales), _ptr(qzeros), 0, N, K,
                                            group_size, _stream(dev)))
     return qweight, scales, qzeros
 
@@ -164,7 +174,8 @@ def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):
     _need(scales, "scales", torch.float16, 2)
     dev = scales.device
     _need(qzeros, "qzeros", torch.int32, 2, dev)
-    N, K = scales.shape[1], scales.shape[0] * group_size
+    _need(qweight, "qweight", torch.int32, 5, dev)
+    N, K = scales.shape[1], qweight.shape[1] * 128
     _need_qweight(qweight, N, K, dev)
     out = torch.empty((N, K), dtype=torch.float16, device=dev)
     with torch.cuda.device(dev):

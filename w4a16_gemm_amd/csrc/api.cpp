@@ -46,6 +46,13 @@ int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
   return W4_OK;
 }
 
+// W4A16 group sizes: 128, or -1 for per-channel (one group over K).
+int check_group_w4a16(const char* fn, int32_t group_size) {
+  if (group_size != 128 && group_size != -1)
+    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1 are implemented)", fn, group_size);
+  return W4_OK;
+}
+
 int check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
   for (auto& p : ptrs) {
     if (p.second == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: %s is NULL", fn, p.first);
@@ -106,28 +113,38 @@ int env_int(const char* name, int dflt) {
 
 extern "C" {
 
-int awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int64_t M, int64_t N, int64_t K,
-             int32_t group_size, void* stream) {
-  const char* fn = "awq_pack";
+static int pack_w4a16(const char* fn, bool symmetric, const void* w, int32_t* qweight, void* scales,
+                      int32_t* qzeros, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
   g_last_error.clear();
-  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_group_w4a16(fn, group_size));
   W4_TRY(check_mnk(fn, M, N, K));
   if (N == 0) return W4_OK;
   W4_TRY(check_ptrs(fn, {{"w", w}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}}));
   W4_TRY(check_device(fn));
-  return launched(fn, w4::launch_awq_pack(w, qweight, scales, qzeros, (int)N, (int)K, (hipStream_t)stream));
+  return launched(fn, w4::launch_awq_pack(w, qweight, scales, qzeros, (int)N, (int)K, group_size, symmetric,
+                                          (hipStream_t)stream));
+}
+
+int awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int64_t M, int64_t N, int64_t K,
+             int32_t group_size, void* stream) {
+  return pack_w4a16("awq_pack", false, w, qweight, scales, qzeros, M, N, K, group_size, stream);
+}
+
+int awq_pack_sym(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int64_t M, int64_t N, int64_t K,
+                 int32_t group_size, void* stream) {
+  return pack_w4a16("awq_pack_sym", true, w, qweight, scales, qzeros, M, N, K, group_size, stream);
 }
 
 int awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros, void* w_out, int64_t N,
                        int64_t K, int32_t group_size, void* stream) {
   const char* fn = "awq_unpack_dequant";
   g_last_error.clear();
-  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_group_w4a16(fn, group_size));
   W4_TRY(check_mnk(fn, 0, N, K));
   if (N == 0) return W4_OK;
   W4_TRY(check_ptrs(fn, {{"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"w_out", w_out}}));
   W4_TRY(check_device(fn));
-  return launched(fn, w4::launch_awq_unpack_dequant(qweight, scales, qzeros, w_out, (int)N, (int)K,
+  return launched(fn, w4::launch_awq_unpack_dequant(qweight, scales, qzeros, w_out, (int)N, (int)K, group_size,
                                                     (hipStream_t)stream));
 }
 
@@ -145,7 +162,9 @@ int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void
 }
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
-  if (group_size != 128 || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if ((group_size != 128 && group_size != -1) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
+      K > kMaxDim)
+    return 0;
   return awq_ws(M, N, K);
 }
 
@@ -154,7 +173,7 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
              void* stream) {
   const char* fn = "awq_gemm";
   g_last_error.clear();
-  if (group_size != 128) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only 128 is implemented)", fn, group_size);
+  W4_TRY(check_group_w4a16(fn, group_size));
   W4_TRY(check_mnk(fn, M, N, K));
   if (M == 0 || N == 0) return W4_OK;
   W4_TRY(check_ptrs(fn, {{"x", x}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"y", y}}));
@@ -167,8 +186,12 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   }
   W4_TRY(check_device(fn));
   hipError_t e;
-  if (M <= 64) e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, (hipStream_t)stream);
-  else e = w4::launch_gemm(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, (hipStream_t)stream);
+  if (M <= 64)
+    e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
+                          (hipStream_t)stream);
+  else
+    e = w4::launch_gemm(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
+                        (hipStream_t)stream);
   return launched(fn, e);
 }
 

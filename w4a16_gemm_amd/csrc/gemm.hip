@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
                                                             const uint32_t* __restrict__ qzeros,
                                                             half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                             float* __restrict__ partials, int M, int N, int K,
-                                                            int tiles_m, int tiles_n, int splits, int kps) {
+                                                            int tiles_m, int tiles_n, int splits, int kps,
+                                                            int gmask) {
   constexpr int BM = 32 * MI, BN = 128 * NF;
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
   __shared__ u32x4 lds[2][BM * 8];
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   auto load_sz = [&](int g) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      zraw[f] = qzeros[(int64_t)g * nzw + (nclamp[f] >> 3)];
-      sraw[f] = scales[(int64_t)g * N + nclamp[f]];
+      zraw[f] = qzeros[(int64_t)(g & gmask) * nzw + (nclamp[f] >> 3)];
+      sraw[f] = scales[(int64_t)(g & gmask) * N + nclamp[f]];
     }
   };
   half2_t c1024[NF], c64[NF], s2[NF];
@@ -311,15 +312,16 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
 }
 
 hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                       void* y, void* ws, int M, int N, int K, hipStream_t stream) {
+                       void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
   const GemmPlan p = gemm_plan(M, N, K);
+  const int gmask = group_mask(group_size);
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int blocks = p.tiles_m * p.tiles_n * p.splits;
 #define GEMM_LAUNCH(MI, NF)                                                                                   \
   hipLaunchKernelGGL((gemm_kernel<MI, NF>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,          \
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, gmask)
   if (p.mi == 4 && p.nf == 2) GEMM_LAUNCH(4, 2);
   else if (p.mi == 4) GEMM_LAUNCH(4, 1);
   else if (p.nf == 2) GEMM_LAUNCH(2, 2);

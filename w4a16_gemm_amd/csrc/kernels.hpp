@@ -77,21 +77,25 @@ struct W4A8Plan {
 };
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 
+// W4A16 scales and zero points are read at group row (g & group_mask): per-channel
+// weights (group_size -1) keep a single row, read for every 128-group.
+inline int group_mask(int group_size) { return group_size == -1 ? 0 : -1; }
+
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
-                           hipStream_t stream);
+                           int group_size, bool symmetric, hipStream_t stream);
 hipError_t launch_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, hipStream_t stream);
 hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                                     void* out, int N, int K, hipStream_t stream);
+                                     void* out, int N, int K, int group_size, hipStream_t stream);
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
                             int two_level, hipStream_t stream);
 
 size_t skinny_workspace_bytes(int M, int N, int K);
 hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                         void* y, void* ws, int M, int N, int K, hipStream_t stream);
+                         void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                       void* y, void* ws, int M, int N, int K, hipStream_t stream);
+                       void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream);
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
                                  int K, hipStream_t stream);

@@ -5,6 +5,13 @@
 //    AutoAWQ's pseudo-quantize) and packing into the plain nibble order (packed
 //    weight format of the Triton AWQ kernels in "Implement AWQ quantization support
 //    for LLaMA", vllm-project/vllm PR 1032: pack_num = 8 codes per 32-bit word).
+//    Per-channel weights (group_size -1: one group over K, a reading of the
+//    per-channel variant named on "[Feature] support qqq(w4a8) for lmdeploy") take
+//    their row statistics from awq_rowstats first.  Symmetric weights (the W4A16
+//    preset beside W4A16_ASYM in the same compressed-tensors thread, read with the
+//    W4A8 per-channel constants) use s = fp16(max(max|w| / 7, 1e-5)) and the fixed zero
+//    point 8, so code = clamp(rint(w / s) + 8, 0, 15) = clamp(rint(w / s), -8, 7) + 8 is
+//    the asymmetric code formula with z = 8.
 //  * awq_unpack_dequant: fp16((q - z) * s), the GEMM's dequantization, exported.
 //  * w4a8_pack: symmetric int4 weights for the W4A8 GEMM, per-channel or two-level
 //    with int8 group scales ("[Feature] support qqq(w4a8) for lmdeploy", section
@@ -17,14 +24,70 @@
 
 namespace w4 {
 
+// Scale and zero point of one group (or row) from its statistics: asymmetric
+// s = fp16(max((max - min) / 15, 1e-5)), z = clamp(rint(-min / s), 0, 15); symmetric
+// s = fp16(max(max(|min|, |max|) / 7, 1e-5)), z = 8.
+__device__ __forceinline__ void group_scale_zero(float mn, float mx, int sym, half_t& s16, float& z) {
+  if (sym) {
+    s16 = (half_t)fmaxf(fmaxf(-mn, mx) / 7.0f, 1e-5f);
+    z = 8.0f;
+  } else {
+    s16 = (half_t)fmaxf((mx - mn) / 15.0f, 1e-5f);
+    z = fminf(fmaxf(rintf(-mn / (float)s16), 0.0f), 15.0f);
+  }
+}
+
+// Per-channel statistics: one workgroup per 8 rows, one wave per 2 rows; min and max of
+// each row over K give its scale (scales[n]) and zero point (the 8 nibbles of
+// qzeros[n / 8]).
+__global__ __launch_bounds__(256) void awq_rowstats_kernel(const half_t* __restrict__ w, half_t* __restrict__ scales,
+                                                            int32_t* __restrict__ qzeros, int N, int K, int sym) {
+  __shared__ uint32_t znib[8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * 8;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int i = wave * 2 + rr;
+    const int n = n0 + i;
+    uint32_t zb = 0;
+    if (n < N) {
+      const half8_t* row = reinterpret_cast<const half8_t*>(w + (int64_t)n * K);
+      float mn = INFINITY, mx = -INFINITY;
+      for (int j = lane; j < K / 8; j += kWave) {
+        const half8_t v = row[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mn = fminf(mn, (float)v[e]);
+          mx = fmaxf(mx, (float)v[e]);
+        }
+      }
+      mn = -wave_max(-mn);
+      mx = wave_max(mx);
+      half_t s16;
+      float z;
+      group_scale_zero(mn, mx, sym, s16, z);
+      if (lane == 0) scales[n] = s16;
+      zb = ((uint32_t)z) << (4 * i);
+    }
+    if (lane == 0) znib[i] = zb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= znib[i];
+    qzeros[n0 / 8] = (int32_t)word;
+  }
+}
+
 // One thread per (group g, row n), n fastest, over npad = N rounded up to 16 rows:
 // the 8 threads of a zero-point word are 8 consecutive lanes, and padding rows
-// (n >= N) write code 0 so that the whole tiled array is defined.
+// (n >= N) write code 0 so that the whole tiled array is defined.  Per-channel
+// (perchan = 1): scale and zero point come from awq_rowstats and are not rewritten.
 __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict__ w,
                                                         uint32_t* __restrict__ qweight,
                                                         half_t* __restrict__ scales,
                                                         int32_t* __restrict__ qzeros,
-                                                        int N, int K, int npad) {
+                                                        int N, int K, int npad, int perchan, int sym) {
   const int ng = K / 128;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = tid < (int64_t)npad * ng;
@@ -39,18 +102,22 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) raw[i] = src[i];
     const half_t* h = reinterpret_cast<const half_t*>(raw);
-    float mn = (float)h[0], mx = (float)h[0];
+    half_t s16;
+    float z;
+    if (perchan) {
+      s16 = scales[n];
+      z = (float)((((uint32_t)qzeros[n / 8]) >> (4 * (n & 7))) & 15u);
+    } else {
+      float mn = (float)h[0], mx = (float)h[0];
 #pragma unroll
-    for (int i = 1; i < 128; ++i) {
-      const float v = (float)h[i];
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+      for (int i = 1; i < 128; ++i) {
+        const float v = (float)h[i];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      group_scale_zero(mn, mx, sym, s16, z);
     }
-    float s32 = (mx - mn) / 15.0f;
-    s32 = fmaxf(s32, 1e-5f);
-    const half_t s16 = (half_t)s32;
     const float s = (float)s16;
-    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f);
     uint32_t* ow = reinterpret_cast<uint32_t*>(out);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -62,7 +129,7 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
       }
       ow[j] = word;
     }
-    scales[(int64_t)g * N + n] = s16;
+    if (!perchan) scales[(int64_t)g * N + n] = s16;
     zbits = ((uint32_t)z) << (4 * (n & 7));
   }
   if (live) {
@@ -73,14 +140,15 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
   zbits |= __shfl_xor(zbits, 1, kWave);
   zbits |= __shfl_xor(zbits, 2, kWave);
   zbits |= __shfl_xor(zbits, 4, kWave);
-  if (valid && (n & 7) == 0) qzeros[(int64_t)g * ((N + 7) / 8) + n / 8] = (int32_t)zbits;
+  if (!perchan && valid && (n & 7) == 0) qzeros[(int64_t)g * ((N + 7) / 8) + n / 8] = (int32_t)zbits;
 }
 
 // One thread per packed word (n, j): eight fp16 outputs.
 __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t* __restrict__ qweight,
                                                                   const half_t* __restrict__ scales,
                                                                   const uint32_t* __restrict__ qzeros,
-                                                                  half_t* __restrict__ out, int N, int K) {
+                                                                  half_t* __restrict__ out, int N, int K,
+                                                                  int gmask) {
   const int wpr = K / 8;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (tid >= (int64_t)N * wpr) return;
@@ -88,8 +156,8 @@ __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t*
   const int j = (int)(tid % wpr);
   const int g = j / 16;
   const int nzw = (N + 7) / 8;
-  const uint32_t z = (qzeros[(int64_t)g * nzw + n / 8] >> (4 * (n & 7))) & 15u;
-  const half_t s = scales[(int64_t)g * N + n];
+  const uint32_t z = (qzeros[(int64_t)(g & gmask) * nzw + n / 8] >> (4 * (n & 7))) & 15u;
+  const half_t s = scales[(int64_t)(g & gmask) * N + n];
   const half2_t negz2 = splat2(-(half_t)(1024 + z));
   const uint32_t word = qweight[tiled_chunk(n, g, (j & 15) >> 2, K / 128) + (j & 3)];
   const half8_t v = dequant8(word, negz2, splat2(s));
@@ -193,22 +261,29 @@ hipError_t launch_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int6
 }
 
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
-                           hipStream_t stream) {
+                           int group_size, bool symmetric, hipStream_t stream) {
+  const int perchan = group_size == -1 ? 1 : 0;
+  if (perchan) {
+    hipLaunchKernelGGL(awq_rowstats_kernel, dim3((N + 7) / 8), dim3(256), 0, stream, (const half_t*)w,
+                       (half_t*)scales, qzeros, N, K, symmetric ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int npad = (N + 15) / 16 * 16;
   const int64_t total = (int64_t)npad * (K / 128);
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(awq_pack_kernel, dim3(blocks), dim3(256), 0, stream, (const half_t*)w, (uint32_t*)qweight,
-                     (half_t*)scales, qzeros, N, K, npad);
+                     (half_t*)scales, qzeros, N, K, npad, perchan, symmetric ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                                     void* out, int N, int K, hipStream_t stream) {
+                                     void* out, int N, int K, int group_size, hipStream_t stream) {
   const int64_t total = (int64_t)N * (K / 8);
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(awq_unpack_dequant_kernel, dim3(blocks), dim3(256), 0, stream,
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros,
-                     (half_t*)out, N, K);
+                     (half_t*)out, N, K, group_mask(group_size));
   return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
                                            const uint32_t* __restrict__ qweight,
                                            const half_t* __restrict__ scales,
                                            const uint32_t* __restrict__ qzeros, int g, int n0, int lane,
-                                           int M, int N, int K) {
+                                           int M, int N, int K, int gmask) {
   const int ng = K / 128;
   const int nzw = (N + 7) / 8;
   const int slot = lane >> 4;
@@ -61,8 +61,8 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     // l % 16 of the tile, words 4 (l / 16) .. + 3 of the group
     const int tile = min((n0 >> 4) + t, last_tile);
     r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
-    r.s[t] = scales[(int64_t)g * N + nc];
-    r.zw[t] = qzeros[(int64_t)g * nzw + (nc >> 3)];
+    r.s[t] = scales[(int64_t)(g & gmask) * N + nc];
+    r.zw[t] = qzeros[(int64_t)(g & gmask) * nzw + (nc >> 3)];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
                                                                half_t* __restrict__ y,
                                                                unsigned* __restrict__ counters,
                                                                float* __restrict__ partials, int M, int N, int K,
-                                                               int splits, int gps, int drain) {
+                                                               int splits, int gps, int drain, int gmask) {
   constexpr int kT = WAVES * kWave;
   constexpr int kCols = 16 * T;           // output columns of one workgroup
   constexpr int kOut = MT * 16 * kCols;   // outputs of one workgroup
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   const int g = gbeg + wave;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K);
+    load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K, gmask);
   // Steady state without conditions (the wait before each compute then covers only its
   // own register set), then the remaining < D groups; all counts are wave-uniform.
   const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
@@ -160,7 +160,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       compute_group<MT, T>(r[d], yacc, n0, lane, N);
-      load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
+      load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K,
+                        gmask);
     }
   }
 #pragma unroll
@@ -268,10 +269,10 @@ template <int T>
 __device__ __forceinline__ void load_wstage(WStage<T>& r, const uint32_t* __restrict__ qweight,
                                             const half_t* __restrict__ scales,
                                             const uint32_t* __restrict__ qzeros, int g, int tile0, int lane,
-                                            int N, int ng, int nzw) {
+                                            int N, int ng, int nzw, int gmask) {
   const int last_tile = (N - 1) >> 4;
-  const half_t* srow = scales + (int64_t)g * N;
-  const uint32_t* zrow = qzeros + (int64_t)g * nzw;
+  const half_t* srow = scales + (int64_t)(g & gmask) * N;
+  const uint32_t* zrow = qzeros + (int64_t)(g & gmask) * nzw;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int tile = min(tile0 + t, last_tile);
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
                                                          const uint32_t* __restrict__ qzeros,
                                                          half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                          float* __restrict__ partials, int M, int N, int K,
-                                                         int splits, int gps, int wn_count, int drain) {
+                                                         int splits, int gps, int wn_count, int drain, int gmask) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nthreads = blockDim.x;
   const int lane = threadIdx.x & 63;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   const int glast = gend - 1;
   const int g = gbeg + wk;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_wstage<T>(r[d], qweight, scales, qzeros, min(g + d * WK, glast), tile0, lane, N, ng, nzw);
+  for (int d = 0; d < D; ++d) load_wstage<T>(r[d], qweight, scales, qzeros, min(g + d * WK, glast), tile0, lane, N, ng, nzw, gmask);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kXChunksPerPass; ++i) {
@@ -463,7 +464,8 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
     for (int d = 0; d < D; ++d) {
       const int gl = g + (it + d) * WK - gbeg;
       compute_wstage<T, ONE_ROW>(r[d], xrow + gl * 128, sp + gl * 32, yacc, zsh, lane);
-      load_wstage<T>(r[d], qweight, scales, qzeros, min(gbeg + gl + D * WK, glast), tile0, lane, N, ng, nzw);
+      load_wstage<T>(r[d], qweight, scales, qzeros, min(gbeg + gl + D * WK, glast), tile0, lane, N, ng, nzw,
+                     gmask);
     }
   }
 #pragma unroll
@@ -614,8 +616,9 @@ size_t skinny_workspace_bytes(int M, int N, int K) {
 }
 
 hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                         void* y, void* ws, int M, int N, int K, hipStream_t stream) {
+                         void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
   const SkinnyPlan p = skinny_plan(M, N, K);
+  const int gmask = group_mask(group_size);
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const dim3 grid(p.row_blocks, p.splits);
@@ -628,7 +631,7 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
     const dim3 block(64 * p.wn * p.wk);
 #define LDS_LAUNCH1(T, D, ONE)                                                                                \
   hipLaunchKernelGGL((skinny_lds_kernel<T, D, ONE>), grid, block, p.smem, stream, xh, qw, sc, qz, yh, counters, \
-                     partials, M, N, K, p.splits, p.gps, p.wn, p.drain)
+                     partials, M, N, K, p.splits, p.gps, p.wn, p.drain, gmask)
 #define LDS_LAUNCH(T, D) \
   if (M == 1) LDS_LAUNCH1(T, D, true); else LDS_LAUNCH1(T, D, false)
     if (p.tiles == 1) { if (p.depth == 4) LDS_LAUNCH(1, 4); else LDS_LAUNCH(1, 8); }
@@ -640,7 +643,7 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
   }
 #define SKINNY_LAUNCH(MT, T, D)                                                                          \
   hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, counters, \
-                     partials, M, N, K, p.splits, p.gps, p.drain)
+                     partials, M, N, K, p.splits, p.gps, p.drain, gmask)
 #define SKINNY_LAUNCH_T(MT)                    \
   if (p.tiles == 4) SKINNY_LAUNCH(MT, 4, 2);   \
   else if (p.tiles == 2) SKINNY_LAUNCH(MT, 2, 2); \
