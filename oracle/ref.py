@@ -65,6 +65,15 @@ Readings where the pages are silent:
   ``s = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s), -8, 7)`` (the R5
   per-channel constants), stored as the code ``q + 8`` with zero point 8, so
   ``(code - 8) * s = q * s`` dequantizes it with the asymmetric formula.
+* R15 W8A8 ([AWQ-vLLM], reply on an 8-bit-weight method built with SmoothQuant
+  that raised throughput; [AWQ-fixes], replies on presets: W8A8 quantizes weights
+  and activations to 8 bits): weights per output channel symmetric int8 with the
+  first level of R5's two-level rule, ``s = fp16(max(max|w| / 127, 1e-5))``,
+  ``q = clamp(rint(w / s), -127, 127)``; activations per token as R6; the GEMM
+  accumulates ``sum_k xq q`` exactly in int32 and outputs ``acc * s_a * s``.
+  SmoothQuant's calibrated per-input-channel smoothing is an offline rescaling of
+  X and W that leaves this GEMM unchanged; it needs calibration data and is not
+  part of the oracle.
 * R12 SiLU-gated activations ([QQQ-lmdeploy], "Modification": online
   quantization fused with element-wise operations such as SiLU; gate and up
   weights fused into one weight): the fused gate+up output ``[M, 2I]`` holds gate
@@ -87,7 +96,7 @@ __all__ = [
     "pack_nibbles", "unpack_nibbles", "tile_words", "untile_words",
     "quantize_asym", "quantize_sym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
-    "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref",
+    "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref", "quantize_w8a8",
     "w4a8_acc_ref", "w4a8_linear_ref", "silu_ref", "silu_mul_quant_ref",
 ]
 
@@ -311,6 +320,20 @@ def quantize_w4a8(w16: np.ndarray, group_size: int = -1):
     sg = np.minimum(np.maximum(F32(1), np.ceil(m / F32(7))), F32(18))
     q = np.clip(np.rint(w8g / sg[:, :, None]), F32(-7), F32(7))
     return q.reshape(N, K).astype(np.int8), s16, sg.astype(np.int8)
+
+
+def quantize_w8a8(w16: np.ndarray):
+    """Per-channel symmetric int8 weights for W8A8 (R15): ``(q int8 [N, K] in
+    [-127, 127], s fp16 [N])`` with ``s = fp16(max(max|w| / 127, 1e-5))`` and
+    ``q = clamp(rint(w / s), -127, 127)``, decisions in fp32.  The integer GEMM and the
+    output are :func:`w4a8_acc_ref` (no group scales) and :func:`w4a8_linear_ref`."""
+    w16 = np.asarray(w16)
+    if w16.dtype != F16 or w16.ndim != 2:
+        raise ValueError("w16 must be a 2-D float16 array")
+    w = w16.astype(F32)
+    s16 = np.maximum(np.abs(w).max(axis=1) / F32(127.0), F32(1e-5)).astype(F16)
+    q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-127), F32(127))
+    return q.astype(np.int8), s16
 
 
 def pack_w4a8(q: np.ndarray, cscale: np.ndarray, gscale):

@@ -420,6 +420,38 @@ def pin_variants_constructed_exact(ora):
     assert ref2["scales"].shape == (1, N) and ref2["qzeros"].shape == (1, 2)
 
 
+# ----------------------------------------------------------------- W8A8
+def pin_w8a8_worked(ora):
+    """The first level of the hand-worked two-level row TL (tests/golden/w4a8_worked.txt)
+    is the W8A8 rule: s = 0x2008 and codes 127, 6, -13 | 32."""
+    case = [c for c in read_cases("w4a8_worked.txt") if c["name"] == "TL"][0]
+    q, s = ora.quantize_w8a8(case["values"][None, :])
+    assert s[0].view(np.uint16) == case["cscale"].view(np.uint16)
+    assert q[0, :3].tolist() == [127, 6, -13] and q[0, 128] == 32 and not q[0, 3:128].any()
+
+
+def pin_w8a8_properties(ora):
+    """Codes in [-127, 127], |w - q s| <= s / 2, the row maximum maps to +-127, negating
+    W negates the codes; with w = q' 2^-7 and each row holding +-127 the codes are q'
+    exactly, so the integer accumulator is the exact product."""
+    rng = _rng(51)
+    w = (rng.standard_normal((40, 640)) * 0.02).astype(F16)
+    q, s = ora.quantize_w8a8(w)
+    sv = s.astype(F64)[:, None]
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.all(np.abs(w.astype(F64) - q * sv) <= sv / 2 + 1e-12)
+    am = np.argmax(np.abs(w.astype(F64)), axis=1)
+    assert np.all(np.abs(q[np.arange(40), am]) == 127)
+    qn, sn = ora.quantize_w8a8(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    qp = rng.integers(-127, 128, size=(16, 256))
+    qp[:, 5] = -127
+    q2, s2 = ora.quantize_w8a8((qp * 2.0**-7).astype(F16))
+    assert np.all(s2.astype(F64) == 2.0**-7) and np.array_equal(q2.astype(np.int64), qp)
+    xq = rng.integers(-127, 128, size=(3, 256))
+    assert np.array_equal(ora.w4a8_acc_ref(xq, q2, None, 128), xq @ qp.T)
+
+
 def pin_w4a8_acc_bruteforce(ora):
     """Integer accumulators against Python-int loops, both weight variants."""
     rng = _rng(31)
@@ -454,4 +486,5 @@ ALL_PINS = [
     pin_w4a8_worked, pin_w4a8_exhaustive, pin_quant_act_closed_forms, pin_w4a8_acc_bruteforce,
     pin_silu_worked, pin_silu_closed_forms, pin_silu_special_cases,
     pin_variants_worked, pin_sym_properties, pin_variants_constructed_exact,
+    pin_w8a8_worked, pin_w8a8_properties,
 ]

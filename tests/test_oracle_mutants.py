@@ -45,6 +45,8 @@ MUTANTS = [
     ("sym max without abs", "amax = np.abs(w).max(axis=2)", "amax = w.max(axis=2)"),
     ("sym zero point 7", "codes = (q + F32(8)).reshape(N, K).astype(np.uint8)", "codes = (q + F32(7)).reshape(N, K).astype(np.uint8)"),
     ("per-channel as g128", "G = K if int(group_size) == -1 else int(group_size)\n    if G <= 0", "G = 128 if int(group_size) == -1 else int(group_size)\n    if G <= 0"),
+    ("w8a8 divisor 128", "s16 = np.maximum(np.abs(w).max(axis=1) / F32(127.0), F32(1e-5)).astype(F16)", "s16 = np.maximum(np.abs(w).max(axis=1) / F32(128.0), F32(1e-5)).astype(F16)"),
+    ("w8a8 clamp 126", "q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-127), F32(127))\n    return q.astype(np.int8), s16", "q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-126), F32(126))\n    return q.astype(np.int8), s16"),
     ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
 ]
 
