@@ -71,6 +71,10 @@ Readings where the pages are silent:
   first level of R5's two-level rule, ``s = fp16(max(max|w| / 127, 1e-5))``,
   ``q = clamp(rint(w / s), -127, 127)``; activations per token as R6; the GEMM
   accumulates ``sum_k xq q`` exactly in int32 and outputs ``acc * s_a * s``.
+  Layout (a design choice, like R4): int8 [ceil(N/16), K/128, 4, 2, 16, 16], code
+  (n, k) at ``[n // 16, k // 128, kc % 4, kc // 4, n % 16, k % 16]`` with
+  ``kc = (k % 128) // 16``: one 2 KB block per 16 rows x 128 k whose 16-byte chunks
+  of one ``kc % 4`` lie together for all 16 rows and both ``kc // 4``.
   SmoothQuant's calibrated per-input-channel smoothing is an offline rescaling of
   X and W that leaves this GEMM unchanged; it needs calibration data and is not
   part of the oracle.
@@ -97,6 +101,7 @@ __all__ = [
     "quantize_asym", "quantize_sym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref", "quantize_w8a8",
+    "tile_w8a8", "untile_w8a8",
     "w4a8_acc_ref", "w4a8_linear_ref", "silu_ref", "silu_mul_quant_ref",
 ]
 
@@ -334,6 +339,28 @@ def quantize_w8a8(w16: np.ndarray):
     s16 = np.maximum(np.abs(w).max(axis=1) / F32(127.0), F32(1e-5)).astype(F16)
     q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-127), F32(127))
     return q.astype(np.int8), s16
+
+
+def tile_w8a8(q: np.ndarray) -> np.ndarray:
+    """int8 codes [N, K] -> the tiled W8A8 qweight int8 [ceil(N/16), K/128, 4, 2, 16, 16]
+    (R15 layout): with ``kc = (k % 128) // 16``, code (n, k) goes to
+    ``[n // 16, k // 128, kc % 4, kc // 4, n % 16, k % 16]``; rows past N hold 0."""
+    q = np.asarray(q)
+    if q.dtype != np.int8 or q.ndim != 2 or q.shape[1] % 128:
+        raise ValueError("q must be int8 [N, K] with K a multiple of 128")
+    N, K = q.shape
+    Np = -(-N // 16) * 16
+    full = np.zeros((Np, K), np.int8)
+    full[:N] = q
+    # [n16, r, g, h, c, b] -> [n16, g, c, h, r, b]
+    return np.ascontiguousarray(full.reshape(Np // 16, 16, K // 128, 2, 4, 16).transpose(0, 2, 4, 3, 1, 5))
+
+
+def untile_w8a8(tiled: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of :func:`tile_w8a8`: tiled int8 -> codes [N, K]."""
+    t = np.asarray(tiled)
+    n16, ng = t.shape[0], t.shape[1]
+    return np.ascontiguousarray(t.transpose(0, 4, 1, 3, 2, 5)).reshape(n16 * 16, ng * 128)[:N]
 
 
 def pack_w4a8(q: np.ndarray, cscale: np.ndarray, gscale):

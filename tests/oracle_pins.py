@@ -430,6 +430,28 @@ def pin_w8a8_worked(ora):
     assert q[0, :3].tolist() == [127, 6, -13] and q[0, 128] == 32 and not q[0, 3:128].any()
 
 
+def pin_w8a8_tile_layout(ora):
+    """Tiled int8 order: a single code placed at (n, k) lands at the flat byte offset
+    computed by hand from the layout rule, with kc = (k % 128) / 16,
+    ((n/16 * K/128 + k/128) * 4 + kc % 4) * 512 + (kc / 4) * 256 + (n % 16) * 16 + k % 16;
+    tile/untile are inverse bijections; pad rows are 0."""
+    N, K = 37, 256
+    for (n, k, c) in ((17, 200, 9), (0, 0, -127), (36, 255, 1), (15, 127, 64), (16, 128, -3)):
+        q = np.zeros((N, K), np.int8)
+        q[n, k] = c
+        flat = ora.tile_w8a8(q).reshape(-1)
+        kc = (k % 128) // 16
+        off = ((n // 16 * (K // 128) + k // 128) * 4 + kc % 4) * 512 + (kc // 4) * 256 + (n % 16) * 16 + k % 16
+        assert flat.size == 48 * K
+        assert int(flat[off]) == c and np.count_nonzero(flat) == 1, (n, k)
+    rng = _rng(7)
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    t = ora.tile_w8a8(q)
+    assert t.shape == (3, 2, 4, 2, 16, 16)
+    assert np.array_equal(ora.untile_w8a8(t, N), q)
+    assert not ora.untile_w8a8(t, 48)[N:].any()
+
+
 def pin_w8a8_properties(ora):
     """Codes in [-127, 127], |w - q s| <= s / 2, the row maximum maps to +-127, negating
     W negates the codes; with w = q' 2^-7 and each row holding +-127 the codes are q'
@@ -486,5 +508,5 @@ ALL_PINS = [
     pin_w4a8_worked, pin_w4a8_exhaustive, pin_quant_act_closed_forms, pin_w4a8_acc_bruteforce,
     pin_silu_worked, pin_silu_closed_forms, pin_silu_special_cases,
     pin_variants_worked, pin_sym_properties, pin_variants_constructed_exact,
-    pin_w8a8_worked, pin_w8a8_properties,
+    pin_w8a8_worked, pin_w8a8_properties, pin_w8a8_tile_layout,
 ]

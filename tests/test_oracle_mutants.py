@@ -47,6 +47,7 @@ MUTANTS = [
     ("per-channel as g128", "G = K if int(group_size) == -1 else int(group_size)\n    if G <= 0", "G = 128 if int(group_size) == -1 else int(group_size)\n    if G <= 0"),
     ("w8a8 divisor 128", "s16 = np.maximum(np.abs(w).max(axis=1) / F32(127.0), F32(1e-5)).astype(F16)", "s16 = np.maximum(np.abs(w).max(axis=1) / F32(128.0), F32(1e-5)).astype(F16)"),
     ("w8a8 clamp 126", "q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-127), F32(127))\n    return q.astype(np.int8), s16", "q = np.clip(np.rint(w / s16.astype(F32)[:, None]), F32(-126), F32(126))\n    return q.astype(np.int8), s16"),
+    ("w8a8 tile c and h swapped", "transpose(0, 2, 4, 3, 1, 5))\n", "transpose(0, 2, 3, 4, 1, 5)).reshape(-1, (q.shape[1]) // 128, 4, 2, 16, 16)\n"),
     ("acc ignores group scale", "q = q * np.repeat(np.asarray(gscale_ng, dtype=np.int64), G, axis=1)", "q = q"),
 ]
 
