@@ -364,6 +364,23 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
                 "frac_f16": round(ops / t / 1e12 / F16_PEAK_TFLOPS, 4), "quant_act_us": round(tq * 1e6, 2)}
         del copies, qw, gs, cs
     out["w4a8_5120x13824"] = w8
+    # W8A8 on the same shape (row-major int8 weights, per-channel scales)
+    log("detail: w8a8")
+    w88 = {}
+    qw8, cs8 = w4.w8a8_pack(wdev)
+    copies8 = [(torch.roll(qw8, 7 * r, 0).contiguous(), torch.roll(cs8, 112 * r, 0).contiguous()) for r in range(8)]
+    for M in (1, 16, 256, 4096):
+        x = inp.x[:M].contiguous().to(dev)
+        xq, sa = w4.w4a8_quant_act(x, inp.gamma.to(dev))
+        y = torch.empty((M, 13824), dtype=torch.float16, device=dev)
+        calls = [w4.bind_w8a8_gemm(xq, sa, c[0], c[1], y) for c in copies8]
+        t = _time_calls(torch, calls, max(it, 16) if M < 4096 else max(4, it // 2))
+        b = 13824 * 5120 + 2 * 13824 + M * 5120 + 4 * M + 2 * M * 13824
+        ops = 2.0 * M * 13824 * 5120
+        w88[f"M{M}"] = {"gemm_us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1), "TOPs": round(ops / t / 1e12, 2),
+                        "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3), "frac_i8": round(ops / t / 1e12 / I8_PEAK_TOPS, 4)}
+    del copies8, qw8, cs8
+    out["w8a8_5120x13824"] = w88
     # SiLU-gated quantization of the down projection's input (I = 13824), 4 rotated inputs
     log("detail: silu_mul_quant")
     smq = {}

@@ -41,6 +41,9 @@
  *            q + 8 (q in [-8, 7]; padding rows q = 0),
  *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
  *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
+ *   (W8A8)   qweight int8 [ceil(N/16), K/128, 4, 2, 16, 16]: code (n, k) at
+ *            [n/16][k/128][kc%4][kc/4][n%16][k%16] with kc = (k%128)/16 (2 KB per 16 rows
+ *            x 128 k; padding rows 0), cscale fp16 [N].
  *
  * Sizes: M >= 0, N >= 0 (M == 0 or N == 0 is a no-op returning W4_OK), K a positive
  * multiple of 128.  group_size: 128 or -1 (per-channel), for W4A16 and W4A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
@@ -162,6 +165,37 @@ int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, floa
 int w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a,
                         int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
 
+/*
+ * w8a8_pack -- per-channel symmetric int8 weights for W8A8 (an 8-bit-weight method built
+ * with SmoothQuant is reported on "Implement AWQ quantization support for LLaMA",
+ * vllm-project/vllm PR 1032; "Some fixes for AWQ" names W8A8 as 8-bit weights and
+ * activations; the constants are a reading, those of the first level of the two-level
+ * W4A8 rule): cscale fp16 [N] = fp16(max(max|w| / 127, 1e-5)),
+ * qweight (tiled int8 above) = clamp(rint(w / cscale), -127, 127).  fp32 decisions,
+ * bit-exact.  group_size must be -1; M is unused (>= 0).  SmoothQuant's calibrated
+ * smoothing is an offline rescaling of W and X that the caller applies beforehand.
+ */
+int w8a8_pack(const void* w, int8_t* qweight, void* cscale,
+              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/* w8a8_gemm_workspace_bytes -- as awq_gemm_workspace_bytes, for w8a8_gemm / _i32. */
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * w8a8_gemm -- Y [M, N] = fp16(acc[m, n] * s_a[m] * cscale[n]) with
+ * acc[m, n] = sum_k xq[m, k] * qweight[n, k] exact in int32, on the int8 MFMA kernels of
+ * w4a8_gemm (M <= 16: 16x16x64; larger M: LDS-staged 32x32x32), the weights loaded as
+ * they are.  xq, s_a from w4a8_quant_act or w4a8_silu_mul_quant.  group_size must be -1.
+ * K a positive multiple of 128, at most 131072 (as for w4a8_gemm).
+ */
+int w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
+              void* workspace, size_t workspace_bytes,
+              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/* w8a8_gemm_i32 -- the raw int32 accumulators acc [M, N] of w8a8_gemm.  Bit-exact. */
+int w8a8_gemm_i32(const int8_t* xq, const int8_t* qweight, int32_t* acc, void* workspace, size_t workspace_bytes,
+                  int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
 /* w4a8_gemm_workspace_bytes -- as awq_gemm_workspace_bytes, for w4a8_gemm / _i32. */
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
 
@@ -170,7 +204,8 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_
  * acc[m, n] = sum_k xq[m, k] * q[n, k] * s_g[n, k / G] (s_g = 1 for group_size == -1) is
  * computed exactly in int32 on the int8 MFMA units (M <= 16: bandwidth-bound kernel on
  * 16x16x64 int8 MFMA; larger M: LDS-staged 32x32x32 int8 MFMA GEMM).  gscale is NULL iff
- * group_size == -1.
+ * group_size == -1.  K is at most 131072 (2^17), which keeps every int32 partial sum
+ * in range (127 * 128 per term); larger K returns W4_ERR_UNSUPPORTED.
  */
 int w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
               const void* cscale, void* y, void* workspace, size_t workspace_bytes,

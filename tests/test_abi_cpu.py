@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
               "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
-              "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant", "awq_pack_sym"):
+              "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant", "awq_pack_sym", "w8a8_pack", "w8a8_gemm",
+              "w8a8_gemm_i32", "w8a8_gemm_workspace_bytes"):
         assert n in names
 
 
@@ -111,6 +112,18 @@ def test_w4a8_validation(lib):
     assert "qweight is NULL" in lib.w4_last_error().decode()
     assert lib.awq_pack_sym(None, None, None, None, 0, 0, 256, -1, None) == 0
     assert lib.awq_unpack_dequant(f, f, f, f, 64, 200, -1, None) == 1
+    assert lib.w8a8_pack(f, f, f, 0, 64, 256, 128, None) == 2
+    assert lib.w8a8_pack(f, f, None, 0, 64, 256, -1, None) == 1
+    assert "cscale is NULL" in lib.w4_last_error().decode()
+    assert lib.w8a8_gemm(f, f, f, f, f, None, 0, 4, 64, 256, 128, None) == 2
+    assert lib.w8a8_gemm(f, None, f, f, f, None, 0, 4, 64, 256, -1, None) == 1
+    assert "s_a is NULL" in lib.w4_last_error().decode()
+    assert lib.w8a8_gemm_i32(f, f, None, None, 0, 4, 64, 256, -1, None) == 1
+    assert lib.w8a8_gemm(f, f, f, f, f, None, 0, 4, 64, 1 << 18, -1, None) == 2
+    assert "131072" in lib.w4_last_error().decode()
+    assert lib.w4a8_gemm(f, f, f, None, f, f, None, 0, 4, 64, 1 << 18, -1, None) == 2
+    assert lib.w8a8_gemm(None, None, None, None, None, None, 0, 0, 64, 256, -1, None) == 0
+    assert lib.w8a8_gemm(f, f, f, f, f, None, 0, 1, 256, 5120, -1, None) == 3  # narrow N splits K
 
 
 def test_workspace_sizes(lib):
@@ -120,5 +133,8 @@ def test_workspace_sizes(lib):
     assert lib.awq_gemm_workspace_bytes(16, 5120, 200, 128) == 0
     assert lib.awq_gemm_workspace_bytes(1, 256, 5120, -1) == lib.awq_gemm_workspace_bytes(1, 256, 5120, 128)
     assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 64) == 0
+    assert lib.w8a8_gemm_workspace_bytes(1, 256, 5120, -1) > 0
+    assert lib.w8a8_gemm_workspace_bytes(1, 256, 5120, 128) == 0
+    assert lib.w8a8_gemm_workspace_bytes(1, 256, 1 << 18, -1) == 0
     assert lib.w4a8_gemm_workspace_bytes(1, 256, 5120, -1) > 0  # narrow N splits K
     assert lib.w4a8_gemm_workspace_bytes(4096, 13824, 5120, 128) == 0

@@ -24,4 +24,10 @@ from ._lib import (  # noqa: F401
     w4a8_quant_act,
     w4a8_silu_mul_quant,
     w4_pack_codes,
+    w8a8_pack,
+    w8a8_qweight_shape,
+    w8a8_gemm,
+    w8a8_gemm_i32,
+    w8a8_gemm_workspace_bytes,
+    bind_w8a8_gemm,
 )

@@ -57,12 +57,15 @@ def load():
             "w4a8_gemm": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4a8_gemm_i32": [P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w4_pack_codes": [P, P, I64, I64, P],
+            "w8a8_pack": [P, P, P, I64, I64, I64, I32, P],
+            "w8a8_gemm": [P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
+            "w8a8_gemm_i32": [P, P, P, P, SZ, I64, I64, I64, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
-        for name in ("awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes"):
+        for name in ("awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w8a8_gemm_workspace_bytes"):
             fn = getattr(lib, name)
             fn.argtypes = [I64, I64, I64, I32]
             fn.restype = ctypes.c_size_t
@@ -402,5 +405,91 @@ def bind_w4a8_silu_mul_quant(gate_up, xq, s_a):
         rc = fn(*args)
         if rc != W4_OK:
             _check("w4a8_silu_mul_quant", rc)
+        return keep
+    return call
+
+
+# ------------------------------------------------------------------- W8A8
+def w8a8_qweight_shape(N: int, K: int):
+    """Shape of the tiled W8A8 weights: int8 [ceil(N/16), K/128, 4, 2, 16, 16]."""
+    return ((N + 15) // 16, K // 128, 4, 2, 16, 16)
+
+
+def w8a8_pack(w: torch.Tensor):
+    """fp16 W [N, K] -> (qweight int8 tiled [ceil(N/16), K/128, 4, 2, 16, 16], cscale fp16
+    [N]), per-channel."""
+    _need(w, "w", torch.float16, 2)
+    N, K = w.shape
+    dev = w.device
+    qweight = torch.empty(w8a8_qweight_shape(N, K), dtype=torch.int8, device=dev)
+    cscale = torch.empty((N,), dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        _check("w8a8_pack", load().w8a8_pack(_ptr(w), _ptr(qweight), _ptr(cscale), 0, N, K, -1, _stream(dev)))
+    return qweight, cscale
+
+
+def w8a8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().w8a8_gemm_workspace_bytes(M, N, K, -1))
+
+
+def _w8a8_args(xq, qweight, N):
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(qweight, "qweight", torch.int8, 6, dev)
+    M, K = xq.shape
+    if tuple(qweight.shape) != w8a8_qweight_shape(N, K):
+        raise ValueError(f"qweight shape {tuple(qweight.shape)} != {w8a8_qweight_shape(N, K)} for N={N}, K={K}")
+    return dev, M, N, K
+
+
+def w8a8_gemm(xq, s_a, qweight, cscale, out=None):
+    """Y [M, N] = fp16(acc * s_a[m] * cscale[n]), acc = xq . qweight^T exact in int32."""
+    _need(cscale, "cscale", torch.float16, 1)
+    dev, M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(cscale, "cscale", torch.float16, 1, dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    else:
+        _need(out, "out", torch.float16, 2, dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w8a8_gemm_workspace_bytes(M, N, K, -1))
+        _check("w8a8_gemm", lib.w8a8_gemm(_ptr(xq), _ptr(s_a), _ptr(qweight), _ptr(cscale), _ptr(out), _ptr(ws), nb,
+                                          M, N, K, -1, _stream(dev)))
+    return out
+
+
+def w8a8_gemm_i32(xq, qweight, N: int):
+    """The raw int32 accumulators [M, N] of w8a8_gemm."""
+    dev, M, N, K = _w8a8_args(xq, qweight, N)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w8a8_gemm_workspace_bytes(M, N, K, -1))
+        _check("w8a8_gemm_i32", lib.w8a8_gemm_i32(_ptr(xq), _ptr(qweight), _ptr(acc), _ptr(ws), nb, M, N, K, -1,
+                                                  _stream(dev)))
+    return acc
+
+
+def bind_w8a8_gemm(xq, s_a, qweight, cscale, out):
+    """As bind_awq_gemm, for w8a8_gemm."""
+    _need(cscale, "cscale", torch.float16, 1)
+    dev, M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
+    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(cscale, "cscale", torch.float16, 1, dev)
+    _need(out, "out", torch.float16, 2, dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        ws, nb = _workspace(dev, lib.w8a8_gemm_workspace_bytes(M, N, K, -1))
+        stream = _stream(dev)
+    args = (_ptr(xq), _ptr(s_a), _ptr(qweight), _ptr(cscale), _ptr(out), _ptr(ws), nb, M, N, K, -1, stream)
+    fn = lib.w8a8_gemm
+    keep = (xq, s_a, qweight, cscale, out, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w8a8_gemm", rc)
         return keep
     return call

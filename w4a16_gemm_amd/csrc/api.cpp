@@ -46,6 +46,16 @@ int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
   return W4_OK;
 }
 
+// int8 MFMA GEMMs accumulate in int32: |xq w| <= 127 * 128 per term (W4A8 per-channel
+// enters as 16 q), so K <= 2^17 keeps every sum below 2^31.
+constexpr int64_t kMaxKInt8 = int64_t(1) << 17;
+
+int check_k_int8(const char* fn, int64_t K) {
+  if (K > kMaxKInt8)
+    return fail(W4_ERR_UNSUPPORTED, "%s: K=%lld above 131072 (int32 accumulator range)", fn, (long long)K);
+  return W4_OK;
+}
+
 // W4A16 group sizes: 128, or -1 for per-channel (one group over K).
 int check_group_w4a16(const char* fn, int32_t group_size) {
   if (group_size != 128 && group_size != -1)
@@ -241,9 +251,65 @@ int w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int64_t M, 
   return launched(fn, w4::launch_w4a8_silu_mul_quant(gate_up, xq, s_a, (int)M, (int)K, (hipStream_t)stream));
 }
 
+int w8a8_pack(const void* w, int8_t* qweight, void* cscale, int64_t M, int64_t N, int64_t K, int32_t group_size,
+              void* stream) {
+  const char* fn = "w8a8_pack";
+  g_last_error.clear();
+  if (group_size != -1) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only -1, per-channel)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"w", w}, {"qweight", qweight}, {"cscale", cscale}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w8a8_pack(w, qweight, cscale, (int)N, (int)K, (hipStream_t)stream));
+}
+
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (group_size != -1 || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxKInt8)
+    return 0;
+  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, -1);
+}
+
+static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const int8_t* qweight,
+                       const void* cscale, void* y, int32_t* acc, void* workspace, size_t workspace_bytes, int64_t M,
+                       int64_t N, int64_t K, int32_t group_size, void* stream) {
+  g_last_error.clear();
+  if (group_size != -1) return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (only -1, per-channel)", fn, group_size);
+  W4_TRY(check_mnk(fn, M, N, K));
+  W4_TRY(check_k_int8(fn, K));
+  if (M == 0 || N == 0) return W4_OK;
+  if (acc) {
+    W4_TRY(check_ptrs(fn, {{"xq", xq}, {"qweight", qweight}, {"acc", acc}}));
+  } else {
+    W4_TRY(check_ptrs(fn, {{"xq", xq}, {"s_a", s_a}, {"qweight", qweight}, {"cscale", cscale}, {"y", y}}));
+  }
+  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, -1);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  }
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_w8a8_gemm(xq, s_a, qweight, cscale, y, acc, workspace, (int)M, (int)N, (int)K,
+                                           (hipStream_t)stream));
+}
+
+int w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
+              void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size,
+              void* stream) {
+  return w8a8_common("w8a8_gemm", xq, s_a, qweight, cscale, y, nullptr, workspace, workspace_bytes, M, N, K,
+                     group_size, stream);
+}
+
+int w8a8_gemm_i32(const int8_t* xq, const int8_t* qweight, int32_t* acc, void* workspace, size_t workspace_bytes,
+                  int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
+  return w8a8_common("w8a8_gemm_i32", xq, nullptr, qweight, nullptr, nullptr, acc, workspace, workspace_bytes, M, N,
+                     K, group_size, stream);
+}
+
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if ((group_size != 128 && group_size != -1) || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim ||
-      N > kMaxDim || K > kMaxDim)
+      N > kMaxDim || K > kMaxKInt8)
     return 0;
   return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, group_size);
 }
@@ -255,6 +321,7 @@ static int w4a8_common(const char* fn, const int8_t* xq, const float* s_a, const
   if (group_size != 128 && group_size != -1)
     return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1)", fn, group_size);
   W4_TRY(check_mnk(fn, M, N, K));
+  W4_TRY(check_k_int8(fn, K));
   if (M == 0 || N == 0) return W4_OK;
   if (acc) {
     W4_TRY(check_ptrs(fn, {{"xq", xq}, {"qweight", qweight}, {"acc", acc}}));

@@ -106,5 +106,16 @@ size_t w4a8_workspace_bytes(int M, int N, int K, int group_size);
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
                             const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
                             int group_size, hipStream_t stream);
+// Byte offset of the 16-byte chunk kc (k = 128 g + 16 kc .. + 15) of row n in the tiled
+// W8A8 weights int8 [ceil(N/16), K/128, 4, 2, 16, 16]: 2 KB per 16 rows x 128 k, chunk
+// (kc % 4, kc / 4) of the 16 rows stored together.
+__device__ __forceinline__ int64_t tiled8_offset(int n, int g, int kc, int ng) {
+  return (((int64_t)(n >> 4) * ng + g) * 4 + (kc & 3)) * 512 + (kc >> 2) * 256 + (n & 15) * 16;
+}
+
+// W8A8: tiled int8 weights with per-channel scales, on the W4A8 kernels.
+hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
+                            int32_t* acc_out, void* ws, int M, int N, int K, hipStream_t stream);
+hipError_t launch_w8a8_pack(const void* w, int8_t* qweight, void* cscale, int N, int K, hipStream_t stream);
 
 }  // namespace w4

@@ -16,6 +16,11 @@
 //  * w4a8_pack: symmetric int4 weights for the W4A8 GEMM, per-channel or two-level
 //    with int8 group scales ("[Feature] support qqq(w4a8) for lmdeploy", section
 //    "Benchmark": QQQ per-channel and QQQ-g128 variants).
+//  * w8a8_pack: per-channel symmetric int8 weights for W8A8 (the 8-bit-weight method
+//    mentioned on the vLLM AWQ page, and W8A8 as named on the compressed-tensors
+//    page; constants as the first level of the two-level W4A8 rule):
+//    s = fp16(max(max|w| / 127, 1e-5)), q = clamp(rint(w / s), -127, 127), stored in
+//    the tiled int8 layout (tiled8_offset); padding rows hold 0.
 //
 // Every quantization decision is made in fp32 with IEEE division and
 // round-half-to-even (rintf), and there is no a*b+c in these expressions, so the
@@ -284,6 +289,54 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
   hipLaunchKernelGGL(awq_unpack_dequant_kernel, dim3(blocks), dim3(256), 0, stream,
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros,
                      (half_t*)out, N, K, group_mask(group_size));
+  return hipGetLastError();
+}
+
+// One workgroup (256 threads) per row: amax over the row, then the codes, 8 per store
+// (half of a 16-byte chunk).  Workgroups past N (up to N rounded to 16) write the
+// padding rows' zeros.
+__global__ __launch_bounds__(256) void w8a8_pack_kernel(const half_t* __restrict__ w, int8_t* __restrict__ qweight,
+                                                         half_t* __restrict__ cscale, int N, int K) {
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  const int ng = K / 128;
+  const int nv = K / 8;
+  auto dst = [&](int j) {  // 8-byte half j & 1 of chunk j / 2 of row n
+    return reinterpret_cast<uint64_t*>(qweight + tiled8_offset(n, j >> 4, (j >> 1) & 7, ng) + (j & 1) * 8);
+  };
+  if (n >= N) {
+    for (int j = threadIdx.x; j < nv; j += 256) *dst(j) = 0;
+    return;
+  }
+  const half8_t* row = reinterpret_cast<const half8_t*>(w + (int64_t)n * K);
+  float amax = 0.0f;
+  for (int j = threadIdx.x; j < nv; j += 256) {
+    const half8_t v = row[j];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const half_t s16 = (half_t)fmaxf(amax / 127.0f, 1e-5f);
+  const float s = (float)s16;
+  if (threadIdx.x == 0) cscale[n] = s16;
+  for (int j = threadIdx.x; j < nv; j += 256) {
+    const half8_t v = row[j];
+    uint64_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = fminf(fmaxf(rintf((float)v[i] / s), -127.0f), 127.0f);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
+    }
+    *dst(j) = packed;
+  }
+}
+
+hipError_t launch_w8a8_pack(const void* w, int8_t* qweight, void* cscale, int N, int K, hipStream_t stream) {
+  hipLaunchKernelGGL(w8a8_pack_kernel, dim3((N + 15) / 16 * 16), dim3(256), 0, stream, (const half_t*)w, qweight,
+                     (half_t*)cscale, N, K);
   return hipGetLastError();
 }
 

@@ -287,18 +287,23 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
 // weights enter as q * s_g, expanded per group in registers (|q s_g| <= 126 fits int8),
 // so both variants accumulate the exact integer sum in one int32 accumulator set.
 constexpr int WBN = 256, WBK = 128;
+// Weight formats of the int8 MFMA kernels: int4 per-channel (entering as 16 q), int4
+// two-level (entering as q s_g), and plain row-major int8 [N, K] (W8A8).
+constexpr int kI4PerChannel = 0, kI4TwoLevel = 1, kI8 = 2;
 constexpr int kWThreads = 256;
 
 __device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 __device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { return cs ? cs[n] : (half_t)1; }
 
-template <int MI, bool TWO>
+template <int MI, int MODE>
 __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
     const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
     int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
     int K, int tiles_m, int tiles_n, int splits, int gps) {
   constexpr int BM = 32 * MI;
+  constexpr bool TWO = MODE == kI4TwoLevel;
+  constexpr int NB = MODE == kI8 ? 4 : 2;  // 16-byte weight chunks per lane, fragment and group
   __shared__ u32x4 lds[2][BM * 8];
 
   const int total = tiles_m * tiles_n * splits;
@@ -356,13 +361,22 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   int nclamp[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) nclamp[f] = min(nrow[f], N - 1);
-  u32x4 breg[2][2];
-  auto load_b = [&](int g, u32x4 (&dst)[2][2]) {
-    // words 8h .. 8h + 7 of the group = slots 2h and 2h + 1 of the tiled layout
+  u32x4 breg[2][NB];
+  auto load_b = [&](int g, u32x4 (&dst)[2][NB]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      dst[f][0] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h, ng));
-      dst[f][1] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h + 1, ng));
+      if (MODE == kI8) {
+        // tiled int8: chunks 4 h + c (k = 64 h + 16 c .. + 15) of this lane's row, one
+        // per k32-step c; each load of the wave is two contiguous 512-byte runs
+        const int8_t* w8 = reinterpret_cast<const int8_t*>(qweight);
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+          dst[f][c] = *reinterpret_cast<const u32x4*>(w8 + tiled8_offset(nclamp[f], g, 4 * h + c, ng));
+      } else {
+        // words 8h .. 8h + 7 of the group = slots 2h and 2h + 1 of the tiled layout
+        dst[f][0] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h, ng));
+        dst[f][1] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], g, 2 * h + 1, ng));
+      }
     }
   };
 
@@ -396,7 +410,7 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     }
     // next group's loads, unconditional (clamped on the last iteration; see the W4A16 GEMM)
     const int gn = min(g + 1, gend - 1);
-    u32x4 bnext[2][2];
+    u32x4 bnext[2][NB];
     load_a(gn);
     load_b(gn, bnext);
     load_sg(gn, sgraw);
@@ -406,6 +420,11 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
       int4_t bf[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
+        if (MODE == kI8) {
+          const u32x4 v = breg[f][s];
+          bf[f] = int4_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+          continue;
+        }
         const uint32_t w0 = breg[f][s >> 1][(s & 1) * 2];
         const uint32_t w1 = breg[f][s >> 1][(s & 1) * 2 + 1];
         uint32_t a0, a1, a2, a3;
@@ -428,13 +447,12 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     }
     store_a(buf ^ 1);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      breg[f][0] = bnext[f][0];
-      breg[f][1] = bnext[f][1];
-    }
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) breg[f][c] = bnext[f][c];
     __syncthreads();
   }
-  if (!TWO) {
+  if (MODE == kI4PerChannel) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -501,24 +519,34 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
 // of the chunk (16 k) expanded to int8 (16 q per-channel, q s_g two-level).  The int32
 // accumulators need no per-group work: the sum is exact, so the cross-wave (LDS) and
 // split-K reductions are exact in any order.
-template <int T, bool TWO>
+template <int T, int MODE>
 struct W8Regs {
-  u32x4 b[T];      // code chunk of this lane's row in each n-tile
-  int4_t a[2];     // xq: k = 32 slot + 16 j .. + 15, j = 0, 1
-  int32_t gsv[T];  // group scale of this lane's row in each n-tile (two-level)
+  u32x4 b[T][MODE == kI8 ? 2 : 1];  // codes of this lane's row and k-slot in each n-tile
+  int4_t a[2];                      // xq: k = 32 slot + 16 j .. + 15, j = 0, 1
+  int32_t gsv[T];                   // group scale of this lane's row in each n-tile (two-level)
 };
 
-template <int T, bool TWO>
-__device__ __forceinline__ void w8_load(W8Regs<T, TWO>& r, const int8_t* __restrict__ xq,
+template <int T, int MODE>
+__device__ __forceinline__ void w8_load(W8Regs<T, MODE>& r, const int8_t* __restrict__ xq,
                                         const uint32_t* __restrict__ qweight, const int8_t* __restrict__ gscale,
                                         int g, int n0, int lane, int M, int N, int K) {
   const int ng = K / 128;
   const int last_tile = (N - 1) >> 4;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int tile = min((n0 >> 4) + t, last_tile);
-    r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
-    if (TWO) r.gsv[t] = gscale[(int64_t)g * N + min(n0 + 16 * t + (lane & 15), N - 1)];
+    if (MODE == kI8) {
+      // tiled int8 weights: chunks 2 slot and 2 slot + 1 (k = 32 slot .. + 31) of this
+      // lane's row; each load of the wave is two contiguous 512-byte runs
+      const int8_t* w8 = reinterpret_cast<const int8_t*>(qweight);
+      const int nc = min(n0 + 16 * t + (lane & 15), 16 * last_tile + 15);
+      const int slot = lane >> 4;
+      r.b[t][0] = *reinterpret_cast<const u32x4*>(w8 + tiled8_offset(nc, g, 2 * slot, ng));
+      r.b[t][1] = *reinterpret_cast<const u32x4*>(w8 + tiled8_offset(nc, g, 2 * slot + 1, ng));
+    } else {
+      const int tile = min((n0 >> 4) + t, last_tile);
+      r.b[t][0] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+    }
+    if (MODE == kI4TwoLevel) r.gsv[t] = gscale[(int64_t)g * N + min(n0 + 16 * t + (lane & 15), N - 1)];
   }
   const int m = min(lane & 15, M - 1);
   const int4_t* src = reinterpret_cast<const int4_t*>(xq + (int64_t)m * K + g * 128 + (lane >> 4) * 32);
@@ -526,10 +554,19 @@ __device__ __forceinline__ void w8_load(W8Regs<T, TWO>& r, const int8_t* __restr
   r.a[1] = src[1];
 }
 
-template <int T, bool TWO>
-__device__ __forceinline__ void w8_compute(const W8Regs<T, TWO>& r, int4_t (&acc)[T]) {
+template <int T, int MODE>
+__device__ __forceinline__ void w8_compute(const W8Regs<T, MODE>& r, int4_t (&acc)[T]) {
+  constexpr bool TWO = MODE == kI4TwoLevel;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
+    if (MODE == kI8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 v = r.b[t][j];
+        acc[t] = mfma16_i8(r.a[j], int4_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3]}, acc[t]);
+      }
+      continue;
+    }
     u16x2 sp = {1, 1}, cp = {0, 0};
     if (TWO) {
       const unsigned short g16 = (unsigned short)r.gsv[t];
@@ -540,7 +577,7 @@ __device__ __forceinline__ void w8_compute(const W8Regs<T, TWO>& r, int4_t (&acc
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t e[4];
-      const uint32_t w0 = r.b[t][2 * j], w1 = r.b[t][2 * j + 1];
+      const uint32_t w0 = r.b[t][0][2 * j], w1 = r.b[t][0][2 * j + 1];
       if (TWO) {
         unpack_i4_scaled(w0, sp, cp, e[0], e[1]);
         unpack_i4_scaled(w1, sp, cp, e[2], e[3]);
@@ -554,7 +591,7 @@ __device__ __forceinline__ void w8_compute(const W8Regs<T, TWO>& r, int4_t (&acc
   }
 }
 
-template <int T, int D, bool TWO>
+template <int T, int D, int MODE>
 __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
     const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
@@ -572,24 +609,24 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
   int4_t acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = int4_t{0, 0, 0, 0};
-  W8Regs<T, TWO> r[D];
+  W8Regs<T, MODE> r[D];
   const int glast = gend - 1;
   const int g = gbeg + wave;
 #pragma unroll
-  for (int d = 0; d < D; ++d) w8_load<T, TWO>(r[d], xq, qweight, gscale, min(g + d * WAVES, glast), n0, lane, M, N, K);
+  for (int d = 0; d < D; ++d) w8_load<T, MODE>(r[d], xq, qweight, gscale, min(g + d * WAVES, glast), n0, lane, M, N, K);
   // steady state without conditions, then the remaining < D groups (wave-uniform counts)
   const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
   int it = 0;
   for (; it + D <= mine; it += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      w8_compute<T, TWO>(r[d], acc);
-      w8_load<T, TWO>(r[d], xq, qweight, gscale, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
+      w8_compute<T, MODE>(r[d], acc);
+      w8_load<T, MODE>(r[d], xq, qweight, gscale, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
     }
   }
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (it + d < mine) w8_compute<T, TWO>(r[d], acc);
+    if (it + d < mine) w8_compute<T, MODE>(r[d], acc);
 
   // Cross-wave reduction: element (t, i) of lane l is row 4 (l / 16) + i, column
   // n0 + 16 t + l % 16.
@@ -607,7 +644,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
     for (int w = 0; w < WAVES; ++w) v += red[w][idx];
     if (n >= N) continue;
     if (splits == 1) {
-      if (!TWO) v >>= 4;  // exact: every term was 16 q
+      if (MODE == kI4PerChannel) v >>= 4;  // exact: every term was 16 q
       if (acc_out) acc_out[(int64_t)m * N + n] = v;
       else y[(int64_t)m * N + n] = (half_t)(((float)v * s_a[m]) * (float)cscale[n]);
     } else {
@@ -621,7 +658,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
     if (n >= N) continue;
     int32_t v = 0;
     for (int sp_ = 0; sp_ < splits; ++sp_) v += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + n);
-    if (!TWO) v >>= 4;
+    if (MODE == kI4PerChannel) v >>= 4;
     if (acc_out) acc_out[(int64_t)m * N + n] = v;
     else y[(int64_t)m * N + n] = (half_t)(((float)v * s_a[m]) * (float)cscale[n]);
   }
@@ -685,9 +722,11 @@ size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(int32_t);
 }
 
-hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
-                            const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
-                            int group_size, hipStream_t stream) {
+namespace {
+
+hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const void* qweight,
+                            const int8_t* gscale, const void* cscale, void* y, int32_t* acc_out, void* ws, int M,
+                            int N, int K, int group_size, hipStream_t stream) {
   const W4A8Plan p = w4a8_plan(M, N, K, group_size);
   unsigned* counters = (unsigned*)ws;
   int32_t* partials = ws ? (int32_t*)((char*)ws + kCounterRegionBytes) : nullptr;
@@ -696,39 +735,51 @@ hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* q
   const uint32_t* qw = (const uint32_t*)qweight;
   const half_t* cs = (const half_t*)cscale;
   half_t* yh = (half_t*)y;
-  const int8_t* gs = group_size == -1 ? nullptr : gscale;
+  const int8_t* gs = mode == kI4TwoLevel ? gscale : nullptr;
   if (p.skinny) {
     const dim3 sgrid(p.tiles_n, p.splits), sblock(256);
-#define W4A8_SKINNY(T, D, TWO)                                                                                  \
-  hipLaunchKernelGGL((w4a8_skinny_kernel<T, D, TWO>), sgrid, sblock, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out, \
+#define W4A8_SKINNY(T, D, MODE)                                                                                  \
+  hipLaunchKernelGGL((w4a8_skinny_kernel<T, D, MODE>), sgrid, sblock, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out, \
                      counters, partials, M, N, K, p.splits, p.kt_per_split)
-    if (gs) {
-      if (p.tiles == 4) W4A8_SKINNY(4, 2, true);
-      else if (p.tiles == 2) W4A8_SKINNY(2, 2, true);
-      else W4A8_SKINNY(1, 4, true);
-    } else {
-      if (p.tiles == 4) W4A8_SKINNY(4, 2, false);
-      else if (p.tiles == 2) W4A8_SKINNY(2, 2, false);
-      else W4A8_SKINNY(1, 4, false);
-    }
+#define W4A8_SKINNY_T(MODE)                      \
+  if (p.tiles == 4) W4A8_SKINNY(4, 2, MODE);     \
+  else if (p.tiles == 2) W4A8_SKINNY(2, 2, MODE); \
+  else W4A8_SKINNY(1, 4, MODE)
+    if (mode == kI4TwoLevel) { W4A8_SKINNY_T(kI4TwoLevel); }
+    else if (mode == kI8) { W4A8_SKINNY_T(kI8); }
+    else { W4A8_SKINNY_T(kI4PerChannel); }
+#undef W4A8_SKINNY_T
 #undef W4A8_SKINNY
     return hipGetLastError();
   }
-#define W4A8_LAUNCH(MI, TWO)                                                                                  \
-  hipLaunchKernelGGL((w4a8_gemm_kernel<MI, TWO>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
+#define W4A8_LAUNCH(MI, MODE)                                                                                  \
+  hipLaunchKernelGGL((w4a8_gemm_kernel<MI, MODE>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
                      counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
+#define W4A8_LAUNCH_MI(MODE)                   \
+  if (mi == 1) W4A8_LAUNCH(1, MODE);           \
+  else if (mi == 2) W4A8_LAUNCH(2, MODE);      \
+  else W4A8_LAUNCH(4, MODE)
   const int mi = p.bm / 32;
-  if (gs) {
-    if (mi == 1) W4A8_LAUNCH(1, true);
-    else if (mi == 2) W4A8_LAUNCH(2, true);
-    else W4A8_LAUNCH(4, true);
-  } else {
-    if (mi == 1) W4A8_LAUNCH(1, false);
-    else if (mi == 2) W4A8_LAUNCH(2, false);
-    else W4A8_LAUNCH(4, false);
-  }
+  if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); }
+  else if (mode == kI8) { W4A8_LAUNCH_MI(kI8); }
+  else { W4A8_LAUNCH_MI(kI4PerChannel); }
+#undef W4A8_LAUNCH_MI
 #undef W4A8_LAUNCH
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
+                            const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
+                            int group_size, hipStream_t stream) {
+  return launch_int8_gemm(group_size == -1 ? kI4PerChannel : kI4TwoLevel, xq, s_a, qweight, gscale, cscale, y,
+                          acc_out, ws, M, N, K, group_size, stream);
+}
+
+hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
+                            int32_t* acc_out, void* ws, int M, int N, int K, hipStream_t stream) {
+  return launch_int8_gemm(kI8, xq, s_a, qweight, nullptr, cscale, y, acc_out, ws, M, N, K, -1, stream);
 }
 
 }  // namespace w4
