@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--detail-iters", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w4a8", "copy"],
-                    help="decode (default, the reported metric); prefill / w4a8 / copy run one kernel family "
+                    help="decode (default, the reported metric); prefill / w4a8 (the int8 path) / copy run one kernel family "
                          "alone (for profiling); copy is a plain device copy of known size that calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
@@ -247,7 +247,7 @@ def single_workload(args, dev, torch, np, synth, w4):
             y = torch.empty((4096, N), dtype=torch.float16, device=dev)
             calls.append(w4.bind_awq_gemm(x, qw, sc, qz, y))
         res["flops_per_round"] = sum(2.0 * 4096 * N * K for (K, N) in ((5120, 27648), (5120, 5120), (13824, 5120)))
-    else:  # w4a8 at M = 4096, both weight variants
+    else:  # the int8 path at M = 4096: quant_act, W4A8 (both weight variants), W8A8, silu_mul_quant
         inp = synth.make_linear(4096, 13824, 5120, seed=0, outliers=True, rms_spread=True, with_gamma=True)
         x = inp.x.to(dev)
         g = inp.gamma.to(dev)
@@ -258,6 +258,13 @@ def single_workload(args, dev, torch, np, synth, w4):
             qw, gs, cs = w4.w4a8_pack(inp.w.to(dev), group)
             y = torch.empty((4096, 13824), dtype=torch.float16, device=dev)
             calls.append(w4.bind_w4a8_gemm(xq, sa, qw, gs, cs, y, group))
+        qw8, cs8 = w4.w8a8_pack(inp.w.to(dev))
+        y8 = torch.empty((4096, 13824), dtype=torch.float16, device=dev)
+        calls.append(w4.bind_w8a8_gemm(xq, sa, qw8, cs8, y8))
+        gu = synth.make_activations(4096, 2 * 13824, seed=5, rms_spread=True).to(dev)
+        xq2 = torch.empty((4096, 13824), dtype=torch.int8, device=dev)
+        sa2 = torch.empty((4096,), dtype=torch.float32, device=dev)
+        calls.append(w4.bind_w4a8_silu_mul_quant(gu, xq2, sa2))
     for _ in range(args.warmup):
         for c in calls:
             c()
@@ -352,10 +359,15 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
             sa = torch.empty((M,), dtype=torch.float32, device=dev)
             qa = w4.bind_w4a8_quant_act(x, inp.gamma.to(dev), xq, sa)
             qa()
+            # the quantizer timed over 8 rotated copies of X (336 MB at M = 4096: beyond
+            # the 256 MB last-level cache, so the M = 4096 figure is HBM-bound)
+            xs_rot = [torch.roll(x, r, 0).contiguous() for r in range(8)]
+            qas = [w4.bind_w4a8_quant_act(xr, inp.gamma.to(dev), xq, sa) for xr in xs_rot]
             y = torch.empty((M, 13824), dtype=torch.float16, device=dev)
             calls = [w4.bind_w4a8_gemm(xq, sa, c[0], c[1], c[2], y, group) for c in copies]
             t = _time_calls(torch, calls, max(it, 16) if M < 4096 else max(4, it // 2))
-            tq = _time_calls(torch, [qa], 8)
+            tq = _time_calls(torch, qas, 16)
+            del xs_rot, qas
             b = w4a8_bytes(M, 13824, 5120, group > 0)
             ops = 2.0 * M * 13824 * 5120
             w8[f"{'g128' if group > 0 else 'pc'}_M{M}"] = {
@@ -386,7 +398,7 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
     smq = {}
     I = 13824
     for M in (1, 16, 256, 4096):
-        nbuf = 4 if M < 4096 else 1
+        nbuf = 4 if M < 4096 else 2  # 2 x 226 MB at M = 4096: beyond the last-level cache
         gus = [synth.make_activations(M, 2 * I, seed=M + r, rms_spread=True).to(dev) for r in range(nbuf)]
         xq = torch.empty((M, I), dtype=torch.int8, device=dev)
         sa = torch.empty((M,), dtype=torch.float32, device=dev)
