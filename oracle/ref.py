@@ -60,6 +60,9 @@ Readings where the pages are silent:
   name per-channel quantization, group_size = -1, beside g128): group_size -1
   means one group spanning all of K; the R1 rule then applies per row; scales
   are fp16 [1, N] and zero points int32 [1, ceil(N/8)].
+* R16 group sizes 64 and 32 ([AWQ-vLLM], the Triton format comment sizes scales
+  as (K // group_size, N): the group size is a parameter): the R1 / R14 rules apply
+  per group of any G dividing K; the GPU library takes G in {32, 64, 128, -1}.
 * R14 W4A16 symmetric ([AWQ-fixes], reply on preset schemes: a W4A16_ASYM preset
   beside W4A16, which is therefore the symmetric one): per (row, group)
   ``s = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s), -8, 7)`` (the R5

@@ -91,7 +91,8 @@ def read_silu_cases():
 
 def read_variant_cases():
     """Cases of golden/w4a16_variants_worked.txt: ``rule``, ``group``, ``values`` (fp16),
-    ``scales`` (fp16 per group), ``zeros`` and ``codes_head`` (per group: leading codes)."""
+    ``scales`` (fp16 per group), ``zeros`` and ``codes_head`` (per 128-k block: leading
+    codes) or ``codes_at`` (k -> code)."""
     cases, cur = [], None
     for line in open(os.path.join(GOLDEN, "w4a16_variants_worked.txt")):
         line = line.strip()
@@ -111,4 +112,6 @@ def read_variant_cases():
             cur["zeros"] = [int(v) for v in rest]
         elif key == "codes_head":
             cur["codes_head"] = [[int(v) for v in part.split()] for part in " ".join(rest).split("|")]
+        elif key == "codes_at":
+            cur["codes_at"] = {int(k): int(v) for k, v in (t.split("=") for t in rest)}
     return cases

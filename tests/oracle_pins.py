@@ -372,8 +372,10 @@ def pin_variants_worked(ora):
         codes, sc, z = quant(case["values"][None, :], case["group"])
         assert sc[0].view(np.uint16).tolist() == case["scales"].view(np.uint16).tolist(), case["name"]
         assert z[0].tolist() == case["zeros"], case["name"]
-        for b, head in enumerate(case["codes_head"]):
+        for b, head in enumerate(case.get("codes_head", [])):
             assert codes[0, 128 * b:128 * b + len(head)].tolist() == head, (case["name"], b)
+        for k, c in case.get("codes_at", {}).items():
+            assert int(codes[0, k]) == c, (case["name"], k)
 
 
 def pin_sym_properties(ora):
