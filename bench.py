@@ -414,7 +414,7 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
     var = {}
     for (K, N) in ((5120, 27648), (5120, 5120)):
         w = synth.make_linear(0, N, K, seed=0, outliers=True).w.to(dev)
-        for group, sym in ((128, False), (-1, False), (128, True), (-1, True)):
+        for group, sym in ((128, False), (-1, False), (128, True), (-1, True), (64, False), (32, False)):
             pack = w4.awq_pack_sym if sym else w4.awq_pack
             qw, sc, qz = pack(w, group)
             copies = [rotated_awq(qw, sc, qz, r) for r in range(4)]
@@ -423,8 +423,9 @@ def detail(args, dev, torch, np, synth, w4, host, packed):
                 y = torch.empty((M, N), dtype=torch.float16, device=dev)
                 calls = [w4.bind_awq_gemm(x, *c, y, group) for c in copies]
                 t = _time_calls(torch, calls, max(it, 16) if M < 4096 else max(4, it // 2))
-                b = awq_bytes(M, N, K) if group > 0 else awq_bytes(M, N, K) - (2 * N * K // 128 + N * K // 256) + 2 * N + N // 2
-                key = f"{'pc' if group < 0 else 'g128'}_{'sym' if sym else 'asym'}_{K}x{N}_M{M}"
+                ngr = 1 if group < 0 else K // group
+                b = N * K / 2 + 2.5 * N * ngr + 2 * M * K + 2 * M * N
+                key = f"{'pc' if group < 0 else f'g{group}'}_{'sym' if sym else 'asym'}_{K}x{N}_M{M}"
                 var[key] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
                             "TFLOPs": round(2.0 * M * N * K / t / 1e12, 1)}
             del copies, qw, sc, qz

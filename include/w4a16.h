@@ -46,7 +46,9 @@
  *            x 128 k; padding rows 0), cscale fp16 [N].
  *
  * Sizes: M >= 0, N >= 0 (M == 0 or N == 0 is a no-op returning W4_OK), K a positive
- * multiple of 128.  group_size: 128 or -1 (per-channel), for W4A16 and W4A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
+ * multiple of 128.  group_size: 128, 64, 32 or -1 (per-channel) for W4A16 (the group
+ * size is a parameter of the Triton AWQ format on the vLLM page: scales (K // group_size,
+ * N)); 128 or -1 for W4A8; -1 for W8A8.  Every pointer must be 16-byte aligned and non-NULL unless stated otherwise.
  *
  * `stream` is a hipStream_t (NULL = the null stream).  All entry points are
  * asynchronous: they return after validation and launch; a fault inside a kernel
@@ -116,8 +118,9 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
  * fp16 output (round to nearest even).  Dispatch: M <= 64 uses a bandwidth-bound skinny
  * kernel (16x16x32 fp16 MFMA on exact fp16 encodings of the codes, per-group scaling in
  * fp32; for M <= 4 with X staged in LDS); larger M uses the LDS-staged 32x32x16 fp16
- * MFMA GEMM with in-register dequantization.  Results are deterministic (split-K
- * partials are summed in a fixed order).
+ * MFMA GEMM with in-register dequantization.  Group sizes 64 and 32 take the MFMA GEMM
+ * at every M (the skinny kernels apply one scale per 128 k).  Results are deterministic
+ * (split-K partials are summed in a fixed order).
  */
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
              void* y, void* workspace, size_t workspace_bytes,

@@ -53,7 +53,7 @@ FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 200, 128, None), 1, "multiple of 128"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 0, 128, None), 1, "multiple of 128"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, -1, 64, 256, 128, None), 1, "negative"),
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 64, None), 2, "group_size"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 16, None), 2, "group_size"),
     ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 256, 128, None), 1, "aligned"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, 1 << 31, 128, None), 2, "2^30"),
     # a narrow-N shape splits K and needs a workspace (per-channel alike)
@@ -105,8 +105,8 @@ def test_w4a8_validation(lib):
     assert "xq is NULL" in lib.w4_last_error().decode()
     assert lib.w4a8_silu_mul_quant(f, f, f, 4, 0, 1 << 30, 0, None) == 2
     assert lib.w4a8_pack(f, f, None, f, 0, 64, 256, 128, None) == 1
-    assert lib.awq_pack(f, f, f, f, 0, 64, 256, 32, None) == 2
-    assert lib.awq_pack_sym(f, f, f, f, 0, 64, 256, 64, None) == 2
+    assert lib.awq_pack(f, f, f, f, 0, 64, 256, 16, None) == 2
+    assert lib.awq_pack_sym(f, f, f, f, 0, 64, 256, 16, None) == 2
     assert "group_size" in lib.w4_last_error().decode()
     assert lib.awq_pack_sym(f, None, f, f, 0, 64, 256, -1, None) == 1
     assert "qweight is NULL" in lib.w4_last_error().decode()
@@ -132,7 +132,9 @@ def test_workspace_sizes(lib):
     assert lib.awq_gemm_workspace_bytes(4096, 27648, 5120, 128) == 0
     assert lib.awq_gemm_workspace_bytes(16, 5120, 200, 128) == 0
     assert lib.awq_gemm_workspace_bytes(1, 256, 5120, -1) == lib.awq_gemm_workspace_bytes(1, 256, 5120, 128)
-    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 64) == 0
+    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 16) == 0
+    # group sizes 64 and 32 take the MFMA GEMM at every M (its own split-K plan)
+    assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 64) == lib.awq_gemm_workspace_bytes(1, 256, 5120, 32) > 0
     assert lib.w8a8_gemm_workspace_bytes(1, 256, 5120, -1) > 0
     assert lib.w8a8_gemm_workspace_bytes(1, 256, 5120, 128) == 0
     assert lib.w8a8_gemm_workspace_bytes(1, 256, 1 << 18, -1) == 0

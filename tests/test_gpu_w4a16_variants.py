@@ -1,5 +1,5 @@
-"""GPU parity of the W4A16 variants: per-channel weights (group_size -1) and the
-symmetric rule (awq_pack_sym), against the oracle.
+"""GPU parity of the W4A16 variants: per-channel weights (group_size -1), group sizes
+64 and 32, and the symmetric rule (awq_pack_sym), against the oracle.
 
 * awq_pack / awq_pack_sym: bit-exact packed tensors, small ragged shapes, every
   combination of rule and group size, and the hand-worked rows of
@@ -22,8 +22,8 @@ from gpu_util import TOL, announce, device, normalized_error, sample_idx, to_np
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [(-1, False), (128, True), (-1, True)]
-VID = ["pc-asym", "g128-sym", "pc-sym"]
+VARIANTS = [(-1, False), (128, True), (-1, True), (64, False), (32, False), (64, True), (32, True)]
+VID = ["pc-asym", "g128-sym", "pc-sym", "g64-asym", "g32-asym", "g64-sym", "g32-sym"]
 
 
 def _pack_gpu(w, group, sym):
@@ -63,8 +63,10 @@ def test_pack_golden_rows():
         codes, scales, zeros = ora.unpack_awq(to_np(qw), to_np(sc), to_np(qz), w.shape[1])
         assert scales[0].view(np.uint16).tolist() == c["scales"].view(np.uint16).tolist(), c["name"]
         assert zeros[0].tolist() == c["zeros"], c["name"]
-        for b, head in enumerate(c["codes_head"]):
+        for b, head in enumerate(c.get("codes_head", [])):
             assert codes[2, 128 * b:128 * b + len(head)].tolist() == head, (c["name"], b)
+        for k, code in c.get("codes_at", {}).items():
+            assert int(codes[2, k]) == code, (c["name"], k)
 
 
 # shapes for each kernel family: register-X skinny (M <= 64, N and K <= 8192 at M <= 4),
@@ -124,3 +126,21 @@ def test_full_size_end_to_end_sampled(group, sym, M, N, K):
     err = normalized_error(yg, ref["y"], np.linalg.norm(x.numpy()[ms].astype(np.float64), axis=1),
                            np.linalg.norm(ref["w_deq"], axis=1))
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("group", [32, 64, -1])
+def test_identity_probe_bit_exact(group):
+    """X rows are unit vectors e_k (k on both sides of group boundaries): Y[m, n] is the
+    fp16 dequantized weight bit for bit, so every lane reads the scale and zero point of
+    its own group."""
+    dev = device()
+    N, K, M = 320, 1024, 96
+    announce(f"identity probe group={group}")
+    w = synth.make_linear(0, N, K, seed=19, outliers=True).w.numpy()
+    ref, (qw, sc, qz) = _oracle_packed(w, group, False, dev)
+    ks = sample_idx(K, M, seed=group + 5, must=(0, 31, 32, 63, 64, 95, 96, 127, 128, 1023))[:M]
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(len(ks)), ks] = 1
+    y = to_np(w4.awq_gemm(torch.from_numpy(x).to(dev), qw, sc, qz, group_size=group))
+    expect = ref["w_deq"][:, ks].T.astype(np.float16)
+    assert np.array_equal(y[:len(ks)].view(np.uint16), expect.view(np.uint16))

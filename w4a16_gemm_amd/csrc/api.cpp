@@ -56,12 +56,20 @@ int check_k_int8(const char* fn, int64_t K) {
   return W4_OK;
 }
 
-// W4A16 group sizes: 128, or -1 for per-channel (one group over K).
+// W4A16 group sizes: 128, 64, 32, or -1 for per-channel (one group over K).
+bool group_ok_w4a16(int32_t group_size) {
+  return group_size == 128 || group_size == 64 || group_size == 32 || group_size == -1;
+}
+
 int check_group_w4a16(const char* fn, int32_t group_size) {
-  if (group_size != 128 && group_size != -1)
-    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1 are implemented)", fn, group_size);
+  if (!group_ok_w4a16(group_size))
+    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128, 64, 32 or -1 are implemented)", fn, group_size);
   return W4_OK;
 }
+
+// The skinny kernels apply one scale per 128-k unit (group sizes 128 and -1); smaller
+// groups take the MFMA GEMM at every M.
+bool use_skinny(int64_t M, int32_t group_size) { return M <= 64 && (group_size == 128 || group_size == -1); }
 
 int check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
   for (auto& p : ptrs) {
@@ -98,9 +106,10 @@ int launched(const char* fn, hipError_t e) {
   return W4_OK;
 }
 
-size_t awq_ws(int64_t M, int64_t N, int64_t K) {
+size_t awq_ws(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M <= 0 || N <= 0) return 0;
-  return M <= 64 ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K) : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
+  return use_skinny(M, group_size) ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K)
+                                   : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
 }
 
 #define W4_TRY(expr)          \
@@ -172,10 +181,10 @@ int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void
 }
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
-  if ((group_size != 128 && group_size != -1) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
+  if (!group_ok_w4a16(group_size) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
       K > kMaxDim)
     return 0;
-  return awq_ws(M, N, K);
+  return awq_ws(M, N, K, group_size);
 }
 
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros, void* y,
@@ -187,7 +196,7 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   W4_TRY(check_mnk(fn, M, N, K));
   if (M == 0 || N == 0) return W4_OK;
   W4_TRY(check_ptrs(fn, {{"x", x}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"y", y}}));
-  const size_t need = awq_ws(M, N, K);
+  const size_t need = awq_ws(M, N, K, group_size);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -196,7 +205,7 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   }
   W4_TRY(check_device(fn));
   hipError_t e;
-  if (M <= 64)
+  if (use_skinny(M, group_size))
     e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
                           (hipStream_t)stream);
   else

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
                                                             half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                             float* __restrict__ partials, int M, int N, int K,
                                                             int tiles_m, int tiles_n, int splits, int kps,
-                                                            int gmask) {
+                                                            int glog) {
   constexpr int BM = 32 * MI, BN = 128 * NF;
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
   __shared__ u32x4 lds[2][BM * 8];
@@ -138,11 +138,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   // fp16 pairs -(1024 + z) and s used by dequant8.
   uint32_t zraw[NF];
   half_t sraw[NF];
-  auto load_sz = [&](int g) {
+  auto load_sz = [&](int kt) {
+    // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
+    const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      zraw[f] = qzeros[(int64_t)(g & gmask) * nzw + (nclamp[f] >> 3)];
-      sraw[f] = scales[(int64_t)(g & gmask) * N + nclamp[f]];
+      zraw[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
+      sraw[f] = scales[row * N + nclamp[f]];
     }
   };
   half2_t c1024[NF], c64[NF], s2[NF];
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   if (kbeg < kend) {
     load_a(kbeg);
     load_b(kbeg, breg);
-    load_sz(kbeg >> 1);  // 2 BK steps per 128-group
+    load_sz(kbeg);
     store_a(0);
     set_sz();
   }
@@ -172,11 +174,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   for (int kt = kbeg; kt < kend; ++kt) {
     const int buf = (kt - kbeg) & 1;
     const int kn = min(kt + 1, kend - 1);
-    const bool new_group = ((kt + 1) & 1) == 0;
+    const bool new_group = glog < 7 || ((kt + 1) & 1) == 0;  // G = 128: 2 BK steps per group
     u32x4 bnext[NF];
     load_a(kn);
     load_b(kn, bnext);
-    load_sz(kn >> 1);
+    load_sz(kn);
     // keep these loads here, ahead of the MFMAs (the scheduler would otherwise sink them
     // next to their use at the end of the step and expose the full memory latency)
     __builtin_amdgcn_sched_barrier(0);
@@ -314,14 +316,14 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
 hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
                        void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
   const GemmPlan p = gemm_plan(M, N, K);
-  const int gmask = group_mask(group_size);
+  const int glog = group_log2(group_size);
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int blocks = p.tiles_m * p.tiles_n * p.splits;
 #define GEMM_LAUNCH(MI, NF)                                                                                   \
   hipLaunchKernelGGL((gemm_kernel<MI, NF>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,          \
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, gmask)
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, glog)
   if (p.mi == 4 && p.nf == 2) GEMM_LAUNCH(4, 2);
   else if (p.mi == 4) GEMM_LAUNCH(4, 1);
   else if (p.nf == 2) GEMM_LAUNCH(2, 2);

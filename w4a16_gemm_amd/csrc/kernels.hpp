@@ -77,9 +77,14 @@ struct W4A8Plan {
 };
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 
-// W4A16 scales and zero points are read at group row (g & group_mask): per-channel
-// weights (group_size -1) keep a single row, read for every 128-group.
+// W4A16 scales and zero points.  The skinny kernels (group_size 128 or -1) read them at
+// group row (g & group_mask) for 128-k unit g: per-channel weights keep a single row.
+// The GEMM, the pack and the unpack kernels read the row of element k as
+// k >> group_log2 (30 for per-channel: every k < 2^30 maps to row 0).
 inline int group_mask(int group_size) { return group_size == -1 ? 0 : -1; }
+inline int group_log2(int group_size) {
+  return group_size == 32 ? 5 : group_size == 64 ? 6 : group_size == 128 ? 7 : 30;
+}
 
 hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_t* qzeros, int N, int K,
                            int group_size, bool symmetric, hipStream_t stream);

@@ -84,22 +84,28 @@ __global__ __launch_bounds__(256) void awq_rowstats_kernel(const half_t* __restr
   }
 }
 
-// One thread per (group g, row n), n fastest, over npad = N rounded up to 16 rows:
+// One thread per (128-k unit g, row n), n fastest, over npad = N rounded up to 16 rows:
 // the 8 threads of a zero-point word are 8 consecutive lanes, and padding rows
-// (n >= N) write code 0 so that the whole tiled array is defined.  Per-channel
-// (perchan = 1): scale and zero point come from awq_rowstats and are not rewritten.
+// (n >= N) write code 0 so that the whole tiled array is defined.  The unit holds SUB
+// groups of 128 / SUB k (group sizes 128, 64, 32).  Per-channel (perchan = 1, SUB = 1):
+// scale and zero point come from awq_rowstats and are not rewritten.
+template <int SUB>
 __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict__ w,
                                                         uint32_t* __restrict__ qweight,
                                                         half_t* __restrict__ scales,
                                                         int32_t* __restrict__ qzeros,
                                                         int N, int K, int npad, int perchan, int sym) {
+  constexpr int GS = 128 / SUB;
   const int ng = K / 128;
+  const int nzw = (N + 7) / 8;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = tid < (int64_t)npad * ng;
   const int g = live ? (int)(tid / npad) : 0;
   const int n = live ? (int)(tid % npad) : 0;
   const bool valid = live && n < N;
-  uint32_t zbits = 0;
+  uint32_t zbits[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) zbits[u] = 0;
   u32x4 out[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   if (valid) {
     const u32x4* src = reinterpret_cast<const u32x4*>(w + (int64_t)n * K + (int64_t)g * 128);
@@ -107,45 +113,56 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) raw[i] = src[i];
     const half_t* h = reinterpret_cast<const half_t*>(raw);
-    half_t s16;
-    float z;
+    half_t s16[SUB];
+    float z[SUB];
     if (perchan) {
-      s16 = scales[n];
-      z = (float)((((uint32_t)qzeros[n / 8]) >> (4 * (n & 7))) & 15u);
+      s16[0] = scales[n];
+      z[0] = (float)((((uint32_t)qzeros[n / 8]) >> (4 * (n & 7))) & 15u);
     } else {
-      float mn = (float)h[0], mx = (float)h[0];
 #pragma unroll
-      for (int i = 1; i < 128; ++i) {
-        const float v = (float)h[i];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+      for (int u = 0; u < SUB; ++u) {
+        float mn = (float)h[u * GS], mx = (float)h[u * GS];
+#pragma unroll
+        for (int i = 1; i < GS; ++i) {
+          const float v = (float)h[u * GS + i];
+          mn = fminf(mn, v);
+          mx = fmaxf(mx, v);
+        }
+        group_scale_zero(mn, mx, sym, s16[u], z[u]);
       }
-      group_scale_zero(mn, mx, sym, s16, z);
     }
-    const float s = (float)s16;
     uint32_t* ow = reinterpret_cast<uint32_t*>(out);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+      const int u = (8 * j) / GS;
+      const float s = (float)s16[u];
       uint32_t word = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float q = fminf(fmaxf(rintf((float)h[8 * j + i] / s) + z, 0.0f), 15.0f);
+        const float q = fminf(fmaxf(rintf((float)h[8 * j + i] / s) + z[u], 0.0f), 15.0f);
         word |= ((uint32_t)q) << (4 * i);
       }
       ow[j] = word;
     }
-    if (!perchan) scales[(int64_t)g * N + n] = s16;
-    zbits = ((uint32_t)z) << (4 * (n & 7));
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      if (!perchan) scales[((int64_t)g * SUB + u) * N + n] = s16[u];
+      zbits[u] = ((uint32_t)z[u]) << (4 * (n & 7));
+    }
   }
   if (live) {
 #pragma unroll
     for (int slot = 0; slot < 4; ++slot) *reinterpret_cast<u32x4*>(qweight + tiled_chunk(n, g, slot, ng)) = out[slot];
   }
-  // OR the 8 nibbles of the zero-point word across the 8 consecutive lanes.
-  zbits |= __shfl_xor(zbits, 1, kWave);
-  zbits |= __shfl_xor(zbits, 2, kWave);
-  zbits |= __shfl_xor(zbits, 4, kWave);
-  if (!perchan && valid && (n & 7) == 0) qzeros[(int64_t)g * ((N + 7) / 8) + n / 8] = (int32_t)zbits;
+  // OR the 8 nibbles of each zero-point word across the 8 consecutive lanes.
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    uint32_t zb = zbits[u];
+    zb |= __shfl_xor(zb, 1, kWave);
+    zb |= __shfl_xor(zb, 2, kWave);
+    zb |= __shfl_xor(zb, 4, kWave);
+    if (!perchan && valid && (n & 7) == 0) qzeros[((int64_t)g * SUB + u) * nzw + n / 8] = (int32_t)zb;
+  }
 }
 
 // One thread per packed word (n, j): eight fp16 outputs.
@@ -153,7 +170,7 @@ __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t*
                                                                   const half_t* __restrict__ scales,
                                                                   const uint32_t* __restrict__ qzeros,
                                                                   half_t* __restrict__ out, int N, int K,
-                                                                  int gmask) {
+                                                                  int glog) {
   const int wpr = K / 8;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (tid >= (int64_t)N * wpr) return;
@@ -161,8 +178,9 @@ __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t*
   const int j = (int)(tid % wpr);
   const int g = j / 16;
   const int nzw = (N + 7) / 8;
-  const uint32_t z = (qzeros[(int64_t)(g & gmask) * nzw + n / 8] >> (4 * (n & 7))) & 15u;
-  const half_t s = scales[(int64_t)(g & gmask) * N + n];
+  const int64_t row = (8 * j) >> glog;
+  const uint32_t z = (qzeros[row * nzw + n / 8] >> (4 * (n & 7))) & 15u;
+  const half_t s = scales[row * N + n];
   const half2_t negz2 = splat2(-(half_t)(1024 + z));
   const uint32_t word = qweight[tiled_chunk(n, g, (j & 15) >> 2, K / 128) + (j & 3)];
   const half8_t v = dequant8(word, negz2, splat2(s));
@@ -277,8 +295,13 @@ hipError_t launch_awq_pack(const void* w, int32_t* qweight, void* scales, int32_
   const int npad = (N + 15) / 16 * 16;
   const int64_t total = (int64_t)npad * (K / 128);
   const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(awq_pack_kernel, dim3(blocks), dim3(256), 0, stream, (const half_t*)w, (uint32_t*)qweight,
-                     (half_t*)scales, qzeros, N, K, npad, perchan, symmetric ? 1 : 0);
+#define W4_AWQ_PACK(SUB)                                                                                   \
+  hipLaunchKernelGGL(awq_pack_kernel<SUB>, dim3(blocks), dim3(256), 0, stream, (const half_t*)w,            \
+                     (uint32_t*)qweight, (half_t*)scales, qzeros, N, K, npad, perchan, symmetric ? 1 : 0)
+  if (group_size == 32) W4_AWQ_PACK(4);
+  else if (group_size == 64) W4_AWQ_PACK(2);
+  else W4_AWQ_PACK(1);
+#undef W4_AWQ_PACK
   return hipGetLastError();
 }
 
@@ -288,7 +311,7 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(awq_unpack_dequant_kernel, dim3(blocks), dim3(256), 0, stream,
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros,
-                     (half_t*)out, N, K, group_mask(group_size));
+                     (half_t*)out, N, K, group_log2(group_size));
   return hipGetLastError();
 }
 
