@@ -144,3 +144,23 @@ def test_identity_probe_bit_exact(group):
     y = to_np(w4.awq_gemm(torch.from_numpy(x).to(dev), qw, sc, qz, group_size=group))
     expect = ref["w_deq"][:, ks].T.astype(np.float16)
     assert np.array_equal(y[:len(ks)].view(np.uint16), expect.view(np.uint16))
+
+
+@pytest.mark.parametrize("group", [64, 32])
+@pytest.mark.parametrize("tiles", ["1", "2", "4"])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (16, 520, 5120), (5, 130, 13824), (40, 96, 768)])
+def test_dequantizing_skinny_every_tile_width(group, tiles, M, N, K, monkeypatch):
+    """Group sizes 64 and 32 at M <= 64 take the dequantizing register-X kernel: each tile
+    width (forced through its tuning variable), split K, ragged N."""
+    dev = device()
+    monkeypatch.setenv("W4_SKINNY_TILES", tiles)
+    announce(f"dequantizing skinny group={group} tiles={tiles} M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N + group, outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), group, False, dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, group_size=group, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err

@@ -67,9 +67,7 @@ int check_group_w4a16(const char* fn, int32_t group_size) {
   return W4_OK;
 }
 
-// The skinny kernels apply one scale per 128-k unit (group sizes 128 and -1); smaller
-// groups take the MFMA GEMM at every M.
-bool use_skinny(int64_t M, int32_t group_size) { return M <= 64 && (group_size == 128 || group_size == -1); }
+bool use_skinny(int64_t M) { return M <= 64; }
 
 int check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
   for (auto& p : ptrs) {
@@ -108,8 +106,8 @@ int launched(const char* fn, hipError_t e) {
 
 size_t awq_ws(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M <= 0 || N <= 0) return 0;
-  return use_skinny(M, group_size) ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K)
-                                   : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
+  return use_skinny(M) ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K, group_size)
+                       : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
 }
 
 #define W4_TRY(expr)          \
@@ -205,7 +203,7 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   }
   W4_TRY(check_device(fn));
   hipError_t e;
-  if (use_skinny(M, group_size))
+  if (use_skinny(M))
     e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
                           (hipStream_t)stream);
   else

@@ -62,7 +62,7 @@ struct SkinnyPlan {
   int smem;        // LDS kernel: dynamic LDS bytes per workgroup
   int drain;       // 1: wait for all loads in flight once per D groups
 };
-SkinnyPlan skinny_plan(int M, int N, int K);
+SkinnyPlan skinny_plan(int M, int N, int K, int group_size);
 
 // Tile plan of the large-M W4A16 GEMM.
 struct GemmPlan {
@@ -77,11 +77,8 @@ struct W4A8Plan {
 };
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 
-// W4A16 scales and zero points.  The skinny kernels (group_size 128 or -1) read them at
-// group row (g & group_mask) for 128-k unit g: per-channel weights keep a single row.
-// The GEMM, the pack and the unpack kernels read the row of element k as
+// W4A16 scales and zero points: every kernel reads the row of element k as
 // k >> group_log2 (30 for per-channel: every k < 2^30 maps to row 0).
-inline int group_mask(int group_size) { return group_size == -1 ? 0 : -1; }
 inline int group_log2(int group_size) {
   return group_size == 32 ? 5 : group_size == 64 ? 6 : group_size == 128 ? 7 : 30;
 }
@@ -94,7 +91,7 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
                             int two_level, hipStream_t stream);
 
-size_t skinny_workspace_bytes(int M, int N, int K);
+size_t skinny_workspace_bytes(int M, int N, int K, int group_size);
 hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
                          void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream);
 

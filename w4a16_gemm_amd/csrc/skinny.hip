@@ -44,16 +44,19 @@ struct GroupRegs {
 // row depends only on its own A row and an output column only on its own B column
 // (and scale / zero point), so clamped data only reaches outputs that are never
 // stored.
-template <int MT, int T>
+template <int MT, int T, bool DQ>
 __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __restrict__ x,
                                            const uint32_t* __restrict__ qweight,
                                            const half_t* __restrict__ scales,
                                            const uint32_t* __restrict__ qzeros, int g, int n0, int lane,
-                                           int M, int N, int K, int gmask) {
+                                           int M, int N, int K, int glog) {
   const int ng = K / 128;
   const int nzw = (N + 7) / 8;
   const int slot = lane >> 4;
   const int last_tile = (N - 1) >> 4;
+  // scale / zero-point row: of the 128-k unit (group sizes 128 and -1), or, in the
+  // dequantizing variant, of this lane's 32 k (any group size >= 32)
+  const int64_t row = (((int64_t)g << 7) + (DQ ? 32 * slot : 0)) >> glog;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
@@ -61,8 +64,8 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     // l % 16 of the tile, words 4 (l / 16) .. + 3 of the group
     const int tile = min((n0 >> 4) + t, last_tile);
     r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
-    r.s[t] = scales[(int64_t)(g & gmask) * N + nc];
-    r.zw[t] = qzeros[(int64_t)(g & gmask) * nzw + (nc >> 3)];
+    r.s[t] = scales[row * N + nc];
+    r.zw[t] = qzeros[row * nzw + (nc >> 3)];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -109,11 +112,37 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
   }
 }
 
+// Dequantizing variant (group sizes 64 and 32, whose groups split the k range of one
+// MFMA): every word becomes fp16 (q - z) s in registers (one rounding per element, the
+// large-M GEMM's dequantization) with the scale and zero point of this lane's own 32 k,
+// and the MFMAs accumulate Y directly.
+template <int MT, int T>
+__device__ __forceinline__ void compute_group_dq(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T], int n0,
+                                                 int lane, int N) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
+    // fp16 bit patterns built with integer ops: -(1024 + z) is 0xE400 | z; the scale's
+    // 16 bits in both halves
+    const uint32_t z = (r.zw[t] >> (4 * (nc & 7))) & 15u;
+    const half2_t negz2 = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
+    const uint32_t sb = __builtin_bit_cast(uint16_t, r.s[t]);
+    const half2_t s2 = __builtin_bit_cast(half2_t, sb * 0x00010001u);
+    half8_t bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = dequant8(r.b[t][j], negz2, s2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yacc[mt][t] = mfma16(r.a[mt][j], bv[j], yacc[mt][t]);
+  }
+}
+
 // WAVES waves per workgroup take the groups of the workgroup's K range round robin.
 // D register sets rotate (loop unrolled by D, no register copies), so while a wave
 // computes one group the loads of its next D groups are in flight (D * T KB per wave).
 // A workgroup owns 16 T output columns (T 16-row tiles; all its waves share them).
-template <int MT, int T, int D, int WAVES>
+template <int MT, int T, int D, int WAVES, bool DQ>
 __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __restrict__ x,
                                                                const uint32_t* __restrict__ qweight,
                                                                const half_t* __restrict__ scales,
@@ -121,7 +150,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
                                                                half_t* __restrict__ y,
                                                                unsigned* __restrict__ counters,
                                                                float* __restrict__ partials, int M, int N, int K,
-                                                               int splits, int gps, int drain, int gmask) {
+                                                               int splits, int gps, int drain, int glog) {
   constexpr int kT = WAVES * kWave;
   constexpr int kCols = 16 * T;           // output columns of one workgroup
   constexpr int kOut = MT * 16 * kCols;   // outputs of one workgroup
@@ -150,7 +179,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   const int g = gbeg + wave;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K, gmask);
+    load_group<MT, T, DQ>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K, glog);
   // Steady state without conditions (the wait before each compute then covers only its
   // own register set), then the remaining < D groups; all counts are wave-uniform.
   const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
@@ -159,14 +188,18 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
     if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      compute_group<MT, T>(r[d], yacc, n0, lane, N);
-      load_group<MT, T>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K,
-                        gmask);
+      if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
+      else compute_group<MT, T>(r[d], yacc, n0, lane, N);
+      load_group<MT, T, DQ>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N,
+                            K, glog);
     }
   }
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (it + d < mine) compute_group<MT, T>(r[d], yacc, n0, lane, N);
+    if (it + d < mine) {
+      if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
+      else compute_group<MT, T>(r[d], yacc, n0, lane, N);
+    }
 
   // Cross-wave reduction.  Element (mt, t, i) of lane l is output row
   // m = 16 mt + 4 (l / 16) + i, column n = n0 + 16 t + (l % 16).
@@ -269,10 +302,11 @@ template <int T>
 __device__ __forceinline__ void load_wstage(WStage<T>& r, const uint32_t* __restrict__ qweight,
                                             const half_t* __restrict__ scales,
                                             const uint32_t* __restrict__ qzeros, int g, int tile0, int lane,
-                                            int N, int ng, int nzw, int gmask) {
+                                            int N, int ng, int nzw, int glog) {
   const int last_tile = (N - 1) >> 4;
-  const half_t* srow = scales + (int64_t)(g & gmask) * N;
-  const uint32_t* zrow = qzeros + (int64_t)(g & gmask) * nzw;
+  const int64_t row = ((int64_t)g << 7) >> glog;  // group sizes 128 and -1
+  const half_t* srow = scales + row * N;
+  const uint32_t* zrow = qzeros + row * nzw;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int tile = min(tile0 + t, last_tile);
@@ -381,7 +415,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
                                                          const uint32_t* __restrict__ qzeros,
                                                          half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                          float* __restrict__ partials, int M, int N, int K,
-                                                         int splits, int gps, int wn_count, int drain, int gmask) {
+                                                         int splits, int gps, int wn_count, int drain, int glog) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nthreads = blockDim.x;
   const int lane = threadIdx.x & 63;
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   const int glast = gend - 1;
   const int g = gbeg + wk;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_wstage<T>(r[d], qweight, scales, qzeros, min(g + d * WK, glast), tile0, lane, N, ng, nzw, gmask);
+  for (int d = 0; d < D; ++d) load_wstage<T>(r[d], qweight, scales, qzeros, min(g + d * WK, glast), tile0, lane, N, ng, nzw, glog);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kXChunksPerPass; ++i) {
@@ -465,7 +499,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
       const int gl = g + (it + d) * WK - gbeg;
       compute_wstage<T, ONE_ROW>(r[d], xrow + gl * 128, sp + gl * 32, yacc, zsh, lane);
       load_wstage<T>(r[d], qweight, scales, qzeros, min(gbeg + gl + D * WK, glast), tile0, lane, N, ng, nzw,
-                     gmask);
+                     glog);
     }
   }
 #pragma unroll
@@ -520,7 +554,7 @@ static int skinny_waves(int) { return 4; }
 // stores, arrival counter, reads of the partials by the last workgroup), so the plan
 // first narrows the workgroups: the widest T in {4, 2, 1} that still gives at least
 // kMinBlocks workgroups; only when even T = 1 does not (N < 16 kMinBlocks) is K split.
-SkinnyPlan skinny_plan(int M, int N, int K) {
+SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   SkinnyPlan p;
   const int ng = K / 128;
   p.lds = 0;
@@ -533,7 +567,9 @@ SkinnyPlan skinny_plan(int M, int N, int K) {
   constexpr int kLdsBudget = 65536 - 256;  // dynamic LDS; the split-K flag is static
   // X slice M (128 gps + 8) halves plus S, P (32 floats per group) within the budget
   const int lds_gmax = max(1, (kLdsBudget - 16 * M) / (256 * M + 128));
-  const bool lds_ok = M <= 16 && !(ng > lds_gmax && (N + 15) / 16 >= kMaxCounters);
+  // (group sizes below 128 take the dequantizing register-X kernel)
+  const bool lds_ok = M <= 16 && !(ng > lds_gmax && (N + 15) / 16 >= kMaxCounters) &&
+                      (group_size == 128 || group_size == -1);
   // Default kernel and shape, from sweeps on the MI355X over the Llama-2-13B projection
   // shapes at M = 1, 4, 16: the LDS kernel wins for M <= 4 except on narrow, short
   // matrices (N and K <= 8192), where its X staging is not repaid; above M = 4 the
@@ -609,16 +645,17 @@ SkinnyPlan skinny_plan(int M, int N, int K) {
   return p;
 }
 
-size_t skinny_workspace_bytes(int M, int N, int K) {
-  const SkinnyPlan p = skinny_plan(M, N, K);
+size_t skinny_workspace_bytes(int M, int N, int K, int group_size) {
+  const SkinnyPlan p = skinny_plan(M, N, K, group_size);
   if (p.splits == 1) return 0;
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(float);
 }
 
 hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
                          void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
-  const SkinnyPlan p = skinny_plan(M, N, K);
-  const int gmask = group_mask(group_size);
+  const SkinnyPlan p = skinny_plan(M, N, K, group_size);
+  const int glog = group_log2(group_size);
+  const bool dq = group_size == 64 || group_size == 32;
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const dim3 grid(p.row_blocks, p.splits);
@@ -631,7 +668,7 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
     const dim3 block(64 * p.wn * p.wk);
 #define LDS_LAUNCH1(T, D, ONE)                                                                                \
   hipLaunchKernelGGL((skinny_lds_kernel<T, D, ONE>), grid, block, p.smem, stream, xh, qw, sc, qz, yh, counters, \
-                     partials, M, N, K, p.splits, p.gps, p.wn, p.drain, gmask)
+                     partials, M, N, K, p.splits, p.gps, p.wn, p.drain, glog)
 #define LDS_LAUNCH(T, D) \
   if (M == 1) LDS_LAUNCH1(T, D, true); else LDS_LAUNCH1(T, D, false)
     if (p.tiles == 1) { if (p.depth == 4) LDS_LAUNCH(1, 4); else LDS_LAUNCH(1, 8); }
@@ -641,9 +678,13 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
 #undef LDS_LAUNCH1
     return hipGetLastError();
   }
-#define SKINNY_LAUNCH(MT, T, D)                                                                          \
-  hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, counters, \
-                     partials, M, N, K, p.splits, p.gps, p.drain, gmask)
+#define SKINNY_LAUNCH(MT, T, D)                                                                             \
+  if (dq)                                                                                                   \
+    hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, true>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, \
+                       counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                        \
+  else                                                                                                      \
+    hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, false>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz,    \
+                       yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog)
 #define SKINNY_LAUNCH_T(MT)                    \
   if (p.tiles == 4) SKINNY_LAUNCH(MT, 4, 2);   \
   else if (p.tiles == 2) SKINNY_LAUNCH(MT, 2, 2); \
