@@ -241,3 +241,38 @@ def test_w4a8_random_shapes(group, M, N, K):
     xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
     acc = to_np(w4.w4a8_gemm_i32(torch.from_numpy(xq).to(dev), qw, gsd, group, N=N))
     assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, gs, 128))
+
+
+@pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("M", [1, 16, 256])
+def test_down_projection_chain_full_size(group, M):
+    """The W4A8 MLP tail at its real shape: fused gate+up output [M, 2 x 13824] ->
+    silu_mul_quant -> down projection (K = 13824, N = 5120) on the int8 GEMM.  Codes
+    within the SiLU near-tie rule; accumulators on the GPU's codes bit-exact against the
+    oracle's integer sum; fp16 outputs within 2e-3 of the oracle chain."""
+    dev = device()
+    I, N = 13824, 5120
+    announce(f"down-projection chain M={M} group={group}")
+    gu = synth.make_activations(M, 2 * I, seed=M + 77, rms_spread=True)
+    w = synth.make_linear(0, N, I, seed=5, outliers=True).w
+    qw, gs, cs = w4.w4a8_pack(w.to(dev), group)
+    xq, sa = w4.w4a8_silu_mul_quant(gu.to(dev))
+    y = w4.w4a8_gemm(xq, sa, qw, gs, cs, group)
+    acc = w4.w4a8_gemm_i32(xq, qw, gs, group, N=N)
+    torch.cuda.synchronize()
+    rxq, rsa, t = ora.silu_mul_quant_ref(gu.numpy())
+    gq = to_np(xq).astype(np.int64)
+    diff = np.abs(gq - rxq.astype(np.int64))
+    assert diff.max() <= 1
+    assert np.all(np.abs(np.abs(t - np.trunc(t)) - 0.5)[diff == 1] < NEAR_TIE_SILU)
+    ms = sample_idx(M, 24, seed=M)
+    ns = sample_idx(N, 192, seed=11, must=range(0, 16))
+    q, rcs, rgs = ora.quantize_w4a8(w.numpy()[ns], group)
+    racc = ora.w4a8_acc_ref(gq[ms], q, rgs, 128)
+    assert np.array_equal(to_np(acc)[np.ix_(ms, ns)].astype(np.int64), racc)
+    yr = ora.w4a8_linear_ref(ora.w4a8_acc_ref(rxq[ms], q, rgs, 128), rsa[ms], rcs)
+    qs = q.astype(np.float64) * (1 if rgs is None else np.repeat(rgs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * rcs.astype(np.float64)
+    xn = np.linalg.norm(rxq[ms].astype(np.float64), axis=1) * rsa[ms].astype(np.float64)
+    err = normalized_error(to_np(y)[np.ix_(ms, ns)].astype(np.float64), yr, xn, wn)
+    assert err <= TOL, err
