@@ -278,7 +278,7 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
 // Tile BM x 256 x 128 (one group of 128 k per step), 256 threads; the 4 waves split N
 // (64 columns each = two 32-column fragments) and share all BM = 32 * MI rows (MI
 // 32-row fragments).  A (xq) tiles go through LDS as 128-byte rows of 8 16-byte
-// chunks (chunk c of row r at c ^ (r % 8)).  B: lane l (column l % 32, K-slot h = l / 32)
+// chunks (chunk c of row r at c ^ ((r / 2) % 8)).  B: lane l (column l % 32, K-slot h = l / 32)
 // loads words 8h..8h+7 of its row for this step (two 16-byte chunks); k32-step s uses
 // words 8h + 2s, 8h + 2s + 1 (16 codes, k = 8 (8h + 2s) .. + 15), and A is read from
 // LDS with the same slot assignment.
@@ -292,7 +292,10 @@ constexpr int WBN = 256, WBK = 128;
 constexpr int kI4PerChannel = 0, kI4TwoLevel = 1, kI8 = 2;
 constexpr int kWThreads = 256;
 
-__device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// chunk c of row r at c ^ ((r / 2) % 8): two consecutive 128-byte rows fill one 256-byte
+// bank window, so 16 consecutive rows read at one chunk hit 16 distinct bank groups
+// (with c ^ (r % 8), rows r and r + 8 collided: 40 % of LDS cycles were bank conflicts)
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 __device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { return cs ? cs[n] : (half_t)1; }
 
 template <int MI, int MODE>
