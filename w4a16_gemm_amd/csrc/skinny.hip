@@ -620,26 +620,36 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   // traffic is 4 M / T bytes per weight byte).  Split-K target: 320 workgroups, or 512
   // for 8 < M <= 16 (and 4 < M <= 8 with long K) unless the columns alone give 320
   // (sweeps on the projection shapes).
+  const int pct = env_int("W4_SKINNY_PARTIAL_PCT", 10);
+  // Split-K factor for tile width tt (row blocks of 16 tt columns in rb).
+  auto plan_splits = [&](int tt, int& rb) {
+    rb = (N + 16 * tt - 1) / (16 * tt);
+    const int tgt = env_int("W4_SKINNY_BLOCKS", (M > 4 && M <= 16 && rb < 320 && (M > 8 || K > 8192)) ? 512 : 320);
+    int sp = (tgt + rb - 1) / rb;
+    sp = min(sp, ng / waves);  // at least one group per wave
+    // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the
+    // codes (N * K / 2 bytes): splits <= K / (160 M)
+    sp = min(sp, max(1, (int)((int64_t)K * pct / (1600LL * M))));
+    sp = max(1, sp);
+    // a full wave of workgroups needs no split (the fixup costs ~1.5 us on short calls)
+    if (rb >= 256 || rb >= kMaxCounters) sp = 1;
+    return sp;
+  };
   t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4) {
     if (M <= 4) t = (N <= 16 * 320) ? 1 : ((N <= 32 * 480) ? 2 : 4);
     else if (M <= 8) t = N > 16384 ? 4 : 2;
     else if (M <= 16) t = 4;
     else t = ((N + 63) / 64 >= 128) ? 4 : 2;
+    int rb1 = 0, rb2 = 0;
+    // M <= 8: narrower tiles when they fill the chip without split-K
+    if (M <= 8 && t > 1 && (N + 16 * t - 1) / (16 * t) < 256 && (N + 8 * t - 1) / (8 * t) >= 256) t /= 2;
+    // 8 < M <= 16: 4 tiles share each X fragment, unless that leaves under 128 workgroups
+    if (M > 8 && M <= 16 && t == 4 && plan_splits(4, rb1) * rb1 < 128 && plan_splits(2, rb2) * rb2 >= 128) t = 2;
   }
   p.tiles = t;
   p.depth = t == 1 ? 4 : 2;
-  p.row_blocks = (N + 16 * t - 1) / (16 * t);
-  target = env_int("W4_SKINNY_BLOCKS",
-                   (M > 4 && M <= 16 && p.row_blocks < 320 && (M > 8 || K > 8192)) ? 512 : 320);
-  int splits = (target + p.row_blocks - 1) / p.row_blocks;
-  splits = min(splits, ng / waves);  // at least one group per wave
-  // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the codes
-  // (N * K / 2 bytes): splits <= K / (160 M)
-  const int pct = env_int("W4_SKINNY_PARTIAL_PCT", 10);
-  splits = min(splits, max(1, (int)((int64_t)K * pct / (1600LL * M))));
-  splits = max(1, splits);
-  if (p.row_blocks >= kMaxCounters) splits = 1;
+  int splits = plan_splits(t, p.row_blocks);
   p.gps = (ng + splits - 1) / splits;
   p.splits = (ng + p.gps - 1) / p.gps;
   return p;
