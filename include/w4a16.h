@@ -115,7 +115,7 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
 
 /*
  * awq_gemm -- Y [M, N] = X [M, K] . dequant(qweight, scales, qzeros)^T, fp32 accumulate,
- * fp16 output (round to nearest even).  Dispatch: M <= 64 uses a bandwidth-bound skinny
+ * fp16 output (round to nearest even).  Dispatch: M <= 32 uses a bandwidth-bound skinny
  * kernel (16x16x32 fp16 MFMA on exact fp16 encodings of the codes, per-group scaling in
  * fp32; for M <= 4 with X staged in LDS); larger M uses the LDS-staged 32x32x16 fp16
  * MFMA GEMM with in-register dequantization.  Group sizes 64 and 32 take the MFMA GEMM

@@ -1,7 +1,7 @@
 """GPU parity of awq_gemm (W4A16) against the oracle.
 
 * small shapes spanning several tiles and ragged tails, oracle-packed weights fed to
-  the GPU GEMM (isolates the GEMM), both kernels (M <= 64 skinny, M > 64 MFMA GEMM),
+  the GPU GEMM (isolates the GEMM), both kernels (M <= 32 skinny, M > 32 MFMA GEMM),
   with and without split-K, outputs pre-poisoned with NaN;
 * bit-exact identity probe and constructed-exact GEMMs;
 * determinism and workspace reuse;
@@ -148,9 +148,9 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
 
 
 @pytest.mark.parametrize("tiles", ["1", "2", "4"])
-@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (33, 96, 768), (64, 300, 640)])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (17, 96, 768), (32, 300, 640)])
 def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
-    """Each tile width / prefetch-depth variant of the register-X M <= 64 kernel (forced
+    """Each tile width / prefetch-depth variant of the register-X M <= 32 kernel (forced
     through its tuning variables), against the oracle."""
     dev = device()
     monkeypatch.setenv("W4_SKINNY_TILES", tiles)
@@ -197,7 +197,7 @@ def test_skinny_lds_variants(variant, M, N, K, monkeypatch):
 @pytest.mark.parametrize("shape", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048)])
 def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
-    """Each tile shape of the M > 64 MFMA GEMM (forced through its tuning variable;
+    """Each tile shape of the M > 32 MFMA GEMM (forced through its tuning variable;
     128x256, 128x128, 64x256, 64x128), with ragged M and N, against the oracle."""
     dev = device()
     monkeypatch.setenv("W4_GEMM_SHAPE", shape)

@@ -69,9 +69,9 @@ def test_pack_golden_rows():
             assert int(codes[2, k]) == code, (c["name"], k)
 
 
-# shapes for each kernel family: register-X skinny (M <= 64, N and K <= 8192 at M <= 4),
-# LDS skinny (M <= 4 with N or K > 8192; split K), MFMA GEMM (M > 64; split K for few tiles)
-GEMM_SHAPES = [(1, 200, 1024), (4, 1000, 2048), (16, 520, 5120), (33, 96, 768), (64, 300, 640),
+# shapes for each kernel family: register-X skinny (M <= 32, N and K <= 8192 at M <= 4),
+# LDS skinny (M <= 4 with N or K > 8192; split K), MFMA GEMM (M > 32; split K for few tiles)
+GEMM_SHAPES = [(1, 200, 1024), (4, 1000, 2048), (16, 520, 5120), (24, 130, 1024), (33, 96, 768), (64, 300, 640),
                (1, 200, 9216), (3, 8320, 1024), (65, 300, 640), (130, 520, 1024), (257, 1030, 2048)]
 
 
@@ -148,9 +148,9 @@ def test_identity_probe_bit_exact(group):
 
 @pytest.mark.parametrize("group", [64, 32])
 @pytest.mark.parametrize("tiles", ["1", "2", "4"])
-@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (16, 520, 5120), (5, 130, 13824), (40, 96, 768)])
+@pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (16, 520, 5120), (5, 130, 13824), (24, 96, 768)])
 def test_dequantizing_skinny_every_tile_width(group, tiles, M, N, K, monkeypatch):
-    """Group sizes 64 and 32 at M <= 64 take the dequantizing register-X kernel: each tile
+    """Group sizes 64 and 32 at M <= 32 take the dequantizing register-X kernel: each tile
     width (forced through its tuning variable), split K, ragged N."""
     dev = device()
     monkeypatch.setenv("W4_SKINNY_TILES", tiles)

@@ -67,7 +67,9 @@ int check_group_w4a16(const char* fn, int32_t group_size) {
   return W4_OK;
 }
 
-bool use_skinny(int64_t M) { return M <= 64; }
+// M <= 32: the skinny kernels; above, the MFMA GEMM (faster from M = 48 on the
+// Llama-2-13B projection shapes, equal at 33..47 within a few percent).
+bool use_skinny(int64_t M) { return M <= 32; }
 
 int check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
   for (auto& p : ptrs) {

@@ -272,7 +272,7 @@ GemmPlan gemm_plan(int M, int N, int K) {
   const int min_tiles = env_int("W4_GEMM_MIN_TILES", 256);
   const int forced = env_int("W4_GEMM_SHAPE", 0);  // 1..4 selects kShapes[forced - 1]
   int pick = 3;
-  // 64 < M <= 512: narrow (128-column) tiles and split-K to at least 320 workgroups
+  // 32 < M <= 512: narrow (128-column) tiles and split-K to at least 320 workgroups
   // (sweeps on K = 5120, N in {5120, 13824}, M = 96 .. 512).
   const bool mid = M <= 512 && forced == 0;
   if (forced >= 1 && forced <= 4) {

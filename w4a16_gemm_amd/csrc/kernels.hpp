@@ -49,9 +49,9 @@ constexpr size_t kCounterRegionBytes = kMaxCounters * sizeof(unsigned);
 // Host-side tuning knob: integer environment variable, or `dflt` when unset.
 int env_int(const char* name, int dflt);
 
-// Tile plan of the skinny (M <= 64) W4A16 kernel.
+// Tile plan of the skinny (M <= 32) W4A16 kernel.
 struct SkinnyPlan {
-  int mt;          // 16-row M tiles (1, 2 or 4)
+  int mt;          // 16-row M tiles (1 or 2)
   int tiles;       // 16-column tiles per workgroup (1, 2 or 4)
   int depth;       // groups in flight per wave (register sets)
   int row_blocks;  // ceil(N / (16 tiles))

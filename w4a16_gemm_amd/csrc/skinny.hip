@@ -1,4 +1,4 @@
-// Skinny W4A16 GEMM for M <= 64 (decode): bandwidth-bound, every packed weight byte
+// Skinny W4A16 GEMM for M <= 32 (decode): bandwidth-bound, every packed weight byte
 // is read once.
 //
 // The pages single out the small-batch regime ("Implement AWQ quantization support
@@ -14,7 +14,7 @@
 // subtract or multiply); S_g comes from one extra MFMA against a B operand of ones.
 // fp16 x (1024 + q) products are exact in fp32; only the fp32 sums round.
 //
-// Work split (register-X kernel, 16 < M <= 64; the M <= 16 kernel further below stages X
+// Work split (register-X kernel, M <= 32; the M <= 16 kernel further below stages X
 // in LDS): a workgroup (4 waves) owns 16 T output columns n (T = 1, 2 or 4 tiles of 16)
 // and a contiguous range of K groups (split-K across workgroups only for narrow N); its
 // waves take the groups of that range round robin.  Per group, lane l of a wave loads
@@ -614,7 +614,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     p.smem = max(xbytes, rbytes);
     return p;
   }
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.mt = M <= 16 ? 1 : 2;  // M <= 32
   const int waves = skinny_waves(p.mt);
   // Tiles per workgroup: with more rows each X fragment should serve more tiles (X
   // traffic is 4 M / T bytes per weight byte).  Split-K target: 320 workgroups, or 512
@@ -700,8 +700,7 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
   else if (p.tiles == 2) SKINNY_LAUNCH(MT, 2, 2); \
   else SKINNY_LAUNCH(MT, 1, 4)
   if (p.mt == 1) { SKINNY_LAUNCH_T(1); }
-  else if (p.mt == 2) { SKINNY_LAUNCH_T(2); }
-  else { SKINNY_LAUNCH_T(4); }
+  else { SKINNY_LAUNCH_T(2); }
 #undef SKINNY_LAUNCH_T
 #undef SKINNY_LAUNCH
   return hipGetLastError();
