@@ -207,7 +207,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 (int4 weights, fp32 accumulate)",
+        "dtype": "f16",
         "data": "synthetic (seeded; W~N(0,0.02) with 1% outlier input channels x10, X~N(0,1))",
         "config": {"workload": "Llama-2-13B decode projection set: QKV 5120x15360, O 5120x5120, "
                                "gate+up 5120x27648, down 13824x5120 at M in {1,4,16}; g128 asymmetric uint4",
