@@ -165,7 +165,7 @@ def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("variant", ["1,4,1,4,0", "1,8,1,8,0", "2,4,2,4,0", "2,4,1,2,5", "4,2,1,4,0", "4,2,2,2,2",
+@pytest.mark.parametrize("variant", ["1,4,1,4,0", "1,4,1,8,0", "1,8,1,8,0", "2,4,2,4,0", "2,4,1,2,5", "4,2,1,4,0", "4,2,2,2,2",
                                      "1,4,2,2,3",
                                      "lds-off"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 5120), (7, 130, 13824)])

@@ -572,12 +572,14 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
                       (group_size == 128 || group_size == -1);
   // Default kernel and shape, from sweeps on the MI355X over the Llama-2-13B projection
   // shapes at M = 1, 4, 16: the LDS kernel wins for M <= 4 except on narrow, short
-  // matrices (N and K <= 8192), where its X staging is not repaid; above M = 4 the
-  // register-X kernel wins (the LDS slice then limits the K range per workgroup).
-  int use_lds = lds_ok && M <= 4 && !(N <= 8192 && K <= 8192);
+  // matrices (N and K <= 8192), where its X staging is not repaid, and at M = 1 with
+  // K <= 8192 and N <= 16384 (QKV); above M = 4 the register-X kernel wins (the LDS
+  // slice then limits the K range per workgroup).
+  int use_lds = lds_ok && M <= 4 && !(N <= 8192 && K <= 8192) && !(M == 1 && K <= 8192 && N <= 16384);
   int t = 1, d = 4, wn = 1, wk = 4, target = 256;
   if (N > 16384) { t = 4; d = 2; }
   else if (N > 8192) { wn = 2; }
+  else if (M == 1) { wk = 8; }  // narrow N, long K, one row: 8 K-waves, no split-K
   else { wn = 2; wk = 2; target = 512; }
   use_lds = env_int("W4_SKINNY_LDS", use_lds) && lds_ok;
   if (use_lds) {
