@@ -690,14 +690,18 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   p.skinny = 0;
   if (M <= 16 && env_int("W4_W4A8_SKINNY", 1)) {
     const int ng = K / 128;
+    // Tiles and split target from sweeps on the Llama-2-13B decode shapes (M = 1, 4, 16):
+    // splitting K never paid once the column blocks give 160 workgroups (the int32
+    // partials are M N 4 bytes per split, and their fixup costs ~1.5 us); for M > 1 wide
+    // tiles share each xq fragment between more columns.
     int t = env_int("W4_W4A8_TILES", 0);
-    if (t != 1 && t != 2 && t != 4) t = M <= 4 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : 4;
+    if (t != 1 && t != 2 && t != 4) t = M == 1 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : (N > 8192 ? 4 : 2);
     p.skinny = 1;
     p.bm = 16;
     p.tiles_m = 1;
     p.tiles_n = (N + 16 * t - 1) / (16 * t);
     p.tiles = t;
-    const int target = env_int("W4_W4A8_SKINNY_BLOCKS", 320);
+    const int target = env_int("W4_W4A8_SKINNY_BLOCKS", 160);
     int splits = (target + p.tiles_n - 1) / p.tiles_n;
     splits = max(1, min(splits, ng / 4));
     if (p.tiles_n >= kMaxCounters) splits = 1;
