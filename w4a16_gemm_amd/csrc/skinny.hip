@@ -619,14 +619,15 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   p.mt = M <= 16 ? 1 : 2;  // M <= 32
   const int waves = skinny_waves(p.mt);
   // Tiles per workgroup: with more rows each X fragment should serve more tiles (X
-  // traffic is 4 M / T bytes per weight byte).  Split-K target: 320 workgroups, or 512
-  // for 8 < M <= 16 (and 4 < M <= 8 with long K) unless the columns alone give 320
-  // (sweeps on the projection shapes).
+  // traffic is 4 M / T bytes per weight byte); split K only below 160 column blocks.
+  // From sweeps on the Llama-2-13B projection shapes and 4096 x 4096 at M = 1 .. 16.
   const int pct = env_int("W4_SKINNY_PARTIAL_PCT", 10);
   // Split-K factor for tile width tt (row blocks of 16 tt columns in rb).
   auto plan_splits = [&](int tt, int& rb) {
     rb = (N + 16 * tt - 1) / (16 * tt);
-    const int tgt = env_int("W4_SKINNY_BLOCKS", (M > 4 && M <= 16 && rb < 320 && (M > 8 || K > 8192)) ? 512 : 320);
+    // (split only below 160 column blocks: the fixup and the partial traffic cost more
+    // than the extra parallelism above that, on every decode shape swept)
+    const int tgt = env_int("W4_SKINNY_BLOCKS", 160);
     int sp = (tgt + rb - 1) / rb;
     sp = min(sp, ng / waves);  // at least one group per wave
     // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the
@@ -639,13 +640,14 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   };
   t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4) {
-    if (M <= 4) t = (N <= 16 * 320) ? 1 : ((N <= 32 * 480) ? 2 : 4);
-    else if (M <= 8) t = N > 16384 ? 4 : 2;
-    else if (M <= 16) t = 4;
+    if (M <= 4) t = N > 32 * 480 ? 4 : 2;
+    else if (M <= 8) t = N > 8192 ? 4 : 2;
+    else if (M <= 16) t = (N > 8192 || K > 8192) ? 4 : 2;
     else t = ((N + 63) / 64 >= 128) ? 4 : 2;
     int rb1 = 0, rb2 = 0;
-    // M <= 8: narrower tiles when they fill the chip without split-K
-    if (M <= 8 && t > 1 && (N + 16 * t - 1) / (16 * t) < 256 && (N + 8 * t - 1) / (8 * t) >= 256) t /= 2;
+    // M <= 8: narrower tiles while the column blocks alone give under 160 workgroups
+    // and half the width does not
+    while (M <= 8 && t > 1 && (N + 16 * t - 1) / (16 * t) < 160 && (N + 8 * t - 1) / (8 * t) >= 160) t /= 2;
     // 8 < M <= 16: 4 tiles share each X fragment, unless that leaves under 128 workgroups
     if (M > 8 && M <= 16 && t == 4 && plan_splits(4, rb1) * rb1 < 128 && plan_splits(2, rb2) * rb2 >= 128) t = 2;
   }
