@@ -550,10 +550,10 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 // up to ~512 workgroups are resident at once (no second, partly idle round).
 static int skinny_waves(int) { return 4; }
 
-// Columns per workgroup (16 T) and split-K.  Split-K costs a serial tail (partial
-// stores, arrival counter, reads of the partials by the last workgroup), so the plan
-// first narrows the workgroups: the widest T in {4, 2, 1} that still gives at least
-// kMinBlocks workgroups; only when even T = 1 does not (N < 16 kMinBlocks) is K split.
+// Kernel, columns per workgroup (16 T) and split-K.  Split-K costs a serial tail
+// (partial stores, arrival counter, reads of the partials by the last workgroup), so
+// at small M the plan first narrows the workgroups until the column blocks alone give
+// ~160 workgroups, and splits K only when they still do not.
 SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   SkinnyPlan p;
   const int ng = K / 128;
