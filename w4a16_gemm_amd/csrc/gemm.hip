@@ -133,18 +133,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
     for (int f = 0; f < NF; ++f)
       dst[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
   };
-  // Scale and zero point of this lane's rows for one 128-group: the raw words are
-  // prefetched one BK step ahead together with the codes, then converted to the packed
-  // fp16 pairs -(1024 + z) and s used by dequant8.
-  uint32_t zraw[NF];
-  half_t sraw[NF];
+  // Scale and zero point of this lane's rows for its group: the raw words are prefetched
+  // one BK step ahead together with the codes, then converted (every step, so that the
+  // loads are consumed unconditionally and stay with the prefetch) to the packed fp16
+  // pairs -(1024 + z), -(64 + z) and s, built as bit patterns: -(1024 + z) is 0xE400 | z
+  // (unit steps at 2^10), -(64 + z) is 0xD400 | 16 z (steps of 1/16 at 2^6).
+  uint32_t zraw[NF], sraw[NF];
+  const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
   auto load_sz = [&](int kt) {
     // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
     const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       zraw[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
-      sraw[f] = scales[row * N + nclamp[f]];
+      sraw[f] = sbits[row * N + nclamp[f]];
     }
   };
   half2_t c1024[NF], c64[NF], s2[NF];
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const uint32_t z = (zraw[f] >> (4 * (nclamp[f] & 7))) & 15u;
-      c1024[f] = splat2(-(half_t)(1024u + z));
-      c64[f] = splat2(-(half_t)(64u + z));
-      s2[f] = splat2(sraw[f]);
+      c1024[f] = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
+      c64[f] = __builtin_bit_cast(half2_t, (0xD400u | (z << 4)) * 0x00010001u);
+      s2[f] = __builtin_bit_cast(half2_t, sraw[f] * 0x00010001u);
     }
   };
   const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
@@ -174,7 +176,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   for (int kt = kbeg; kt < kend; ++kt) {
     const int buf = (kt - kbeg) & 1;
     const int kn = min(kt + 1, kend - 1);
-    const bool new_group = glog < 7 || ((kt + 1) & 1) == 0;  // G = 128: 2 BK steps per group
     u32x4 bnext[NF];
     load_a(kn);
     load_b(kn, bnext);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
     store_a(buf ^ 1);  // the other buffer was last read before the previous barrier
 #pragma unroll
     for (int f = 0; f < NF; ++f) breg[f] = bnext[f];
-    if (new_group) set_sz();
+    set_sz();
     __syncthreads();
   }
 
