@@ -117,10 +117,11 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
  * awq_gemm -- Y [M, N] = X [M, K] . dequant(qweight, scales, qzeros)^T, fp32 accumulate,
  * fp16 output (round to nearest even).  Dispatch: M <= 32 uses a bandwidth-bound skinny
  * kernel (16x16x32 fp16 MFMA on exact fp16 encodings of the codes, per-group scaling in
- * fp32; for M <= 4 with X staged in LDS); larger M uses the LDS-staged 32x32x16 fp16
- * MFMA GEMM with in-register dequantization.  Group sizes 64 and 32 take the MFMA GEMM
- * at every M (the skinny kernels apply one scale per 128 k).  Results are deterministic
- * (split-K partials are summed in a fixed order).
+ * fp32; X staged in LDS at M = 1 on wide matrices with K <= 8192); larger M uses the
+ * LDS-staged 32x32x16 fp16 MFMA GEMM with in-register dequantization.  Group sizes 64
+ * and 32 take a dequantizing variant of the skinny kernel at M <= 32 (each lane scales
+ * its own 32 k) and the MFMA GEMM above.  Results are deterministic (split-K partials
+ * are summed in a fixed order).
  */
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
              void* y, void* workspace, size_t workspace_bytes,

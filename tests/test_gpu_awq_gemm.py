@@ -147,16 +147,22 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("tiles", ["1", "2", "4"])
+@pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (17, 96, 768), (32, 300, 640)])
 def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
-    """Each tile width / prefetch-depth variant of the register-X M <= 32 kernel (forced
-    through its tuning variables), against the oracle."""
+    """Each compiled variant of the register-X M <= 32 kernel -- tile width, or
+    (tiles, prefetch depth, waves) -- forced through its tuning variables, against the
+    oracle (a variant that is not compiled for the shape's m-tiles falls back to the
+    default one)."""
     dev = device()
-    monkeypatch.setenv("W4_SKINNY_TILES", tiles)
+    t, *rest = tiles.split(",")
+    monkeypatch.setenv("W4_SKINNY_TILES", t)
+    if rest:
+        monkeypatch.setenv("W4_SKINNY_RDEPTH", rest[0])
+        monkeypatch.setenv("W4_SKINNY_WAVES", rest[1])
     monkeypatch.setenv("W4_SKINNY_LDS", "0")
     announce(f"skinny tiles={tiles} M={M} N={N} K={K}")
-    inp = synth.make_linear(M, N, K, seed=M + N + int(tiles), outliers=True)
+    inp = synth.make_linear(M, N, K, seed=M + N + int(t), outliers=True)
     ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
     y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz)).astype(np.float64)
     yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])

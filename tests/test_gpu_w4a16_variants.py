@@ -147,7 +147,7 @@ def test_identity_probe_bit_exact(group):
 
 
 @pytest.mark.parametrize("group", [64, 32])
-@pytest.mark.parametrize("tiles", ["1", "2", "4"])
+@pytest.mark.parametrize("tiles", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (16, 520, 5120), (5, 130, 13824), (24, 96, 768)])
 def test_dequantizing_skinny_every_tile_width(group, tiles, M, N, K, monkeypatch):
     """Group sizes 64 and 32 at M <= 32 take the dequantizing register-X kernel: each tile

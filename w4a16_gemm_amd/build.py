@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["api.cpp", "pack.hip", "skinny.hip", "gemm.hip", "w4a8.hip"]
+# Per-file flags.  The skinny kernels keep their few MFMA accumulators in VGPRs (the
+# per-group epilogue reads them with plain VALU operations instead of v_accvgpr_read).
+EXTRA = {"skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -42,7 +45,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(cmds))) as ex:
         results = list(ex.map(_run, cmds))
     for cmd, (rc, out) in zip(cmds, results):

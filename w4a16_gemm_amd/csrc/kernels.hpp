@@ -52,7 +52,7 @@ int env_int(const char* name, int dflt);
 // Tile plan of the skinny (M <= 32) W4A16 kernel.
 struct SkinnyPlan {
   int mt;          // 16-row M tiles (1 or 2)
-  int tiles;       // 16-column tiles per workgroup (1, 2 or 4)
+  int tiles;       // 16-column tiles per workgroup (1, 2, 4; register-X kernel also 8)
   int depth;       // groups in flight per wave (register sets)
   int row_blocks;  // ceil(N / (16 tiles))
   int splits;      // split-K factor over groups
@@ -61,6 +61,7 @@ struct SkinnyPlan {
   int wn, wk;      // LDS kernel: waves per workgroup = wn column groups x wk K-waves
   int smem;        // LDS kernel: dynamic LDS bytes per workgroup
   int drain;       // 1: wait for all loads in flight once per D groups
+  int waves;       // register-X kernel: waves per workgroup (4 or 8)
 };
 SkinnyPlan skinny_plan(int M, int N, int K, int group_size);
 

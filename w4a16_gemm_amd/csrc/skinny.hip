@@ -6,24 +6,26 @@
 // on par with FP16 at batch 16) and say that dequantization is the tricky part.
 // Here the dequantization is folded into per-group fp32 arithmetic:
 //
-//   Y[m,n] = sum_g s[n,g] * ( T_g[m,n] - (1024 + z[n,g]) * S_g[m] ),
-//   T_g[m,n] = sum_{k in g} X[m,k] * (1024 + q[n,k]),   S_g[m] = sum_{k in g} X[m,k],
+//   Y[m,n] = sum_g s[n,g] * ( T_g[m,n] - P_g[m] - z[n,g] * S_g[m] ),
+//   T_g[m,n] = sum_{k in g} X[m,k] * (c_k + q[n,k]),   S_g[m] = sum_{k in g} X[m,k],
+//   P_g[m] = sum_{k in g} c_k X[m,k],   c_k = 1024 for even k, 64 for odd k,
 //
 // which equals sum_k X[m,k] * (q - z) * s exactly in real arithmetic.  The MFMA
-// consumes the raw fp16 values 1024 + q (nine VALU ops per 8 codes, no per-element
-// subtract or multiply); S_g comes from one extra MFMA against a B operand of ones.
-// fp16 x (1024 + q) products are exact in fp32; only the fp32 sums round.
+// consumes the raw fp16 values c_k + q (five VALU ops per 8 codes, X taken in the
+// matching k order; no per-element subtract or multiply); fp16 x (c_k + q) products
+// are exact in fp32, only the fp32 sums round.
 //
-// Work split (register-X kernel, M <= 32; the M <= 16 kernel further below stages X
-// in LDS): a workgroup (4 waves) owns 16 T output columns n (T = 1, 2 or 4 tiles of 16)
-// and a contiguous range of K groups (split-K across workgroups only for narrow N); its
-// waves take the groups of that range round robin.  Per group, lane l of a wave loads
-// one 16-byte chunk (32 codes) of row n0 + 16t + (l % 16) for each tile t -- with the tiled
-// weight layout the 64 lanes read one contiguous 1 KB block -- and the 64 bytes of X
-// it needs; the four MFMAs of a group use word j of every lane's chunk, and A is
-// loaded with the same K-slot assignment.  Partial sums are reduced across the
-// waves in LDS, then across split-K workgroups through the workspace by the last
-// arriving workgroup, in a fixed order.
+// Work split (register-X kernel, M <= 32; the kernel further below stages X in LDS and
+// is the default only at M = 1 on wide, short matrices): a workgroup (4 or 8 waves) owns 16 T output columns n (T = 1, 2, 4 or 8 tiles
+// of 16) and a contiguous range of K groups (split-K across workgroups only for narrow
+// N); its waves take the groups of that range round robin.  Per group, lane l of a wave
+// loads one 16-byte chunk (32 codes) of row n0 + 16t + (l % 16) for each tile t -- with
+// the tiled weight layout the 64 lanes read one contiguous 1 KB block -- the 64 bytes of
+// X it needs, and one scale and one zero-point word per 64 columns; the four MFMAs of a
+// group use word j of every lane's chunk, and A is loaded with the same K-slot
+// assignment.  S_g and -P_g come from two MFMA chains against constant B operands.
+// Partial sums are reduced across the waves in LDS, then across split-K workgroups
+// through the workspace by the last arriving workgroup, in a fixed order.
 #include "kernels.hpp"
 
 namespace w4 {
@@ -31,13 +33,53 @@ namespace w4 {
 namespace {
 
 
+// Scales and zero points are loaded once per 64 columns (a column per lane) and moved
+// to the MFMA output layout with lane swaps; kChunks<T> such loads cover T n-tiles.
+template <int T>
+constexpr int kChunks = (T + 3) / 4;
+
 template <int MT, int T>
 struct GroupRegs {
-  u32x4 b[T];         // packed codes: 4 words (32 k) for each of the T n-tiles
-  half8_t a[MT][4];   // X fragments: MT m-tiles x 4 MFMAs
-  half_t s[T];        // scale of this lane's row in each n-tile (raw fp16; converted at use)
-  uint32_t zw[T];     // packed zero-point word holding this lane's row in each n-tile
+  u32x4 b[T];              // packed codes: 4 words (32 k) for each of the T n-tiles
+  half8_t a[MT][4];        // X fragments: MT m-tiles x 4 MFMAs
+  half_t s[T];             // dequantizing variant: scale of this lane's row in each n-tile
+  uint32_t zw[T];          // dequantizing variant: zero-point word of that row
+  uint16_t sc[kChunks<T>]; // scale bits of column n0 + 64 c + (lane % (16 T)), per chunk c
+  uint32_t zc[kChunks<T>]; // zero-point word holding that column
 };
+
+// Column (within the workgroup's 16 T) whose scale and zero point lane `lane` loads in
+// chunk c: 64 c + lane for T >= 4; for T < 4 the 16 T columns repeat over the lanes.
+template <int T>
+__device__ __forceinline__ int chunk_col(int c, int lane) {
+  return 64 * c + (lane & (16 * (T < 4 ? T : 4) - 1));
+}
+
+// v holds, in 16-lane row r of chunk c, the value of n-tile 4 c + r (rows repeat for
+// T < 4); w[t] gets n-tile t's values in every row (lane l: column 16 t + l % 16).
+// v_permlane32_swap of two copies gives rows (0,1,0,1) and (2,3,2,3); v_permlane16_swap
+// of two copies of each gives a row repeated four times in each result.
+template <int T>
+__device__ __forceinline__ void rows_to_tiles(const uint32_t (&v)[kChunks<T>], uint32_t (&w)[T]) {
+  if constexpr (T == 1) {
+    w[0] = v[0];
+  } else if constexpr (T == 2) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v[0], v[0], false, false);
+    w[0] = p[0];
+    w[1] = p[1];
+  } else {
+#pragma unroll
+    for (int c = 0; c < kChunks<T>; ++c) {
+      const auto h = __builtin_amdgcn_permlane32_swap(v[c], v[c], false, false);
+      const auto p = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+      const auto q = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+      w[4 * c] = p[0];
+      w[4 * c + 1] = p[1];
+      w[4 * c + 2] = q[0];
+      w[4 * c + 3] = q[1];
+    }
+  }
+}
 
 // Loads are branch-free so that all of them are issued back to back: out-of-range rows
 // (n >= N, m >= M) read a clamped, valid row.  Nothing needs zeroing: an MFMA output
@@ -59,13 +101,23 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
   const int64_t row = (((int64_t)g << 7) + (DQ ? 32 * slot : 0)) >> glog;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
     // tiled layout: lane l reads chunk l of the 1 KB block (16 rows x 128 k) -- row
     // l % 16 of the tile, words 4 (l / 16) .. + 3 of the group
     const int tile = min((n0 >> 4) + t, last_tile);
     r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
-    r.s[t] = scales[row * N + nc];
-    r.zw[t] = qzeros[row * nzw + (nc >> 3)];
+    if (DQ) {
+      const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
+      r.s[t] = scales[row * N + nc];
+      r.zw[t] = qzeros[row * nzw + (nc >> 3)];
+    }
+  }
+  if (!DQ) {
+#pragma unroll
+    for (int c = 0; c < kChunks<T>; ++c) {
+      const int nc = min(n0 + chunk_col<T>(c, lane), N - 1);
+      r.sc[c] = __builtin_bit_cast(uint16_t, scales[row * N + nc]);
+      r.zc[c] = qzeros[row * nzw + (nc >> 3)];
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -76,37 +128,73 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
   }
 }
 
+__device__ __forceinline__ half8_t unpack_mixed(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t e1024,
+                                                uint32_t e64) {
+  const uint32_t w8 = w >> 8;
+  u32x4 r;
+  r[0] = and_or(w, mlo, e1024);   // 1024 + q0, 1024 + q4
+  r[1] = and_or(w, mhi, e64);     //   64 + q1,   64 + q5
+  r[2] = and_or(w8, mlo, e1024);  // 1024 + q2, 1024 + q6
+  r[3] = and_or(w8, mhi, e64);    //   64 + q3,   64 + q7
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// Eight halves of X in the k order 0,4,1,5,2,6,3,7 (the order unpack_mixed produces).
+__device__ __forceinline__ half8_t permute_x(half8_t a) {
+  const u32x4 v = __builtin_bit_cast(u32x4, a);
+  u32x4 o;
+  o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // x0, x4
+  o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // x1, x5
+  o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // x2, x6
+  o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // x3, x7
+  return __builtin_bit_cast(half8_t, o);
+}
+
+// One group.  The X fragments are permuted to the k order of unpack_mixed (four
+// v_perm_b32 per fragment, shared by the T n-tiles), so each code word costs five VALU
+// operations.  Two MFMA chains against constant B operands give, per row, S_g (ones)
+// and -P_g (-1024 on even k, -64 on odd k); -P_g seeds every n-tile's chain, which then
+// holds T_g - P_g = sum_k X (q + 0) and the fold is y += s (T_g - P_g - z S_g).
 template <int MT, int T>
-__device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T], int n0, int lane,
-                                              int N) {
-  float c[T];  // 1024 + zero point of this lane's row in each n-tile
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
-    c[t] = (float)(1024u + ((r.zw[t] >> (4 * (nc & 7))) & 15u));
-  }
+__device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T],
+                                              const int (&zsh)[kChunks<T>]) {
   const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
-  float4_t ssum[MT];
+  const half8_t negmagic = {-1024, -1024, -64, -64, -1024, -1024, -64, -64};
+  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+  half8_t a[MT][4];
+  float4_t ssum[MT], negp[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     ssum[mt] = float4_t{0, 0, 0, 0};
+    negp[mt] = float4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ssum[mt] = mfma16(r.a[mt][j], ones, ssum[mt]);
+    for (int j = 0; j < 4; ++j) {
+      a[mt][j] = permute_x(r.a[mt][j]);
+      ssum[mt] = mfma16(a[mt][j], ones, ssum[mt]);
+      negp[mt] = mfma16(a[mt][j], negmagic, negp[mt]);
+    }
   }
+  // scale bits | zero point << 16 of the loaded column, moved to the MFMA layout
+  uint32_t szc[kChunks<T>], sz[T];
+#pragma unroll
+  for (int c = 0; c < kChunks<T>; ++c) szc[c] = (uint32_t)r.sc[c] | (((r.zc[c] >> zsh[c]) & 15u) << 16);
+  rows_to_tiles<T>(szc, sz);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     half8_t bv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = unpack_1024(r.b[t][j]);
+    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mlo, mhi, e1024, e64);
+    const float z = (float)((sz[t] >> 16) & 0xffu);
+    const float sc = (float)__builtin_bit_cast(half2_t, sz[t])[0];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float4_t tacc = {0, 0, 0, 0};
+      float4_t tacc = negp[mt];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tacc = mfma16(r.a[mt][j], bv[j], tacc);
+      for (int j = 0; j < 4; ++j) tacc = mfma16(a[mt][j], bv[j], tacc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float d = fmaf(-c[t], ssum[mt][i], tacc[i]);
-        yacc[mt][t][i] = fmaf((float)r.s[t], d, yacc[mt][t][i]);
+        const float d = fmaf(-z, ssum[mt][i], tacc[i]);
+        yacc[mt][t][i] = fmaf(sc, d, yacc[mt][t][i]);
       }
     }
   }
@@ -174,6 +262,9 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   // Prefetches are issued unconditionally (a group index past the range is clamped to
   // the last valid group and its data is never used): with no conditional loads in the
   // loop, the waits before each compute only cover the group being computed.
+  int zsh[kChunks<T>];  // bit offset of the loaded column's zero point in its word, per chunk
+#pragma unroll
+  for (int c = 0; c < kChunks<T>; ++c) zsh[c] = 4 * (min(n0 + chunk_col<T>(c, lane), N - 1) & 7);
   GroupRegs<MT, T> r[D];
   const int glast = gend - 1;
   const int g = gbeg + wave;
@@ -189,7 +280,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
-      else compute_group<MT, T>(r[d], yacc, n0, lane, N);
+      else compute_group<MT, T>(r[d], yacc, zsh);
       load_group<MT, T, DQ>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N,
                             K, glog);
     }
@@ -198,7 +289,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   for (int d = 0; d < D; ++d)
     if (it + d < mine) {
       if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
-      else compute_group<MT, T>(r[d], yacc, n0, lane, N);
+      else compute_group<MT, T>(r[d], yacc, zsh);
     }
 
   // Cross-wave reduction.  Element (mt, t, i) of lane l is output row
@@ -315,17 +406,6 @@ __device__ __forceinline__ void load_wstage(WStage<T>& r, const uint32_t* __rest
     r.s[t] = srow[nc];
     r.zw[t] = zrow[nc >> 3];
   }
-}
-
-__device__ __forceinline__ half8_t unpack_mixed(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t e1024,
-                                                uint32_t e64) {
-  const uint32_t w8 = w >> 8;
-  u32x4 r;
-  r[0] = and_or(w, mlo, e1024);   // 1024 + q0, 1024 + q4
-  r[1] = and_or(w, mhi, e64);     //   64 + q1,   64 + q5
-  r[2] = and_or(w8, mlo, e1024);  // 1024 + q2, 1024 + q6
-  r[3] = and_or(w8, mhi, e64);    //   64 + q3,   64 + q7
-  return __builtin_bit_cast(half8_t, r);
 }
 
 // DPP row moves (16-lane rows): quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror,
@@ -546,6 +626,20 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 
 }  // namespace
 
+// Compiled register-X variants (m-tiles, n-tiles, depth, waves); the dequantizing
+// kernels (group sizes 64, 32) are compiled for the default depth and 4 waves only.
+#define SKINNY_VARIANTS(V)                                                                                   \
+  V(1, 4, 2, 4) V(1, 2, 2, 4) V(1, 1, 4, 4) V(2, 4, 2, 4) V(2, 2, 2, 4) V(2, 1, 4, 4) V(1, 8, 2, 4)          \
+  V(1, 4, 3, 4) V(1, 2, 4, 4) V(1, 1, 8, 4) V(1, 4, 2, 8) V(1, 2, 2, 8) V(1, 8, 2, 8) V(2, 8, 2, 4)
+static int variant_key(int mt, int t, int d, int w) { return ((mt * 10 + t) * 10 + d) * 10 + w; }
+static bool skinny_variant_compiled(const SkinnyPlan& p) {
+  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves);
+#define V(MT, T, D, W) if (key == variant_key(MT, T, D, W)) return true;
+  SKINNY_VARIANTS(V)
+#undef V
+  return false;
+}
+
 // Waves per workgroup: 4.  At ~190 VGPRs two 4-wave workgroups fit per CU, so grids of
 // up to ~512 workgroups are resident at once (no second, partly idle round).
 static int skinny_waves(int) { return 4; }
@@ -562,6 +656,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   p.wk = 4;
   p.smem = 0;
   p.drain = env_int("W4_SKINNY_DRAIN", 0);
+  p.waves = 4;
   // (Very wide N with a K too long for one LDS slice would need more arrival counters
   // than the workspace holds; such shapes take the register-X kernel below.)
   constexpr int kLdsBudget = 65536 - 256;  // dynamic LDS; the split-K flag is static
@@ -571,11 +666,10 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   const bool lds_ok = M <= 16 && !(ng > lds_gmax && (N + 15) / 16 >= kMaxCounters) &&
                       (group_size == 128 || group_size == -1);
   // Default kernel and shape, from sweeps on the MI355X over the Llama-2-13B projection
-  // shapes at M = 1, 4, 16: the LDS kernel wins for M <= 4 except on narrow, short
-  // matrices (N and K <= 8192), where its X staging is not repaid, and at M = 1 with
-  // K <= 8192 and N <= 16384 (QKV); above M = 4 the register-X kernel wins (the LDS
-  // slice then limits the K range per workgroup).
-  int use_lds = lds_ok && M <= 4 && !(N <= 8192 && K <= 8192) && !(M == 1 && K <= 8192 && N <= 16384);
+  // shapes at M = 1, 4, 8, 16: the register-X kernel (one scale and one zero-point load
+  // per 64 columns, five-op unpack) wins everywhere except one row against a wide, short
+  // matrix (gate+up 5120 x 27648 at M = 1: 14.8 us against 15.0-15.4).
+  int use_lds = lds_ok && M == 1 && N > 16384 && K <= 8192;
   int t = 1, d = 4, wn = 1, wk = 4, target = 256;
   if (N > 16384) { t = 4; d = 2; }
   else if (N > 8192) { wn = 2; }
@@ -629,7 +723,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // than the extra parallelism above that, on every decode shape swept)
     const int tgt = env_int("W4_SKINNY_BLOCKS", 160);
     int sp = (tgt + rb - 1) / rb;
-    sp = min(sp, ng / waves);  // at least one group per wave
+    sp = min(sp, ng / max(waves, p.waves));  // at least one group per wave
     // keep the split-K partial traffic (2 * splits * M * N * 4 bytes) near 10% of the
     // codes (N * K / 2 bytes): splits <= K / (160 M)
     sp = min(sp, max(1, (int)((int64_t)K * pct / (1600LL * M))));
@@ -639,9 +733,8 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     return sp;
   };
   t = env_int("W4_SKINNY_TILES", 0);
-  if (t != 1 && t != 2 && t != 4) {
-    if (M <= 4) t = N > 32 * 480 ? 4 : 2;
-    else if (M <= 8) t = N > 8192 ? 4 : 2;
+  if (t != 1 && t != 2 && t != 4 && t != 8) {
+    if (M <= 8) t = N > 8192 ? 4 : 2;
     else if (M <= 16) t = (N > 8192 || K > 8192) ? 4 : 2;
     else t = ((N + 63) / 64 >= 128) ? 4 : 2;
     int rb1 = 0, rb2 = 0;
@@ -650,9 +743,25 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     while (M <= 8 && t > 1 && (N + 16 * t - 1) / (16 * t) < 160 && (N + 8 * t - 1) / (8 * t) >= 160) t /= 2;
     // 8 < M <= 16: 4 tiles share each X fragment, unless that leaves under 128 workgroups
     if (M > 8 && M <= 16 && t == 4 && plan_splits(4, rb1) * rb1 < 128 && plan_splits(2, rb2) * rb2 >= 128) t = 2;
+    // 4 < M <= 16 on wide matrices: 8 tiles halve the X loads per weight byte and still
+    // leave > 160 column blocks (gate+up 5120 x 27648 at M = 16: 20.8 -> 17.7 us)
+    if (M > 4 && M <= 16 && N > 16384) t = 8;
   }
+  if (t == 8 && (group_size == 64 || group_size == 32)) t = 4;  // (no 8-tile dequantizing kernel)
   p.tiles = t;
   p.depth = t == 1 ? 4 : 2;
+  // 8 waves for narrow workgroups at M <= 8 (more groups in flight per column block:
+  // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
+  // and for the 8-tile ones
+  p.waves = (p.mt == 1 && ((M <= 8 && t <= 2) || t == 8)) ? 8 : 4;
+  if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
+  if (group_size != 64 && group_size != 32) {
+    // variants (sweeps): prefetch depth, 8-wave workgroups
+    SkinnyPlan q = p;
+    q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
+    q.waves = env_int("W4_SKINNY_WAVES", p.waves);
+    if (skinny_variant_compiled(q)) p = q;
+  }
   int splits = plan_splits(t, p.row_blocks);
   p.gps = (ng + splits - 1) / splits;
   p.splits = (ng + p.gps - 1) / p.gps;
@@ -692,22 +801,31 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
 #undef LDS_LAUNCH1
     return hipGetLastError();
   }
-#define SKINNY_LAUNCH(MT, T, D)                                                                             \
-  if (dq)                                                                                                   \
-    hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, true>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, \
-                       counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                        \
-  else                                                                                                      \
-    hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, false>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz,    \
-                       yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog)
-#define SKINNY_LAUNCH_T(MT)                    \
-  if (p.tiles == 4) SKINNY_LAUNCH(MT, 4, 2);   \
-  else if (p.tiles == 2) SKINNY_LAUNCH(MT, 2, 2); \
-  else SKINNY_LAUNCH(MT, 1, 4)
-  if (p.mt == 1) { SKINNY_LAUNCH_T(1); }
-  else { SKINNY_LAUNCH_T(2); }
-#undef SKINNY_LAUNCH_T
-#undef SKINNY_LAUNCH
-  return hipGetLastError();
+  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves);
+  if (dq) {
+#define DQ_LAUNCH(MT, T, D)                                                                                    \
+  hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, true>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, \
+                     counters, partials, M, N, K, p.splits, p.gps, p.drain, glog)
+    switch (p.mt * 10 + p.tiles) {
+      case 14: DQ_LAUNCH(1, 4, 2); break;
+      case 12: DQ_LAUNCH(1, 2, 2); break;
+      case 11: DQ_LAUNCH(1, 1, 4); break;
+      case 24: DQ_LAUNCH(2, 4, 2); break;
+      case 22: DQ_LAUNCH(2, 2, 2); break;
+      default: DQ_LAUNCH(2, 1, 4); break;
+    }
+#undef DQ_LAUNCH
+    return hipGetLastError();
+  }
+#define V(MT, T, D, W)                                                                                       \
+  if (key == variant_key(MT, T, D, W)) {                                                                     \
+    hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false>), grid, dim3(W * kWave), 0, stream, xh, qw, sc,        \
+                       qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                 \
+    return hipGetLastError();                                                                                \
+  }
+  SKINNY_VARIANTS(V)
+#undef V
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4
