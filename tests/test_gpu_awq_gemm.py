@@ -217,6 +217,41 @@ def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("M,N,K,scale,div,expect", [
+    (640, 1000, 2048, 1, 32, 2),   # 20 tiles on 16 slots: the last 4 tiles split in two
+    (600, 520, 2048, 3, 128, 4),   # 15 tiles on 12 slots: the last 3 split 4 ways (forced); ragged M, N
+    (1400, 500, 2048, 1, 32, 2),   # 22 tiles on 16 slots: the last 6 split in two
+    (1100, 300, 4096, 1, 64, 8),   # 18 tiles on 8 slots: remainder 2 split 8 ways (forced)
+])
+def test_gemm_tail_split(M, N, K, scale, div, expect, monkeypatch):
+    """The 128x256 GEMM with the last tiles split over their BK steps (the remainder of
+    the tile count over the resident workgroups; the slot count is scaled down through
+    the tuning variables so that small shapes reach it), against the oracle; outputs
+    pre-poisoned with NaN.  The workspace size shows the tail split is active."""
+    dev = device()
+    monkeypatch.setenv("W4_GEMM_SHAPE", "1")
+    monkeypatch.setenv("W4_GEMM_MIN_TILES", "2")
+    monkeypatch.setenv("W4_GEMM_SLOTS_SCALE", str(scale))
+    monkeypatch.setenv("W4_GEMM_SLOTS_DIV", str(div))
+    monkeypatch.setenv("W4_GEMM_TAIL_PARTS", str(expect))
+    tiles = -(-M // 128) * -(-N // 256)
+    slots = 512 * scale // div
+    rem = tiles % slots
+    assert w4.awq_gemm_workspace_bytes(M, N, K) == 16384 + rem * expect * 128 * 256 * 4
+    announce(f"gemm tail split M={M} N={N} K={K} tiles={tiles} slots={slots} parts={expect}")
+    inp = synth.make_linear(M, N, K, seed=M + N, outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    for _ in range(2):  # a second call reuses the workspace (arrival counters back at zero)
+        y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+        assert np.all(np.isfinite(y)), "output not fully written"
+        yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+        err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                               np.linalg.norm(ref["w_deq"], axis=1))
+        assert err <= TOL, err
+        out.fill_(float("nan"))
+
+
 def _random_shapes(n, seed):
     rng = np.random.default_rng(seed)
     out = []

@@ -52,15 +52,35 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
                                                             half_t* __restrict__ y, unsigned* __restrict__ counters,
                                                             float* __restrict__ partials, int M, int N, int K,
                                                             int tiles_m, int tiles_n, int splits, int kps,
-                                                            int glog) {
+                                                            int glog, int n_full, int tail_splits) {
   constexpr int BM = 32 * MI, BN = 128 * NF;
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
   __shared__ u32x4 lds[2][BM * 8];
 
-  const int total = tiles_m * tiles_n * splits;
-  const int id = xcd_remap(blockIdx.x, total);
-  const int tile = id / splits;
-  const int split = id % splits;
+  const int ktiles = K / BK;
+  // Work item of this workgroup.  Uniform mode (tail_splits == 0): every tile split
+  // `splits` ways over its BK steps.  Tail mode: workgroups [0, n_full) take tiles
+  // 0 .. n_full - 1 whole, the rest take the remaining tiles split tail_splits ways; each
+  // range is remapped for the XCDs on its own, so every XCD gets the same mix.
+  int tile, split, nsplit, kpl;
+  if (tail_splits == 0) {
+    const int id = xcd_remap(blockIdx.x, tiles_m * tiles_n * splits);
+    tile = id / splits;
+    split = id % splits;
+    nsplit = splits;
+    kpl = kps;
+  } else if ((int)blockIdx.x < n_full) {
+    tile = xcd_remap(blockIdx.x, n_full);
+    split = 0;
+    nsplit = 1;
+    kpl = ktiles;
+  } else {
+    const int j = xcd_remap(blockIdx.x - n_full, gridDim.x - n_full);
+    tile = n_full + j / tail_splits;
+    split = j % tail_splits;
+    nsplit = tail_splits;
+    kpl = (ktiles + tail_splits - 1) / tail_splits;
+  }
   // grouped ordering: walk kGroupM M-tiles for each N-tile
   const int per_group = kGroupM * tiles_n;
   const int grp = tile / per_group;
@@ -71,9 +91,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   const int tn = in_grp / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int ktiles = K / BK;
-  const int kbeg = split * kps;
-  const int kend = min(ktiles, kbeg + kps);
+  const int kbeg = split * kpl;
+  const int kend = min(ktiles, kbeg + kpl);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
@@ -216,7 +235,40 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
   }
 
   // Output element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f].
-  if (splits > 1) {
+  if (tail_splits > 0 && nsplit > 1) {
+    // Tail tile j: partial sums in a compact [j][split][BM][BN] fp32 region; the last
+    // arriving workgroup adds them in split order (its own from registers: the same
+    // value it stored) and writes the tile.
+    const int j = tile - n_full;
+    float* base = partials + (int64_t)j * nsplit * BM * BN;
+    const int lc0 = wave * 32 * NF + col;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          st_coherent(base + ((int64_t)split * BM + lr) * BN + lc0 + f * 32, acc[i][f][r]);
+        }
+    if (!splitk_arrive(counters + j, nsplit)) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        float16_t sum;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            sum[r] += sp == split ? acc[i][f][r] : ld_coherent(base + ((int64_t)sp * BM + lr) * BN + lc0 + f * 32);
+          }
+        }
+        acc[i][f] = sum;
+      }
+  } else if (splits > 1) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -267,6 +319,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 // (2, 1) 64 x 128.  The plan takes the first shape that gives at least kMinTiles tiles
 // (a full wave of workgroups); split-K only when even the smallest does not.
 static const int kShapes[4][2] = {{4, 2}, {4, 1}, {2, 2}, {2, 1}};
+// Workgroups resident per CU for each shape (2 waves per SIMD at 239 VGPRs, 3 at 152 and
+// 167, 4 at 116), and the MI355X's CU count.
+static const int kResidentPerCU[4] = {2, 3, 3, 4};
+constexpr int kCUs = 256;
 
 GemmPlan gemm_plan(int M, int N, int K) {
   GemmPlan p;
@@ -305,11 +361,35 @@ GemmPlan gemm_plan(int M, int N, int K) {
   if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ktiles + splits - 1) / splits;
   p.splits = (ktiles + p.kt_per_split - 1) / p.kt_per_split;
+  // Tail split: with `slots` workgroups resident at once, tiles = q * slots + R with a
+  // small remainder R leaves the last round mostly empty (M = 4096, N = 5120: 640 tiles
+  // on 512 slots is 1.25 rounds).  The R last tiles are then split in two over their BK
+  // steps, so that the last round is shorter and spread over more CUs (measured at
+  // M = 4096: O 5120 x 5120 290 -> 262 us, down 13824 x 5120 739 -> 657 us; four parts
+  // gave 295 / 685 us, the partial sums costing more than the finer balance).
+  p.n_full = 0;
+  p.tail_splits = 0;
+  const int slots = kCUs * kResidentPerCU[pick] * env_int("W4_GEMM_SLOTS_SCALE", 1) /
+                    env_int("W4_GEMM_SLOTS_DIV", 1);
+  const int rem = tiles % slots;
+  if (p.splits == 1 && !mid && env_int("W4_GEMM_TAIL", 1) && tiles > slots && rem > 0 && 2 * rem <= slots &&
+      ktiles >= 16) {
+    const int ts = max(2, min(8, env_int("W4_GEMM_TAIL_PARTS", 2)));
+    p.n_full = tiles - rem;
+    p.tail_splits = ts;
+  }
   return p;
+}
+
+// Workspace of the tail split: counters, then [R][tail_splits][BM][BN] fp32 partials.
+static size_t tail_bytes(const GemmPlan& p) {
+  const int tiles = p.tiles_m * p.tiles_n;
+  return kCounterRegionBytes + (size_t)(tiles - p.n_full) * p.tail_splits * (32 * p.mi) * (128 * p.nf) * sizeof(float);
 }
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
   const GemmPlan p = gemm_plan(M, N, K);
+  if (p.tail_splits > 0) return tail_bytes(p);
   if (p.splits == 1) return 0;
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(float);
 }
@@ -320,11 +400,13 @@ hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales
   const int glog = group_log2(group_size);
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
-  const int blocks = p.tiles_m * p.tiles_n * p.splits;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int blocks = p.tail_splits > 0 ? p.n_full + (tiles - p.n_full) * p.tail_splits : tiles * p.splits;
 #define GEMM_LAUNCH(MI, NF)                                                                                   \
   hipLaunchKernelGGL((gemm_kernel<MI, NF>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,          \
                      (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, glog)
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, glog, p.n_full, \
+                     p.tail_splits)
   if (p.mi == 4 && p.nf == 2) GEMM_LAUNCH(4, 2);
   else if (p.mi == 4) GEMM_LAUNCH(4, 1);
   else if (p.nf == 2) GEMM_LAUNCH(2, 2);

@@ -69,6 +69,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size);
 struct GemmPlan {
   int mi, nf;  // tile = (32 mi) x (128 nf)
   int tiles_m, tiles_n, splits, kt_per_split;
+  int n_full, tail_splits;  // tail split: tiles >= n_full are split tail_splits ways (0: off)
 };
 GemmPlan gemm_plan(int M, int N, int K);
 
