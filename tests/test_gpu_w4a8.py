@@ -168,6 +168,38 @@ def test_w4a8_gemm_small(group, M, N, K):
 
 
 @pytest.mark.parametrize("group", [-1, 128])
+@pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
+def test_w4a8_gemm_tail_split(group, M, N, K, div, parts, monkeypatch):
+    """The 128-row int8 GEMM with the last tiles split over their groups (the remainder
+    of the tile count over the resident workgroups; the slot count scaled down through
+    the tuning variables so small shapes reach it): int32 accumulators bit-exact, fp16
+    outputs within 2e-3, and a second call on the same workspace."""
+    dev = device()
+    monkeypatch.setenv("W4_W4A8_SPLIT_TARGET", "1")
+    monkeypatch.setenv("W4_W4A8_TAIL", "1")
+    monkeypatch.setenv("W4_W4A8_SLOTS_DIV", str(div))
+    monkeypatch.setenv("W4_W4A8_TAIL_PARTS", str(parts))
+    tiles = -(-M // 128) * -(-N // 256)
+    rem = tiles % (512 // div)
+    assert w4.w4a8_gemm_workspace_bytes(M, N, K, group) == 16384 + rem * parts * 128 * 256 * 4
+    announce(f"w4a8 tail split M={M} N={N} K={K} group={group} tiles={tiles} parts={parts}")
+    inp = synth.make_linear(M, N, K, seed=M * 5 + N, outliers=True, rms_spread=True, with_gamma=True)
+    q, cs, gs, (qw, gsd, csd) = _oracle_w4a8(inp.w.numpy(), group, dev)
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    xqd, sad = torch.from_numpy(xq).to(dev), torch.from_numpy(sa).to(dev)
+    racc = ora.w4a8_acc_ref(xq, q, gs, 128)
+    yr = ora.w4a8_linear_ref(racc, sa, cs)
+    qs = q.astype(np.float64) * (1 if gs is None else np.repeat(gs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * cs.astype(np.float64)
+    xn = np.linalg.norm(xq.astype(np.float64), axis=1) * sa.astype(np.float64)
+    for _ in range(2):
+        acc = to_np(w4.w4a8_gemm_i32(xqd, qw, gsd, group, N=N))
+        assert np.array_equal(acc.astype(np.int64), racc)
+        y = to_np(w4.w4a8_gemm(xqd, sad, qw, gsd, csd, group)).astype(np.float64)
+        assert normalized_error(y, yr, xn, wn) <= TOL
+
+
+@pytest.mark.parametrize("group", [-1, 128])
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_w4a8_full_size_sampled(group, M):
     """C5 shapes (K = 5120, N = 13824) end to end on the GPU: pack, quant_act (RMSNorm),

@@ -85,6 +85,33 @@ def test_w8a8_skinny_variants(tiles, M, N, K, monkeypatch):
     assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
 
 
+@pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
+def test_w8a8_gemm_tail_split(M, N, K, div, parts, monkeypatch):
+    """The 128-row int8 GEMM (W8A8 weights) with the last tiles split over their groups
+    (slot count scaled down through the tuning variables): int32 accumulators bit-exact
+    and fp16 outputs within 2e-3."""
+    dev = device()
+    monkeypatch.setenv("W4_W4A8_SPLIT_TARGET", "1")
+    monkeypatch.setenv("W4_W4A8_TAIL", "1")
+    monkeypatch.setenv("W4_W4A8_SLOTS_DIV", str(div))
+    monkeypatch.setenv("W4_W4A8_TAIL_PARTS", str(parts))
+    tiles = -(-M // 128) * -(-N // 256)
+    rem = tiles % (512 // div)
+    assert w4.w8a8_gemm_workspace_bytes(M, N, K) == 16384 + rem * parts * 128 * 256 * 4
+    announce(f"w8a8 tail split M={M} N={N} K={K} tiles={tiles} parts={parts}")
+    inp = synth.make_linear(M, N, K, seed=M * 7 + N, outliers=True, rms_spread=True, with_gamma=True)
+    q, cs = ora.quantize_w8a8(inp.w.numpy())
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    xqd, sad = torch.from_numpy(xq).to(dev), torch.from_numpy(sa).to(dev)
+    qd, csd = torch.from_numpy(ora.tile_w8a8(q)).to(dev), torch.from_numpy(cs).to(dev)
+    acc = to_np(w4.w8a8_gemm_i32(xqd, qd, N))
+    assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.w8a8_gemm(xqd, sad, qd, csd, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    _check_fp16(y, xq, sa, q, cs)
+
+
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_w8a8_full_size_sampled(M):
     """K = 5120, N = 13824 end to end on the GPU: pack, quant_act (RMSNorm), GEMM;

@@ -303,22 +303,40 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
     const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
     int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
-    int K, int tiles_m, int tiles_n, int splits, int gps) {
+    int K, int tiles_m, int tiles_n, int splits, int gps, int n_full, int tail_splits) {
   constexpr int BM = 32 * MI;
   constexpr bool TWO = MODE == kI4TwoLevel;
   constexpr int NB = MODE == kI8 ? 4 : 2;  // 16-byte weight chunks per lane, fragment and group
   __shared__ u32x4 lds[2][BM * 8];
 
-  const int total = tiles_m * tiles_n * splits;
-  const int id = xcd_remap(blockIdx.x, total);
-  const int tile = id / splits;
-  const int split = id % splits;
+  const int ng = K / WBK;
+  // Work item: uniform split-K (tail_splits == 0), or tail mode -- workgroups [0, n_full)
+  // take tiles 0 .. n_full - 1 whole, the rest take the remaining tiles split
+  // tail_splits ways; each range is remapped for the XCDs on its own.
+  int tile, split, nsplit, gpl;
+  if (tail_splits == 0) {
+    const int id = xcd_remap(blockIdx.x, tiles_m * tiles_n * splits);
+    tile = id / splits;
+    split = id % splits;
+    nsplit = splits;
+    gpl = gps;
+  } else if ((int)blockIdx.x < n_full) {
+    tile = xcd_remap(blockIdx.x, n_full);
+    split = 0;
+    nsplit = 1;
+    gpl = ng;
+  } else {
+    const int j = xcd_remap(blockIdx.x - n_full, gridDim.x - n_full);
+    tile = n_full + j / tail_splits;
+    split = j % tail_splits;
+    nsplit = tail_splits;
+    gpl = (ng + tail_splits - 1) / tail_splits;
+  }
   const int tm = tile % tiles_m;
   const int tn = tile / tiles_m;
   const int m0 = tm * BM, n0 = tn * WBN;
-  const int ng = K / WBK;
-  const int gbeg = split * gps;
-  const int gend = min(ng, gbeg + gps);
+  const int gbeg = split * gpl;
+  const int gend = min(ng, gbeg + gpl);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
@@ -465,7 +483,35 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   }
 
   // element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f]
-  if (splits > 1) {
+  if (tail_splits > 0 && nsplit > 1) {
+    // Tail tile j: int32 partials in a compact [j][split][BM][WBN] region; the last
+    // arriving workgroup adds the others' to its own (exact in any order).
+    const int j = tile - n_full;
+    int32_t* base = partials + (int64_t)j * nsplit * BM * WBN;
+    const int lc0 = wave * 64 + col;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          st_coherent(base + ((int64_t)split * BM + lr) * WBN + lc0 + f * 32, acc[i][f][r]);
+        }
+    if (!splitk_arrive(counters + j, nsplit)) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        for (int sp_ = 0; sp_ < nsplit; ++sp_) {
+          if (sp_ == split) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            acc[i][f][r] += ld_coherent(base + ((int64_t)sp_ * BM + lr) * WBN + lc0 + f * 32);
+          }
+        }
+  } else if (splits > 1) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -688,6 +734,8 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   (void)group_size;
   W4A8Plan p;
   p.skinny = 0;
+  p.n_full = 0;
+  p.tail_splits = 0;
   if (M <= 16 && env_int("W4_W4A8_SKINNY", 1)) {
     const int ng = K / 128;
     // Tiles and split target from sweeps on the Llama-2-13B decode shapes (M = 1, 4, 16):
@@ -720,11 +768,27 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ng + splits - 1) / splits;
   p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
+  // Tail split (128-row tiles, two resident per CU: 512 slots on 256 CUs): a last round
+  // under half full split in two over its groups.  Off by default: at M = 4096,
+  // N = 13824 (1728 tiles = 3 rounds + 192) it measured 431 -> 464 us (per-channel),
+  // 490 -> 533 (two-level), 448 -> 440 (W8A8), unlike the fp16 GEMM.
+  p.n_full = 0;
+  p.tail_splits = 0;
+  const int slots = 512 * env_int("W4_W4A8_SLOTS_SCALE", 1) / env_int("W4_W4A8_SLOTS_DIV", 1);
+  const int rem = tiles % slots;
+  if (p.bm == 128 && p.splits == 1 && env_int("W4_W4A8_TAIL", 0) && tiles > slots && rem > 0 && 2 * rem <= slots &&
+      ng >= 8) {
+    p.n_full = tiles - rem;
+    p.tail_splits = max(2, min(8, env_int("W4_W4A8_TAIL_PARTS", 2)));
+  }
   return p;
 }
 
 size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
   const W4A8Plan p = w4a8_plan(M, N, K, group_size);
+  if (p.tail_splits > 0)
+    return kCounterRegionBytes +
+           (size_t)(p.tiles_m * p.tiles_n - p.n_full) * p.tail_splits * p.bm * WBN * sizeof(int32_t);
   if (p.splits == 1) return 0;
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(int32_t);
 }
@@ -737,7 +801,8 @@ hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const 
   const W4A8Plan p = w4a8_plan(M, N, K, group_size);
   unsigned* counters = (unsigned*)ws;
   int32_t* partials = ws ? (int32_t*)((char*)ws + kCounterRegionBytes) : nullptr;
-  const int blocks = p.tiles_m * p.tiles_n * p.splits;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int blocks = p.tail_splits > 0 ? p.n_full + (tiles - p.n_full) * p.tail_splits : tiles * p.splits;
   const dim3 grid(blocks), block(kWThreads);
   const uint32_t* qw = (const uint32_t*)qweight;
   const half_t* cs = (const half_t*)cscale;
@@ -761,7 +826,8 @@ hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const 
   }
 #define W4A8_LAUNCH(MI, MODE)                                                                                  \
   hipLaunchKernelGGL((w4a8_gemm_kernel<MI, MODE>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split)
+                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, p.n_full,  \
+                     p.tail_splits)
 #define W4A8_LAUNCH_MI(MODE)                   \
   if (mi == 1) W4A8_LAUNCH(1, MODE);           \
   else if (mi == 2) W4A8_LAUNCH(2, MODE);      \
