@@ -217,6 +217,29 @@ def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("depth", ["3", "4", "6"])
+@pytest.mark.parametrize("M,N,K,splits", [(65, 300, 640, "1"), (130, 520, 1024, "2"), (257, 1030, 2048, "4"),
+                                          (40, 129, 128, "1")])
+def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
+    """The 64x128 GEMM with 3, 4 or 6 register sets of loads in flight (rotating sets,
+    steady state plus a tail of fewer steps than sets), split and unsplit, with ragged M
+    and N and a single BK-step pair (K = 128), against the oracle."""
+    dev = device()
+    monkeypatch.setenv("W4_GEMM_SHAPE", "4")
+    monkeypatch.setenv("W4_GEMM_DEPTH", depth)
+    monkeypatch.setenv("W4_GEMM_SPLITS", splits)
+    announce(f"gemm depth={depth} M={M} N={N} K={K} splits={splits}")
+    inp = synth.make_linear(M, N, K, seed=M + N + int(depth), outliers=True, rms_spread=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("M,N,K,scale,div,expect", [
     (640, 1000, 2048, 1, 32, 2),   # 20 tiles on 16 slots: the last 4 tiles split in two
     (600, 520, 2048, 3, 128, 4),   # 15 tiles on 12 slots: the last 3 split 4 ways (forced); ragged M, N

@@ -44,7 +44,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 
 // Tile BM x BN = (32 MI) x (128 NF): wave w owns columns [32 NF w, 32 NF (w + 1)) as NF
 // 32-column fragments and all BM rows as MI 32-row fragments.
-template <int MI, int NF>
+template <int MI, int NF, int PD>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restrict__ x,
                                                             const uint32_t* __restrict__ qweight,
                                                             const half_t* __restrict__ scales,
@@ -119,139 +119,258 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  // global -> register staging of one X tile (BM x 64 halves).  Loads are branch-free
-  // so they issue back to back: rows past M read a clamped valid row (it only reaches
-  // output rows that are never stored).
-  u32x4 areg[kAPer];
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-      const int cid = threadIdx.x + i * kThreads;
-      const int r = cid >> 3, c = cid & 7;
-      const int m = min(m0 + r, M - 1);
-      areg[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + kt * BK + c * 8);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-      const int cid = threadIdx.x + i * kThreads;
-      const u32x4 v = areg[i];
-      u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching dequant_mixed
-      o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-      o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-      o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-      o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-      lds[buf][swz(cid >> 3, cid & 7)] = o;
-    }
-  };
-  u32x4 breg[NF];
-  auto load_b = [&](int kt, u32x4 (&dst)[NF]) {
-    // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-      dst[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
-  };
-  // Scale and zero point of this lane's rows for its group: the raw words are prefetched
-  // one BK step ahead together with the codes, then converted (every step, so that the
-  // loads are consumed unconditionally and stay with the prefetch) to the packed fp16
-  // pairs -(1024 + z), -(64 + z) and s, built as bit patterns: -(1024 + z) is 0xE400 | z
-  // (unit steps at 2^10), -(64 + z) is 0xD400 | 16 z (steps of 1/16 at 2^6).
-  uint32_t zraw[NF], sraw[NF];
-  const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
-  auto load_sz = [&](int kt) {
-    // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
-    const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      zraw[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
-      sraw[f] = sbits[row * N + nclamp[f]];
-    }
-  };
-  half2_t c1024[NF], c64[NF], s2[NF];
-  auto set_sz = [&]() {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const uint32_t z = (zraw[f] >> (4 * (nclamp[f] & 7))) & 15u;
-      c1024[f] = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
-      c64[f] = __builtin_bit_cast(half2_t, (0xD400u | (z << 4)) * 0x00010001u);
-      s2[f] = __builtin_bit_cast(half2_t, sraw[f] * 0x00010001u);
-    }
-  };
-  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
-
-  if (kbeg < kend) {
-    load_a(kbeg);
-    load_b(kbeg, breg);
-    load_sz(kbeg);
-    store_a(0);
-    set_sz();
-  }
-  __syncthreads();
-
-  // The next step's loads are issued unconditionally (clamped to the last step on the
-  // final iteration) so that no load sits in a conditional block and the waits before
-  // the MFMAs cover only what they consume.
-  for (int kt = kbeg; kt < kend; ++kt) {
-    const int buf = (kt - kbeg) & 1;
-    const int kn = min(kt + 1, kend - 1);
-    u32x4 bnext[NF];
-    load_a(kn);
-    load_b(kn, bnext);
-    load_sz(kn);
-    // keep these loads here, ahead of the MFMAs (the scheduler would otherwise sink them
-    // next to their use at the end of the step and expose the full memory latency)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8_t bf[NF];
-#pragma unroll
+  if constexpr (PD == 1) {
+  // PD == 1: the next step's loads are issued at the top of each step (one set of X
+  // registers, short lifetimes: the 128 x 256 tile fits two workgroups per CU).
+    // global -> register staging of one X tile (BM x 64 halves).  Loads are branch-free
+    // so they issue back to back: rows past M read a clamped valid row (it only reaches
+    // output rows that are never stored).
+    u32x4 areg[kAPer];
+    auto load_a = [&](int kt) {
+  #pragma unroll
+      for (int i = 0; i < kAPer; ++i) {
+        const int cid = threadIdx.x + i * kThreads;
+        const int r = cid >> 3, c = cid & 7;
+        const int m = min(m0 + r, M - 1);
+        areg[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + kt * BK + c * 8);
+      }
+    };
+    auto store_a = [&](int buf) {
+  #pragma unroll
+      for (int i = 0; i < kAPer; ++i) {
+        const int cid = threadIdx.x + i * kThreads;
+        const u32x4 v = areg[i];
+        u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching dequant_mixed
+        o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+        o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+        o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+        o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+        lds[buf][swz(cid >> 3, cid & 7)] = o;
+      }
+    };
+    u32x4 breg[NF];
+    auto load_b = [&](int kt, u32x4 (&dst)[NF]) {
+      // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
+  #pragma unroll
+      for (int f = 0; f < NF; ++f)
+        dst[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
+    };
+    // Scale and zero point of this lane's rows for its group: the raw words are prefetched
+    // one BK step ahead together with the codes, then converted (every step, so that the
+    // loads are consumed unconditionally and stay with the prefetch) to the packed fp16
+    // pairs -(1024 + z), -(64 + z) and s, built as bit patterns: -(1024 + z) is 0xE400 | z
+    // (unit steps at 2^10), -(64 + z) is 0xD400 | 16 z (steps of 1/16 at 2^6).
+    uint32_t zraw[NF], sraw[NF];
+    const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
+    auto load_sz = [&](int kt) {
+      // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
+      const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
+  #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const uint32_t w = breg[f][s];
-        const uint32_t w8 = w >> 8;
-        half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
-        half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
-        half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
-        half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
-        p0 = (p0 + c1024[f]) * s2[f];
-        p1 = (p1 + c64[f]) * s2[f];
-        p2 = (p2 + c1024[f]) * s2[f];
-        p3 = (p3 + c64[f]) * s2[f];
-        bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        zraw[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
+        sraw[f] = sbits[row * N + nclamp[f]];
       }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
-        const half8_t a = __builtin_bit_cast(half8_t, av);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[i][f] = mfma32(a, bf[f], acc[i][f]);
+    };
+    half2_t c1024[NF], c64[NF], s2[NF];
+    auto set_sz = [&]() {
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint32_t z = (zraw[f] >> (4 * (nclamp[f] & 7))) & 15u;
+        c1024[f] = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
+        c64[f] = __builtin_bit_cast(half2_t, (0xD400u | (z << 4)) * 0x00010001u);
+        s2[f] = __builtin_bit_cast(half2_t, sraw[f] * 0x00010001u);
       }
+    };
+    const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+
+    if (kbeg < kend) {
+      load_a(kbeg);
+      load_b(kbeg, breg);
+      load_sz(kbeg);
+      store_a(0);
+      set_sz();
     }
-    store_a(buf ^ 1);  // the other buffer was last read before the previous barrier
-#pragma unroll
-    for (int f = 0; f < NF; ++f) breg[f] = bnext[f];
-    set_sz();
     __syncthreads();
+
+    // The next step's loads are issued unconditionally (clamped to the last step on the
+    // final iteration) so that no load sits in a conditional block and the waits before
+    // the MFMAs cover only what they consume.
+    for (int kt = kbeg; kt < kend; ++kt) {
+      const int buf = (kt - kbeg) & 1;
+      const int kn = min(kt + 1, kend - 1);
+      u32x4 bnext[NF];
+      load_a(kn);
+      load_b(kn, bnext);
+      load_sz(kn);
+      // keep these loads here, ahead of the MFMAs (the scheduler would otherwise sink them
+      // next to their use at the end of the step and expose the full memory latency)
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t bf[NF];
+  #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint32_t w = breg[f][s];
+          const uint32_t w8 = w >> 8;
+          half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
+          half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
+          half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
+          half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
+          p0 = (p0 + c1024[f]) * s2[f];
+          p1 = (p1 + c64[f]) * s2[f];
+          p2 = (p2 + c1024[f]) * s2[f];
+          p3 = (p3 + c64[f]) * s2[f];
+          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+  #pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
+          const half8_t a = __builtin_bit_cast(half8_t, av);
+  #pragma unroll
+          for (int f = 0; f < NF; ++f) acc[i][f] = mfma32(a, bf[f], acc[i][f]);
+        }
+      }
+      store_a(buf ^ 1);  // the other buffer was last read before the previous barrier
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) breg[f] = bnext[f];
+      set_sz();
+      __syncthreads();
+    }
+  } else {
+  // PD >= 2: PD register sets rotate; loads run PD - 1 steps ahead of their use
+  // (small tiles at mid M, where one step of compute does not hide the latency).
+    // One BK step's loads: the X tile (BM x 64 halves, staged to LDS at the end of the
+    // previous step), this lane's weight chunks and the raw scale / zero-point words.
+    // Loads are branch-free so they issue back to back: rows past M read a clamped valid
+    // row (it only reaches output rows that are never stored).
+    struct Stage {
+      u32x4 a[kAPer];
+      u32x4 b[NF];
+      uint32_t z[NF], s[NF];
+    };
+    const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
+    auto issue = [&](int kt, Stage& S) {
+  #pragma unroll
+      for (int i = 0; i < kAPer; ++i) {
+        const int cid = threadIdx.x + i * kThreads;
+        const int r = cid >> 3, c = cid & 7;
+        const int m = min(m0 + r, M - 1);
+        S.a[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + kt * BK + c * 8);
+      }
+      // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
+  #pragma unroll
+      for (int f = 0; f < NF; ++f)
+        S.b[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
+      // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
+      const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        S.z[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
+        S.s[f] = sbits[row * N + nclamp[f]];
+      }
+    };
+    auto store_a = [&](const Stage& S, int buf) {
+  #pragma unroll
+      for (int i = 0; i < kAPer; ++i) {
+        const int cid = threadIdx.x + i * kThreads;
+        const u32x4 v = S.a[i];
+        u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching the dequantization
+        o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+        o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+        o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+        o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+        lds[buf][swz(cid >> 3, cid & 7)] = o;
+      }
+    };
+    const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+    // One BK step t on register set `cur` (B, scales, zero points) and LDS buffer
+    // (t - kbeg) & 1 (its X tile); then the X tile of step t + 1 (set `nxt`) goes to the
+    // other buffer, and after the barrier set `cur` is refilled with step t + PD's loads
+    // (clamped to the last step: no conditional loads, so every wait covers only what it
+    // consumes).  The scale and zero point become the packed fp16 pairs -(1024 + z),
+    // -(64 + z) and s, built as bit patterns: -(1024 + z) is 0xE400 | z (unit steps at
+    // 2^10), -(64 + z) is 0xD400 | 16 z (steps of 1/16 at 2^6).
+    Stage st[PD];
+    auto step = [&](int t, Stage& S, const Stage& Snext) {
+      const int buf = (t - kbeg) & 1;
+      half2_t c1024[NF], c64[NF], s2[NF];
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint32_t z = (S.z[f] >> (4 * (nclamp[f] & 7))) & 15u;
+        c1024[f] = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
+        c64[f] = __builtin_bit_cast(half2_t, (0xD400u | (z << 4)) * 0x00010001u);
+        s2[f] = __builtin_bit_cast(half2_t, S.s[f] * 0x00010001u);
+      }
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t bf[NF];
+  #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint32_t w = S.b[f][s];
+          const uint32_t w8 = w >> 8;
+          half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
+          half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
+          half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
+          half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
+          p0 = (p0 + c1024[f]) * s2[f];
+          p1 = (p1 + c64[f]) * s2[f];
+          p2 = (p2 + c1024[f]) * s2[f];
+          p3 = (p3 + c64[f]) * s2[f];
+          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+  #pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
+          const half8_t a = __builtin_bit_cast(half8_t, av);
+  #pragma unroll
+          for (int f = 0; f < NF; ++f) acc[i][f] = mfma32(a, bf[f], acc[i][f]);
+        }
+      }
+      store_a(Snext, buf ^ 1);  // the other buffer was last read before the previous barrier
+      __syncthreads();
+      issue(min(t + PD, kend - 1), S);
+    };
+
+    const int nsteps = kend - kbeg;
+    if (nsteps > 0) {
+  #pragma unroll
+      for (int d = 0; d < PD; ++d) issue(min(kbeg + d, kend - 1), st[d]);
+      store_a(st[0], 0);
+    }
+    __syncthreads();
+    int it = 0;
+    for (; it + PD <= nsteps; it += PD) {
+  #pragma unroll
+      for (int d = 0; d < PD; ++d) step(kbeg + it + d, st[d], st[(d + 1) % PD]);
+    }
+  #pragma unroll
+    for (int d = 0; d < PD; ++d)
+      if (it + d < nsteps) step(kbeg + it + d, st[d], st[(d + 1) % PD]);
   }
 
   // Output element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f].
-  if (tail_splits > 0 && nsplit > 1) {
-    // Tail tile j: partial sums in a compact [j][split][BM][BN] fp32 region; the last
-    // arriving workgroup adds them in split order (its own from registers: the same
-    // value it stored) and writes the tile.
-    const int j = tile - n_full;
-    float* base = partials + (int64_t)j * nsplit * BM * BN;
-    const int lc0 = wave * 32 * NF + col;
+  if (nsplit > 1) {
+    // Split K: every part writes its fp32 partial sums, the last arriving workgroup
+    // re-reads all of them (its own included) and adds them in split order.  Uniform
+    // mode keeps the partials as [split][M][N]; a tail tile j (tail mode) as a compact
+    // [j][split][BM][BN] region.  One code path for both (two made the compiler spill).
+    const bool tail = tail_splits > 0;
+    float* pbase = tail ? partials + (int64_t)(tile - n_full) * nsplit * BM * BN : partials + (int64_t)m0 * N + n0;
+    const int64_t ld = tail ? (int64_t)BN : (int64_t)N;
+    const int64_t sstride = tail ? (int64_t)BM * BN : (int64_t)M * N;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NF; ++f) {
+        if (!nok[f]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          st_coherent(base + ((int64_t)split * BM + lr) * BN + lc0 + f * 32, acc[i][f][r]);
+          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M) st_coherent(pbase + split * sstride + (m - m0) * ld + (nrow[f] - n0), acc[i][f][r]);
         }
-    if (!splitk_arrive(counters + j, nsplit)) return;
+      }
+    if (!splitk_arrive(counters + (tail ? tile - n_full : tile), nsplit)) return;
+    // one 16-value fragment at a time (its 16 loads in flight together)
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -262,39 +381,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
         for (int sp = 0; sp < nsplit; ++sp) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            sum[r] += sp == split ? acc[i][f][r] : ld_coherent(base + ((int64_t)sp * BM + lr) * BN + lc0 + f * 32);
-          }
-        }
-        acc[i][f] = sum;
-      }
-  } else if (splits > 1) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (!nok[f]) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
-        }
-      }
-    if (!splitk_arrive(counters + tile, splits)) return;
-    // Last workgroup: re-read every partial (its own included) and sum in split order,
-    // one 16-value fragment at a time (its 16 loads in flight together).
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        float16_t sum;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
             const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), M - 1);
-            sum[r] += ld_coherent(partials + ((int64_t)sp * M + m) * N + nclamp[f]);
+            sum[r] += ld_coherent(pbase + sp * sstride + (m - m0) * ld + (nclamp[f] - n0));
           }
         }
         acc[i][f] = sum;
@@ -323,6 +411,15 @@ static const int kShapes[4][2] = {{4, 2}, {4, 1}, {2, 2}, {2, 1}};
 // 167, 4 at 116), and the MI355X's CU count.
 static const int kResidentPerCU[4] = {2, 3, 3, 4};
 constexpr int kCUs = 256;
+// Compiled (MI, NF, prefetch depth) variants.
+#define GEMM_VARIANTS(V) \
+  V(4, 2, 1) V(4, 1, 1) V(2, 2, 1) V(2, 1, 1) V(2, 1, 3) V(2, 1, 4) V(2, 1, 6)
+static bool gemm_variant_compiled(int mi, int nf, int pd) {
+#define V(MI, NF, PD) if (mi == MI && nf == NF && pd == PD) return true;
+  GEMM_VARIANTS(V)
+#undef V
+  return false;
+}
 
 GemmPlan gemm_plan(int M, int N, int K) {
   GemmPlan p;
@@ -335,7 +432,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
   if (forced >= 1 && forced <= 4) {
     pick = forced - 1;
   } else if (mid) {
-    pick = (M >= 96 && (N >= 8192 || M >= 256)) ? 1 : 3;
+    // 64 x 128 tiles with 4 register sets in flight up to M = 256 (K = 5120, N = 13824:
+    // M = 64 30.2 -> 26.9 us, M = 128 45.2 -> 37.5, M = 256 62.7 -> 54.2 against the
+    // one-step-ahead 128 x 128 / 64 x 128 plans); 128 x 128 above
+    pick = (M > 256 && (N >= 8192 || M >= 384)) ? 1 : 3;
   } else {
     for (int i = 0; i < 4; ++i) {
       const int tm = (M + 32 * kShapes[i][0] - 1) / (32 * kShapes[i][0]);
@@ -348,6 +448,9 @@ GemmPlan gemm_plan(int M, int N, int K) {
   }
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
+  // register sets in flight (BK steps of loads ahead of the MFMAs)
+  p.depth = env_int("W4_GEMM_DEPTH", (mid && pick == 3) ? 4 : 1);
+  if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
   p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
   const int ktiles = K / BK;
@@ -402,17 +505,17 @@ hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int tiles = p.tiles_m * p.tiles_n;
   const int blocks = p.tail_splits > 0 ? p.n_full + (tiles - p.n_full) * p.tail_splits : tiles * p.splits;
-#define GEMM_LAUNCH(MI, NF)                                                                                   \
-  hipLaunchKernelGGL((gemm_kernel<MI, NF>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,          \
-                     (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, glog, p.n_full, \
-                     p.tail_splits)
-  if (p.mi == 4 && p.nf == 2) GEMM_LAUNCH(4, 2);
-  else if (p.mi == 4) GEMM_LAUNCH(4, 1);
-  else if (p.nf == 2) GEMM_LAUNCH(2, 2);
-  else GEMM_LAUNCH(2, 1);
+#define GEMM_LAUNCH(MI, NF, PD)                                                                               \
+  if (p.mi == MI && p.nf == NF && p.depth == PD) {                                                            \
+    hipLaunchKernelGGL((gemm_kernel<MI, NF, PD>), dim3(blocks), dim3(kThreads), 0, stream, (const half_t*)x,     \
+                       (const uint32_t*)qweight, (const half_t*)scales, (const uint32_t*)qzeros, (half_t*)y,   \
+                       counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, glog, p.n_full, \
+                       p.tail_splits);                                                                        \
+    return hipGetLastError();                                                                                 \
+  }
+  GEMM_VARIANTS(GEMM_LAUNCH)
 #undef GEMM_LAUNCH
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4

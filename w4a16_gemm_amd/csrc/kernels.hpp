@@ -70,6 +70,7 @@ struct GemmPlan {
   int mi, nf;  // tile = (32 mi) x (128 nf)
   int tiles_m, tiles_n, splits, kt_per_split;
   int n_full, tail_splits;  // tail split: tiles >= n_full are split tail_splits ways (0: off)
+  int depth;                // BK steps of loads in flight (register sets)
 };
 GemmPlan gemm_plan(int M, int N, int K);
 

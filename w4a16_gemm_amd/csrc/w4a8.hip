@@ -483,35 +483,15 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
   }
 
   // element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f]
-  if (tail_splits > 0 && nsplit > 1) {
-    // Tail tile j: int32 partials in a compact [j][split][BM][WBN] region; the last
-    // arriving workgroup adds the others' to its own (exact in any order).
-    const int j = tile - n_full;
-    int32_t* base = partials + (int64_t)j * nsplit * BM * WBN;
-    const int lc0 = wave * 64 + col;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          st_coherent(base + ((int64_t)split * BM + lr) * WBN + lc0 + f * 32, acc[i][f][r]);
-        }
-    if (!splitk_arrive(counters + j, nsplit)) return;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-        for (int sp_ = 0; sp_ < nsplit; ++sp_) {
-          if (sp_ == split) continue;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            acc[i][f][r] += ld_coherent(base + ((int64_t)sp_ * BM + lr) * WBN + lc0 + f * 32);
-          }
-        }
-  } else if (splits > 1) {
+  if (nsplit > 1) {
+    // Split K: every part writes its int32 partial sums, the last arriving workgroup
+    // adds the others' to its own (exact in any order).  Uniform mode keeps the partials
+    // as [split][M][N]; a tail tile j (tail mode) as a compact [j][split][BM][WBN]
+    // region.  One code path for both (two made the compiler spill).
+    const bool tail = tail_splits > 0;
+    int32_t* pbase = tail ? partials + (int64_t)(tile - n_full) * nsplit * BM * WBN : partials + (int64_t)m0 * N + n0;
+    const int64_t ld = tail ? (int64_t)WBN : (int64_t)N;
+    const int64_t sstride = tail ? (int64_t)BM * WBN : (int64_t)M * N;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -520,22 +500,21 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) st_coherent(partials + ((int64_t)split * M + m) * N + nrow[f], acc[i][f][r]);
+          if (m < M) st_coherent(pbase + split * sstride + (m - m0) * ld + (nrow[f] - n0), acc[i][f][r]);
         }
       }
-    if (!splitk_arrive(counters + tile, splits)) return;
-    // Last workgroup: add the other splits' partials to its own (integer sums are exact
-    // in any order), one 16-value fragment at a time (its loads in flight together).
+    if (!splitk_arrive(counters + (tail ? tile - n_full : tile), nsplit)) return;
+    // one 16-value fragment at a time (its loads in flight together)
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int f = 0; f < 2; ++f)
-        for (int sp_ = 0; sp_ < splits; ++sp_) {
+        for (int sp_ = 0; sp_ < nsplit; ++sp_) {
           if (sp_ == split) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), M - 1);
-            acc[i][f][r] += ld_coherent(partials + ((int64_t)sp_ * M + m) * N + nclamp[f]);
+            acc[i][f][r] += ld_coherent(pbase + sp_ * sstride + (m - m0) * ld + (nclamp[f] - n0));
           }
         }
   }
