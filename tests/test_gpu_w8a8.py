@@ -85,6 +85,25 @@ def test_w8a8_skinny_variants(tiles, M, N, K, monkeypatch):
     assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
 
 
+@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1"])
+@pytest.mark.parametrize("M,N,K,target", [(70, 300, 1280, "1"), (200, 520, 2048, "128"), (40, 129, 128, "1")])
+def test_w8a8_gemm_tiles_and_depths(bm_depth, M, N, K, target, monkeypatch):
+    """Each compiled row-tile height and prefetch depth of the int8 GEMM on W8A8
+    weights, split and unsplit, ragged shapes: int32 accumulators bit-exact."""
+    dev = device()
+    bm, depth = bm_depth.split(",")
+    monkeypatch.setenv("W4_W4A8_BM", bm)
+    monkeypatch.setenv("W4_W4A8_DEPTH", depth)
+    monkeypatch.setenv("W4_W4A8_SPLIT_TARGET", target)
+    announce(f"w8a8 bm={bm} depth={depth} M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N + int(depth), outliers=True, rms_spread=True, with_gamma=True)
+    q, cs = ora.quantize_w8a8(inp.w.numpy())
+    xq, sa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    qd = torch.from_numpy(ora.tile_w8a8(q)).to(dev)
+    acc = to_np(w4.w8a8_gemm_i32(torch.from_numpy(xq).to(dev), qd, N))
+    assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
+
+
 @pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
 def test_w8a8_gemm_tail_split(M, N, K, div, parts, monkeypatch):
     """The 128-row int8 GEMM (W8A8 weights) with the last tiles split over their groups
@@ -93,6 +112,8 @@ def test_w8a8_gemm_tail_split(M, N, K, div, parts, monkeypatch):
     dev = device()
     monkeypatch.setenv("W4_W4A8_SPLIT_TARGET", "1")
     monkeypatch.setenv("W4_W4A8_TAIL", "1")
+    monkeypatch.setenv("W4_W4A8_BM", "128")
+    monkeypatch.setenv("W4_W4A8_DEPTH", "1")
     monkeypatch.setenv("W4_W4A8_SLOTS_DIV", str(div))
     monkeypatch.setenv("W4_W4A8_TAIL_PARTS", str(parts))
     tiles = -(-M // 128) * -(-N // 256)

@@ -78,6 +78,7 @@ struct W4A8Plan {
   int tiles_m, tiles_n, splits, kt_per_split, bm;
   int skinny, tiles;        // M <= 16 skinny kernel and its 16-column tiles per workgroup
   int n_full, tail_splits;  // tail split of the tiled GEMM (0: off)
+  int depth;                // tiled GEMM: groups of loads in flight (register sets)
 };
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 

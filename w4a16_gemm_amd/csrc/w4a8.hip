@@ -298,8 +298,10 @@ constexpr int kWThreads = 256;
 __device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 __device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { return cs ? cs[n] : (half_t)1; }
 
-template <int MI, int MODE>
-__global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
+// Two workgroups per CU for the one-group-ahead loop; the deeper variants (mid M, grids
+// of a few hundred workgroups) may take a CU's whole register file.
+template <int MI, int MODE, int PD>
+__global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
     const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
     int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
@@ -410,44 +412,29 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
     }
   };
 
-  if (gbeg < gend) {
-    load_a(gbeg);
-    load_b(gbeg, breg);
-    load_sg(gbeg, sgraw);
-    store_a(0);
-  }
-  __syncthreads();
-
-  for (int g = gbeg; g < gend; ++g) {
-    const int buf = (g - gbeg) & 1;
+  // One group's MFMAs: B chunks of this lane (expanded to int8), A from LDS buffer buf.
+  auto compute = [&](const u32x4 (&bq)[2][NB], const int (&sgv)[2], int buf) {
     u16x2 sp[2], cp[2];
     if (TWO) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const int sg = sgraw[f];
+        const int sg = sgv[f];
         sp[f] = u16x2{(unsigned short)sg, (unsigned short)sg};
         cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
       }
     }
-    // next group's loads, unconditional (clamped on the last iteration; see the W4A16 GEMM)
-    const int gn = min(g + 1, gend - 1);
-    u32x4 bnext[2][NB];
-    load_a(gn);
-    load_b(gn, bnext);
-    load_sg(gn, sgraw);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       int4_t bf[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         if (MODE == kI8) {
-          const u32x4 v = breg[f][s];
+          const u32x4 v = bq[f][s];
           bf[f] = int4_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
           continue;
         }
-        const uint32_t w0 = breg[f][s >> 1][(s & 1) * 2];
-        const uint32_t w1 = breg[f][s >> 1][(s & 1) * 2 + 1];
+        const uint32_t w0 = bq[f][s >> 1][(s & 1) * 2];
+        const uint32_t w1 = bq[f][s >> 1][(s & 1) * 2 + 1];
         uint32_t a0, a1, a2, a3;
         if (TWO) {
           unpack_i4_scaled(w0, sp[f], cp[f], a0, a1);
@@ -466,12 +453,86 @@ __global__ __launch_bounds__(kWThreads, 2) void w4a8_gemm_kernel(
         for (int f = 0; f < 2; ++f) acc[i][f] = mfma32_i8(a, bf[f], acc[i][f]);
       }
     }
-    store_a(buf ^ 1);
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int c = 0; c < NB; ++c) breg[f][c] = bnext[f][c];
+  };
+
+  if constexpr (PD == 1) {
+    // the next group's loads are issued at the top of each step (one set of A registers)
+    if (gbeg < gend) {
+      load_a(gbeg);
+      load_b(gbeg, breg);
+      load_sg(gbeg, sgraw);
+      store_a(0);
+    }
     __syncthreads();
+    for (int g = gbeg; g < gend; ++g) {
+      const int buf = (g - gbeg) & 1;
+      const int sgcur[2] = {sgraw[0], sgraw[1]};
+      // next group's loads, unconditional (clamped on the last iteration; see the W4A16 GEMM)
+      const int gn = min(g + 1, gend - 1);
+      u32x4 bnext[2][NB];
+      load_a(gn);
+      load_b(gn, bnext);
+      load_sg(gn, sgraw);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
+      compute(breg, sgcur, buf);
+      store_a(buf ^ 1);
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int c = 0; c < NB; ++c) breg[f][c] = bnext[f][c];
+      __syncthreads();
+    }
+  } else {
+    // PD register sets rotate: group t's MFMAs use set t % PD, then the next group's
+    // xq chunks go to the other LDS buffer and, after the barrier, the set is refilled
+    // with group t + PD's loads (clamped: no conditional loads).
+    struct Stage {
+      u32x4 a[kPer];
+      u32x4 b[2][NB];
+      int sg[2];
+    };
+    Stage st[PD];
+    auto issue = [&](int g, Stage& S) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int cid = threadIdx.x + i * kWThreads;
+        const int r = cid >> 3, c = cid & 7;
+        const int m = min(m0 + r, M - 1);
+        S.a[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)m * K + g * WBK + c * 16);
+      }
+      load_b(g, S.b);
+      S.sg[0] = S.sg[1] = 1;
+      load_sg(g, S.sg);
+    };
+    auto store_s = [&](const Stage& S, int buf) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int cid = threadIdx.x + i * kWThreads;
+        if (cid < kChunks) lds[buf][swz8(cid >> 3, cid & 7)] = S.a[i];
+      }
+    };
+    auto step = [&](int t, Stage& S, const Stage& Snext) {
+      const int buf = (t - gbeg) & 1;
+      compute(S.b, S.sg, buf);
+      store_s(Snext, buf ^ 1);
+      __syncthreads();
+      issue(min(t + PD, gend - 1), S);
+    };
+    const int nsteps = gend - gbeg;
+    if (nsteps > 0) {
+#pragma unroll
+      for (int d = 0; d < PD; ++d) issue(min(gbeg + d, gend - 1), st[d]);
+      store_s(st[0], 0);
+    }
+    __syncthreads();
+    int it = 0;
+    for (; it + PD <= nsteps; it += PD) {
+#pragma unroll
+      for (int d = 0; d < PD; ++d) step(gbeg + it + d, st[d], st[(d + 1) % PD]);
+    }
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+      if (it + d < nsteps) step(gbeg + it + d, st[d], st[(d + 1) % PD]);
   }
   if (MODE == kI4PerChannel) {
 #pragma unroll
@@ -715,6 +776,7 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   p.skinny = 0;
   p.n_full = 0;
   p.tail_splits = 0;
+  p.depth = 1;
   if (M <= 16 && env_int("W4_W4A8_SKINNY", 1)) {
     const int ng = K / 128;
     // Tiles and split target from sweeps on the Llama-2-13B decode shapes (M = 1, 4, 16):
@@ -736,7 +798,15 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
     p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
     return p;
   }
-  p.bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+  // Row-tile height and register sets of loads in flight (1: one group ahead), from
+  // sweeps at K = 5120, N = 13824 over the three weight formats: 32-row tiles four
+  // groups deep up to M = 128 (M = 128 per-channel 54.0 -> 23.0 us), 64-row tiles four
+  // deep up to 256 (57.6 -> 34.3), 64-row tiles one ahead up to 512, 128 rows above.
+  p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
+  if (p.bm != 32 && p.bm != 64) p.bm = 128;
+  p.depth = env_int("W4_W4A8_DEPTH", M <= 256 ? 4 : 1);
+  if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4))))
+    p.depth = 1;
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + WBN - 1) / WBN;
   const int ng = K / WBK;
@@ -803,21 +873,23 @@ hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const 
 #undef W4A8_SKINNY
     return hipGetLastError();
   }
-#define W4A8_LAUNCH(MI, MODE)                                                                                  \
-  hipLaunchKernelGGL((w4a8_gemm_kernel<MI, MODE>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out,     \
-                     counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, p.n_full,  \
-                     p.tail_splits)
-#define W4A8_LAUNCH_MI(MODE)                   \
-  if (mi == 1) W4A8_LAUNCH(1, MODE);           \
-  else if (mi == 2) W4A8_LAUNCH(2, MODE);      \
-  else W4A8_LAUNCH(4, MODE)
+#define W4A8_LAUNCH(MI, MODE, PD)                                                                              \
+  if (mi == MI && p.depth == PD) {                                                                              \
+    hipLaunchKernelGGL((w4a8_gemm_kernel<MI, MODE, PD>), grid, block, 0, stream, xq, s_a, qw, gs, cs, yh, acc_out, \
+                       counters, partials, M, N, K, p.tiles_m, p.tiles_n, p.splits, p.kt_per_split, p.n_full,    \
+                       p.tail_splits);                                                                          \
+    return hipGetLastError();                                                                                   \
+  }
+#define W4A8_LAUNCH_MI(MODE) \
+  W4A8_LAUNCH(1, MODE, 1) W4A8_LAUNCH(2, MODE, 1) W4A8_LAUNCH(4, MODE, 1) W4A8_LAUNCH(1, MODE, 4) \
+  W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4)
   const int mi = p.bm / 32;
   if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); }
   else if (mode == kI8) { W4A8_LAUNCH_MI(kI8); }
   else { W4A8_LAUNCH_MI(kI4PerChannel); }
 #undef W4A8_LAUNCH_MI
 #undef W4A8_LAUNCH
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
