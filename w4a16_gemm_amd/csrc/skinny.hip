@@ -33,11 +33,6 @@ namespace w4 {
 namespace {
 
 
-// Scales and zero points are loaded once per 64 columns (a column per lane) and moved
-// to the MFMA output layout with lane swaps; kChunks<T> such loads cover T n-tiles.
-template <int T>
-constexpr int kChunks = (T + 3) / 4;
-
 template <int MT, int T>
 struct GroupRegs {
   u32x4 b[T];              // packed codes: 4 words (32 k) for each of the T n-tiles
@@ -47,39 +42,6 @@ struct GroupRegs {
   uint16_t sc[kChunks<T>]; // scale bits of column n0 + 64 c + (lane % (16 T)), per chunk c
   uint32_t zc[kChunks<T>]; // zero-point word holding that column
 };
-
-// Column (within the workgroup's 16 T) whose scale and zero point lane `lane` loads in
-// chunk c: 64 c + lane for T >= 4; for T < 4 the 16 T columns repeat over the lanes.
-template <int T>
-__device__ __forceinline__ int chunk_col(int c, int lane) {
-  return 64 * c + (lane & (16 * (T < 4 ? T : 4) - 1));
-}
-
-// v holds, in 16-lane row r of chunk c, the value of n-tile 4 c + r (rows repeat for
-// T < 4); w[t] gets n-tile t's values in every row (lane l: column 16 t + l % 16).
-// v_permlane32_swap of two copies gives rows (0,1,0,1) and (2,3,2,3); v_permlane16_swap
-// of two copies of each gives a row repeated four times in each result.
-template <int T>
-__device__ __forceinline__ void rows_to_tiles(const uint32_t (&v)[kChunks<T>], uint32_t (&w)[T]) {
-  if constexpr (T == 1) {
-    w[0] = v[0];
-  } else if constexpr (T == 2) {
-    const auto p = __builtin_amdgcn_permlane16_swap(v[0], v[0], false, false);
-    w[0] = p[0];
-    w[1] = p[1];
-  } else {
-#pragma unroll
-    for (int c = 0; c < kChunks<T>; ++c) {
-      const auto h = __builtin_amdgcn_permlane32_swap(v[c], v[c], false, false);
-      const auto p = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
-      const auto q = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
-      w[4 * c] = p[0];
-      w[4 * c + 1] = p[1];
-      w[4 * c + 2] = q[0];
-      w[4 * c + 3] = q[1];
-    }
-  }
-}
 
 // Loads are branch-free so that all of them are issued back to back: out-of-range rows
 // (n >= N, m >= M) read a clamped, valid row.  Nothing needs zeroing: an MFMA output

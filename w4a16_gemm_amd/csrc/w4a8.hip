@@ -612,7 +612,7 @@ template <int T, int MODE>
 struct W8Regs {
   u32x4 b[T][MODE == kI8 ? 2 : 1];  // codes of this lane's row and k-slot in each n-tile
   int4_t a[2];                      // xq: k = 32 slot + 16 j .. + 15, j = 0, 1
-  int32_t gsv[T];                   // group scale of this lane's row in each n-tile (two-level)
+  int32_t gsc[kChunks<T>];          // two-level: group scale of column n0 + chunk_col(c, lane)
 };
 
 template <int T, int MODE>
@@ -635,7 +635,11 @@ __device__ __forceinline__ void w8_load(W8Regs<T, MODE>& r, const int8_t* __rest
       const int tile = min((n0 >> 4) + t, last_tile);
       r.b[t][0] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
     }
-    if (MODE == kI4TwoLevel) r.gsv[t] = gscale[(int64_t)g * N + min(n0 + 16 * t + (lane & 15), N - 1)];
+  }
+  if (MODE == kI4TwoLevel) {
+    // one load per 64 columns; moved to the MFMA layout in w8_compute
+#pragma unroll
+    for (int c = 0; c < kChunks<T>; ++c) r.gsc[c] = gscale[(int64_t)g * N + min(n0 + chunk_col<T>(c, lane), N - 1)];
   }
   const int m = min(lane & 15, M - 1);
   const int4_t* src = reinterpret_cast<const int4_t*>(xq + (int64_t)m * K + g * 128 + (lane >> 4) * 32);
@@ -646,6 +650,13 @@ __device__ __forceinline__ void w8_load(W8Regs<T, MODE>& r, const int8_t* __rest
 template <int T, int MODE>
 __device__ __forceinline__ void w8_compute(const W8Regs<T, MODE>& r, int4_t (&acc)[T]) {
   constexpr bool TWO = MODE == kI4TwoLevel;
+  uint32_t gsv[T];  // group scale of this lane's column in each n-tile
+  if (TWO) {
+    uint32_t gsc[kChunks<T>];
+#pragma unroll
+    for (int c = 0; c < kChunks<T>; ++c) gsc[c] = (uint32_t)r.gsc[c];
+    rows_to_tiles<T>(gsc, gsv);
+  }
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (MODE == kI8) {
@@ -658,9 +669,9 @@ __device__ __forceinline__ void w8_compute(const W8Regs<T, MODE>& r, int4_t (&ac
     }
     u16x2 sp = {1, 1}, cp = {0, 0};
     if (TWO) {
-      const unsigned short g16 = (unsigned short)r.gsv[t];
+      const unsigned short g16 = (unsigned short)(int)gsv[t];
       sp = u16x2{g16, g16};
-      const unsigned short c16 = (unsigned short)(-8 * r.gsv[t]);
+      const unsigned short c16 = (unsigned short)(-8 * (int)gsv[t]);
       cp = u16x2{c16, c16};
     }
 #pragma unroll
