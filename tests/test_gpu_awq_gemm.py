@@ -147,7 +147,8 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8"])
+@pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",
+                                   "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (17, 96, 768), (32, 300, 640)])
 def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
     """Each compiled variant of the register-X M <= 32 kernel -- tile width, or
@@ -160,6 +161,8 @@ def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
     if rest:
         monkeypatch.setenv("W4_SKINNY_RDEPTH", rest[0])
         monkeypatch.setenv("W4_SKINNY_WAVES", rest[1])
+    if rest[2:] == ["xs"]:  # M <= 4: one X load per group, fragments formed in LDS
+        monkeypatch.setenv("W4_SKINNY_XS", "1")
     monkeypatch.setenv("W4_SKINNY_LDS", "0")
     announce(f"skinny tiles={tiles} M={M} N={N} K={K}")
     inp = synth.make_linear(M, N, K, seed=M + N + int(t), outliers=True)

@@ -48,7 +48,7 @@ struct GroupRegs {
 // row depends only on its own A row and an output column only on its own B column
 // (and scale / zero point), so clamped data only reaches outputs that are never
 // stored.
-template <int MT, int T, bool DQ>
+template <int MT, int T, bool DQ, bool XS = false>
 __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __restrict__ x,
                                            const uint32_t* __restrict__ qweight,
                                            const half_t* __restrict__ scales,
@@ -80,6 +80,12 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
       r.sc[c] = __builtin_bit_cast(uint16_t, scales[row * N + nc]);
       r.zc[c] = qzeros[row * nzw + (nc >> 3)];
     }
+  }
+  if (XS) {
+    // M <= 4: one load brings the group's X for all rows -- lane l takes 16-byte chunk
+    // l % 16 of row l / 16 (rows past M clamped); compute_group forms the fragments in LDS
+    r.a[0][0] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(lane >> 4, M - 1) * K + g * 128 + (lane & 15) * 8);
+    return;
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -117,21 +123,34 @@ __device__ __forceinline__ half8_t permute_x(half8_t a) {
 // operations.  Two MFMA chains against constant B operands give, per row, S_g (ones)
 // and -P_g (-1024 on even k, -64 on odd k); -P_g seeds every n-tile's chain, which then
 // holds T_g - P_g = sum_k X (q + 0) and the fold is y += s (T_g - P_g - z S_g).
-template <int MT, int T>
+template <int MT, int T, bool XS = false>
 __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T],
-                                              const int (&zsh)[kChunks<T>]) {
+                                              const int (&zsh)[kChunks<T>], half_t* xb = nullptr, int lane = 0) {
   const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
   const half8_t negmagic = {-1024, -1024, -64, -64, -1024, -1024, -64, -64};
   const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
   half8_t a[MT][4];
   float4_t ssum[MT], negp[MT];
+  if (XS) {
+    // The group's 4 rows x 256 bytes through this wave's 1 KB of LDS: chunk c of row q at
+    // chunk c ^ q (the 4 rows of one fragment read fall in distinct banks).  Fragment j
+    // of lane l is chunk 4 (l / 16) + j of row (l % 16) % 4 (rows 4..15 of the MFMA only
+    // reach outputs that are never stored when M <= 4).  LDS operations of one wave
+    // execute in order, so the reads see the whole wave's writes.
+    const int q = lane >> 4, c = lane & 15;
+    *reinterpret_cast<half8_t*>(xb + q * 128 + (c ^ q) * 8) = r.a[0][0];
+    const int rr = lane & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[0][j] = *reinterpret_cast<const half8_t*>(xb + rr * 128 + ((4 * q + j) ^ rr) * 8);
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     ssum[mt] = float4_t{0, 0, 0, 0};
     negp[mt] = float4_t{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[mt][j] = permute_x(r.a[mt][j]);
+      a[mt][j] = permute_x(XS ? a[mt][j] : r.a[mt][j]);
       ssum[mt] = mfma16(a[mt][j], ones, ssum[mt]);
       negp[mt] = mfma16(a[mt][j], negmagic, negp[mt]);
     }
@@ -192,7 +211,7 @@ __device__ __forceinline__ void compute_group_dq(const GroupRegs<MT, T>& r, floa
 // D register sets rotate (loop unrolled by D, no register copies), so while a wave
 // computes one group the loads of its next D groups are in flight (D * T KB per wave).
 // A workgroup owns 16 T output columns (T 16-row tiles; all its waves share them).
-template <int MT, int T, int D, int WAVES, bool DQ>
+template <int MT, int T, int D, int WAVES, bool DQ, bool XS = false>
 __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __restrict__ x,
                                                                const uint32_t* __restrict__ qweight,
                                                                const half_t* __restrict__ scales,
@@ -206,6 +225,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   constexpr int kOut = MT * 16 * kCols;   // outputs of one workgroup
   constexpr int kPer = kOut / kT;         // outputs per thread in the epilogue (MT * T)
   __shared__ float red[WAVES][MT * T * 4 * kWave];
+  __shared__ __align__(16) half_t xbuf[XS ? WAVES : 1][XS ? 512 : 8];  // M <= 4: X rows of a group
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int rb = blockIdx.x;
@@ -232,7 +252,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   const int g = gbeg + wave;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    load_group<MT, T, DQ>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K, glog);
+    load_group<MT, T, DQ, XS>(r[d], x, qweight, scales, qzeros, min(g + d * WAVES, glast), n0, lane, M, N, K, glog);
   // Steady state without conditions (the wait before each compute then covers only its
   // own register set), then the remaining < D groups; all counts are wave-uniform.
   const int mine = g < gend ? (gend - g + WAVES - 1) / WAVES : 0;
@@ -242,8 +262,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
-      else compute_group<MT, T>(r[d], yacc, zsh);
-      load_group<MT, T, DQ>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N,
+      else compute_group<MT, T, XS>(r[d], yacc, zsh, xbuf[wave], lane);
+      load_group<MT, T, DQ, XS>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N,
                             K, glog);
     }
   }
@@ -251,7 +271,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   for (int d = 0; d < D; ++d)
     if (it + d < mine) {
       if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
-      else compute_group<MT, T>(r[d], yacc, zsh);
+      else compute_group<MT, T, XS>(r[d], yacc, zsh, xbuf[wave], lane);
     }
 
   // Cross-wave reduction.  Element (mt, t, i) of lane l is output row
@@ -591,12 +611,14 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 // Compiled register-X variants (m-tiles, n-tiles, depth, waves); the dequantizing
 // kernels (group sizes 64, 32) are compiled for the default depth and 4 waves only.
 #define SKINNY_VARIANTS(V)                                                                                   \
-  V(1, 4, 2, 4) V(1, 2, 2, 4) V(1, 1, 4, 4) V(2, 4, 2, 4) V(2, 2, 2, 4) V(2, 1, 4, 4) V(1, 8, 2, 4)          \
-  V(1, 4, 3, 4) V(1, 2, 4, 4) V(1, 1, 8, 4) V(1, 4, 2, 8) V(1, 2, 2, 8) V(1, 8, 2, 8) V(2, 8, 2, 4)
-static int variant_key(int mt, int t, int d, int w) { return ((mt * 10 + t) * 10 + d) * 10 + w; }
+  V(1, 4, 2, 4, 0) V(1, 2, 2, 4, 0) V(1, 1, 4, 4, 0) V(2, 4, 2, 4, 0) V(2, 2, 2, 4, 0) V(2, 1, 4, 4, 0)          \
+  V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
+  V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
+  V(1, 4, 2, 8, 1)
+static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 10 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
-  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves);
-#define V(MT, T, D, W) if (key == variant_key(MT, T, D, W)) return true;
+  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
+#define V(MT, T, D, W, XS) if (key == variant_key(MT, T, D, W, XS)) return true;
   SKINNY_VARIANTS(V)
 #undef V
   return false;
@@ -619,6 +641,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   p.smem = 0;
   p.drain = env_int("W4_SKINNY_DRAIN", 0);
   p.waves = 4;
+  p.xs = 0;
   // (Very wide N with a K too long for one LDS slice would need more arrival counters
   // than the workspace holds; such shapes take the register-X kernel below.)
   constexpr int kLdsBudget = 65536 - 256;  // dynamic LDS; the split-K flag is static
@@ -716,12 +739,16 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
   // and for the 8-tile ones
   p.waves = (p.mt == 1 && ((M <= 8 && t <= 2) || t == 8)) ? 8 : 4;
+  p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
     // variants (sweeps): prefetch depth, 8-wave workgroups
     SkinnyPlan q = p;
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
     q.waves = env_int("W4_SKINNY_WAVES", p.waves);
+    // one X load per group (fragments formed in LDS) at 1 < M <= 4 on wide matrices:
+    // gate+up 5120 x 27648 at M = 4 15.8 -> 14.7 us; 2-5 % slower on QKV, O and down
+    q.xs = (M <= 4 && p.mt == 1) ? env_int("W4_SKINNY_XS", M > 1 && N > 16384) : 0;
     if (skinny_variant_compiled(q)) p = q;
   }
   int splits = plan_splits(t, p.row_blocks);
@@ -763,7 +790,7 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
 #undef LDS_LAUNCH1
     return hipGetLastError();
   }
-  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves);
+  const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
   if (dq) {
 #define DQ_LAUNCH(MT, T, D)                                                                                    \
   hipLaunchKernelGGL((skinny_kernel<MT, T, D, 4, true>), grid, dim3(4 * kWave), 0, stream, xh, qw, sc, qz, yh, \
@@ -779,9 +806,9 @@ hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scal
 #undef DQ_LAUNCH
     return hipGetLastError();
   }
-#define V(MT, T, D, W)                                                                                       \
-  if (key == variant_key(MT, T, D, W)) {                                                                     \
-    hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false>), grid, dim3(W * kWave), 0, stream, xh, qw, sc,        \
+#define V(MT, T, D, W, XS)                                                                                   \
+  if (key == variant_key(MT, T, D, W, XS)) {                                                                 \
+    hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, XS != 0>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, \
                        qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                 \
     return hipGetLastError();                                                                                \
   }
