@@ -721,7 +721,9 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   if (t != 1 && t != 2 && t != 4 && t != 8) {
     if (M <= 8) t = N > 8192 ? 4 : 2;
     else if (M <= 16) t = (N > 8192 || K > 8192) ? 4 : 2;
-    else t = ((N + 63) / 64 >= 128) ? 4 : 2;
+    // 16 < M <= 32 (two m-tiles): 8 tiles on wide matrices, 4 when N gives >= 128
+    // column blocks or K is long (gate+up at M = 32 31.0 -> 23.9 us, down 30.0 -> 21.0)
+    else t = N > 16384 ? 8 : (((N + 63) / 64 >= 128 || K > 8192) ? 4 : 2);
     int rb1 = 0, rb2 = 0;
     // M <= 8: narrower tiles while the column blocks alone give under 160 workgroups
     // and half the width does not
