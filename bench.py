@@ -196,6 +196,8 @@ def main():
             shape_detail[f"{name}_M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
                                             "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 3)}
 
+    copy_gbs = _copy_bandwidth(torch, dev)
+    log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write)")
     result = {
         "metric": "W4A16-g128 GEMM GB/s (M<=16) & TFLOP/s (M>=256) vs roofline, 13B shapes",
         "value": round(gbs, 2),
@@ -217,7 +219,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(avg_us, 3),
                      "algorithmic_bytes_per_launch": int(step_bytes / per_step),
-                     "traffic": profiled_traffic("skinny_decode_13b")},
+                     "traffic": profiled_traffic("skinny_decode_13b"),
+                     # context: what a plain 1 GiB device copy (torch) reaches on this part
+                     "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)},
         "per_shape": shape_detail,
     }
 
@@ -279,6 +283,25 @@ def single_workload(args, dev, torch, np, synth, w4):
     torch.cuda.synchronize()
     res["ms_per_round"] = a0.elapsed_time(a1) / args.steps
     return res
+
+
+def _copy_bandwidth(torch, dev, nbytes=1 << 30, iters=5):
+    """Read + write bytes per second of torch's device copy of nbytes (context for the
+    HBM fraction: the bandwidth a plain streaming kernel reaches here)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / iters
+    del a, b
+    return 2 * nbytes / t / 1e9
 
 
 def _time_calls(torch, calls, iters):
