@@ -719,7 +719,10 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   };
   t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4 && t != 8) {
-    if (M <= 8) t = N > 8192 ? 4 : 2;
+    // (4 < M <= 8 with long K: 4 tiles, 8 waves, split K -- down 13824 x 5120 at M = 8:
+    // 13.1 -> 11.9 us)
+    const bool longk = M > 4 && M <= 8 && K > 8192;
+    if (M <= 8) t = (N > 8192 || longk) ? 4 : 2;
     else if (M <= 16) t = (N > 8192 || K > 8192) ? 4 : 2;
     // 16 < M <= 32 (two m-tiles): 8 tiles on wide matrices, 4 when N gives >= 128
     // column blocks or K is long (gate+up at M = 32 31.0 -> 23.9 us, down 30.0 -> 21.0)
@@ -727,7 +730,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     int rb1 = 0, rb2 = 0;
     // M <= 8: narrower tiles while the column blocks alone give under 160 workgroups
     // and half the width does not
-    while (M <= 8 && t > 1 && (N + 16 * t - 1) / (16 * t) < 160 && (N + 8 * t - 1) / (8 * t) >= 160) t /= 2;
+    while (M <= 8 && !longk && t > 1 && (N + 16 * t - 1) / (16 * t) < 160 && (N + 8 * t - 1) / (8 * t) >= 160) t /= 2;
     // 8 < M <= 16: 4 tiles share each X fragment, unless that leaves under 128 workgroups
     if (M > 8 && M <= 16 && t == 4 && plan_splits(4, rb1) * rb1 < 128 && plan_splits(2, rb2) * rb2 >= 128) t = 2;
     // 4 < M <= 16 on wide matrices: 8 tiles halve the X loads per weight byte and still
@@ -740,7 +743,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   // 8 waves for narrow workgroups at M <= 8 (more groups in flight per column block:
   // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
   // and for the 8-tile ones
-  p.waves = (p.mt == 1 && ((M <= 8 && t <= 2) || t == 8)) ? 8 : 4;
+  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8)) ? 8 : 4;
   p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
