@@ -57,7 +57,7 @@ struct SkinnyPlan {
   int row_blocks;  // ceil(N / (16 tiles))
   int splits;      // split-K factor over groups
   int gps;         // groups per split
-  int lds;         // 1: M <= 16 kernel with X staged in LDS (mt == 1)
+  int lds;         // 1: the kernel with X staged in LDS (M <= 16, mt == 1)
   int wn, wk;      // LDS kernel: waves per workgroup = wn column groups x wk K-waves
   int smem;        // LDS kernel: dynamic LDS bytes per workgroup
   int drain;       // 1: wait for all loads in flight once per D groups

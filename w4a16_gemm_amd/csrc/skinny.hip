@@ -341,7 +341,9 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
 
 
 // ---------------------------------------------------------------------------------
-// M <= 16: X staged in LDS, codes unpacked in five VALU operations per word.
+// M <= 16: X staged in LDS, codes unpacked in five VALU operations per word (the plan
+// takes this kernel by default for one row against a wide, short matrix only; it is
+// kept for every M <= 16 behind its tuning variable and tested that way).
 //
 // The workgroup copies its slice of X (M rows x its K range) into LDS once; the
 // per-group register sets that are prefetched D deep then carry only what comes from
@@ -608,8 +610,9 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 
 }  // namespace
 
-// Compiled register-X variants (m-tiles, n-tiles, depth, waves); the dequantizing
-// kernels (group sizes 64, 32) are compiled for the default depth and 4 waves only.
+// Compiled register-X variants (m-tiles, n-tiles, depth, waves, one X load per group);
+// the dequantizing kernels (group sizes 64, 32) are compiled for the default depth and
+// 4 waves only.
 #define SKINNY_VARIANTS(V)                                                                                   \
   V(1, 4, 2, 4, 0) V(1, 2, 2, 4, 0) V(1, 1, 4, 4, 0) V(2, 4, 2, 4, 0) V(2, 2, 2, 4, 0) V(2, 1, 4, 4, 0)          \
   V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
