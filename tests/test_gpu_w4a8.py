@@ -29,7 +29,7 @@ NEAR_TIE = 2.5e-4
 
 
 # widths cover every launch variant: 256 threads with 1, 2, 4 and 8 vectors of 8 per
-# thread, 1024 threads with 4, and the streaming variant
+# thread, 128 threads with 5 (K = 5120), 1024 threads with 4, and the streaming variant
 @pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (7, 5120), (64, 13824), (300, 5120), (5, 20096), (2, 40064),
                                  (4096, 5120), (4096, 13824)])
 def test_quant_act_no_norm_bit_exact(M, K):
@@ -77,7 +77,8 @@ NEAR_TIE_SILU = 2.5e-4
 
 
 # widths cover every launch variant: 256 threads with 1, 2, 4 and 8 vectors per thread,
-# 1024 threads with 4 and 8, and the streaming variant; I = 8 leaves 255 threads idle
+# 128 threads with 5 (I = 5120), 1024 threads with 4 and 8, and the streaming variant;
+# I = 8 leaves 255 threads idle
 @pytest.mark.parametrize("M,I", [(1, 8), (2, 1000), (3, 2056), (64, 5120), (1, 13824), (16, 13824),
                                  (257, 13824), (5, 20000), (4, 40000), (3, 70008), (4096, 13824)])
 def test_silu_mul_quant_near_ties_only(M, I):

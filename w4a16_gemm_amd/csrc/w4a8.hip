@@ -78,10 +78,13 @@ __device__ __forceinline__ uint2 pack_codes8(const float* y, float inv) {
 
 // Launch a row kernel template K<T, R> for rows of nv vectors of 8 (R8_1024: whether
 // K<1024, 8> fits the 128 VGPRs of a 1024-thread workgroup; else such rows stream).
+// Rows of 513..640 vectors (K = 5120) take two waves of five vectors per thread: the
+// block reductions then span two waves (RMSNorm quant_act at M = 4096: 17.6 -> 15.1 us).
 #define W4_ROW_DISPATCH(KERNEL, R8_1024, nv, grid, stream, ...)                                      \
   do {                                                                                               \
     if ((nv) <= 256) hipLaunchKernelGGL((KERNEL<256, 1>), grid, dim3(256), 0, stream, __VA_ARGS__);   \
     else if ((nv) <= 512) hipLaunchKernelGGL((KERNEL<256, 2>), grid, dim3(256), 0, stream, __VA_ARGS__); \
+    else if ((nv) <= 640 && env_int("W4_ROW_T128", 1)) hipLaunchKernelGGL((KERNEL<128, 5>), grid, dim3(128), 0, stream, __VA_ARGS__); \
     else if ((nv) <= 1024) hipLaunchKernelGGL((KERNEL<256, 4>), grid, dim3(256), 0, stream, __VA_ARGS__); \
     else if ((nv) <= 2048) hipLaunchKernelGGL((KERNEL<256, 8>), grid, dim3(256), 0, stream, __VA_ARGS__); \
     else if ((nv) <= 4096) hipLaunchKernelGGL((KERNEL<1024, 4>), grid, dim3(1024), 0, stream, __VA_ARGS__); \
