@@ -702,7 +702,8 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   const int waves = skinny_waves(p.mt);
   // Tiles per workgroup: with more rows each X fragment should serve more tiles (X
   // traffic is 4 M / T bytes per weight byte); split K only below 160 column blocks.
-  // From sweeps on the Llama-2-13B projection shapes and 4096 x 4096 at M = 1 .. 16.
+  // From sweeps on the Llama-2-13B projection shapes and 4096 x 4096 at M = 1 .. 16,
+  // with enough weight copies rotated that every call streams its weights from HBM.
   const int pct = env_int("W4_SKINNY_PARTIAL_PCT", 10);
   // Split-K factor for tile width tt (row blocks of 16 tt columns in rb).
   auto plan_splits = [&](int tt, int& rb) {
@@ -726,7 +727,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // 13.1 -> 11.9 us)
     const bool longk = M > 4 && M <= 8 && K > 8192;
     if (M <= 8) t = (N > 8192 || longk) ? 4 : 2;
-    else if (M <= 16) t = (N > 8192 || K > 8192) ? 4 : 2;
+    else if (M <= 16) t = 4;  // (2 below when 4 leaves under 128 workgroups)
     // 16 < M <= 32 (two m-tiles): 8 tiles on wide matrices, 4 when N gives >= 128
     // column blocks or K is long (gate+up at M = 32 31.0 -> 23.9 us, down 30.0 -> 21.0)
     else t = N > 16384 ? 8 : (((N + 63) / 64 >= 128 || K > 8192) ? 4 : 2);
@@ -750,6 +751,10 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
+    // 4-tile, 4-wave workgroups below 16384 columns keep a third group of loads in
+    // flight (weights streamed from HBM: QKV 5120 x 15360 at M = 1-8 ~11.0 -> ~9.9 us,
+    // O 5120 x 5120 at M = 16 9.7 -> 9.2 us, down 13824 x 5120 at M = 16 15.9 -> 15.5 us)
+    if (p.mt == 1 && p.tiles == 4 && p.waves == 4 && N <= 16384) p.depth = 3;
     // variants (sweeps): prefetch depth, 8-wave workgroups
     SkinnyPlan q = p;
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
