@@ -299,7 +299,7 @@ def test_w4a8_random_shapes(group, M, N, K):
 
 
 @pytest.mark.parametrize("group", [-1, 128])
-@pytest.mark.parametrize("M", [1, 16, 256])
+@pytest.mark.parametrize("M", [1, 4, 16, 256])
 def test_down_projection_chain_full_size(group, M):
     """The W4A8 MLP tail at its real shape: fused gate+up output [M, 2 x 13824] ->
     silu_mul_quant -> down projection (K = 13824, N = 5120) on the int8 GEMM.  Codes

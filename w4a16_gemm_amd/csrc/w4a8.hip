@@ -796,9 +796,13 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
     // Tiles and split target from sweeps on the Llama-2-13B decode shapes (M = 1, 4, 16):
     // splitting K never paid once the column blocks give 160 workgroups (the int32
     // partials are M N 4 bytes per split, and their fixup costs ~1.5 us); for M > 1 wide
-    // tiles share each xq fragment between more columns.
+    // tiles share each xq fragment between more columns, except at M <= 4 on narrow
+    // matrices, where one-tile workgroups (more of them in flight) win with the weights
+    // streamed from HBM (13824 x 5120 at M = 4: g128 14.5 -> 12.1 us, per-channel
+    // 11.8 -> 11.0; 5120 x 5120: 7.3 -> 6.5, 6.3 -> 6.0).
     int t = env_int("W4_W4A8_TILES", 0);
-    if (t != 1 && t != 2 && t != 4) t = M == 1 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : (N > 8192 ? 4 : 2);
+    if (t != 1 && t != 2 && t != 4)
+      t = M == 1 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : (N > 8192 ? 4 : (M <= 4 && N <= 5120 ? 1 : 2));
     p.skinny = 1;
     p.bm = 16;
     p.tiles_m = 1;
