@@ -275,7 +275,7 @@ int w8a8_pack(const void* w, int8_t* qweight, void* cscale, int64_t M, int64_t N
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (group_size != -1 || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxKInt8)
     return 0;
-  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, -1);
+  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, 0);
 }
 
 static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const int8_t* qweight,
@@ -291,7 +291,7 @@ static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const
   } else {
     W4_TRY(check_ptrs(fn, {{"xq", xq}, {"s_a", s_a}, {"qweight", qweight}, {"cscale", cscale}, {"y", y}}));
   }
-  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, -1);
+  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, 0);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

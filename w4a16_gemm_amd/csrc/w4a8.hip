@@ -785,7 +785,6 @@ hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_
 // M <= 16 takes the skinny kernel (tiles of 16 columns per workgroup, split-K towards
 // 320 workgroups while each wave keeps a group); larger M the tiled MFMA GEMM.
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
-  (void)group_size;
   W4A8Plan p;
   p.skinny = 0;
   p.n_full = 0;
@@ -800,9 +799,13 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
     // matrices, where one-tile workgroups (more of them in flight) win with the weights
     // streamed from HBM (13824 x 5120 at M = 4: g128 14.5 -> 12.1 us, per-channel
     // 11.8 -> 11.0; 5120 x 5120: 7.3 -> 6.5, 6.3 -> 6.0).
+    // W8A8 (group_size 0: 8-bit codes, twice the bytes per tile) keeps two tiles there
+    // (13824 x 5120 at M = 1-4: 16.6-17.4 -> 14.6-15.0 us against one tile).
     int t = env_int("W4_W4A8_TILES", 0);
-    if (t != 1 && t != 2 && t != 4)
-      t = M == 1 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : (N > 8192 ? 4 : (M <= 4 && N <= 5120 ? 1 : 2));
+    if (t != 1 && t != 2 && t != 4) {
+      if (group_size == 0 && M <= 4 && N <= 5120) t = 2;
+      else t = M == 1 ? (N <= 5120 ? 1 : (N <= 16384 ? 2 : 4)) : (N > 8192 ? 4 : (M <= 4 && N <= 5120 ? 1 : 2));
+    }
     p.skinny = 1;
     p.bm = 16;
     p.tiles_m = 1;
@@ -921,7 +924,7 @@ hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* q
 
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
                             int32_t* acc_out, void* ws, int M, int N, int K, hipStream_t stream) {
-  return launch_int8_gemm(kI8, xq, s_a, qweight, nullptr, cscale, y, acc_out, ws, M, N, K, -1, stream);
+  return launch_int8_gemm(kI8, xq, s_a, qweight, nullptr, cscale, y, acc_out, ws, M, N, K, 0, stream);
 }
 
 }  // namespace w4
