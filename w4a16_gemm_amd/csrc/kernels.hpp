@@ -81,7 +81,6 @@ struct W4A8Plan {
   int n_full, tail_splits;  // tail split of the tiled GEMM (0: off)
   int depth;                // tiled GEMM: groups of loads in flight (register sets)
 };
-// group_size: -1 per-channel W4A8, 128 two-level W4A8, 0 W8A8 (8-bit codes)
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size);
 
 // W4A16 scales and zero points: every kernel reads the row of element k as

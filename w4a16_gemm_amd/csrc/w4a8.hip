@@ -784,6 +784,7 @@ hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_
 
 // M <= 16 takes the skinny kernel (tiles of 16 columns per workgroup, split-K towards
 // 320 workgroups while each wave keeps a group); larger M the tiled MFMA GEMM.
+// group_size: -1 per-channel W4A8, 128 two-level W4A8, 0 W8A8 (8-bit codes).
 W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   W4A8Plan p;
   p.skinny = 0;
