@@ -158,7 +158,9 @@ int w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, floa
  * gate_up: fp16 [M, 2K] row-major, the fused gate+up projection output, gate in columns
  * 0..K-1 and up in K..2K-1.  y = silu(gate) * up with silu(g) = g / (1 + exp(-g)), in
  * fp32 with no fp16 round trip; then the rule of w4a8_quant_act on y: xq int8 [M, K],
- * s_a fp32 [M]; a row with max|y| < 2^-64 (zero rows included) gives xq = 0, s_a = 1.
+ * s_a fp32 [M]; a row gives xq = 0, s_a = 1 only where the rule has no value: max|y| = 0,
+ * or fp32(127 / max|y|) not finite (max|y| below about 2^-121).  Tiny rows are kept
+ * (y is formed scaled by 2^64 inside the kernel), so s_a may be an fp32 subnormal.
  * K must be a positive multiple of 8 (at most 2^29); N and group_size are unused.  The
  * caller owns every buffer; all pointers are device pointers, 16-byte aligned; the call
  * is asynchronous on `stream`.  y carries about 9 units of fp32 rounding (exp and the

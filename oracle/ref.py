@@ -86,10 +86,10 @@ Readings where the pages are silent:
   weights fused into one weight): the fused gate+up output ``[M, 2I]`` holds gate
   in columns ``0..I-1`` and up in ``I..2I-1``; ``y = silu(gate) * up`` with
   ``silu(g) = g / (1 + exp(-g))``, in fp64 with no fp16 round trip, then the R6
-  quantization decision on ``fp32(y)``.  A row whose largest ``|y|`` is below
-  ``2^-64`` counts as a zero row (``xq = 0``, ``s_a = 1``): silu of a very negative
-  gate reaches the fp32 subnormal range, where ``127 / max|y|`` overflows and the
-  products lose their precision, so the rule is not meaningful there.
+  quantization decision on ``fp32(y)``, unchanged: a row is a zero row
+  (``xq = 0``, ``s_a = 1``) only when its fp32 ``max|y|`` is 0 or when
+  ``fp32(127 / max|y|)`` is not finite, i.e. ``max|y|`` below about ``2^-121``,
+  where the rule itself has no value (fp32 is normal down to ``2^-126``).
 """
 from __future__ import annotations
 
@@ -398,29 +398,29 @@ def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):
     return _quant_rows_int8(y32)
 
 
-def _quant_rows_int8(y32: np.ndarray, zero_below: float = 0.0):
+def _quant_rows_int8(y32: np.ndarray):
     """Per-row symmetric int8 quantization of fp32 values (R6): ``amax = max|y|``,
-    ``xq = clamp(rint(y * fp32(127 / amax)), -127, 127)``, ``s_a = amax / 127``; a zero
-    row (or one with ``amax < zero_below``, R12) gives ``xq = 0, s_a = 1``.  Returns
-    ``(xq, s_a, t)`` with ``t`` the fp32 values that were rounded."""
+    ``inv = fp32(127 / amax)``, ``xq = clamp(rint(fp32(y * inv)), -127, 127)``,
+    ``s_a = fp32(amax / 127)``.  A row for which the rule has no value -- ``amax == 0``,
+    or ``inv`` not finite in fp32 (``amax`` below about ``2^-121``) -- gives ``xq = 0,
+    s_a = 1``.  Returns ``(xq, s_a, t)`` with ``t`` the fp32 values that were rounded."""
     M, K = y32.shape
     amax = np.abs(y32).max(axis=1) if K else np.zeros(M, F32)
     xq = np.zeros((M, K), dtype=np.int8)
     s_a = np.ones(M, dtype=F32)
     t_all = np.zeros((M, K), dtype=F64)
     for m in range(M):
-        if amax[m] == 0 or amax[m] < zero_below:
+        if amax[m] == 0:
             continue
-        inv = F32(127.0) / amax[m]
+        with np.errstate(over="ignore"):
+            inv = F32(127.0) / amax[m]
+        if not np.isfinite(inv):
+            continue
         t = y32[m] * inv
         xq[m] = np.clip(np.rint(t), -127, 127).astype(np.int8)
         s_a[m] = amax[m] / F32(127.0)
         t_all[m] = t
     return xq, s_a, t_all
-
-
-# R12: rows whose largest |silu(g) * u| is below 2^-64 count as zero rows.
-SILU_ZERO_BELOW = 2.0 ** -64
 
 
 def silu_ref(g: np.ndarray) -> np.ndarray:
@@ -436,15 +436,15 @@ def silu_mul_quant_ref(gate_up16: np.ndarray):
     """The SiLU-gated input of the down projection quantized per token (R12): the fused
     gate+up output ``[M, 2I]`` holds gate in columns ``0..I-1`` and up in ``I..2I-1``;
     ``y = silu(gate) * up`` in fp64 (no fp16 round trip), then the per-token int8 rule
-    of :func:`_quant_rows_int8` on ``fp32(y)``; a row with ``max|y| < 2^-64`` counts as
-    a zero row.  Returns ``(xq int8 [M, I], s_a fp32 [M], t fp64 [M, I])``."""
+    of :func:`_quant_rows_int8` on ``fp32(y)``.  Returns ``(xq int8 [M, I], s_a fp32 [M],
+    t fp64 [M, I])``."""
     gu = np.asarray(gate_up16)
     if gu.dtype != F16 or gu.ndim != 2 or gu.shape[1] % 2:
         raise ValueError("gate_up16 must be a 2-D float16 array with an even number of columns")
     I = gu.shape[1] // 2
     g = gu[:, :I].astype(F64)
     u = gu[:, I:].astype(F64)
-    return _quant_rows_int8((silu_ref(g) * u).astype(F32), SILU_ZERO_BELOW)
+    return _quant_rows_int8((silu_ref(g) * u).astype(F32))
 
 
 def w4a8_acc_ref(xq: np.ndarray, q: np.ndarray, gscale_ng, group_size: int) -> np.ndarray:

@@ -351,17 +351,34 @@ def pin_silu_special_cases(ora):
     expect[17] = 127 if sv > 0 else -127
     assert np.array_equal(xo[0].astype(np.int64), expect)
     assert abs(float(so[0]) - abs(2.0 * sv) / 127) <= 1e-7 * abs(2.0 * sv) / 127
-    # |y| <= 50 e^-50 = 9.6e-21 < 2^-64 = 5.4e-20: a zero row; |y| = 45 e^-45 u, up to 1.3e-18,
-    # is above it: a live row, every code negative and the largest magnitude 127
-    lo = np.zeros((2, 2 * I), F16)
+    # Tiny rows keep the plain rule (no threshold of their own): all of a row's y share
+    # the factor silu(g) when the gate is constant, so y / max|y| = u / max|u| and the
+    # codes are -rint(127 u / max u) up to near-ties.  g = -50: max|y| = 50 e^-50 u_max
+    # ~ 1e-20 and g = -45: ~ 1.3e-18, both far above 2^-121, are live rows; g = -90 with
+    # u = 8: max|y| = 720 e^-90 ~ 5.9e-37 >= 127 / (2^128 - 2^104) ~ 3.7e-37, live, and
+    # s_a = max|y| / 127 ~ 4.6e-39 lies in the fp32 subnormal range; g = -90 with u <= 1:
+    # max|y| <= 90 e^-90 ~ 7.4e-38, where fp32(127 / max|y|) overflows: a zero row.
+    lo = np.zeros((4, 2 * I), F16)
     lo[0, :I] = -50.0
     lo[1, :I] = -45.0
-    lo[:, I:] = rng.uniform(0.5, 1.0, size=(2, I)).astype(F16)
-    lo[:, I + 3] = 1.0
+    lo[2, :I] = -90.0
+    lo[3, :I] = -90.0
+    lo[:2, I:] = rng.uniform(0.5, 1.0, size=(2, I)).astype(F16)
+    lo[:2, I + 3] = 1.0
+    lo[2, I:] = rng.uniform(4.0, 8.0, size=I).astype(F16)
+    lo[2, I + 5] = 8.0
+    lo[3, I:] = rng.uniform(0.5, 1.0, size=I).astype(F16)
+    lo[3, I + 5] = 1.0
     xl, sl, _ = ora.silu_mul_quant_ref(lo)
-    assert float(sl[0]) == 1.0 and not xl[0].any()
-    assert xl[1].max() < 0 and xl[1].min() == -127
-    assert abs(float(sl[1]) - 45 * np.exp(-45.0) / 127) <= 1e-6 * 45 * np.exp(-45.0) / 127
+    for m, gv in ((0, -50.0), (1, -45.0), (2, -90.0)):
+        u = lo[m, I:].astype(F64)
+        amax = abs(gv) / (1.0 + np.exp(-gv)) * u.max()
+        assert abs(float(sl[m]) - amax / 127) <= 1e-6 * amax / 127, (m, float(sl[m]), amax / 127)
+        target = 127.0 * u / u.max()
+        assert np.all(xl[m] < 0) and xl[m].min() == -127
+        assert np.all(np.abs(xl[m].astype(F64) + target) <= 0.5 + 1e-5)
+    assert 0.0 < float(sl[2]) < np.finfo(F32).tiny
+    assert float(sl[3]) == 1.0 and not xl[3].any()
 
 
 # ------------------------------------------------------- W4A16 variants

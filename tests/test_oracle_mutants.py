@@ -40,7 +40,8 @@ MUTANTS = [
     ("silu sigmoid of -g", "sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))", "sig = np.where(g >= 0, e / (1.0 + e), 1.0 / (1.0 + e))"),
     ("silu gate and up swapped", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "u = gu[:, :I].astype(F64)\n    g = gu[:, I:].astype(F64)"),
     ("silu gate and up interleaved", "g = gu[:, :I].astype(F64)\n    u = gu[:, I:].astype(F64)", "g = gu[:, 0::2].astype(F64)\n    u = gu[:, 1::2].astype(F64)"),
-    ("silu tiny rows quantized", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32), SILU_ZERO_BELOW)", "    return _quant_rows_int8((silu_ref(g) * u).astype(F32))"),
+    ("tiny rows zeroed below 2^-64", "        if amax[m] == 0:\n", "        if amax[m] < 2.0 ** -64:\n"),
+    ("rows with an infinite 127/amax quantized", "        if not np.isfinite(inv):\n            continue\n", ""),
     ("sym divisor 8", "s16 = np.maximum(amax / F32(7.0), F32(1e-5)).astype(F16)", "s16 = np.maximum(amax / F32(8.0), F32(1e-5)).astype(F16)"),
     ("sym max without abs", "amax = np.abs(w).max(axis=2)", "amax = w.max(axis=2)"),
     ("sym zero point 7", "codes = (q + F32(8)).reshape(N, K).astype(np.uint8)", "codes = (q + F32(7)).reshape(N, K).astype(np.uint8)"),

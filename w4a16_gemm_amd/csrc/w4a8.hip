@@ -195,35 +195,47 @@ __global__ __launch_bounds__(T) void quant_act_kernel(const half_t* __restrict__
 // ------------------------------------------------------- silu_mul_quant
 // The SiLU-gated input of the down projection, quantized per token: row m of the fused
 // gate+up output [M, 2I] holds gate in columns 0..I-1 and up in I..2I-1;
-// y = silu(g) * u = g u / (1 + exp(-g)) in fp32, then the per-token int8 rule of
-// quant_act; a row whose max|y| is below 2^-64 is a zero row (127 / max|y| would
-// overflow, and y there comes from subnormal products).
+// y = silu(g) * u = g u / (1 + exp(-g)), then the per-token int8 rule of quant_act.
+//
+// The kernel works on y' = 2^64 y: silu of a very negative gate makes y tiny (g = -90
+// gives |y| ~ 1e-37 u), and with y' the reciprocal, y' itself and the row maximum stay
+// in the fp32 normal range down to the rule's own limit (a zero row only where
+// fp32(127 / max|y|) overflows, max|y| below about 2^-121), while the large end stays
+// finite (|y'| <= 65504^2 2^64 < 2^97).  y' = g u / ((1 + exp(-g)) 2^-64), with the
+// denominator formed as 2^-64 + 2^(xh - 64) (1 + xl ln 2): a power-of-two scaling of
+// every factor, so y' carries the rounding of the unscaled formula.  Then
+// amax = 2^-64 max|y'| (exact), inv = fp32(127 / amax) and s_a = fp32(amax / 127) as
+// in quant_act, and the codes are rint(y' (2^-64 inv)) = rint(y inv).
 //
 // The kernel is arithmetic-bound unless y is cheap: per element it spends about 16 VALU
 // operations.  exp(-g) = 2^xh * 2^xl with xh = fp32(-g log2 e) and xl the rounding
 // residual of that product (exact by fma, plus the residual of the fp32 constant), and
 // 2^xl = 1 + xl ln 2 to first order (|xl| < 2^-16 wherever 2^xh is neither 0 nor inf);
-// 2^xh and the reciprocal are the 1-ulp hardware approximations.  exp(-g) = inf for very
-// negative g gives y = +-0.
-constexpr float kSiluZeroBelow = 0x1p-64f;
-
-__device__ __forceinline__ float silu_mul(float g, float u) {
+// 2^xh and the reciprocal are the 1-ulp hardware approximations.  2^(xh - 64) = inf for
+// very negative g gives y' = +-0.
+__device__ __forceinline__ float silu_mul_scaled(float g, float u) {
   constexpr float kL = 1.44269502162933349609375f;   // fp32(log2 e)
   constexpr float kLlo = 1.925963e-08f;              // log2 e - kL
   constexpr float kLn2 = 0.693147182f;
   const float xh = g * -kL;
   const float xl = fmaf(g, -kLlo, fmaf(g, -kL, -xh));
-  const float e = __builtin_amdgcn_exp2f(xh) * fmaf(xl, kLn2, 1.0f);
-  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+  const float e = __builtin_amdgcn_exp2f(xh - 64.0f) * fmaf(xl, kLn2, 1.0f);  // 2^-64 exp(-g)
+  return (g * u) * __builtin_amdgcn_rcpf(0x1p-64f + e);
 }
 
 __device__ __forceinline__ void silu_mul8(const half8_t& g, const half8_t& u, float* y) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = silu_mul((float)g[i], (float)u[i]);
+  for (int i = 0; i < 8; ++i) y[i] = silu_mul_scaled((float)g[i], (float)u[i]);
 }
 
-__device__ __forceinline__ float silu_inv(float amax) { return amax >= kSiluZeroBelow ? 127.0f / amax : 0.0f; }
-__device__ __forceinline__ float silu_scale(float amax) { return amax >= kSiluZeroBelow ? amax / 127.0f : 1.0f; }
+// From the row maximum of |y'|: the code multiplier for y' (0 for a zero row) and s_a.
+__device__ __forceinline__ float silu_row_scales(float amax_scaled, float* sa) {
+  const float amax = amax_scaled * 0x1p-64f;
+  const float inv = 127.0f / amax;
+  const bool live = amax > 0.0f && inv <= 3.40282347e38f;  // false for inf (and nan)
+  *sa = live ? amax / 127.0f : 1.0f;
+  return live ? inv * 0x1p-64f : 0.0f;
+}
 
 template <int T, int R>
 __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restrict__ gu, int8_t* __restrict__ xq,
@@ -251,8 +263,9 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[r][i]));
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = silu_inv(amax);
-      if (threadIdx.x == 0) s_a[row] = silu_scale(amax);
+      float sa;
+      const float inv = silu_row_scales(amax, &sa);
+      if (threadIdx.x == 0) s_a[row] = sa;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int j = (int)threadIdx.x + r * T;
@@ -266,8 +279,9 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
       }
       amax = block_max_t<T>(amax, red);
-      const float inv = silu_inv(amax);
-      if (threadIdx.x == 0) s_a[row] = silu_scale(amax);
+      float sa;
+      const float inv = silu_row_scales(amax, &sa);
+      if (threadIdx.x == 0) s_a[row] = sa;
       for (int j = threadIdx.x; j < nv; j += T) {
         float y[8];
         silu_mul8(g8[j], u8[j], y);
