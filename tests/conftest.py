@@ -7,6 +7,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The variant tests force kernel plans through W4_* variables, which the library reads
+# only when W4_TUNING=1 is set before its first plan (set here, before any test loads it).
+os.environ["W4_TUNING"] = "1"
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -91,19 +91,50 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _need(t, name, dtype, ndim=None, device=None):
+def _need(t, name, dtype, shape=None, ndim=None):
+    """Type, dtype, rank, shape and contiguity of one tensor argument.  Devices are
+    checked afterwards by :func:`_gpu`, so that every shape of a call is validated
+    before anything else (and before any C call)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is None and shape is not None:
+        ndim = len(shape)
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _gpu(**tensors):
+    """All given tensors (None entries skipped) on one GPU device; returns it."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev
+
+
+def _groups(K: int, group_size: int, allowed) -> int:
+    """Rows of the scale / zero-point arrays (K / G; 1 per-channel)."""
+    if group_size not in allowed:
+        raise ValueError(f"group_size={group_size} is not one of {sorted(allowed)}")
+    if K <= 0 or K % 128:
+        raise ValueError(f"K={K} must be a positive multiple of 128")
+    return 1 if group_size == -1 else K // group_size
+
+
+W4A16_GROUPS = (128, 64, 32, -1)
+W4A8_GROUPS = (128, -1)
 
 
 # Workspaces: one zero-filled buffer per (device, stream), grown on demand.  The
@@ -129,10 +160,16 @@ def qweight_shape(N: int, K: int):
     return ((N + 15) // 16, K // 128, 4, 16, 4)
 
 
-def _need_qweight(qweight, N, K, dev):
-    _need(qweight, "qweight", torch.int32, 5, dev)
-    if tuple(qweight.shape) != qweight_shape(N, K):
-        raise ValueError(f"qweight shape {tuple(qweight.shape)} != {qweight_shape(N, K)} for N={N}, K={K}")
+def _need_qweight(qweight, N, K):
+    _need(qweight, "qweight", torch.int32, qweight_shape(N, K))
+
+
+def _need_w4a16(qweight, scales, qzeros, N, K, group_size):
+    """qweight, scales [K/G, N] and qzeros [K/G, ceil(N/8)] of an N x K W4A16 matrix."""
+    ng = _groups(K, group_size, W4A16_GROUPS)
+    _need_qweight(qweight, N, K)
+    _need(scales, "scales", torch.float16, (ng, N))
+    _need(qzeros, "qzeros", torch.int32, (ng, (N + 7) // 8))
 
 
 # ------------------------------------------------------------------ W4A16
@@ -148,9 +185,10 @@ def awq_pack_sym(w: torch.Tensor, group_size: int = 128):
 
 
 def _pack_w4a16(name, w, group_size):
-    _need(w, "w", torch.float16, 2)
+    _need(w, "w", torch.float16, ndim=2)
     N, K = w.shape
-    dev = w.device
+    _groups(K, group_size, W4A16_GROUPS)
+    dev = _gpu(w=w)
     G = group_size if group_size > 0 else K
     qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
     scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
@@ -163,8 +201,8 @@ def _pack_w4a16(name, w, group_size):
 
 def w4_pack_codes(codes):
     """uint8 codes [R, C] (values 0..15) -> int32 [R, ceil(C/8)], plain nibble order."""
-    _need(codes, "codes", torch.uint8, 2)
-    dev = codes.device
+    _need(codes, "codes", torch.uint8, ndim=2)
+    dev = _gpu(codes=codes)
     R, C = codes.shape
     out = torch.empty((R, (C + 7) // 8), dtype=torch.int32, device=dev)
     with torch.cuda.device(dev):
@@ -174,12 +212,11 @@ def w4_pack_codes(codes):
 
 def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):
     """Packed weights -> fp16 W_deq [N, K] = fp16((q - z) * s)."""
-    _need(scales, "scales", torch.float16, 2)
-    dev = scales.device
-    _need(qzeros, "qzeros", torch.int32, 2, dev)
-    _need(qweight, "qweight", torch.int32, 5, dev)
+    _need(scales, "scales", torch.float16, ndim=2)
+    _need(qweight, "qweight", torch.int32, ndim=5)
     N, K = scales.shape[1], qweight.shape[1] * 128
-    _need_qweight(qweight, N, K, dev)
+    _need_w4a16(qweight, scales, qzeros, N, K, group_size)
+    dev = _gpu(qweight=qweight, scales=scales, qzeros=qzeros)
     out = torch.empty((N, K), dtype=torch.float16, device=dev)
     with torch.cuda.device(dev):
         _check("awq_unpack_dequant", load().awq_unpack_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out),
@@ -193,19 +230,18 @@ def awq_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = 128) -> i
 
 def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, workspace=None):
     """Y [M, N] = X [M, K] . dequant(W)^T  (fp16 in, fp16 out, fp32 accumulate)."""
-    _need(x, "x", torch.float16, 2)
-    dev = x.device
-    _need(scales, "scales", torch.float16, 2, dev)
-    _need(qzeros, "qzeros", torch.int32, 2, dev)
+    _need(x, "x", torch.float16, ndim=2)
+    _need(scales, "scales", torch.float16, ndim=2)
     M, K = x.shape
     N = scales.shape[1]
-    _need_qweight(qweight, N, K, dev)
+    _need_w4a16(qweight, scales, qzeros, N, K, group_size)
+    if out is not None:
+        _need(out, "out", torch.float16, (M, N))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, ndim=1)
+    dev = _gpu(x=x, qweight=qweight, scales=scales, qzeros=qzeros, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    else:
-        _need(out, "out", torch.float16, 2, dev)
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out has the wrong shape")
     lib = load()
     with torch.cuda.device(dev):
         if workspace is None:
@@ -221,9 +257,10 @@ def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, worksp
 def w4a8_pack(w: torch.Tensor, group_size: int = -1):
     """fp16 W [N, K] -> (qweight int32 [ceil(N/16), K/128, 4, 16, 4] of biased nibbles,
     gscale int8 [K/G, N] or None, cscale fp16 [N])."""
-    _need(w, "w", torch.float16, 2)
+    _need(w, "w", torch.float16, ndim=2)
     N, K = w.shape
-    dev = w.device
+    _groups(K, group_size, W4A8_GROUPS)
+    dev = _gpu(w=w)
     qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
     cscale = torch.empty((N,), dtype=torch.float16, device=dev)
     gscale = torch.empty((K // group_size, N), dtype=torch.int8, device=dev) if group_size > 0 else None
@@ -235,11 +272,11 @@ def w4a8_pack(w: torch.Tensor, group_size: int = -1):
 
 def w4a8_quant_act(x: torch.Tensor, gamma=None, eps: float = 1e-5):
     """fp16 X [M, K] (and optional RMSNorm gamma [K]) -> (xq int8 [M, K], s_a fp32 [M])."""
-    _need(x, "x", torch.float16, 2)
-    dev = x.device
-    if gamma is not None:
-        _need(gamma, "gamma", torch.float16, 1, dev)
+    _need(x, "x", torch.float16, ndim=2)
     M, K = x.shape
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float16, (K,))
+    dev = _gpu(x=x, gamma=gamma)
     xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     s_a = torch.empty((M,), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
@@ -251,11 +288,11 @@ def w4a8_quant_act(x: torch.Tensor, gamma=None, eps: float = 1e-5):
 def w4a8_silu_mul_quant(gate_up: torch.Tensor):
     """fp16 fused gate+up output [M, 2I] (gate columns first) -> (xq int8 [M, I] of
     silu(gate) * up, s_a fp32 [M])."""
-    _need(gate_up, "gate_up", torch.float16, 2)
-    dev = gate_up.device
+    _need(gate_up, "gate_up", torch.float16, ndim=2)
     M, K2 = gate_up.shape
     if K2 % 2:
         raise ValueError("gate_up must have an even number of columns")
+    dev = _gpu(gate_up=gate_up)
     xq = torch.empty((M, K2 // 2), dtype=torch.int8, device=dev)
     s_a = torch.empty((M,), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
@@ -269,20 +306,35 @@ def w4a8_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = -1) -> i
 
 
 def _w4a8_args(xq, qweight, gscale, group_size, N):
-    _need(xq, "xq", torch.int8, 2)
-    dev = xq.device
-    if gscale is not None:
-        _need(gscale, "gscale", torch.int8, 2, dev)
+    """Shapes of the integer operands: xq [M, K], tiled qweight, gscale [K/G, N] for the
+    two-level format (group_size 128) and None per-channel (-1)."""
+    _need(xq, "xq", torch.int8, ndim=2)
     M, K = xq.shape
-    _need_qweight(qweight, N, K, dev)
-    return dev, M, N, K
+    ng = _groups(K, group_size, W4A8_GROUPS)
+    _need_qweight(qweight, N, K)
+    if group_size == -1:
+        if gscale is not None:
+            raise ValueError("gscale must be None for per-channel weights (group_size -1)")
+    else:
+        if gscale is None:
+            raise ValueError("gscale is required for group_size 128")
+        _need(gscale, "gscale", torch.int8, (ng, N))
+    return M, N, K
+
+
+def _w4a8_scales(s_a, cscale, out, M, N):
+    _need(s_a, "s_a", torch.float32, (M,))
+    _need(cscale, "cscale", torch.float16, (N,))
+    if out is not None:
+        _need(out, "out", torch.float16, (M, N))
 
 
 def w4a8_gemm(xq, s_a, qweight, gscale, cscale, group_size: int = -1, out=None):
     """Y [M, N] = fp16(acc * s_a[m] * cscale[n]), acc the exact int32 sum of xq * q * s_g."""
-    _need(cscale, "cscale", torch.float16, 1)
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
-    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(cscale, "cscale", torch.float16, ndim=1)
+    M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
+    _w4a8_scales(s_a, cscale, out, M, N)
+    dev = _gpu(xq=xq, s_a=s_a, qweight=qweight, gscale=gscale, cscale=cscale, out=out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
     lib = load()
@@ -298,7 +350,8 @@ def w4a8_gemm_i32(xq, qweight, gscale, group_size: int = -1, N: int | None = Non
     give it when N is not a multiple of 16)."""
     if N is None:
         N = 16 * qweight.shape[0]
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, N)
+    M, N, K = _w4a8_args(xq, qweight, gscale, group_size, N)
+    dev = _gpu(xq=xq, qweight=qweight, gscale=gscale)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev)
     lib = load()
     with torch.cuda.device(dev):
@@ -312,16 +365,13 @@ def bind_awq_gemm(x, qweight, scales, qzeros, out, group_size: int = 128):
     """Validate once and return a zero-argument callable that enqueues awq_gemm on the
     current stream with pre-marshalled arguments (for tight launch loops: benchmarks,
     stream capture).  The workspace is allocated here, not at call time."""
-    _need(x, "x", torch.float16, 2)
-    dev = x.device
-    _need(scales, "scales", torch.float16, 2, dev)
-    _need(qzeros, "qzeros", torch.int32, 2, dev)
-    _need(out, "out", torch.float16, 2, dev)
+    _need(x, "x", torch.float16, ndim=2)
+    _need(scales, "scales", torch.float16, ndim=2)
     M, K = x.shape
     N = scales.shape[1]
-    _need_qweight(qweight, N, K, dev)
-    if tuple(out.shape) != (M, N):
-        raise ValueError("inconsistent shapes")
+    _need_w4a16(qweight, scales, qzeros, N, K, group_size)
+    _need(out, "out", torch.float16, (M, N))
+    dev = _gpu(x=x, qweight=qweight, scales=scales, qzeros=qzeros, out=out)
     lib = load()
     with torch.cuda.device(dev):
         ws, nb = _workspace(dev, lib.awq_gemm_workspace_bytes(M, N, K, group_size))
@@ -340,10 +390,12 @@ def bind_awq_gemm(x, qweight, scales, qzeros, out, group_size: int = 128):
 
 def bind_w4a8_gemm(xq, s_a, qweight, gscale, cscale, out, group_size: int = -1):
     """As bind_awq_gemm, for w4a8_gemm."""
-    _need(cscale, "cscale", torch.float16, 1)
-    dev, M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
-    _need(s_a, "s_a", torch.float32, 1, dev)
-    _need(out, "out", torch.float16, 2, dev)
+    _need(cscale, "cscale", torch.float16, ndim=1)
+    M, N, K = _w4a8_args(xq, qweight, gscale, group_size, cscale.shape[0])
+    if out is None:
+        raise ValueError("out is required")
+    _w4a8_scales(s_a, cscale, out, M, N)
+    dev = _gpu(xq=xq, s_a=s_a, qweight=qweight, gscale=gscale, cscale=cscale, out=out)
     lib = load()
     with torch.cuda.device(dev):
         ws, nb = _workspace(dev, lib.w4a8_gemm_workspace_bytes(M, N, K, group_size))
@@ -363,13 +415,13 @@ def bind_w4a8_gemm(xq, s_a, qweight, gscale, cscale, out, group_size: int = -1):
 
 def bind_w4a8_quant_act(x, gamma, xq, s_a, eps: float = 1e-5):
     """As bind_awq_gemm, for w4a8_quant_act."""
-    _need(x, "x", torch.float16, 2)
-    dev = x.device
-    if gamma is not None:
-        _need(gamma, "gamma", torch.float16, 1, dev)
-    _need(xq, "xq", torch.int8, 2, dev)
-    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(x, "x", torch.float16, ndim=2)
     M, K = x.shape
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float16, (K,))
+    _need(xq, "xq", torch.int8, (M, K))
+    _need(s_a, "s_a", torch.float32, (M,))
+    dev = _gpu(x=x, gamma=gamma, xq=xq, s_a=s_a)
     lib = load()
     with torch.cuda.device(dev):
         stream = _stream(dev)
@@ -387,13 +439,13 @@ def bind_w4a8_quant_act(x, gamma, xq, s_a, eps: float = 1e-5):
 
 def bind_w4a8_silu_mul_quant(gate_up, xq, s_a):
     """As bind_awq_gemm, for w4a8_silu_mul_quant."""
-    _need(gate_up, "gate_up", torch.float16, 2)
-    dev = gate_up.device
-    _need(xq, "xq", torch.int8, 2, dev)
-    _need(s_a, "s_a", torch.float32, 1, dev)
+    _need(gate_up, "gate_up", torch.float16, ndim=2)
     M, K2 = gate_up.shape
-    if K2 % 2 or tuple(xq.shape) != (M, K2 // 2) or tuple(s_a.shape) != (M,):
-        raise ValueError("shapes: gate_up [M, 2I], xq [M, I], s_a [M]")
+    if K2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    _need(xq, "xq", torch.int8, (M, K2 // 2))
+    _need(s_a, "s_a", torch.float32, (M,))
+    dev = _gpu(gate_up=gate_up, xq=xq, s_a=s_a)
     lib = load()
     with torch.cuda.device(dev):
         stream = _stream(dev)
@@ -418,9 +470,10 @@ def w8a8_qweight_shape(N: int, K: int):
 def w8a8_pack(w: torch.Tensor):
     """fp16 W [N, K] -> (qweight int8 tiled [ceil(N/16), K/128, 4, 2, 16, 16], cscale fp16
     [N]), per-channel."""
-    _need(w, "w", torch.float16, 2)
+    _need(w, "w", torch.float16, ndim=2)
     N, K = w.shape
-    dev = w.device
+    _groups(K, -1, (-1,))
+    dev = _gpu(w=w)
     qweight = torch.empty(w8a8_qweight_shape(N, K), dtype=torch.int8, device=dev)
     cscale = torch.empty((N,), dtype=torch.float16, device=dev)
     with torch.cuda.device(dev):
@@ -433,25 +486,21 @@ def w8a8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def _w8a8_args(xq, qweight, N):
-    _need(xq, "xq", torch.int8, 2)
-    dev = xq.device
-    _need(qweight, "qweight", torch.int8, 6, dev)
+    _need(xq, "xq", torch.int8, ndim=2)
     M, K = xq.shape
-    if tuple(qweight.shape) != w8a8_qweight_shape(N, K):
-        raise ValueError(f"qweight shape {tuple(qweight.shape)} != {w8a8_qweight_shape(N, K)} for N={N}, K={K}")
-    return dev, M, N, K
+    _groups(K, -1, (-1,))
+    _need(qweight, "qweight", torch.int8, w8a8_qweight_shape(N, K))
+    return M, N, K
 
 
 def w8a8_gemm(xq, s_a, qweight, cscale, out=None):
     """Y [M, N] = fp16(acc * s_a[m] * cscale[n]), acc = xq . qweight^T exact in int32."""
-    _need(cscale, "cscale", torch.float16, 1)
-    dev, M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
-    _need(s_a, "s_a", torch.float32, 1, dev)
-    _need(cscale, "cscale", torch.float16, 1, dev)
+    _need(cscale, "cscale", torch.float16, ndim=1)
+    M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
+    _w4a8_scales(s_a, cscale, out, M, N)
+    dev = _gpu(xq=xq, s_a=s_a, qweight=qweight, cscale=cscale, out=out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    else:
-        _need(out, "out", torch.float16, 2, dev)
     lib = load()
     with torch.cuda.device(dev):
         ws, nb = _workspace(dev, lib.w8a8_gemm_workspace_bytes(M, N, K, -1))
@@ -462,7 +511,8 @@ def w8a8_gemm(xq, s_a, qweight, cscale, out=None):
 
 def w8a8_gemm_i32(xq, qweight, N: int):
     """The raw int32 accumulators [M, N] of w8a8_gemm."""
-    dev, M, N, K = _w8a8_args(xq, qweight, N)
+    M, N, K = _w8a8_args(xq, qweight, N)
+    dev = _gpu(xq=xq, qweight=qweight)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev)
     lib = load()
     with torch.cuda.device(dev):
@@ -474,11 +524,12 @@ def w8a8_gemm_i32(xq, qweight, N: int):
 
 def bind_w8a8_gemm(xq, s_a, qweight, cscale, out):
     """As bind_awq_gemm, for w8a8_gemm."""
-    _need(cscale, "cscale", torch.float16, 1)
-    dev, M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
-    _need(s_a, "s_a", torch.float32, 1, dev)
-    _need(cscale, "cscale", torch.float16, 1, dev)
-    _need(out, "out", torch.float16, 2, dev)
+    _need(cscale, "cscale", torch.float16, ndim=1)
+    M, N, K = _w8a8_args(xq, qweight, cscale.shape[0])
+    if out is None:
+        raise ValueError("out is required")
+    _w4a8_scales(s_a, cscale, out, M, N)
+    dev = _gpu(xq=xq, s_a=s_a, qweight=qweight, cscale=cscale, out=out)
     lib = load()
     with torch.cuda.device(dev):
         ws, nb = _workspace(dev, lib.w8a8_gemm_workspace_bytes(M, N, K, -1))

@@ -106,10 +106,24 @@ int launched(const char* fn, hipError_t e) {
   return W4_OK;
 }
 
-size_t awq_ws(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+// The kernel choice and tile plan of one W4A16 call (computed once per call).
+struct AwqPlan {
+  bool skinny;
+  w4::SkinnyPlan sp;
+  w4::GemmPlan gp;
+};
+
+AwqPlan awq_plan(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  AwqPlan p{};
+  p.skinny = use_skinny(M);
+  if (p.skinny) p.sp = w4::skinny_plan((int)M, (int)N, (int)K, group_size);
+  else p.gp = w4::gemm_plan((int)M, (int)N, (int)K);
+  return p;
+}
+
+size_t awq_ws(const AwqPlan& p, int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
-  return use_skinny(M) ? w4::skinny_workspace_bytes((int)M, (int)N, (int)K, group_size)
-                       : w4::gemm_workspace_bytes((int)M, (int)N, (int)K);
+  return p.skinny ? w4::skinny_workspace_bytes(p.sp, (int)M, (int)N) : w4::gemm_workspace_bytes(p.gp, (int)M, (int)N);
 }
 
 #define W4_TRY(expr)          \
@@ -122,6 +136,11 @@ size_t awq_ws(int64_t M, int64_t N, int64_t K, int32_t group_size) {
 
 namespace w4 {
 int env_int(const char* name, int dflt) {
+  static const bool tuning = [] {
+    const char* t = std::getenv("W4_TUNING");
+    return t != nullptr && std::strcmp(t, "1") == 0;
+  }();
+  if (!tuning) return dflt;
   const char* v = std::getenv(name);
   if (v == nullptr || *v == 0) return dflt;
   char* end = nullptr;
@@ -184,7 +203,7 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
   if (!group_ok_w4a16(group_size) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
       K > kMaxDim)
     return 0;
-  return awq_ws(M, N, K, group_size);
+  return awq_ws(awq_plan(M, N, K, group_size), M, N);
 }
 
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros, void* y,
@@ -196,7 +215,8 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   W4_TRY(check_mnk(fn, M, N, K));
   if (M == 0 || N == 0) return W4_OK;
   W4_TRY(check_ptrs(fn, {{"x", x}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"y", y}}));
-  const size_t need = awq_ws(M, N, K, group_size);
+  const AwqPlan plan = awq_plan(M, N, K, group_size);
+  const size_t need = awq_ws(plan, M, N);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -205,11 +225,11 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   }
   W4_TRY(check_device(fn));
   hipError_t e;
-  if (use_skinny(M))
-    e = w4::launch_skinny(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
+  if (plan.skinny)
+    e = w4::launch_skinny(plan.sp, x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
                           (hipStream_t)stream);
   else
-    e = w4::launch_gemm(x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
+    e = w4::launch_gemm(plan.gp, x, qweight, scales, qzeros, y, workspace, (int)M, (int)N, (int)K, group_size,
                         (hipStream_t)stream);
   return launched(fn, e);
 }
@@ -275,7 +295,7 @@ int w8a8_pack(const void* w, int8_t* qweight, void* cscale, int64_t M, int64_t N
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (group_size != -1 || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxKInt8)
     return 0;
-  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, 0);
+  return w4::w4a8_workspace_bytes(w4::w4a8_plan((int)M, (int)N, (int)K, 0), (int)M, (int)N);
 }
 
 static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const int8_t* qweight,
@@ -291,7 +311,8 @@ static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const
   } else {
     W4_TRY(check_ptrs(fn, {{"xq", xq}, {"s_a", s_a}, {"qweight", qweight}, {"cscale", cscale}, {"y", y}}));
   }
-  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, 0);
+  const w4::W4A8Plan plan = w4::w4a8_plan((int)M, (int)N, (int)K, 0);
+  const size_t need = w4::w4a8_workspace_bytes(plan, (int)M, (int)N);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -299,8 +320,8 @@ static int w8a8_common(const char* fn, const int8_t* xq, const float* s_a, const
     if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   }
   W4_TRY(check_device(fn));
-  return launched(fn, w4::launch_w8a8_gemm(xq, s_a, qweight, cscale, y, acc, workspace, (int)M, (int)N, (int)K,
-                                           (hipStream_t)stream));
+  return launched(fn, w4::launch_w8a8_gemm(plan, xq, s_a, qweight, cscale, y, acc, workspace, (int)M, (int)N,
+                                           (int)K, (hipStream_t)stream));
 }
 
 int w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
@@ -320,7 +341,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_
   if ((group_size != 128 && group_size != -1) || M <= 0 || N <= 0 || K <= 0 || K % 128 || M > kMaxDim ||
       N > kMaxDim || K > kMaxKInt8)
     return 0;
-  return w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, group_size);
+  return w4::w4a8_workspace_bytes(w4::w4a8_plan((int)M, (int)N, (int)K, group_size), (int)M, (int)N);
 }
 
 static int w4a8_common(const char* fn, const int8_t* xq, const float* s_a, const int32_t* qweight,
@@ -339,7 +360,8 @@ static int w4a8_common(const char* fn, const int8_t* xq, const float* s_a, const
   }
   if (group_size == 128 && gscale == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale is NULL", fn);
   if (group_size == -1 && gscale != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: gscale must be NULL for group_size=-1", fn);
-  const size_t need = w4::w4a8_workspace_bytes((int)M, (int)N, (int)K, group_size);
+  const w4::W4A8Plan plan = w4::w4a8_plan((int)M, (int)N, (int)K, group_size);
+  const size_t need = w4::w4a8_workspace_bytes(plan, (int)M, (int)N);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -347,8 +369,8 @@ static int w4a8_common(const char* fn, const int8_t* xq, const float* s_a, const
     if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   }
   W4_TRY(check_device(fn));
-  return launched(fn, w4::launch_w4a8_gemm(xq, s_a, qweight, gscale, cscale, y, acc, workspace, (int)M, (int)N,
-                                           (int)K, group_size, (hipStream_t)stream));
+  return launched(fn, w4::launch_w4a8_gemm(plan, xq, s_a, qweight, gscale, cscale, y, acc, workspace, (int)M,
+                                           (int)N, (int)K, group_size, (hipStream_t)stream));
 }
 
 int w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale, const void* cscale,

@@ -490,16 +490,15 @@ static size_t tail_bytes(const GemmPlan& p) {
   return kCounterRegionBytes + (size_t)(tiles - p.n_full) * p.tail_splits * (32 * p.mi) * (128 * p.nf) * sizeof(float);
 }
 
-size_t gemm_workspace_bytes(int M, int N, int K) {
-  const GemmPlan p = gemm_plan(M, N, K);
+size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N) {
   if (p.tail_splits > 0) return tail_bytes(p);
   if (p.splits == 1) return 0;
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(float);
 }
 
-hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                       void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
-  const GemmPlan p = gemm_plan(M, N, K);
+hipError_t launch_gemm(const GemmPlan& p, const void* x, const int32_t* qweight, const void* scales,
+                       const int32_t* qzeros, void* y, void* ws, int M, int N, int K, int group_size,
+                       hipStream_t stream) {
   const int glog = group_log2(group_size);
   unsigned* counters = (unsigned*)ws;
   float* partials = ws ? (float*)((char*)ws + kCounterRegionBytes) : nullptr;

@@ -46,7 +46,10 @@ __device__ __forceinline__ bool splitk_arrive(unsigned* counter, int splits) {
 constexpr int kMaxCounters = 4096;
 constexpr size_t kCounterRegionBytes = kMaxCounters * sizeof(unsigned);
 
-// Host-side tuning knob: integer environment variable, or `dflt` when unset.
+// Host-side tuning knob for sweeps and the variant tests.  Only when the environment
+// holds W4_TUNING=1 at the library's first plan does the integer variable `name`
+// override `dflt`; otherwise every plan takes its built-in defaults and reads no
+// environment variable.
 int env_int(const char* name, int dflt);
 
 // Tile plan of the skinny (M <= 32) W4A16 kernel.
@@ -97,21 +100,25 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
                             int two_level, hipStream_t stream);
 
-size_t skinny_workspace_bytes(int M, int N, int K, int group_size);
-hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                         void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream);
+// Every GEMM entry point plans once per call: the plan sizes the workspace and is then
+// handed to the launcher.
+size_t skinny_workspace_bytes(const SkinnyPlan& p, int M, int N);
+hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const int32_t* qweight, const void* scales,
+                         const int32_t* qzeros, void* y, void* ws, int M, int N, int K, int group_size,
+                         hipStream_t stream);
 
-size_t gemm_workspace_bytes(int M, int N, int K);
-hipError_t launch_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                       void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream);
+size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N);
+hipError_t launch_gemm(const GemmPlan& p, const void* x, const int32_t* qweight, const void* scales,
+                       const int32_t* qzeros, void* y, void* ws, int M, int N, int K, int group_size,
+                       hipStream_t stream);
 
 hipError_t launch_w4a8_quant_act(const void* x, const void* gamma, float eps, int8_t* xq, float* s_a, int M,
                                  int K, hipStream_t stream);
 hipError_t launch_w4a8_silu_mul_quant(const void* gate_up, int8_t* xq, float* s_a, int M, int I,
                                       hipStream_t stream);
 
-size_t w4a8_workspace_bytes(int M, int N, int K, int group_size);
-hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
+size_t w4a8_workspace_bytes(const W4A8Plan& p, int M, int N);
+hipError_t launch_w4a8_gemm(const W4A8Plan& p, const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
                             const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
                             int group_size, hipStream_t stream);
 // Byte offset of the 16-byte chunk kc (k = 128 g + 16 kc .. + 15) of row n in the tiled
@@ -122,7 +129,7 @@ __device__ __forceinline__ int64_t tiled8_offset(int n, int g, int kc, int ng) {
 }
 
 // W8A8: tiled int8 weights with per-channel scales, on the W4A8 kernels.
-hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
+hipError_t launch_w8a8_gemm(const W4A8Plan& p, const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
                             int32_t* acc_out, void* ws, int M, int N, int K, hipStream_t stream);
 hipError_t launch_w8a8_pack(const void* w, int8_t* qweight, void* cscale, int N, int K, hipStream_t stream);
 

@@ -770,15 +770,14 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   return p;
 }
 
-size_t skinny_workspace_bytes(int M, int N, int K, int group_size) {
-  const SkinnyPlan p = skinny_plan(M, N, K, group_size);
+size_t skinny_workspace_bytes(const SkinnyPlan& p, int M, int N) {
   if (p.splits == 1) return 0;
   return kCounterRegionBytes + (size_t)p.splits * M * N * sizeof(float);
 }
 
-hipError_t launch_skinny(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
-                         void* y, void* ws, int M, int N, int K, int group_size, hipStream_t stream) {
-  const SkinnyPlan p = skinny_plan(M, N, K, group_size);
+hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const int32_t* qweight, const void* scales,
+                         const int32_t* qzeros, void* y, void* ws, int M, int N, int K, int group_size,
+                         hipStream_t stream) {
   const int glog = group_log2(group_size);
   const bool dq = group_size == 64 || group_size == 32;
   unsigned* counters = (unsigned*)ws;

@@ -869,8 +869,7 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   return p;
 }
 
-size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
-  const W4A8Plan p = w4a8_plan(M, N, K, group_size);
+size_t w4a8_workspace_bytes(const W4A8Plan& p, int M, int N) {
   if (p.tail_splits > 0)
     return kCounterRegionBytes +
            (size_t)(p.tiles_m * p.tiles_n - p.n_full) * p.tail_splits * p.bm * WBN * sizeof(int32_t);
@@ -880,10 +879,9 @@ size_t w4a8_workspace_bytes(int M, int N, int K, int group_size) {
 
 namespace {
 
-hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const void* qweight,
+hipError_t launch_int8_gemm(const W4A8Plan& p, int mode, const int8_t* xq, const float* s_a, const void* qweight,
                             const int8_t* gscale, const void* cscale, void* y, int32_t* acc_out, void* ws, int M,
-                            int N, int K, int group_size, hipStream_t stream) {
-  const W4A8Plan p = w4a8_plan(M, N, K, group_size);
+                            int N, int K, hipStream_t stream) {
   unsigned* counters = (unsigned*)ws;
   int32_t* partials = ws ? (int32_t*)((char*)ws + kCounterRegionBytes) : nullptr;
   const int tiles = p.tiles_m * p.tiles_n;
@@ -930,16 +928,17 @@ hipError_t launch_int8_gemm(int mode, const int8_t* xq, const float* s_a, const 
 
 }  // namespace
 
-hipError_t launch_w4a8_gemm(const int8_t* xq, const float* s_a, const int32_t* qweight, const int8_t* gscale,
-                            const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
-                            int group_size, hipStream_t stream) {
-  return launch_int8_gemm(group_size == -1 ? kI4PerChannel : kI4TwoLevel, xq, s_a, qweight, gscale, cscale, y,
-                          acc_out, ws, M, N, K, group_size, stream);
+hipError_t launch_w4a8_gemm(const W4A8Plan& p, const int8_t* xq, const float* s_a, const int32_t* qweight,
+                            const int8_t* gscale, const void* cscale, void* y, int32_t* acc_out, void* ws, int M,
+                            int N, int K, int group_size, hipStream_t stream) {
+  return launch_int8_gemm(p, group_size == -1 ? kI4PerChannel : kI4TwoLevel, xq, s_a, qweight, gscale, cscale, y,
+                          acc_out, ws, M, N, K, stream);
 }
 
-hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_a, const int8_t* qweight, const void* cscale, void* y,
-                            int32_t* acc_out, void* ws, int M, int N, int K, hipStream_t stream) {
-  return launch_int8_gemm(kI8, xq, s_a, qweight, nullptr, cscale, y, acc_out, ws, M, N, K, 0, stream);
+hipError_t launch_w8a8_gemm(const W4A8Plan& p, const int8_t* xq, const float* s_a, const int8_t* qweight,
+                            const void* cscale, void* y, int32_t* acc_out, void* ws, int M, int N, int K,
+                            hipStream_t stream) {
+  return launch_int8_gemm(p, kI8, xq, s_a, qweight, nullptr, cscale, y, acc_out, ws, M, N, K, stream);
 }
 
 }  // namespace w4
