@@ -104,6 +104,46 @@ int awq_unpack_dequant(const int32_t* qweight, const void* scales, const int32_t
                        void* w_out, int64_t N, int64_t K, int32_t group_size, void* stream);
 
 /*
+ * Plain (untiled) weight layouts accepted by the import calls below.  "Implement AWQ
+ * quantization support for LLaMA" (vllm-project/vllm PR 1032) prints the Triton AWQ
+ * weight format: codes packed 8 per 32-bit word along K (plain nibble order: element
+ * k = 8j + i of a row in bits 4i..4i+3 of word j), per-group scales, and per-group zero
+ * points packed 8 per word along the group axis (group g in bits 4 (g % 8).. of word
+ * g / 8), stored K-major.  With ng = K / G (1 per-channel):
+ *   W4_LAYOUT_ROWS  per output channel: qweight int32 [N, K/8], scales fp16 [N, ng],
+ *                   qzeros int32 [N, ceil(ng/8)]; W4A8 gscale int8 [N, ng]
+ *   W4_LAYOUT_COLS  the printed (K-major) orientation: qweight int32 [K/8, N], scales
+ *                   fp16 [ng, N], qzeros int32 [ceil(ng/8), N]; W4A8 gscale int8 [ng, N]
+ */
+enum { W4_LAYOUT_ROWS = 0, W4_LAYOUT_COLS = 1 };
+
+/*
+ * awq_import_plain -- convert W4A16 weights quantized elsewhere from a plain layout
+ * (see W4_LAYOUT_*) into the layout awq_gemm reads (tiled qweight, scales [K/G, N],
+ * qzeros [K/G, ceil(N/8)], top of this file).  A pure rearrangement of bits: the
+ * outputs equal what awq_pack writes for the same codes, scales and zero points
+ * (padding rows of qweight are code 0).  All six pointers are device pointers owned by
+ * the caller, 16-byte aligned, non-NULL for N > 0; inputs and outputs must not overlap.
+ * group_size 128, 64, 32 or -1; K a positive multiple of 128; N == 0 is a no-op.
+ * Asynchronous on `stream` (a few small kernels).
+ */
+int awq_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
+                     int32_t* qweight, void* scales, int32_t* qzeros, int64_t N, int64_t K, int32_t group_size,
+                     int32_t layout, void* stream);
+
+/*
+ * w4a8_import_plain -- as awq_import_plain for W4A8 weights: qweight_plain holds biased
+ * nibbles q + 8 ("[Feature] support qqq(w4a8) for lmdeploy", "Modification": exported
+ * QQQ weights are converted to the serving format before the GEMM loads them); the tiled
+ * output's padding rows hold q = 0 (nibble 8).  group_size 128 (two-level: gscale_plain
+ * int8 in the orientation of `layout` -> gscale [K/G, N]) or -1 (per-channel:
+ * gscale_plain and gscale must be NULL).  cscale [N] is the same in every layout and is
+ * not an argument.
+ */
+int w4a8_import_plain(const int32_t* qweight_plain, const int8_t* gscale_plain, int32_t* qweight, int8_t* gscale,
+                      int64_t N, int64_t K, int32_t group_size, int32_t layout, void* stream);
+
+/*
  * awq_gemm_workspace_bytes -- bytes of workspace awq_gemm needs for this shape (0 when
  * the chosen kernels do not split K).  The workspace holds split-K fp32 partial sums and
  * per-tile arrival counters.  It must be zero-filled before its first use; every
@@ -122,6 +162,11 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
  * and 32 take a dequantizing variant of the skinny kernel at M <= 32 (each lane scales
  * its own 32 k) and the MFMA GEMM above.  Results are deterministic (split-K partials
  * are summed in a fixed order).
+ * The packed operands are in this library's layout (top of this file), not the
+ * row-major qweight [N, K/8], scales [N, K/G], qzeros [N, ceil(K/G/8)] of a plain
+ * export: with row-major words every wave load of the decode kernels touched 16
+ * separate 64-byte pieces and ran ~40 % slower than the 1 KB tiles.  Weights in a plain
+ * layout come in once through awq_import_plain.
  */
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,
              void* y, void* workspace, size_t workspace_bytes,
@@ -236,6 +281,28 @@ int w4a8_gemm_i32(const int8_t* xq, const int32_t* qweight, const int8_t* gscale
  * be 16-byte aligned.  Bit-exact.
  */
 int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void* stream);
+
+/*
+ * Measurement helpers: the measured ceilings that the GEMMs are reported against, next
+ * to the specification figures (the pages' point is speed: "[Feature] support qqq(w4a8)
+ * for lmdeploy", "Throughput").  Neither computes anything of the method.
+ *
+ * w4_ceiling_read -- read every byte of buf[0, bytes) once from device memory (16-byte
+ * vector loads, grid-stride over `blocks` workgroups of 256 threads, `unroll` (4 or 8)
+ * loads in flight per thread) and store one xor-fold word per wave to sink (blocks * 4
+ * uint32, device).  bytes a positive multiple of 16; 1 <= blocks <= 65536.
+ *
+ * w4_ceiling_mfma -- `blocks` workgroups of 4 waves, each wave running `iters` rounds of
+ * 4 independent accumulator chains of v_mfma_f32_32x32x16_f16 (kind 0; 32768 flops per
+ * instruction) or v_mfma_i32_32x32x32_i8 (kind 1; 65536 ops) with no memory traffic in
+ * the loop.  A and B operands are 16-byte chunks of `operands` (device, operand_bytes a
+ * positive multiple of 16; constant or random contents select the data the matrix cores
+ * see); out receives one float per thread (blocks * 256, device).  Work per call:
+ * blocks * 4 * iters * 4 instructions.
+ */
+int w4_ceiling_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll, void* stream);
+int w4_ceiling_mfma(const void* operands, int64_t operand_bytes, int32_t kind, int32_t iters, float* out,
+                    int32_t blocks, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* w4_status_string(int status);

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("awq_pack", "awq_gemm", "w4a8_quant_act", "w4a8_gemm", "awq_unpack_dequant", "w4a8_pack",
               "w4a8_gemm_i32", "awq_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
               "w4_last_error", "w4_pack_codes", "w4a8_silu_mul_quant", "awq_pack_sym", "w8a8_pack", "w8a8_gemm",
-              "w8a8_gemm_i32", "w8a8_gemm_workspace_bytes"):
+              "w8a8_gemm_i32", "w8a8_gemm_workspace_bytes", "awq_import_plain", "w4a8_import_plain"):
         assert n in names
 
 
@@ -124,6 +124,26 @@ def test_w4a8_validation(lib):
     assert lib.w4a8_gemm(f, f, f, None, f, f, None, 0, 4, 64, 1 << 18, -1, None) == 2
     assert lib.w8a8_gemm(None, None, None, None, None, None, 0, 0, 64, 256, -1, None) == 0
     assert lib.w8a8_gemm(f, f, f, f, f, None, 0, 1, 256, 5120, -1, None) == 3  # narrow N splits K
+
+
+def test_import_validation(lib):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    assert lib.awq_import_plain(None, None, None, None, None, None, 0, 256, 128, 0, None) == 0  # N == 0
+    assert lib.awq_import_plain(f, f, f, f, f, f, 64, 256, 128, 2, None) == 1
+    assert "layout" in lib.w4_last_error().decode()
+    assert lib.awq_import_plain(f, f, None, f, f, f, 64, 256, 128, 1, None) == 1
+    assert "qzeros_plain is NULL" in lib.w4_last_error().decode()
+    assert lib.awq_import_plain(f, f, f, f, f, P(FAKE + 2), 64, 256, 128, 0, None) == 1
+    assert "aligned" in lib.w4_last_error().decode()
+    assert lib.awq_import_plain(f, f, f, f, f, f, 64, 200, 128, 0, None) == 1
+    assert lib.awq_import_plain(f, f, f, f, f, f, 64, 256, 16, 0, None) == 2
+    assert lib.w4a8_import_plain(f, f, f, f, 64, 256, -1, 0, None) == 1
+    assert "gscale" in lib.w4_last_error().decode()
+    assert lib.w4a8_import_plain(f, None, f, f, 64, 256, 128, 0, None) == 1
+    assert "gscale_plain is NULL" in lib.w4_last_error().decode()
+    assert lib.w4a8_import_plain(f, None, f, None, 64, 256, 64, 0, None) == 2
+    assert lib.w4a8_import_plain(f, None, f, None, -1, 256, -1, 0, None) == 1
 
 
 def test_workspace_sizes(lib):

@@ -7,6 +7,7 @@ from ._lib import (  # noqa: F401
     W4Error,
     awq_gemm,
     awq_gemm_workspace_bytes,
+    awq_import_plain,
     awq_pack,
     awq_pack_sym,
     awq_unpack_dequant,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     w4a8_gemm,
     w4a8_gemm_i32,
     w4a8_gemm_workspace_bytes,
+    w4a8_import_plain,
     w4a8_pack,
     w4a8_quant_act,
     w4a8_silu_mul_quant,

@@ -60,6 +60,10 @@ def load():
             "w8a8_pack": [P, P, P, I64, I64, I64, I32, P],
             "w8a8_gemm": [P, P, P, P, P, P, SZ, I64, I64, I64, I32, P],
             "w8a8_gemm_i32": [P, P, P, P, SZ, I64, I64, I64, I32, P],
+            "awq_import_plain": [P, P, P, P, P, P, I64, I64, I32, I32, P],
+            "w4a8_import_plain": [P, P, P, P, I64, I64, I32, I32, P],
+            "w4_ceiling_read": [P, I64, P, I32, I32, P],
+            "w4_ceiling_mfma": [P, I64, I32, I32, P, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -224,6 +228,42 @@ def awq_unpack_dequant(qweight, scales, qzeros, group_size: int = 128):
     return out
 
 
+LAYOUTS = {"rows": 0, "cols": 1}
+
+
+def _plain_dims(qweight_plain, layout):
+    """(N, K) of plain packed words: rows [N, K/8], cols [K/8, N]."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {layout!r}")
+    _need(qweight_plain, "qweight_plain", torch.int32, ndim=2)
+    a, b = qweight_plain.shape
+    return (a, 8 * b) if layout == "rows" else (b, 8 * a)
+
+
+def _plain_groups(t, name, dtype, N, rows_per_n, layout):
+    _need(t, name, dtype, (N, rows_per_n) if layout == "rows" else (rows_per_n, N))
+
+
+def awq_import_plain(qweight_plain, scales_plain, qzeros_plain, group_size: int = 128, layout: str = "rows"):
+    """Plain W4A16 weights -> (qweight tiled, scales [K/G, N], qzeros [K/G, ceil(N/8)]).
+    layout "rows": qweight [N, K/8], scales [N, K/G], qzeros [N, ceil(K/G/8)]; "cols" (the
+    K-major Triton AWQ orientation): qweight [K/8, N], scales [K/G, N], qzeros
+    [ceil(K/G/8), N]."""
+    N, K = _plain_dims(qweight_plain, layout)
+    ng = _groups(K, group_size, W4A16_GROUPS)
+    _plain_groups(scales_plain, "scales_plain", torch.float16, N, ng, layout)
+    _plain_groups(qzeros_plain, "qzeros_plain", torch.int32, N, (ng + 7) // 8, layout)
+    dev = _gpu(qweight_plain=qweight_plain, scales_plain=scales_plain, qzeros_plain=qzeros_plain)
+    qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
+    scales = torch.empty((ng, N), dtype=torch.float16, device=dev)
+    qzeros = torch.empty((ng, (N + 7) // 8), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check("awq_import_plain", load().awq_import_plain(
+            _ptr(qweight_plain), _ptr(scales_plain), _ptr(qzeros_plain), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+            N, K, group_size, LAYOUTS[layout], _stream(dev)))
+    return qweight, scales, qzeros
+
+
 def awq_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int = 128) -> int:
     return int(load().awq_gemm_workspace_bytes(M, N, K, group_size))
 
@@ -268,6 +308,28 @@ def w4a8_pack(w: torch.Tensor, group_size: int = -1):
         _check("w4a8_pack", load().w4a8_pack(_ptr(w), _ptr(qweight), _ptr(gscale), _ptr(cscale), 0, N, K,
                                              group_size, _stream(dev)))
     return qweight, gscale, cscale
+
+
+def w4a8_import_plain(qweight_plain, gscale_plain=None, group_size: int = -1, layout: str = "rows"):
+    """Plain W4A8 weights (biased nibbles q + 8) -> (qweight tiled, gscale [K/G, N] or
+    None).  layout "rows": qweight [N, K/8], gscale [N, K/G]; "cols": [K/8, N], [K/G, N]."""
+    N, K = _plain_dims(qweight_plain, layout)
+    ng = _groups(K, group_size, W4A8_GROUPS)
+    if group_size == -1:
+        if gscale_plain is not None:
+            raise ValueError("gscale_plain must be None for per-channel weights (group_size -1)")
+    else:
+        if gscale_plain is None:
+            raise ValueError("gscale_plain is required for group_size 128")
+        _plain_groups(gscale_plain, "gscale_plain", torch.int8, N, ng, layout)
+    dev = _gpu(qweight_plain=qweight_plain, gscale_plain=gscale_plain)
+    qweight = torch.empty(qweight_shape(N, K), dtype=torch.int32, device=dev)
+    gscale = torch.empty((ng, N), dtype=torch.int8, device=dev) if group_size > 0 else None
+    with torch.cuda.device(dev):
+        _check("w4a8_import_plain", load().w4a8_import_plain(
+            _ptr(qweight_plain), _ptr(gscale_plain), _ptr(qweight), _ptr(gscale), N, K, group_size,
+            LAYOUTS[layout], _stream(dev)))
+    return qweight, gscale
 
 
 def w4a8_quant_act(x: torch.Tensor, gamma=None, eps: float = 1e-5):
@@ -544,3 +606,53 @@ def bind_w8a8_gemm(xq, s_a, qweight, cscale, out):
             _check("w8a8_gemm", rc)
         return keep
     return call
+
+
+# ------------------------------------------------------ measurement helpers
+def bind_ceiling_read(buf, nbytes: int, blocks: int = 1024, unroll: int = 4):
+    """Zero-argument callable that enqueues w4_ceiling_read over the first `nbytes` of
+    the device buffer `buf` (a read-only HBM stream, the measured bandwidth ceiling)."""
+    _need(buf, "buf", torch.uint8, ndim=1)
+    if nbytes <= 0 or nbytes % 16 or nbytes > buf.numel():
+        raise ValueError(f"nbytes={nbytes} must be a positive multiple of 16 within the buffer")
+    dev = _gpu(buf=buf)
+    sink = torch.empty((blocks * 4,), dtype=torch.int32, device=dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+    args = (_ptr(buf), nbytes, _ptr(sink), blocks, unroll, stream)
+    fn = lib.w4_ceiling_read
+    keep = (buf, sink)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w4_ceiling_read", rc)
+        return keep
+    return call
+
+
+def bind_ceiling_mfma(operands, kind: int, iters: int, blocks: int = 512):
+    """Zero-argument callable that enqueues w4_ceiling_mfma (kind 0 fp16, 1 int8); returns
+    (callable, flops per call)."""
+    _need(operands, "operands", torch.uint8, ndim=1)
+    if operands.numel() < 16 or operands.numel() % 16:
+        raise ValueError("operands must hold a positive multiple of 16 bytes")
+    if kind not in (0, 1):
+        raise ValueError("kind must be 0 (fp16) or 1 (int8)")
+    dev = _gpu(operands=operands)
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+    args = (_ptr(operands), operands.numel(), kind, iters, _ptr(out), blocks, stream)
+    fn = lib.w4_ceiling_mfma
+    keep = (operands, out)
+
+    def call():
+        rc = fn(*args)
+        if rc != W4_OK:
+            _check("w4_ceiling_mfma", rc)
+        return keep
+    flops = blocks * 4 * iters * 4 * (65536 if kind == 1 else 32768)
+    return call, flops

@@ -199,6 +199,49 @@ int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void
   return launched(fn, w4::launch_pack_codes(codes, out, R, C, (hipStream_t)stream));
 }
 
+static int import_common(const char* fn, int64_t N, int64_t K, int32_t layout) {
+  W4_TRY(check_mnk(fn, 0, N, K));
+  if (layout != W4_LAYOUT_ROWS && layout != W4_LAYOUT_COLS)
+    return fail(W4_ERR_INVALID_ARG, "%s: layout=%d (W4_LAYOUT_ROWS 0 or W4_LAYOUT_COLS 1)", fn, layout);
+  return W4_OK;
+}
+
+int awq_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
+                     int32_t* qweight, void* scales, int32_t* qzeros, int64_t N, int64_t K, int32_t group_size,
+                     int32_t layout, void* stream) {
+  const char* fn = "awq_import_plain";
+  g_last_error.clear();
+  W4_TRY(check_group_w4a16(fn, group_size));
+  W4_TRY(import_common(fn, N, K, layout));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"qweight_plain", qweight_plain}, {"scales_plain", scales_plain},
+                         {"qzeros_plain", qzeros_plain}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}}));
+  W4_TRY(check_device(fn));
+  const int ng = group_size == -1 ? 1 : (int)(K / group_size);
+  return launched(fn, w4::launch_import_plain(qweight_plain, scales_plain, qzeros_plain, nullptr, qweight, scales,
+                                              qzeros, nullptr, (int)N, (int)K, ng, layout, 0u, (hipStream_t)stream));
+}
+
+int w4a8_import_plain(const int32_t* qweight_plain, const int8_t* gscale_plain, int32_t* qweight, int8_t* gscale,
+                      int64_t N, int64_t K, int32_t group_size, int32_t layout, void* stream) {
+  const char* fn = "w4a8_import_plain";
+  g_last_error.clear();
+  if (group_size != 128 && group_size != -1)
+    return fail(W4_ERR_UNSUPPORTED, "%s: group_size=%d (128 or -1)", fn, group_size);
+  W4_TRY(import_common(fn, N, K, layout));
+  if (N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"qweight_plain", qweight_plain}, {"qweight", qweight}}));
+  if (group_size == 128) {
+    W4_TRY(check_ptrs(fn, {{"gscale_plain", gscale_plain}, {"gscale", gscale}}));
+  } else if (gscale_plain != nullptr || gscale != nullptr) {
+    return fail(W4_ERR_INVALID_ARG, "%s: gscale_plain and gscale must be NULL for group_size=-1", fn);
+  }
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_import_plain(qweight_plain, nullptr, nullptr, gscale_plain, qweight, nullptr, nullptr,
+                                              gscale, (int)N, (int)K, (int)(K / 128), layout, 0x88888888u,
+                                              (hipStream_t)stream));
+}
+
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (!group_ok_w4a16(group_size) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
       K > kMaxDim)
@@ -384,6 +427,33 @@ int w4a8_gemm_i32(const int8_t* xq, const int32_t* qweight, const int8_t* gscale
                   size_t workspace_bytes, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
   return w4a8_common("w4a8_gemm_i32", xq, nullptr, qweight, gscale, nullptr, nullptr, acc, workspace,
                      workspace_bytes, M, N, K, group_size, stream);
+}
+
+int w4_ceiling_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll, void* stream) {
+  const char* fn = "w4_ceiling_read";
+  g_last_error.clear();
+  if (bytes <= 0 || bytes % 16 != 0) return fail(W4_ERR_INVALID_ARG, "%s: bytes=%lld must be a positive multiple of 16",
+                                                 fn, (long long)bytes);
+  if (blocks < 1 || blocks > 65536) return fail(W4_ERR_INVALID_ARG, "%s: blocks=%d (1..65536)", fn, blocks);
+  if (unroll != 4 && unroll != 8) return fail(W4_ERR_UNSUPPORTED, "%s: unroll=%d (4 or 8)", fn, unroll);
+  W4_TRY(check_ptrs(fn, {{"buf", buf}, {"sink", sink}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_ceiling_read(buf, bytes, sink, blocks, unroll, (hipStream_t)stream));
+}
+
+int w4_ceiling_mfma(const void* operands, int64_t operand_bytes, int32_t kind, int32_t iters, float* out,
+                    int32_t blocks, void* stream) {
+  const char* fn = "w4_ceiling_mfma";
+  g_last_error.clear();
+  if (kind != 0 && kind != 1) return fail(W4_ERR_UNSUPPORTED, "%s: kind=%d (0 fp16, 1 int8)", fn, kind);
+  if (operand_bytes < 16 || operand_bytes % 16 != 0)
+    return fail(W4_ERR_INVALID_ARG, "%s: operand_bytes=%lld must be a positive multiple of 16", fn,
+                (long long)operand_bytes);
+  if (iters < 1) return fail(W4_ERR_INVALID_ARG, "%s: iters=%d must be >= 1", fn, iters);
+  if (blocks < 1 || blocks > 65536) return fail(W4_ERR_INVALID_ARG, "%s: blocks=%d (1..65536)", fn, blocks);
+  W4_TRY(check_ptrs(fn, {{"operands", operands}, {"out", out}}));
+  W4_TRY(check_device(fn));
+  return launched(fn, w4::launch_ceiling_mfma(operands, operand_bytes, kind, iters, out, blocks, (hipStream_t)stream));
 }
 
 const char* w4_status_string(int status) {

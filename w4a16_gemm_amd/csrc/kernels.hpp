@@ -46,6 +46,7 @@ __device__ __forceinline__ bool splitk_arrive(unsigned* counter, int splits) {
 constexpr int kMaxCounters = 4096;
 constexpr size_t kCounterRegionBytes = kMaxCounters * sizeof(unsigned);
 
+
 // Host-side tuning knob for sweeps and the variant tests.  Only when the environment
 // holds W4_TUNING=1 at the library's first plan does the integer variable `name`
 // override `dflt`; otherwise every plan takes its built-in defaults and reads no
@@ -99,6 +100,16 @@ hipError_t launch_awq_unpack_dequant(const int32_t* qweight, const void* scales,
                                      void* out, int N, int K, int group_size, hipStream_t stream);
 hipError_t launch_w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int N, int K,
                             int two_level, hipStream_t stream);
+// Measured ceilings: an HBM read stream and an MFMA issue loop (see ceilings.hip).
+hipError_t launch_ceiling_read(const void* buf, int64_t bytes, uint32_t* sink, int blocks, int unroll,
+                               hipStream_t stream);
+hipError_t launch_ceiling_mfma(const void* operands, int64_t operand_bytes, int kind, int iters, float* out,
+                               int blocks, hipStream_t stream);
+// Plain (untiled) weights -> the library's layout; NULL sources skip that array.
+// cols: the K-major orientation (qweight [K/8, N], per-group arrays [., N]).
+hipError_t launch_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
+                               const int8_t* gscale_plain, int32_t* qweight, void* scales, int32_t* qzeros,
+                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, hipStream_t stream);
 
 // Every GEMM entry point plans once per call: the plan sizes the workspace and is then
 // handed to the launcher.
