@@ -75,10 +75,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--detail-iters", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w4a8", "copy"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "w4a8", "copy", "micro", "small", "midm"],
                     help="decode (default, the reported metric); prefill / w4a8 (the int8 path) / copy run one kernel family "
                          "alone (for profiling); copy is a plain device copy of known size that calibrates "
-                         "the FETCH_SIZE / WRITE_SIZE counters")
+                         "the FETCH_SIZE / WRITE_SIZE counters; micro measures the ceilings (HBM read stream "
+                         "at the decode weight sizes and 1 GiB, fp16 / int8 MFMA loops); small runs the single "
+                         "M=8 GEMM and the O projection at M=1,4,16; midm the crossover shapes M=64,128,256")
     return ap.parse_args()
 
 
@@ -116,6 +119,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w4.load()
+    if args.workload == "micro":
+        print(json.dumps(micro(args, dev, torch, w4)), flush=True)
+        return
     if args.workload != "decode":
         print(json.dumps(single_workload(args, dev, torch, np, synth, w4)), flush=True)
         return
@@ -204,6 +210,13 @@ def main():
 
     copy_gbs = _copy_bandwidth(torch, dev)
     log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write)")
+    # measured ceiling of the same step: a read-only stream kernel reading, launch for
+    # launch, the algorithmic bytes of each of the step's calls from buffers rotated over
+    # 1 GiB (best of a few grid shapes); its per-launch average is what the skinny kernel
+    # could reach if it did nothing but stream its bytes
+    step_sizes = [byts[(name, M)] for M in Ms for name in names]
+    ceil = _read_ceiling(torch, w4, dev, step_sizes, args.steps)
+    log(f"read-stream ceiling of the step: {ceil['GBps']:.0f} GB/s ({ceil['config']})")
     result = {
         "metric": "W4A16-g128 GEMM GB/s (M<=16) & TFLOP/s (M>=256) vs roofline, 13B shapes",
         "value": round(gbs, 2),
@@ -226,6 +239,11 @@ def main():
                      "avg_launch_us": round(avg_us, 3),
                      "algorithmic_bytes_per_launch": int(step_bytes / per_step),
                      "traffic": profiled_traffic("skinny_decode_13b"),
+                     # measured ceiling: a read-only HBM stream kernel over the same byte counts,
+                     # launch for launch (ceilings.hip; profiles/ceilings.md)
+                     "measured_peak": round(ceil["GBps"], 1),
+                     "frac_of_measured": round(achieved / ceil["GBps"], 4),
+                     "measured_peak_kernel": "read_stream_kernel " + ceil["config"],
                      # context: what a plain 1 GiB device copy (torch) reaches on this part
                      "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)},
         "per_shape": shape_detail,
@@ -257,6 +275,29 @@ def single_workload(args, dev, torch, np, synth, w4):
             y = torch.empty((4096, N), dtype=torch.float16, device=dev)
             calls.append(w4.bind_awq_gemm(x, qw, sc, qz, y))
         res["flops_per_round"] = sum(2.0 * 4096 * N * K for (K, N) in ((5120, 27648), (5120, 5120), (13824, 5120)))
+    elif args.workload == "small":
+        # the single M = 8 GEMM (4096 x 4096) and the O projection (5120 x 5120) at
+        # M = 1, 4, 16, each over enough rotated weight copies to stream from HBM
+        calls = []
+        for (M, K, N) in ((8, 4096, 4096), (1, 5120, 5120), (4, 5120, 5120), (16, 5120, 5120)):
+            inp = synth.make_linear(M, N, K, seed=0, outliers=(N != 4096))
+            qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+            x = inp.x.to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            nc = -(-2 * MALL_BYTES // int(awq_bytes(0, N, K)))
+            calls += [w4.bind_awq_gemm(x, *rotated_awq(qw, sc, qz, r), y) for r in range(nc)]
+        res["launches_per_round"] = len(calls)
+    elif args.workload == "midm":
+        # the crossover shape K = 5120, N = 13824 at M = 64, 128, 256 (16 rotated copies)
+        calls = []
+        inp = synth.make_linear(256, 13824, 5120, seed=0, outliers=True)
+        qw, sc, qz = w4.awq_pack(inp.w.to(dev))
+        copies = [rotated_awq(qw, sc, qz, r) for r in range(16)]
+        for M in (64, 128, 256):
+            x = inp.x[:M].contiguous().to(dev)
+            y = torch.empty((M, 13824), dtype=torch.float16, device=dev)
+            calls += [w4.bind_awq_gemm(x, *c, y) for c in copies]
+        res["launches_per_round"] = len(calls)
     else:  # the int8 path at M = 4096: quant_act, W4A8 (both weight variants), W8A8, silu_mul_quant
         inp = synth.make_linear(4096, 13824, 5120, seed=0, outliers=True, rms_spread=True, with_gamma=True)
         x = inp.x.to(dev)
@@ -288,6 +329,94 @@ def single_workload(args, dev, torch, np, synth, w4):
     a1.record()
     torch.cuda.synchronize()
     res["ms_per_round"] = a0.elapsed_time(a1) / args.steps
+    return res
+
+
+READ_CONFIGS = ((512, 4), (1024, 4), (2048, 4), (1024, 8), (2048, 8), (4096, 4))
+
+
+def _read_ceiling(torch, w4, dev, sizes, steps, pool_bytes=1 << 30):
+    """Read-only stream ceiling of a sequence of launches: one w4_ceiling_read launch per
+    entry of `sizes` (bytes), each over a fresh region of a 1 GiB pool (consecutive
+    launches read consecutive regions, so no byte is re-read within 1 GiB: beyond the
+    256 MB Infinity Cache), the sequence repeated `steps` times.  Best over a few grid
+    shapes.  Returns GB/s = bytes / event time and the average launch time."""
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pool.fill_(0x5A)
+    sizes = [int(-(-b // 256) * 256) for b in sizes]
+    best = None
+    for blocks, unroll in READ_CONFIGS:
+        calls, off = [], 0
+        for b in sizes * max(1, min(steps, 64)):
+            if off + b > pool_bytes:
+                off = 0
+            calls.append(w4.bind_ceiling_read(pool[off:off + b], b, blocks, unroll))
+            off += b
+        for c in calls[: len(sizes)]:
+            c()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in calls:
+            c()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        nbytes = float(sum(sizes)) * (len(calls) // len(sizes))
+        r = {"GBps": nbytes / t / 1e9, "avg_launch_us": t / len(calls) * 1e6,
+             "config": f"blocks={blocks} unroll={unroll}"}
+        if best is None or r["GBps"] > best["GBps"]:
+            best = r
+    del pool
+    return best
+
+
+def micro(args, dev, torch, w4):
+    """Measured ceilings: the HBM read stream at each decode call's weight size, the
+    single M=8 GEMM's size and 1 GiB (every grid shape of READ_CONFIGS), and fp16 / int8
+    MFMA issue loops on constant and random operands (a few occupancies)."""
+    import synth
+    res = {"workload": "micro", "read_stream": {}, "mfma": {}}
+    sizes = {"single_m8_4096": awq_bytes(8, 4096, 4096)}
+    for name, (K, N) in synth.LLAMA2_13B.items():
+        sizes[f"{name}_M1"] = awq_bytes(1, N, K)
+    sizes["1GiB"] = float(1 << 30)
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pool.fill_(0x5A)
+    for key, nb in sizes.items():
+        nb = int(-(-nb // 256) * 256)
+        per = {}
+        for blocks, unroll in READ_CONFIGS:
+            n_copies = max(2, min(64, (1 << 30) // nb))
+            calls = [w4.bind_ceiling_read(pool[i * nb:(i + 1) * nb], nb, blocks, unroll) for i in range(n_copies)]
+            t = _time_calls(torch, calls, max(2 * n_copies, 20))
+            per[f"b{blocks}_u{unroll}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+        best = max(per.values(), key=lambda r: r["GBps"])
+        res["read_stream"][key] = {"bytes": nb, "best_GBps": best["GBps"], "best_us": best["us"],
+                                   "frac_of_8TBps": round(best["GBps"] / HBM_PEAK_GBS, 4), "configs": per}
+        log(f"read stream {key}: {best['GBps']} GB/s ({best['us']} us)")
+    del pool
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    n_ops = 1 << 20  # 16 MB of operand chunks
+    ops = {
+        ("f16", "const"): torch.full((n_ops // 2,), 1.0, dtype=torch.float16),
+        ("f16", "random"): torch.randn((n_ops // 2,), generator=gen).to(torch.float16),
+        ("i8", "const"): torch.full((n_ops,), 1, dtype=torch.int8),
+        ("i8", "random"): torch.randint(-127, 128, (n_ops,), generator=gen, dtype=torch.int8),
+    }
+    for (kind, data), t_host in ops.items():
+        buf = t_host.view(torch.uint8).to(dev)
+        per = {}
+        for blocks in (256, 512, 1024, 2048):
+            call, flops = w4.bind_ceiling_mfma(buf, 0 if kind == "f16" else 1, 4000, blocks)
+            t = _time_calls(torch, [call], 6)
+            per[f"b{blocks}"] = round(flops / t / 1e12, 1)
+        best = max(per.values())
+        peak = F16_PEAK_TFLOPS if kind == "f16" else I8_PEAK_TOPS
+        res["mfma"][f"{kind}_{data}"] = {"best_T": best, "frac_of_spec": round(best / peak, 4), "by_blocks": per,
+                                         "unit": "TFLOP/s" if kind == "f16" else "TOP/s"}
+        log(f"mfma {kind} {data}: {best} T/s")
     return res
 
 

@@ -147,6 +147,10 @@ def test_import_validation(lib):
 
 
 def test_workspace_sizes(lib):
+    # empty shapes need no workspace (and are never planned)
+    for fn in (lib.awq_gemm_workspace_bytes, lib.w4a8_gemm_workspace_bytes):
+        assert fn(0, 64, 256, -1) == 0 and fn(4, 0, 256, -1) == 0 and fn(0, 0, 256, 128) == 0
+    assert lib.w8a8_gemm_workspace_bytes(0, 64, 256, -1) == 0 and lib.w8a8_gemm_workspace_bytes(4, 0, 256, -1) == 0
     # decode shapes split K; prefill shapes do not; invalid shapes report 0
     assert lib.awq_gemm_workspace_bytes(1, 256, 5120, 128) > 0
     assert lib.awq_gemm_workspace_bytes(4096, 27648, 5120, 128) == 0
@@ -160,3 +164,24 @@ def test_workspace_sizes(lib):
     assert lib.w8a8_gemm_workspace_bytes(1, 256, 1 << 18, -1) == 0
     assert lib.w4a8_gemm_workspace_bytes(1, 256, 5120, -1) > 0  # narrow N splits K
     assert lib.w4a8_gemm_workspace_bytes(4096, 13824, 5120, 128) == 0
+
+
+def test_plans_of_many_shapes(lib):
+    """The tile planners run on the host for every call: seeded shapes over every dispatch
+    boundary, group size and K must plan without a host fault and report a workspace
+    that covers the counter region whenever K is split."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    Ms = [1, 2, 3, 4, 5, 8, 9, 16, 17, 31, 32, 33, 48, 64, 65, 128, 129, 255, 256, 257, 511, 512, 513, 4096, 5000]
+    for _ in range(600):
+        M = int(rng.choice(Ms))
+        N = int(rng.integers(1, 40000))
+        K = 128 * int(rng.integers(1, 120))
+        for g in (128, 64, 32, -1):
+            b = lib.awq_gemm_workspace_bytes(M, N, K, g)
+            assert b == 0 or b >= 16384
+        for g in (128, -1):
+            b = lib.w4a8_gemm_workspace_bytes(M, N, K, g)
+            assert b == 0 or b >= 16384
+        b = lib.w8a8_gemm_workspace_bytes(M, N, K, -1)
+        assert b == 0 or b >= 16384

@@ -108,6 +108,12 @@ def test_awq_gemm_empty():
     assert tuple(y.shape) == (0, 64)
 
 
+# Achieved normalized error at the full shapes is ~1e-4 or below (fp16 output rounding
+# and, on the MFMA GEMM, fp16 rounding of the dequantized weights); a regression that
+# stays under the 2e-3 acceptance bar but well above this is still caught.
+TIGHT = 5e-4
+
+
 def _full_cases():
     out = []
     for name, cases in synth.workloads().items():
@@ -144,7 +150,10 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
     yg = to_np(y)[np.ix_(ms, ns)].astype(np.float64)
     err = normalized_error(yg, ref["y"], np.linalg.norm(x.numpy()[ms].astype(np.float64), axis=1),
                            np.linalg.norm(ref["w_deq"], axis=1))
+    print(f"[err] awq_gemm {'skinny' if M <= 32 else 'gemm'} M={M} N={N} K={K} normalized {err:.3e}", flush=True)
     assert err <= TOL, err
+    # regression bar near what the kernels achieve (the acceptance bar above is 2e-3)
+    assert err <= TIGHT, err
 
 
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",

@@ -246,6 +246,7 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
   if (!group_ok_w4a16(group_size) || M < 0 || N < 0 || K <= 0 || K % 128 || M > kMaxDim || N > kMaxDim ||
       K > kMaxDim)
     return 0;
+  if (M == 0 || N == 0) return 0;
   return awq_ws(awq_plan(M, N, K, group_size), M, N);
 }
 
