@@ -32,4 +32,6 @@ from ._lib import (  # noqa: F401
     w8a8_gemm_i32,
     w8a8_gemm_workspace_bytes,
     bind_w8a8_gemm,
+    bind_ceiling_read,
+    bind_ceiling_mfma,
 )

@@ -617,7 +617,8 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 4, 2, 4, 0) V(1, 2, 2, 4, 0) V(1, 1, 4, 4, 0) V(2, 4, 2, 4, 0) V(2, 2, 2, 4, 0) V(2, 1, 4, 4, 0)          \
   V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
   V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
-  V(1, 4, 2, 8, 1)
+  V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
+  V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 8, 3, 8, 0)
 static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 10 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
   const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
