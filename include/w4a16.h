@@ -173,6 +173,23 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
              int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
 
 /*
+ * awq_gemm_noalloc -- awq_gemm for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as awq_gemm; the split-K workspace is a static device array
+ * of W4_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the process
+ * ends, so the call makes no hipMalloc, hipFree or other allocating call.  The caller
+ * passes inputs and outputs as for awq_gemm.  A shape whose workspace
+ * (awq_gemm_workspace_bytes) exceeds the array returns W4_ERR_WORKSPACE before any
+ * launch.  All calls on one GPU share the array and it keeps the last call's contents:
+ * calls in stream order are safe, calls that overlap in time on one GPU (different
+ * streams) race.  The first call on a device resolves the array's address and enqueues
+ * one small kernel on `stream` that clears its counter region.
+ */
+#define W4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int awq_gemm_noalloc(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros, void* y,
+                     int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream);
+
+/*
  * w4a8_pack -- quantize fp16 W [N, K] to symmetric int4 for W4A8 and pack it.
  * group_size == -1: per-channel, cscale = fp16(max(max|w|/7, 1e-5)),
  *   q = clamp(rint(w / cscale), -8, 7); gscale must be NULL.

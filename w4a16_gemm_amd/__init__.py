@@ -6,6 +6,7 @@ functions carry the names of the C entry points.
 from ._lib import (  # noqa: F401
     W4Error,
     awq_gemm,
+    awq_gemm_noalloc,
     awq_gemm_workspace_bytes,
     awq_import_plain,
     awq_pack,

@@ -62,6 +62,7 @@ def load():
             "w8a8_gemm_i32": [P, P, P, P, SZ, I64, I64, I64, I32, P],
             "awq_import_plain": [P, P, P, P, P, P, I64, I64, I32, I32, P],
             "w4a8_import_plain": [P, P, P, P, I64, I64, I32, I32, P],
+            "awq_gemm_noalloc": [P, P, P, P, P, I64, I64, I64, I32, P],
             "w4_ceiling_read": [P, I64, P, I32, I32, P],
             "w4_ceiling_mfma": [P, I64, I32, I32, P, I32, P],
         }
@@ -290,6 +291,23 @@ def awq_gemm(x, qweight, scales, qzeros, group_size: int = 128, out=None, worksp
             ws, nb = workspace, workspace.numel() * workspace.element_size()
         _check("awq_gemm", lib.awq_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), _ptr(ws),
                                         nb, M, N, K, group_size, _stream(dev)))
+    return out
+
+
+def awq_gemm_noalloc(x, qweight, scales, qzeros, out, group_size: int = 128):
+    """awq_gemm on the library's static device workspace (no allocation anywhere: the
+    output is the caller's).  Raises W4Error (W4_ERR_WORKSPACE) for a shape whose
+    workspace exceeds the static array."""
+    _need(x, "x", torch.float16, ndim=2)
+    _need(scales, "scales", torch.float16, ndim=2)
+    M, K = x.shape
+    N = scales.shape[1]
+    _need_w4a16(qweight, scales, qzeros, N, K, group_size)
+    _need(out, "out", torch.float16, (M, N))
+    dev = _gpu(x=x, qweight=qweight, scales=scales, qzeros=qzeros, out=out)
+    with torch.cuda.device(dev):
+        _check("awq_gemm_noalloc", load().awq_gemm_noalloc(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                                                           _ptr(out), M, N, K, group_size, _stream(dev)))
     return out
 
 

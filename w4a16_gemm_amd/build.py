@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.cpp", "pack.hip", "layout.hip", "ceilings.hip", "skinny.hip", "gemm.hip", "w4a8.hip"]
+SOURCES = ["api.cpp", "pack.hip", "layout.hip", "ceilings.hip", "noalloc.hip", "skinny.hip", "gemm.hip", "w4a8.hip"]
 # Per-file flags.  The skinny kernels keep their few MFMA accumulators in VGPRs (the
 # per-group epilogue reads them with plain VALU operations instead of v_accvgpr_read).
 EXTRA = {"skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -278,6 +278,36 @@ int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const in
   return launched(fn, e);
 }
 
+int awq_gemm_noalloc(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros, void* y,
+                     int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
+  static_assert(W4_NOALLOC_SCRATCH_BYTES == w4::kNoAllocScratchBytes, "scratch size");
+  const char* fn = "awq_gemm_noalloc";
+  g_last_error.clear();
+  W4_TRY(check_group_w4a16(fn, group_size));
+  W4_TRY(check_mnk(fn, M, N, K));
+  if (M == 0 || N == 0) return W4_OK;
+  W4_TRY(check_ptrs(fn, {{"x", x}, {"qweight", qweight}, {"scales", scales}, {"qzeros", qzeros}, {"y", y}}));
+  const AwqPlan plan = awq_plan(M, N, K, group_size);
+  const size_t need = awq_ws(plan, M, N);
+  if (need > w4::kNoAllocScratchBytes)
+    return fail(W4_ERR_WORKSPACE, "%s: this shape needs %zu bytes of workspace, above the static %zu", fn, need,
+                w4::kNoAllocScratchBytes);
+  W4_TRY(check_device(fn));
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = w4::noalloc_scratch(&ws, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: static workspace: %s", fn, hipGetErrorString(e));
+  }
+  hipError_t e;
+  if (plan.skinny)
+    e = w4::launch_skinny(plan.sp, x, qweight, scales, qzeros, y, ws, (int)M, (int)N, (int)K, group_size,
+                          (hipStream_t)stream);
+  else
+    e = w4::launch_gemm(plan.gp, x, qweight, scales, qzeros, y, ws, (int)M, (int)N, (int)K, group_size,
+                        (hipStream_t)stream);
+  return launched(fn, e);
+}
+
 int w4a8_pack(const void* w, int32_t* qweight, int8_t* gscale, void* cscale, int64_t M, int64_t N, int64_t K,
               int32_t group_size, void* stream) {
   const char* fn = "w4a8_pack";

@@ -46,6 +46,11 @@ __device__ __forceinline__ bool splitk_arrive(unsigned* counter, int splits) {
 constexpr int kMaxCounters = 4096;
 constexpr size_t kCounterRegionBytes = kMaxCounters * sizeof(unsigned);
 
+// Size of the static device workspace of awq_gemm_noalloc (W4_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of that workspace on the current GPU (resolved once per device; the
+// first call also enqueues the clearing of its counter region on `stream`).
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 
 // Host-side tuning knob for sweeps and the variant tests.  Only when the environment
 // holds W4_TUNING=1 at the library's first plan does the integer variable `name`
