@@ -158,7 +158,9 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
 
 
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",
-                                   "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs"])
+                                   "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs", "2,3,8", "2,4,8",
+                                   "2,6,8", "4,3,8", "4,4,4", "8,3,8", "1,4,8", "1,8,8", "1,4,8,xs", "1,8,8,xs",
+                                   "1,4,16", "2,4,8,xs"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (16, 520, 1280), (17, 96, 768), (32, 300, 640)])
 def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
     """Each compiled variant of the register-X M <= 32 kernel -- tile width, or
@@ -213,14 +215,19 @@ def test_skinny_lds_variants(variant, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("depth", ["1", "0", "5"])
 @pytest.mark.parametrize("shape", ["1", "2", "3", "4"])
-@pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048)])
-def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
+@pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048), (33, 128, 128),
+                                   (200, 520, 384)])
+def test_gemm_every_tile_shape(shape, depth, M, N, K, monkeypatch):
     """Each tile shape of the M > 32 MFMA GEMM (forced through its tuning variable;
-    128x256, 128x128, 64x256, 64x128), with ragged M and N, against the oracle."""
+    128x256, 128x128, 64x256, 64x128), with the register-staged X tiles (depth 1) and the
+    direct-to-LDS pipeline (depth 0: steady state, tails of 1-3 steps, K = 128 a single
+    step pair), with ragged M and N, against the oracle."""
     dev = device()
     monkeypatch.setenv("W4_GEMM_SHAPE", shape)
-    announce(f"gemm shape={shape} M={M} N={N} K={K}")
+    monkeypatch.setenv("W4_GEMM_DEPTH", depth)
+    announce(f"gemm shape={shape} depth={depth} M={M} N={N} K={K}")
     inp = synth.make_linear(M, N, K, seed=M + N + int(shape), outliers=True, rms_spread=True)
     ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
     y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz)).astype(np.float64)
@@ -230,9 +237,9 @@ def test_gemm_every_tile_shape(shape, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("depth", ["3", "4", "6"])
+@pytest.mark.parametrize("depth", ["3", "4", "6", "0", "5"])
 @pytest.mark.parametrize("M,N,K,splits", [(65, 300, 640, "1"), (130, 520, 1024, "2"), (257, 1030, 2048, "4"),
-                                          (40, 129, 128, "1")])
+                                          (40, 129, 128, "1"), (100, 260, 1408, "3")])
 def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
     """The 64x128 GEMM with 3, 4 or 6 register sets of loads in flight (rotating sets,
     steady state plus a tail of fewer steps than sets), split and unsplit, with ragged M
@@ -259,7 +266,8 @@ def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
     (1400, 500, 2048, 1, 32, 2),   # 22 tiles on 16 slots: the last 6 split in two
     (1100, 300, 4096, 1, 64, 8),   # 18 tiles on 8 slots: remainder 2 split 8 ways (forced)
 ])
-def test_gemm_tail_split(M, N, K, scale, div, expect, monkeypatch):
+@pytest.mark.parametrize("depth", ["1", "0", "5"])
+def test_gemm_tail_split(M, N, K, scale, div, expect, depth, monkeypatch):
     """The 128x256 GEMM with the last tiles split over their BK steps (the remainder of
     the tile count over the resident workgroups; the slot count is scaled down through
     the tuning variables so that small shapes reach it), against the oracle; outputs
@@ -270,6 +278,7 @@ def test_gemm_tail_split(M, N, K, scale, div, expect, monkeypatch):
     monkeypatch.setenv("W4_GEMM_SLOTS_SCALE", str(scale))
     monkeypatch.setenv("W4_GEMM_SLOTS_DIV", str(div))
     monkeypatch.setenv("W4_GEMM_TAIL_PARTS", str(expect))
+    monkeypatch.setenv("W4_GEMM_DEPTH", depth)
     tiles = -(-M // 128) * -(-N // 256)
     slots = 512 * scale // div
     rem = tiles % slots

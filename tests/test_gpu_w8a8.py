@@ -85,8 +85,9 @@ def test_w8a8_skinny_variants(tiles, M, N, K, monkeypatch):
     assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
 
 
-@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1"])
-@pytest.mark.parametrize("M,N,K,target", [(70, 300, 1280, "1"), (200, 520, 2048, "128"), (40, 129, 128, "1")])
+@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1", "64,0", "128,0"])
+@pytest.mark.parametrize("M,N,K,target", [(70, 300, 1280, "1"), (200, 520, 2048, "128"), (40, 129, 128, "1"),
+                                          (300, 260, 1152, "4")])
 def test_w8a8_gemm_tiles_and_depths(bm_depth, M, N, K, target, monkeypatch):
     """Each compiled row-tile height and prefetch depth of the int8 GEMM on W8A8
     weights, split and unsplit, ragged shapes: int32 accumulators bit-exact."""
@@ -105,7 +106,8 @@ def test_w8a8_gemm_tiles_and_depths(bm_depth, M, N, K, target, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
-def test_w8a8_gemm_tail_split(M, N, K, div, parts, monkeypatch):
+@pytest.mark.parametrize("depth", ["1", "0"])
+def test_w8a8_gemm_tail_split(M, N, K, div, parts, depth, monkeypatch):
     """The 128-row int8 GEMM (W8A8 weights) with the last tiles split over their groups
     (slot count scaled down through the tuning variables): int32 accumulators bit-exact
     and fp16 outputs within 2e-3."""
@@ -113,7 +115,7 @@ def test_w8a8_gemm_tail_split(M, N, K, div, parts, monkeypatch):
     monkeypatch.setenv("W4_W4A8_SPLIT_TARGET", "1")
     monkeypatch.setenv("W4_W4A8_TAIL", "1")
     monkeypatch.setenv("W4_W4A8_BM", "128")
-    monkeypatch.setenv("W4_W4A8_DEPTH", "1")
+    monkeypatch.setenv("W4_W4A8_DEPTH", depth)
     monkeypatch.setenv("W4_W4A8_SLOTS_DIV", str(div))
     monkeypatch.setenv("W4_W4A8_TAIL_PARTS", str(parts))
     tiles = -(-M // 128) * -(-N // 256)

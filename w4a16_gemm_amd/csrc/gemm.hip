@@ -39,13 +39,18 @@ namespace {
 constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+constexpr int kRing = 4;  // X tiles in flight in the direct-to-LDS pipeline
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n (< 64) vector-memory
+// operations are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // Tile BM x BN = (32 MI) x (128 NF): wave w owns columns [32 NF w, 32 NF (w + 1)) as NF
 // 32-column fragments and all BM rows as MI 32-row fragments.
 template <int MI, int NF, int PD>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restrict__ x,
+__global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const half_t* __restrict__ x,
                                                             const uint32_t* __restrict__ qweight,
                                                             const half_t* __restrict__ scales,
                                                             const uint32_t* __restrict__ qzeros,
@@ -55,7 +60,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
                                                             int glog, int n_full, int tail_splits) {
   constexpr int BM = 32 * MI, BN = 128 * NF;
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
-  __shared__ u32x4 lds[2][BM * 8];
+  // PD == 0: X goes global -> LDS directly into a ring of kRing tiles (separate arrays,
+  // see below); otherwise two register-staged buffers
+  constexpr bool kDma = PD == 0 || PD == 5;
+  __shared__ u32x4 lds[kDma ? 1 : 2][kDma ? 1 : BM * 8];
 
   const int ktiles = K / BK;
   // Work item of this workgroup.  Uniform mode (tail_splits == 0): every tile split
@@ -119,7 +127,129 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const half_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  if constexpr (PD == 1) {
+  if constexpr (kDma) {
+  // Direct-to-LDS pipeline.  The X tile of BK step t lands in LDS slot t % kRing straight
+  // from global memory (global_load_lds_dwordx4: no registers, no VALU), issued kRing - 1
+  // steps ahead; this lane's weight chunks and raw scale / zero-point words of step t sit
+  // in register set t % kRing, issued as far ahead.  Each step: wait until the loads of
+  // step t are complete (every step issues the same kPerStage loads per thread, so that is
+  // "at most 2 kPerStage loads outstanding"), barrier (every wave's part of the tile is in
+  // LDS, and every wave is done with the slot and set of step t - 1), issue step t + 3's
+  // loads into that freed slot and set, then the MFMAs of step t.  Loads past the last step
+  // are clamped to it (they refill slots no later step reads), so the counts stay uniform.
+  //
+  // With X in LDS in its natural k order, each code word is expanded in natural order too:
+  // byte p of the word holds k = 2p (low nibble) and 2p + 1 (high nibble); v_perm_b32 puts
+  // it under fp16 1024 in the low half and under fp16 64 in the high half, and one AND keeps
+  // the low nibble and the high nibble respectively: (1024 + q_2p, 64 + q_2p+1).  Then the
+  // exact subtraction of (1024 + z, 64 + z) and the multiply by s (one rounding).
+    constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
+    constexpr int kWaitImm = vmcnt_imm(2 * kPerStage);
+    // thread's chunk i of a tile lands at LDS position (4 i + wave) * 64 + lane (each wave
+    // instruction writes 1 KB contiguously) and must hold the X chunk that the swizzle puts
+    // there: row r = P / 8, k-chunk (P % 8) ^ ((r / 2) % 8)
+    // (element offsets fit 32 bits: the plan takes this pipeline only for M K < 2^31)
+    uint32_t xoff[kAPer];
+  #pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int pos = (4 * i + wave) * 64 + lane;
+      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
+      xoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)(c * 8);
+    }
+    // One LDS array per ring slot: the compiler's wait insertion tells direct-to-LDS loads
+    // into distinct arrays apart, so reading slot t does not wait for the loads in flight
+    // into the other slots (with one array it waited for all of them).
+    __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8];
+    auto ring = [&](int j) -> u32x4* { return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3; };
+    struct BSet {
+      u32x4 b[NF];
+      uint32_t z[NF], s[NF];
+    };
+    BSet bs[kRing];
+    const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
+    auto issue = [&](int kt, int slot, BSet& S) {
+      // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
+  #pragma unroll
+      for (int f = 0; f < NF; ++f)
+        S.b[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
+      // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
+      const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        S.z[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
+        S.s[f] = sbits[row * N + nclamp[f]];
+      }
+  #pragma unroll
+      for (int i = 0; i < kAPer; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(x + xoff[i] + kt * BK),
+                                         (__attribute__((address_space(3))) void*)(ring(slot) + (4 * i + wave) * 64), 16, 0,
+                                         0);
+    };
+    const uint32_t magic = vreg(0x00005464u);  // bytes 0x64 (fp16 1024 high byte), 0x54 (fp16 64)
+    const uint32_t keep = vreg(0xfff0ff0fu);
+    auto step = [&](int t, int j) {
+      __builtin_amdgcn_s_waitcnt(kWaitImm);
+      __builtin_amdgcn_s_barrier();
+      issue(min(t + kRing - 1, kend - 1), (j + kRing - 1) % kRing, bs[(j + kRing - 1) % kRing]);
+      const BSet& S = bs[j];
+      half2_t cz[NF], s2[NF];
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint32_t z = (S.z[f] >> (4 * (nclamp[f] & 7))) & 15u;
+        cz[f] = __builtin_bit_cast(half2_t, (0xE400u | z) | ((0xD400u | (z << 4)) << 16));
+        s2[f] = __builtin_bit_cast(half2_t, S.s[f] * 0x00010001u);
+      }
+      const u32x4* xa = ring(j);
+      half8_t afr[2][MI];  // A fragments of k16 steps s (in use) and s + 1 (in flight)
+  #pragma unroll
+      for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4)]);
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+  #pragma unroll
+          for (int i = 0; i < MI; ++i)
+            afr[(s + 1) & 1][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4 + s + 1)]);
+        }
+        half8_t bf[NF];
+  #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint32_t w = S.b[f][s];
+          u32x4 pr;
+  #pragma unroll
+          for (int p = 0; p < 4; ++p)
+            pr[p] = __builtin_amdgcn_perm(magic, w, (5u << 24) | ((uint32_t)p << 16) | (4u << 8) | (uint32_t)p) & keep;
+          half2_t p0 = __builtin_bit_cast(half2_t, (uint32_t)pr[0]);
+          half2_t p1 = __builtin_bit_cast(half2_t, (uint32_t)pr[1]);
+          half2_t p2 = __builtin_bit_cast(half2_t, (uint32_t)pr[2]);
+          half2_t p3 = __builtin_bit_cast(half2_t, (uint32_t)pr[3]);
+          p0 = (p0 + cz[f]) * s2[f];
+          p1 = (p1 + cz[f]) * s2[f];
+          p2 = (p2 + cz[f]) * s2[f];
+          p3 = (p3 + cz[f]) * s2[f];
+          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+  #pragma unroll
+        for (int i = 0; i < MI; ++i)
+  #pragma unroll
+          for (int f = 0; f < NF; ++f) acc[i][f] = mfma32(afr[s & 1][i], bf[f], acc[i][f]);
+      }
+    };
+    const int nsteps = kend - kbeg;
+    if (nsteps > 0) {
+  #pragma unroll
+      for (int d = 0; d < kRing - 1; ++d) issue(min(kbeg + d, kend - 1), d, bs[d]);
+      int it = 0;
+      for (; it + kRing <= nsteps; it += kRing) {
+  #pragma unroll
+        for (int j = 0; j < kRing; ++j) step(kbeg + it + j, j);
+      }
+  #pragma unroll
+      for (int j = 0; j < kRing; ++j)
+        if (it + j < nsteps) step(kbeg + it + j, j);
+      // no LDS write may still be in flight when the workgroup's LDS is released
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+  } else if constexpr (PD == 1) {
   // PD == 1: the next step's loads are issued at the top of each step (one set of X
   // registers, short lifetimes: the 128 x 256 tile fits two workgroups per CU).
     // global -> register staging of one X tile (BM x 64 halves).  Loads are branch-free
@@ -413,7 +543,8 @@ static const int kResidentPerCU[4] = {2, 3, 3, 4};
 constexpr int kCUs = 256;
 // Compiled (MI, NF, prefetch depth) variants.
 #define GEMM_VARIANTS(V) \
-  V(4, 2, 1) V(4, 1, 1) V(2, 2, 1) V(2, 1, 1) V(2, 1, 3) V(2, 1, 4) V(2, 1, 6)
+  V(4, 2, 1) V(4, 1, 1) V(2, 2, 1) V(2, 1, 1) V(2, 1, 3) V(2, 1, 4) V(2, 1, 6) V(4, 2, 0) V(4, 1, 0) V(2, 2, 0) \
+  V(2, 1, 0) V(4, 1, 5) V(2, 2, 5) V(2, 1, 5)
 static bool gemm_variant_compiled(int mi, int nf, int pd) {
 #define V(MI, NF, PD) if (mi == MI && nf == NF && pd == PD) return true;
   GEMM_VARIANTS(V)
@@ -449,8 +580,18 @@ GemmPlan gemm_plan(int M, int N, int K) {
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
   // register sets in flight (BK steps of loads ahead of the MFMAs)
-  p.depth = env_int("W4_GEMM_DEPTH", (mid && pick == 3) ? 4 : 1);
+  // Loop: depth 1 keeps the next step's X tile in registers (two workgroups per CU:
+  // best for the large tiles at prefill sizes, 0.94-1.02 PFLOP/s at M = 4096 with the
+  // clocks warm); depth 0 is the direct-to-LDS pipeline with X tiles four steps ahead
+  // (one workgroup of 4 waves per CU for 128-row tiles), which wins at mid M where
+  // each workgroup is latency-bound: K = 5120, N = 13824 at M = 64 / 128 / 256 / 512
+  // 26.9 -> 23.3, 37.7 -> 31.2, 57.4 -> 52.0, 95.2 -> 88.1 us (register-staged, 3-4
+  // sets ahead before).  Depths 3, 4, 6 (register sets in flight, 64 x 128 tiles) and 5
+  // (direct-to-LDS, two workgroups per CU) stay compiled for sweeps.
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? 0 : 1);
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
+  // the direct-to-LDS pipeline addresses X with 32-bit element offsets
+  if ((p.depth == 0 || p.depth == 5) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;
   p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
   p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
   const int ktiles = K / BK;

@@ -223,7 +223,9 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   constexpr int kT = WAVES * kWave;
   constexpr int kCols = 16 * T;           // output columns of one workgroup
   constexpr int kOut = MT * 16 * kCols;   // outputs of one workgroup
-  constexpr int kPer = kOut / kT;         // outputs per thread in the epilogue (MT * T)
+  // outputs per thread in the epilogue (MT * T; 1 when the workgroup has more threads than
+  // outputs: threads past the last output only read a clamped entry and store nothing)
+  constexpr int kPer = (kOut + kT - 1) / kT;
   __shared__ float red[WAVES][MT * T * 4 * kWave];
   __shared__ __align__(16) half_t xbuf[XS ? WAVES : 1][XS ? 512 : 8];  // M <= 4: X rows of a group
   const int lane = threadIdx.x & 63;
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
   float vals[kPer];
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
-    const int o = it * kT + threadIdx.x;
+    const int o = min(it * kT + (int)threadIdx.x, kOut - 1);
     const int m = o / kCols, nl = o % kCols;
     const int t = nl >> 4, ln = nl & 15;
     const int mt = m >> 4, i = m & 3, lq = (m & 15) >> 2;
@@ -618,8 +620,9 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
   V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
-  V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 8, 3, 8, 0)
-static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 10 + w) * 2 + xs; }
+  V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 8, 3, 8, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
+  V(1, 1, 8, 8, 1) V(1, 1, 4, 16, 0) V(1, 2, 4, 8, 1)
+static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 100 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
   const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
 #define V(MT, T, D, W, XS) if (key == variant_key(MT, T, D, W, XS)) return true;

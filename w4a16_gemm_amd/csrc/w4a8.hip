@@ -316,6 +316,10 @@ constexpr int kWThreads = 256;
 // bank window, so 16 consecutive rows read at one chunk hit 16 distinct bank groups
 // (with c ^ (r % 8), rows r and r + 8 collided: 40 % of LDS cycles were bank conflicts)
 __device__ __forceinline__ int swz8(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+// xq tiles in flight in the direct-to-LDS pipeline, and the s_waitcnt immediate (gfx9
+// encoding) that waits until at most n (< 64) vector-memory operations are outstanding.
+constexpr int kRing8 = 4;
+constexpr int vmcnt_imm8(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 __device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { return cs ? cs[n] : (half_t)1; }
 
 // Two workgroups per CU for the one-group-ahead loop; the deeper variants (mid M, grids
@@ -329,7 +333,8 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
   constexpr int BM = 32 * MI;
   constexpr bool TWO = MODE == kI4TwoLevel;
   constexpr int NB = MODE == kI8 ? 4 : 2;  // 16-byte weight chunks per lane, fragment and group
-  __shared__ u32x4 lds[2][BM * 8];
+  constexpr bool kDma = PD == 0;
+  __shared__ u32x4 lds[kDma ? 1 : 2][kDma ? 1 : BM * 8];
 
   const int ng = K / WBK;
   // Work item: uniform split-K (tail_splits == 0), or tail mode -- workgroups [0, n_full)
@@ -475,7 +480,110 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
     }
   };
 
-  if constexpr (PD == 1) {
+  if constexpr (kDma) {
+    // Direct-to-LDS pipeline (as in the fp16 GEMM): the xq tile of group t lands in LDS
+    // ring slot t % kRing8 straight from global memory, issued kRing8 - 1 groups ahead, with
+    // this lane's weight chunks and group scales in register set t % kRing8.  Every group
+    // issues the same kPerStage loads per thread, so "at most 2 kPerStage outstanding" means
+    // group t's loads are complete; a barrier then makes the whole tile visible and frees
+    // the slot and set of group t - 1 for group t + 3.  Loads past the range are clamped.
+    constexpr int kPerStage = kPer + 2 * NB + (TWO ? 2 : 0);
+    constexpr int kWaitImm = vmcnt_imm8(2 * kPerStage);
+    // chunk i of this thread lands at LDS position (4 i + wave) * 64 + lane and holds the
+    // xq chunk the swizzle puts there: row r = P / 8, k-chunk (P % 8) ^ ((r / 2) % 8)
+    uint32_t aoff[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int pos = (4 * i + wave) * 64 + lane;
+      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
+      aoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)(c * 16);
+    }
+    // one LDS array per ring slot (the compiler's wait insertion tells loads into distinct
+    // arrays apart)
+    __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8];
+    auto ring = [&](int j) -> u32x4* { return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3; };
+    struct Stage {
+      u32x4 b[2][NB];
+      int sg[2];
+    };
+    Stage st[kRing8];
+    auto issue = [&](int g, int slot, Stage& S) {
+      load_b(g, S.b);
+      S.sg[0] = S.sg[1] = 1;
+      load_sg(g, S.sg);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(xq + aoff[i] + g * WBK),
+                                         (__attribute__((address_space(3))) void*)(ring(slot) + (4 * i + wave) * 64), 16, 0,
+                                         0);
+    };
+    auto step = [&](int t, int j) {
+      __builtin_amdgcn_s_waitcnt(kWaitImm);
+      __builtin_amdgcn_s_barrier();
+      issue(min(t + kRing8 - 1, gend - 1), (j + kRing8 - 1) % kRing8, st[(j + kRing8 - 1) % kRing8]);
+      const Stage& S = st[j];
+      const u32x4* xa = ring(j);
+      u16x2 sp[2], cp[2];
+      if (TWO) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int sg = S.sg[f];
+          sp[f] = u16x2{(unsigned short)sg, (unsigned short)sg};
+          cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
+        }
+      }
+      int4_t afr[2][MI];  // A fragments of k32 steps s (in use) and s + 1 (in flight)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            afr[(s + 1) & 1][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4 + s + 1)]);
+        }
+        int4_t bf[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          if (MODE == kI8) {
+            const u32x4 v = S.b[f][s];
+            bf[f] = int4_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+            continue;
+          }
+          const uint32_t w0 = S.b[f][s >> 1][(s & 1) * 2];
+          const uint32_t w1 = S.b[f][s >> 1][(s & 1) * 2 + 1];
+          uint32_t a0, a1, a2, a3;
+          if (TWO) {
+            unpack_i4_scaled(w0, sp[f], cp[f], a0, a1);
+            unpack_i4_scaled(w1, sp[f], cp[f], a2, a3);
+          } else {
+            unpack_i4x16(w0, a0, a1);
+            unpack_i4x16(w1, a2, a3);
+          }
+          bf[f] = int4_t{(int)a0, (int)a1, (int)a2, (int)a3};
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int f = 0; f < 2; ++f) acc[i][f] = mfma32_i8(afr[s & 1][i], bf[f], acc[i][f]);
+      }
+    };
+    const int nsteps = gend - gbeg;
+    if (nsteps > 0) {
+#pragma unroll
+      for (int d = 0; d < kRing8 - 1; ++d) issue(min(gbeg + d, gend - 1), d, st[d]);
+      int it = 0;
+      for (; it + kRing8 <= nsteps; it += kRing8) {
+#pragma unroll
+        for (int j = 0; j < kRing8; ++j) step(gbeg + it + j, j);
+      }
+#pragma unroll
+      for (int j = 0; j < kRing8; ++j)
+        if (it + j < nsteps) step(gbeg + it + j, j);
+      // no LDS write may still be in flight when the workgroup's LDS is released
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm8(0));
+    }
+  } else if constexpr (PD == 1) {
     // the next group's loads are issued at the top of each step (one set of A registers)
     if (gbeg < gend) {
       load_a(gbeg);
@@ -844,7 +952,9 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
   p.depth = env_int("W4_W4A8_DEPTH", M <= 256 ? 4 : 1);
-  if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4))))
+  // depth 0: the direct-to-LDS pipeline (64- and 128-row tiles; 32-bit xq offsets)
+  if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4)) ||
+        (p.depth == 0 && p.bm >= 64 && (int64_t)M * K < (int64_t(1) << 31))))
     p.depth = 1;
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + WBN - 1) / WBN;
@@ -919,7 +1029,7 @@ hipError_t launch_int8_gemm(const W4A8Plan& p, int mode, const int8_t* xq, const
   }
 #define W4A8_LAUNCH_MI(MODE) \
   W4A8_LAUNCH(1, MODE, 1) W4A8_LAUNCH(2, MODE, 1) W4A8_LAUNCH(4, MODE, 1) W4A8_LAUNCH(1, MODE, 4) \
-  W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4)
+  W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4) W4A8_LAUNCH(4, MODE, 0) W4A8_LAUNCH(2, MODE, 0)
   const int mi = p.bm / 32;
   if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); }
   else if (mode == kI8) { W4A8_LAUNCH_MI(kI8); }
