@@ -128,10 +128,10 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
   if constexpr (kDma) {
-  // Direct-to-LDS pipeline.  The X tile of BK step t lands in LDS slot t % kRing straight
-  // from global memory (global_load_lds_dwordx4: no registers, no VALU), issued kRing - 1
+  // Direct-to-LDS pipeline.  The X tile of BK step t lands in LDS slot t % R straight
+  // from global memory (global_load_lds_dwordx4: no registers, no VALU), issued R - 1
   // steps ahead; this lane's weight chunks and raw scale / zero-point words of step t sit
-  // in register set t % kRing, issued as far ahead.  Each step: wait until the loads of
+  // in register set t % R, issued as far ahead.  Each step: wait until the loads of
   // step t are complete (every step issues the same kPerStage loads per thread, so that is
   // "at most 2 kPerStage loads outstanding"), barrier (every wave's part of the tile is in
   // LDS, and every wave is done with the slot and set of step t - 1), issue step t + 3's
@@ -143,8 +143,10 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   // it under fp16 1024 in the low half and under fp16 64 in the high half, and one AND keeps
   // the low nibble and the high nibble respectively: (1024 + q_2p, 64 + q_2p+1).  Then the
   // exact subtraction of (1024 + z, 64 + z) and the multiply by s (one rounding).
+    // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5, registers)
+    constexpr int R = PD == 5 ? 3 : kRing;
     constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
-    constexpr int kWaitImm = vmcnt_imm(2 * kPerStage);
+    constexpr int kWaitImm = vmcnt_imm((R - 2) * kPerStage);
     // thread's chunk i of a tile lands at LDS position (4 i + wave) * 64 + lane (each wave
     // instruction writes 1 KB contiguously) and must hold the X chunk that the swizzle puts
     // there: row r = P / 8, k-chunk (P % 8) ^ ((r / 2) % 8)
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
       u32x4 b[NF];
       uint32_t z[NF], s[NF];
     };
-    BSet bs[kRing];
+    BSet bs[R];
     const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
     auto issue = [&](int kt, int slot, BSet& S) {
       // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     auto step = [&](int t, int j) {
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_s_barrier();
-      issue(min(t + kRing - 1, kend - 1), (j + kRing - 1) % kRing, bs[(j + kRing - 1) % kRing]);
+      issue(min(t + R - 1, kend - 1), (j + R - 1) % R, bs[(j + R - 1) % R]);
       const BSet& S = bs[j];
       half2_t cz[NF], s2[NF];
   #pragma unroll
@@ -200,15 +202,24 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         s2[f] = __builtin_bit_cast(half2_t, S.s[f] * 0x00010001u);
       }
       const u32x4* xa = ring(j);
-      half8_t afr[2][MI];  // A fragments of k16 steps s (in use) and s + 1 (in flight)
+      // A fragments of k16 steps s (in use) and s + 1 (in flight) with one wave per SIMD;
+      // with two, the other wave covers the LDS latency and the registers are short
+      constexpr bool kAhead = PD == 0;
+      half8_t afr[2][MI];
+      if (kAhead) {
   #pragma unroll
-      for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4)]);
+        for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4)]);
+      }
   #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if (s < 3) {
+        if (kAhead && s < 3) {
   #pragma unroll
           for (int i = 0; i < MI; ++i)
             afr[(s + 1) & 1][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4 + s + 1)]);
+        }
+        if (!kAhead) {
+  #pragma unroll
+          for (int i = 0; i < MI; ++i) afr[s & 1][i] = __builtin_bit_cast(half8_t, xa[swz(i * 32 + col, h * 4 + s)]);
         }
         half8_t bf[NF];
   #pragma unroll
@@ -237,14 +248,14 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     const int nsteps = kend - kbeg;
     if (nsteps > 0) {
   #pragma unroll
-      for (int d = 0; d < kRing - 1; ++d) issue(min(kbeg + d, kend - 1), d, bs[d]);
+      for (int d = 0; d < R - 1; ++d) issue(min(kbeg + d, kend - 1), d, bs[d]);
       int it = 0;
-      for (; it + kRing <= nsteps; it += kRing) {
+      for (; it + R <= nsteps; it += R) {
   #pragma unroll
-        for (int j = 0; j < kRing; ++j) step(kbeg + it + j, j);
+        for (int j = 0; j < R; ++j) step(kbeg + it + j, j);
       }
   #pragma unroll
-      for (int j = 0; j < kRing; ++j)
+      for (int j = 0; j < R; ++j)
         if (it + j < nsteps) step(kbeg + it + j, j);
       // no LDS write may still be in flight when the workgroup's LDS is released
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
