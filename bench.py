@@ -444,11 +444,20 @@ def _copy_bandwidth(torch, dev, nbytes=1 << 30, iters=5):
     return 2 * nbytes / t / 1e9
 
 
-def _time_calls(torch, calls, iters):
-    """Average time per call of a list of bound calls run round robin (HIP events)."""
+def _time_calls(torch, calls, iters, warm_s=0.03):
+    """Average time per call of a list of bound calls run round robin (HIP events), after
+    running them for about warm_s seconds so that the clocks are in their steady state
+    (the compute-bound GEMMs read ~7 % slower right after an idle gap)."""
     for fn in calls[: min(len(calls), 4)]:
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            calls[i % len(calls)]()
+            i += 1
+        torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
