@@ -215,7 +215,7 @@ def test_skinny_lds_variants(variant, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("depth", ["1", "0", "5"])
+@pytest.mark.parametrize("depth", ["1", "0", "5", "7"])
 @pytest.mark.parametrize("shape", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048), (33, 128, 128),
                                    (200, 520, 384)])
@@ -237,7 +237,7 @@ def test_gemm_every_tile_shape(shape, depth, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("depth", ["3", "4", "6", "0", "5"])
+@pytest.mark.parametrize("depth", ["3", "4", "6", "0", "5", "7"])
 @pytest.mark.parametrize("M,N,K,splits", [(65, 300, 640, "1"), (130, 520, 1024, "2"), (257, 1030, 2048, "4"),
                                           (40, 129, 128, "1"), (100, 260, 1408, "3")])
 def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
@@ -266,7 +266,7 @@ def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
     (1400, 500, 2048, 1, 32, 2),   # 22 tiles on 16 slots: the last 6 split in two
     (1100, 300, 4096, 1, 64, 8),   # 18 tiles on 8 slots: remainder 2 split 8 ways (forced)
 ])
-@pytest.mark.parametrize("depth", ["1", "0", "5"])
+@pytest.mark.parametrize("depth", ["1", "0", "5", "7"])
 def test_gemm_tail_split(M, N, K, scale, div, expect, depth, monkeypatch):
     """The 128x256 GEMM with the last tiles split over their BK steps (the remainder of
     the tile count over the resident workgroups; the slot count is scaled down through

@@ -181,7 +181,7 @@ def test_w4a8_gemm_small(group, M, N, K):
 
 
 @pytest.mark.parametrize("group", [-1, 128])
-@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1", "64,0", "128,0"])
+@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1", "64,0", "128,0", "64,5", "128,5"])
 @pytest.mark.parametrize("M,N,K,target", [(70, 300, 1280, "1"), (200, 520, 2048, "128"), (40, 129, 128, "1"),
                                           (300, 260, 1152, "4")])
 def test_w4a8_gemm_tiles_and_depths(group, bm_depth, M, N, K, target, monkeypatch):
@@ -203,7 +203,7 @@ def test_w4a8_gemm_tiles_and_depths(group, bm_depth, M, N, K, target, monkeypatc
 
 @pytest.mark.parametrize("group", [-1, 128])
 @pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
-@pytest.mark.parametrize("depth", ["1", "0"])
+@pytest.mark.parametrize("depth", ["1", "0", "5"])
 def test_w4a8_gemm_tail_split(group, M, N, K, div, parts, depth, monkeypatch):
     """The 128-row int8 GEMM with the last tiles split over their groups (the remainder
     of the tile count over the resident workgroups; the slot count scaled down through

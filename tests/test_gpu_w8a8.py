@@ -85,7 +85,7 @@ def test_w8a8_skinny_variants(tiles, M, N, K, monkeypatch):
     assert np.array_equal(acc.astype(np.int64), ora.w4a8_acc_ref(xq, q, None, 128))
 
 
-@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1", "64,0", "128,0"])
+@pytest.mark.parametrize("bm_depth", ["32,1", "32,4", "64,1", "64,3", "64,4", "128,1", "64,0", "128,0", "64,5", "128,5"])
 @pytest.mark.parametrize("M,N,K,target", [(70, 300, 1280, "1"), (200, 520, 2048, "128"), (40, 129, 128, "1"),
                                           (300, 260, 1152, "4")])
 def test_w8a8_gemm_tiles_and_depths(bm_depth, M, N, K, target, monkeypatch):
@@ -106,7 +106,7 @@ def test_w8a8_gemm_tiles_and_depths(bm_depth, M, N, K, target, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K,div,parts", [(600, 1000, 2048, 32, 2), (300, 520, 1280, 64, 4)])
-@pytest.mark.parametrize("depth", ["1", "0"])
+@pytest.mark.parametrize("depth", ["1", "0", "5"])
 def test_w8a8_gemm_tail_split(M, N, K, div, parts, depth, monkeypatch):
     """The 128-row int8 GEMM (W8A8 weights) with the last tiles split over their groups
     (slot count scaled down through the tuning variables): int32 accumulators bit-exact

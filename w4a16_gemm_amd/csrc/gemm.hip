@@ -31,6 +31,9 @@
 // that are still too small, with partials summed by the last arriving workgroup in
 // split order (deterministic).
 #include "kernels.hpp"
+#ifndef SFX
+#define SFX true
+#endif
 
 namespace w4 {
 
@@ -62,7 +65,8 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
   // PD == 0: X goes global -> LDS directly into a ring of kRing tiles (separate arrays,
   // see below); otherwise two register-staged buffers
-  constexpr bool kDma = PD == 0 || PD == 5;
+  constexpr bool kDma = PD == 0 || PD == 5 || PD == 7;
+  constexpr bool kBLds = PD == 7;  // the packed weights too go through LDS
   __shared__ u32x4 lds[kDma ? 1 : 2][kDma ? 1 : BM * 8];
 
   const int ktiles = K / BK;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   // the low nibble and the high nibble respectively: (1024 + q_2p, 64 + q_2p+1).  Then the
   // exact subtraction of (1024 + z, 64 + z) and the multiply by s (one rounding).
     // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5, registers)
-    constexpr int R = PD == 5 ? 3 : kRing;
+    constexpr int R = (PD == 5 || PD == 7) ? 3 : kRing;
     constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
     constexpr int kWaitImm = vmcnt_imm((R - 2) * kPerStage);
     // thread's chunk i of a tile lands at LDS position (4 i + wave) * 64 + lane (each wave
@@ -163,8 +167,14 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     // into the other slots (with one array it waited for all of them).
     __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8];
     auto ring = [&](int j) -> u32x4* { return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3; };
+    // PD 7: this lane's weight chunks of step t land in LDS slot t % R at position
+    // (4 f + wave) * 64 + lane (each wave instruction writes 1 KB contiguously) and are read
+    // back by the same lane: no registers held for them while in flight
+    constexpr int kBSlot = kBLds ? NF * 4 * 64 : 1;
+    __shared__ u32x4 bring0[kBSlot], bring1[kBSlot], bring2[kBSlot];
+    auto bring = [&](int j) -> u32x4* { return j == 0 ? bring0 : j == 1 ? bring1 : bring2; };
     struct BSet {
-      u32x4 b[NF];
+      u32x4 b[kBLds ? 1 : NF];
       uint32_t z[NF], s[NF];
     };
     BSet bs[R];
@@ -172,8 +182,15 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     auto issue = [&](int kt, int slot, BSet& S) {
       // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
   #pragma unroll
-      for (int f = 0; f < NF; ++f)
-        S.b[f] = *reinterpret_cast<const u32x4*>(qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng));
+      for (int f = 0; f < NF; ++f) {
+        const uint32_t* src = qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng);
+        if constexpr (kBLds)
+          __builtin_amdgcn_global_load_lds((void*)src,
+                                           (__attribute__((address_space(3))) void*)(bring(slot) + (4 * f + wave) * 64),
+                                           16, 0, 0);
+        else
+          S.b[f] = *reinterpret_cast<const u32x4*>(src);
+      }
       // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
       const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
   #pragma unroll
@@ -189,11 +206,21 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     };
     const uint32_t magic = vreg(0x00005464u);  // bytes 0x64 (fp16 1024 high byte), 0x54 (fp16 64)
     const uint32_t keep = vreg(0xfff0ff0fu);
+    constexpr bool kSchedFence = SFX && !(MI == 2 && NF == 1 && PD == 0);
     auto step = [&](int t, int j) {
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_s_barrier();
+      // nothing that reads this step's registers may be scheduled above the wait (the
+      // compiler's own wait for such a read drains every load in flight)
+      if (kSchedFence) __builtin_amdgcn_sched_barrier(0);
       issue(min(t + R - 1, kend - 1), (j + R - 1) % R, bs[(j + R - 1) % R]);
       const BSet& S = bs[j];
+      u32x4 bw[NF];
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if constexpr (kBLds) bw[f] = bring(j)[(4 * f + wave) * 64 + lane];
+        else bw[f] = S.b[f];
+      }
       half2_t cz[NF], s2[NF];
   #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         half8_t bf[NF];
   #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const uint32_t w = S.b[f][s];
+          const uint32_t w = bw[f][s];
           u32x4 pr;
   #pragma unroll
           for (int p = 0; p < 4; ++p)
@@ -555,7 +582,7 @@ constexpr int kCUs = 256;
 // Compiled (MI, NF, prefetch depth) variants.
 #define GEMM_VARIANTS(V) \
   V(4, 2, 1) V(4, 1, 1) V(2, 2, 1) V(2, 1, 1) V(2, 1, 3) V(2, 1, 4) V(2, 1, 6) V(4, 2, 0) V(4, 1, 0) V(2, 2, 0) \
-  V(2, 1, 0) V(4, 1, 5) V(2, 2, 5) V(2, 1, 5)
+  V(2, 1, 0) V(4, 1, 5) V(2, 2, 5) V(2, 1, 5) V(4, 2, 7) V(4, 1, 7) V(2, 2, 7) V(2, 1, 7)
 static bool gemm_variant_compiled(int mi, int nf, int pd) {
 #define V(MI, NF, PD) if (mi == MI && nf == NF && pd == PD) return true;
   GEMM_VARIANTS(V)
@@ -591,18 +618,21 @@ GemmPlan gemm_plan(int M, int N, int K) {
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
   // register sets in flight (BK steps of loads ahead of the MFMAs)
-  // Loop: depth 1 keeps the next step's X tile in registers (two workgroups per CU:
-  // best for the large tiles at prefill sizes, 0.94-1.02 PFLOP/s at M = 4096 with the
-  // clocks warm); depth 0 is the direct-to-LDS pipeline with X tiles four steps ahead
-  // (one workgroup of 4 waves per CU for 128-row tiles), which wins at mid M where
-  // each workgroup is latency-bound: K = 5120, N = 13824 at M = 64 / 128 / 256 / 512
-  // 26.9 -> 23.3, 37.7 -> 31.2, 57.4 -> 52.0, 95.2 -> 88.1 us (register-staged, 3-4
-  // sets ahead before).  Depths 3, 4, 6 (register sets in flight, 64 x 128 tiles) and 5
-  // (direct-to-LDS, two workgroups per CU) stay compiled for sweeps.
-  p.depth = env_int("W4_GEMM_DEPTH", mid ? 0 : 1);
+  // Loop: depth 7 streams both the X tiles and the packed weights into a three-step LDS
+  // ring (two workgroups per CU, nothing held in registers while in flight): the 128-row
+  // tiles at large M, 1.01-1.11 PFLOP/s at M = 4096 with the clocks warm against
+  // 0.96-1.06 for depth 1 (the next step's X tile in registers); M = 1024, N = 5120 on
+  // 128 x 128 tiles 85.4 -> 73.4 us.  Depth 0 is the
+  // direct-to-LDS pipeline with X tiles four steps ahead (one workgroup of 4 waves per CU
+  // for 128-row tiles), which wins at mid M where each workgroup is latency-bound:
+  // K = 5120, N = 13824 at M = 64 / 128 / 256 / 512 26.9 -> 23.3, 37.7 -> 31.2,
+  // 57.4 -> 52.0, 95.2 -> 88.1 us (register-staged, 3-4 sets ahead before).  Depths 3, 4,
+  // 6 (register sets in flight, 64 x 128 tiles) and 5 (X direct-to-LDS, weights in
+  // registers, two workgroups per CU) stay compiled for sweeps.
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? 0 : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipeline addresses X with 32-bit element offsets
-  if ((p.depth == 0 || p.depth == 5) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;
+  if ((p.depth == 0 || p.depth == 5 || p.depth == 7) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;
   p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
   p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
   const int ktiles = K / BK;

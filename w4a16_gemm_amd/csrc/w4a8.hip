@@ -325,7 +325,7 @@ __device__ __forceinline__ half_t cscale_or_one(const half_t* cs, int n) { retur
 // Two workgroups per CU for the one-group-ahead loop; the deeper variants (mid M, grids
 // of a few hundred workgroups) may take a CU's whole register file.
 template <int MI, int MODE, int PD>
-__global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
+__global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_a, const uint32_t* __restrict__ qweight,
     const int8_t* __restrict__ gscale, const half_t* __restrict__ cscale, half_t* __restrict__ y,
     int32_t* __restrict__ acc_out, unsigned* __restrict__ counters, int32_t* __restrict__ partials, int M, int N,
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
   constexpr int BM = 32 * MI;
   constexpr bool TWO = MODE == kI4TwoLevel;
   constexpr int NB = MODE == kI8 ? 4 : 2;  // 16-byte weight chunks per lane, fragment and group
-  constexpr bool kDma = PD == 0;
+  constexpr bool kDma = PD == 0 || PD == 5;
   __shared__ u32x4 lds[kDma ? 1 : 2][kDma ? 1 : BM * 8];
 
   const int ng = K / WBK;
@@ -487,17 +487,16 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
     // issues the same kPerStage loads per thread, so "at most 2 kPerStage outstanding" means
     // group t's loads are complete; a barrier then makes the whole tile visible and frees
     // the slot and set of group t - 1 for group t + 3.  Loads past the range are clamped.
+    // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5)
+    constexpr int R = PD == 5 ? 3 : kRing8;
     constexpr int kPerStage = kPer + 2 * NB + (TWO ? 2 : 0);
-    constexpr int kWaitImm = vmcnt_imm8(2 * kPerStage);
-    // chunk i of this thread lands at LDS position (4 i + wave) * 64 + lane and holds the
-    // xq chunk the swizzle puts there: row r = P / 8, k-chunk (P % 8) ^ ((r / 2) % 8)
-    uint32_t aoff[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int pos = (4 * i + wave) * 64 + lane;
-      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
-      aoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)(c * 16);
-    }
+    constexpr int kWaitImm = vmcnt_imm8((R - 2) * kPerStage);
+    // chunk i of this thread lands at LDS position P = (4 i + wave) * 64 + lane and holds
+    // the xq chunk the swizzle puts there: row r = P / 8 = 32 i + 8 wave + lane / 8,
+    // k-chunk (P % 8) ^ ((r / 2) % 8), the same chunk for every i (r / 2 moves by 16 per i);
+    // the row offsets are formed at each issue (no registers held for them)
+    const int arow0 = m0 + 8 * wave + (lane >> 3);
+    const uint32_t acol = (uint32_t)((((lane & 7) ^ (((8 * wave + (lane >> 3)) >> 1) & 7))) * 16);
     // one LDS array per ring slot (the compiler's wait insertion tells loads into distinct
     // arrays apart)
     __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8];
@@ -506,21 +505,25 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
       u32x4 b[2][NB];
       int sg[2];
     };
-    Stage st[kRing8];
+    Stage st[R];
     auto issue = [&](int g, int slot, Stage& S) {
       load_b(g, S.b);
       S.sg[0] = S.sg[1] = 1;
       load_sg(g, S.sg);
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(xq + aoff[i] + g * WBK),
+        __builtin_amdgcn_global_load_lds(
+            (void*)(xq + (uint32_t)min(arow0 + 32 * i, M - 1) * (uint32_t)K + acol + g * WBK),
                                          (__attribute__((address_space(3))) void*)(ring(slot) + (4 * i + wave) * 64), 16, 0,
                                          0);
     };
     auto step = [&](int t, int j) {
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_s_barrier();
-      issue(min(t + kRing8 - 1, gend - 1), (j + kRing8 - 1) % kRing8, st[(j + kRing8 - 1) % kRing8]);
+      // nothing that reads this step's registers may be scheduled above the wait (the
+      // compiler's own wait for such a read drains every load in flight)
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(t + R - 1, gend - 1), (j + R - 1) % R, st[(j + R - 1) % R]);
       const Stage& S = st[j];
       const u32x4* xa = ring(j);
       u16x2 sp[2], cp[2];
@@ -532,15 +535,24 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
           cp[f] = u16x2{(unsigned short)(-8 * sg), (unsigned short)(-8 * sg)};
         }
       }
-      int4_t afr[2][MI];  // A fragments of k32 steps s (in use) and s + 1 (in flight)
+      // A fragments of k32 steps s (in use) and s + 1 (in flight) with one wave per SIMD;
+      // with two, the other wave covers the LDS latency and the registers are short
+      constexpr bool kAhead = PD == 0;
+      int4_t afr[2][MI];
+      if (kAhead) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4)]);
+        for (int i = 0; i < MI; ++i) afr[0][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4)]);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if (s < 3) {
+        if (kAhead && s < 3) {
 #pragma unroll
           for (int i = 0; i < MI; ++i)
             afr[(s + 1) & 1][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4 + s + 1)]);
+        }
+        if (!kAhead) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) afr[s & 1][i] = __builtin_bit_cast(int4_t, xa[swz8(i * 32 + col, h * 4 + s)]);
         }
         int4_t bf[2];
 #pragma unroll
@@ -571,14 +583,14 @@ __global__ __launch_bounds__(kWThreads, PD == 1 ? 2 : 1) void w4a8_gemm_kernel(
     const int nsteps = gend - gbeg;
     if (nsteps > 0) {
 #pragma unroll
-      for (int d = 0; d < kRing8 - 1; ++d) issue(min(gbeg + d, gend - 1), d, st[d]);
+      for (int d = 0; d < R - 1; ++d) issue(min(gbeg + d, gend - 1), d, st[d]);
       int it = 0;
-      for (; it + kRing8 <= nsteps; it += kRing8) {
+      for (; it + R <= nsteps; it += R) {
 #pragma unroll
-        for (int j = 0; j < kRing8; ++j) step(gbeg + it + j, j);
+        for (int j = 0; j < R; ++j) step(gbeg + it + j, j);
       }
 #pragma unroll
-      for (int j = 0; j < kRing8; ++j)
+      for (int j = 0; j < R; ++j)
         if (it + j < nsteps) step(gbeg + it + j, j);
       // no LDS write may still be in flight when the workgroup's LDS is released
       __builtin_amdgcn_s_waitcnt(vmcnt_imm8(0));
@@ -945,16 +957,26 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
     p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
     return p;
   }
-  // Row-tile height and register sets of loads in flight (1: one group ahead), from
-  // sweeps at K = 5120, N = 13824 over the three weight formats: 32-row tiles four
-  // groups deep up to M = 128 (M = 128 per-channel 54.0 -> 23.0 us), 64-row tiles four
-  // deep up to 256 (57.6 -> 34.3), 64-row tiles one ahead up to 512, 128 rows above.
+  // Row-tile height and loop, from sweeps at K = 5120, N = 13824 over the three weight
+  // formats (clocks warm, weights streamed from HBM): 32-row tiles with four register
+  // sets of loads in flight up to M = 128 (M = 128 per-channel 54.0 -> 23.0 us against
+  // one ahead); 64-row tiles up to 512 with the four-tile direct-to-LDS ring (depth 0:
+  // per-channel / two-level / int8 weights at M = 256 33.9 / 48.0 / 41.9 us with four
+  // register sets -> 30.5 / 41.0 / 40.0, at M = 512 58.0 / 72.7 / 65.0 one group ahead
+  // -> 46.1 / 62.0 / 61.4); 128-row tiles above 512, per-channel weights with the
+  // three-tile ring at two workgroups per CU (depth 5: M = 4096 321.9 -> 270.5 us), the
+  // others one group ahead.
   p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
-  p.depth = env_int("W4_W4A8_DEPTH", M <= 256 ? 4 : 1);
+  const int dflt = p.bm == 32 ? 4 : p.bm == 64 ? 0 : (group_size == -1 ? 5 : 1);
+  p.depth = env_int("W4_W4A8_DEPTH", dflt);
   // depth 0: the direct-to-LDS pipeline (64- and 128-row tiles; 32-bit xq offsets)
   if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4)) ||
-        (p.depth == 0 && p.bm >= 64 && (int64_t)M * K < (int64_t(1) << 31))))
+        (p.depth == 0 && p.bm >= 64 && (int64_t)M * K < (int64_t(1) << 31)) ||
+        // depth 5: three-tile direct-to-LDS ring, two workgroups per CU (128-row tiles only
+        // with per-channel weights: the other formats' register sets do not fit)
+        (p.depth == 5 && (p.bm == 64 || (p.bm == 128 && group_size == -1)) &&
+         (int64_t)M * K < (int64_t(1) << 31))))
     p.depth = 1;
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + WBN - 1) / WBN;
@@ -1029,11 +1051,12 @@ hipError_t launch_int8_gemm(const W4A8Plan& p, int mode, const int8_t* xq, const
   }
 #define W4A8_LAUNCH_MI(MODE) \
   W4A8_LAUNCH(1, MODE, 1) W4A8_LAUNCH(2, MODE, 1) W4A8_LAUNCH(4, MODE, 1) W4A8_LAUNCH(1, MODE, 4) \
-  W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4) W4A8_LAUNCH(4, MODE, 0) W4A8_LAUNCH(2, MODE, 0)
+  W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4) W4A8_LAUNCH(4, MODE, 0) W4A8_LAUNCH(2, MODE, 0)    \
+  W4A8_LAUNCH(2, MODE, 5)
   const int mi = p.bm / 32;
   if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); }
   else if (mode == kI8) { W4A8_LAUNCH_MI(kI8); }
-  else { W4A8_LAUNCH_MI(kI4PerChannel); }
+  else { W4A8_LAUNCH_MI(kI4PerChannel); W4A8_LAUNCH(4, kI4PerChannel, 5); }
 #undef W4A8_LAUNCH_MI
 #undef W4A8_LAUNCH
   return hipErrorInvalidValue;
