@@ -36,7 +36,10 @@ Readings where the pages are silent:
 * R4 packing is the plain nibble order: element ``8*j + i`` of a packed axis
   lives in bits ``4*i .. 4*i+3`` of word ``j``; pad nibbles are 0.
   Layouts: the codes of row n form words ``j = 0 .. K/8-1`` (packed along K);
-  ``qweight`` stores these words tiled as int32 [ceil(N/16), K/128, 4, 16, 4]:
+  the W4A16 ``qweight`` holds each word with its codes split by parity (the even
+  elements ``i = 0, 2, 4, 6`` in nibbles 0..3, the odd ones ``i = 1, 3, 5, 7``
+  in nibbles 4..7: element i at nibble ``i // 2 + 4 * (i % 2)``), and stores the
+  words tiled as int32 [ceil(N/16), K/128, 4, 16, 4]:
   word j of row n sits at ``[n // 16, j // 16, (j % 16) // 4, n % 16, j % 4]``
   (one 1 KB block holds 16 rows x 128 k; rows past N are padding with code 0,
   or q = 0 for W4A8).  ``scales`` fp16 [K/G, N]; ``qzeros`` int32
@@ -100,7 +103,7 @@ F32 = np.float32
 F64 = np.float64
 
 __all__ = [
-    "pack_nibbles", "unpack_nibbles", "tile_words", "untile_words",
+    "pack_nibbles", "unpack_nibbles", "split_parity", "merge_parity", "tile_words", "untile_words",
     "quantize_asym", "quantize_sym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref", "quantize_w8a8",
@@ -147,6 +150,32 @@ def unpack_nibbles(words: np.ndarray, C: int) -> np.ndarray:
     for i in range(8):
         out[:, i::8] = (u >> (4 * i)) & 0xF
     return out[:, :C]
+
+
+def split_parity(words: np.ndarray) -> np.ndarray:
+    """Plain words -> the W4A16 qweight's word format (R4): element ``i`` of each word
+    (plain nibble i) moves to nibble ``i // 2 + 4 * (i % 2)``, so the even elements fill
+    the low half-word and the odd ones the high half-word, each half in element order."""
+    words = np.asarray(words)
+    if words.dtype != np.int32:
+        raise ValueError("words must be int32")
+    u = words.view(np.uint32).astype(np.int64)
+    out = np.zeros_like(u)
+    for i in range(8):
+        out |= ((u >> (4 * i)) & 0xF) << (4 * (i // 2 + 4 * (i % 2)))
+    return out.astype(np.uint32).view(np.int32)
+
+
+def merge_parity(words: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`split_parity`."""
+    words = np.asarray(words)
+    if words.dtype != np.int32:
+        raise ValueError("words must be int32")
+    u = words.view(np.uint32).astype(np.int64)
+    out = np.zeros_like(u)
+    for i in range(8):
+        out |= ((u >> (4 * (i // 2 + 4 * (i % 2)))) & 0xF) << (4 * i)
+    return out.astype(np.uint32).view(np.int32)
 
 
 def tile_words(words: np.ndarray, pad_word: int = 0) -> np.ndarray:
@@ -244,7 +273,7 @@ def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
     N, K = codes.shape
     if K % 128:
         raise ValueError("K must be a multiple of 128")
-    qweight = tile_words(pack_nibbles(codes))
+    qweight = tile_words(split_parity(pack_nibbles(codes)))
     scales_gn = np.ascontiguousarray(np.asarray(scales, dtype=F16).T)
     qzeros = pack_nibbles(np.ascontiguousarray(np.asarray(zeros).T))
     return qweight, scales_gn, qzeros
@@ -253,7 +282,7 @@ def pack_awq(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
 def unpack_awq(qweight: np.ndarray, scales_gn: np.ndarray, qzeros: np.ndarray, K: int):
     """Packed layout -> ``(codes [N, K], scales fp16 [N, K/G], zeros [N, K/G])``."""
     N = scales_gn.shape[1]
-    codes = unpack_nibbles(untile_words(qweight, N), K)
+    codes = unpack_nibbles(merge_parity(untile_words(qweight, N)), K)
     scales = np.ascontiguousarray(scales_gn.T)
     zeros = np.ascontiguousarray(unpack_nibbles(qzeros, N).T)
     return codes, scales, zeros

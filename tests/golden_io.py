@@ -22,9 +22,9 @@ def _values(tokens):
     return np.array(out, dtype=np.float16)
 
 
-def read_pack_words():
+def read_pack_words(name="pack_words.txt"):
     rows = []
-    for line in open(os.path.join(GOLDEN, "pack_words.txt")):
+    for line in open(os.path.join(GOLDEN, name)):
         line = line.strip()
         if not line or line.startswith("#"):
             continue

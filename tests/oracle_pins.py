@@ -60,6 +60,33 @@ def pin_pack_bijection(ora):
     assert np.all((w2.view(np.uint32)[:, 2] >> 20) == 0)  # 3 pad nibbles are zero
 
 
+def pin_parity_words(ora):
+    """Worked words of the W4A16 qweight's parity-split word format
+    (tests/golden/parity_words.txt): the plain word of the codes, split, gives the
+    listed word; merging it gives the plain word back; and a single code at element i
+    of a word lands, after pack_awq, in nibble i // 2 + 4 (i % 2) of the one nonzero
+    qweight word (element 8 j + i of a row)."""
+    for codes, word in read_pack_words("parity_words.txt"):
+        plain = ora.pack_nibbles(np.array([codes], dtype=np.uint8))
+        got = ora.split_parity(plain)
+        assert int(got.view(np.uint32)[0, 0]) == word, (codes, hex(int(got.view(np.uint32)[0, 0])), hex(word))
+        back = ora.merge_parity(np.array([[np.uint32(word)]], dtype=np.uint32).view(np.int32))
+        assert np.array_equal(back, plain)
+    nib = {0: 0, 1: 4, 2: 1, 3: 5, 4: 2, 5: 6, 6: 3, 7: 7}  # element -> nibble, by hand
+    N, K = 3, 128
+    for k in range(0, 16):
+        codes = np.zeros((N, K), np.uint8)
+        codes[1, k] = 11
+        qw, _, _ = ora.pack_awq(codes, np.ones((N, 1), F16), np.zeros((N, 1), np.uint8))
+        flat = qw.reshape(-1).view(np.uint32)
+        off = ((k % 128) // 32) * 64 + 1 * 4 + (k % 32) // 8
+        assert np.count_nonzero(flat) == 1 and int(flat[off]) == 11 << (4 * nib[k % 8]), k
+    rng = _rng(9)
+    words = rng.integers(0, 2**32, size=(64, 5), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    assert np.array_equal(ora.merge_parity(ora.split_parity(words)), words)
+    assert np.array_equal(ora.split_parity(ora.merge_parity(words)), words)
+
+
 def pin_tile_layout(ora):
     """Tiled word order: a single code placed at (n, k) lands in exactly one word of
     the flat qweight, at the offset computed by hand from the layout rule
@@ -520,7 +547,7 @@ def pin_w4a8_acc_bruteforce(ora):
 
 
 ALL_PINS = [
-    pin_pack_words, pin_pack_bijection, pin_tile_layout,
+    pin_pack_words, pin_pack_bijection, pin_parity_words, pin_tile_layout,
     pin_asym_worked, pin_asym_constructed, pin_asym_roundtrip_bound,
     pin_fraction_bruteforce, pin_identity_probe, pin_per_channel_special_case,
     pin_constructed_exact_gemm,

@@ -21,6 +21,9 @@ MUTANTS = [
     ("dequant drops zero", "(codes.astype(F64) - z) * s", "codes.astype(F64) * s"),
     ("pack nibble order reversed", "words += padded[:, i::8] << (4 * i)", "words += padded[:, i::8] << (4 * (7 - i))"),
     ("unpack nibble order reversed", "out[:, i::8] = (u >> (4 * i)) & 0xF", "out[:, i::8] = (u >> (4 * (7 - i))) & 0xF"),
+    ("parity split reversed", "out |= ((u >> (4 * i)) & 0xF) << (4 * (i // 2 + 4 * (i % 2)))", "out |= ((u >> (4 * i)) & 0xF) << (4 * (4 * (i % 2) + 3 - i // 2))"),
+    ("parity merge identity", "out |= ((u >> (4 * (i // 2 + 4 * (i % 2)))) & 0xF) << (4 * i)", "out |= ((u >> (4 * i)) & 0xF) << (4 * i)"),
+    ("awq qweight without the parity split", "qweight = tile_words(split_parity(pack_nibbles(codes)))", "qweight = tile_words(pack_nibbles(codes))"),
     ("tile rows and slots swapped", "out[:, :, slot, n, w] = full[n::16, slot * 4 + w::16]", "out[:, :, slot, n, w] = full[n::16, (w * 4 + slot)::16]"),
     ("untile rows and slots swapped", "full[n::16, slot * 4 + w::16] = tiled[:, :, slot, n, w]", "full[n::16, (w * 4 + slot)::16] = tiled[:, :, slot, n, w]"),
     ("scales not transposed", "scales = np.ascontiguousarray(scales_gn.T)", "scales = np.ascontiguousarray(scales_gn).reshape(scales_gn.shape[::-1])"),
