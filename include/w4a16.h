@@ -29,8 +29,11 @@
  *   Y        fp16  [M, N]
  *   W        fp16  [N, K]            (out, in)
  *   qweight  int32 [ceil(N/16), K/128, 4, 16, 4]
- *                                    codes packed along K in plain nibble order (element
- *                                    k = 8j+i of row n in bits 4i..4i+3 of that row's word j),
+ *                                    codes packed 8 per word along K, each word split by
+ *                                    parity: element k = 8j+i of row n in nibble
+ *                                    i/2 + 4(i%2) of that row's word j (the even i in the
+ *                                    low half-word, the odd i in the high one, each half in
+ *                                    element order: nibbles hold i = 0,2,4,6,1,3,5,7),
  *                                    words stored tiled: word j of row n sits at
  *                                    [n/16][j/16][(j%16)/4][n%16][j%4], i.e. 1 KB blocks of
  *                                    16 rows x 128 k; rows past N are padding (code 0)
@@ -38,7 +41,8 @@
  *   qzeros   int32 [K/G, ceil(N/8)]  4-bit zero points packed along N, plain nibble
  *                                    order, pad nibbles 0 ([1, ceil(N/8)] per-channel)
  *   (W4A8)   qweight int32 [ceil(N/16), K/128, 4, 16, 4] (same tiling) of biased nibbles
- *            q + 8 (q in [-8, 7]; padding rows q = 0),
+ *            q + 8 in plain nibble order (element 8j+i in bits 4i..4i+3 of word j; q in
+ *            [-8, 7]; padding rows q = 0),
  *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
  *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
  *   (W8A8)   qweight int8 [ceil(N/16), K/128, 4, 2, 16, 16]: code (n, k) at
@@ -119,8 +123,9 @@ enum { W4_LAYOUT_ROWS = 0, W4_LAYOUT_COLS = 1 };
 
 /*
  * awq_import_plain -- convert W4A16 weights quantized elsewhere from a plain layout
- * (see W4_LAYOUT_*) into the layout awq_gemm reads (tiled qweight, scales [K/G, N],
- * qzeros [K/G, ceil(N/8)], top of this file).  A pure rearrangement of bits: the
+ * (see W4_LAYOUT_*) into the layout awq_gemm reads (parity-split words tiled into
+ * qweight, scales [K/G, N], qzeros [K/G, ceil(N/8)], top of this file).  A pure
+ * rearrangement of bits: the
  * outputs equal what awq_pack writes for the same codes, scales and zero points
  * (padding rows of qweight are code 0).  All six pointers are device pointers owned by
  * the caller, 16-byte aligned, non-NULL for N > 0; inputs and outputs must not overlap.
@@ -165,7 +170,9 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_s
  * The packed operands are in this library's layout (top of this file), not the
  * row-major qweight [N, K/8], scales [N, K/G], qzeros [N, ceil(K/G/8)] of a plain
  * export: with row-major words every wave load of the decode kernels touched 16
- * separate 64-byte pieces and ran ~40 % slower than the 1 KB tiles.  Weights in a plain
+ * separate 64-byte pieces and ran ~40 % slower than the 1 KB tiles, and the
+ * parity-split words expand to fp16 in five VALU operations with X in its natural
+ * order (plain words take eight, or five plus a permutation of X).  Weights in a plain
  * layout come in once through awq_import_plain.
  */
 int awq_gemm(const void* x, const int32_t* qweight, const void* scales, const int32_t* qzeros,

@@ -53,12 +53,15 @@ __device__ __forceinline__ int64_t tiled_chunk(int n, int g, int slot, int ng) {
 }
 
 // ------------------------------------------------------ nibble unpacking
-// One packed word holds 8 consecutive elements e_0..e_7 (e_i in bits 4i..4i+3).
-// unpack_1024: four registers of packed fp16 pairs (1024 + e_{2p}, 1024 + e_{2p+1}),
-// p = 0..3, i.e. the 8 elements in natural order as half8, each exactly 1024 + code.
-// 0x6400 is fp16 1024.0; a code c in the low mantissa bits gives 1024 + c exactly.
-// v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7 of the
-// first, 0x0c gives 0.
+// A W4A16 code word holds 8 consecutive elements e_0..e_7 split by parity: e_0, e_2,
+// e_4, e_6 in nibbles 0..3 (the low half-word), e_1, e_3, e_5, e_7 in nibbles 4..7.
+// Masking the word with 0x000f000f puts e_0 and e_1 each in the low mantissa bits of
+// one half; ORing in 0x6400 (fp16 1024, unit steps) makes them fp16 1024 + e exactly.
+// Masking with 0x00f000f0 puts e_2 and e_3 in mantissa bits 4..7, which under fp16 64
+// (0x5400, steps of 1/16) are worth 64 + e exactly.  The word shifted right by 8 gives
+// e_4, e_5 and e_6, e_7 the same way: four registers of fp16 pairs in natural element
+// order, (1024 + e_0, 1024 + e_1), (64 + e_2, 64 + e_3), (1024 + e_4, 1024 + e_5),
+// (64 + e_6, 64 + e_7), in one shift and four v_and_or_b32.
 // (x & mask) | bits in one v_and_or_b32.  VOP3 encodings on gfx9 take no literal
 // constants, so with literal operands the expression compiles to a separate v_and_b32
 // and v_or_b32.  The constants are therefore passed through vreg(), an empty asm that
@@ -74,29 +77,49 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t b
   return (x & mask) | bits;
 }
 
-__device__ __forceinline__ half8_t unpack_1024(uint32_t w) {
-  const uint32_t s = w >> 4;
-  const uint32_t mask = vreg(0x000f000fu), magic = vreg(0x64006400u);
+// The magic constants of the expansion, held in registers: masks 0x000f000f (mlo),
+// 0x00f000f0 (mhi), fp16 pairs 1024 (e1024) and 64 (e64).
+struct Magic {
+  uint32_t mlo, mhi, e1024, e64;
+};
+__device__ __forceinline__ Magic magic_regs() {
+  return Magic{vreg(0x000f000fu), vreg(0x00f000f0u), vreg(0x64006400u), vreg(0x54005400u)};
+}
+__device__ __forceinline__ u32x4 expand_word(uint32_t w, const Magic& c) {
+  const uint32_t w8 = w >> 8;
   u32x4 r;
-  r[0] = and_or(__builtin_amdgcn_perm(s, w, 0x0c040c00u), mask, magic);
-  r[1] = and_or(__builtin_amdgcn_perm(s, w, 0x0c050c01u), mask, magic);
-  r[2] = and_or(__builtin_amdgcn_perm(s, w, 0x0c060c02u), mask, magic);
-  r[3] = and_or(__builtin_amdgcn_perm(s, w, 0x0c070c03u), mask, magic);
-  return __builtin_bit_cast(half8_t, r);
+  r[0] = and_or(w, c.mlo, c.e1024);   // 1024 + e0, 1024 + e1
+  r[1] = and_or(w, c.mhi, c.e64);     //   64 + e2,   64 + e3
+  r[2] = and_or(w8, c.mlo, c.e1024);  // 1024 + e4, 1024 + e5
+  r[3] = and_or(w8, c.mhi, c.e64);    //   64 + e6,   64 + e7
+  return r;
 }
 
-// Exact dequantization of one word: ((1024 + q) - (1024 + z)) is the exact integer
-// q - z in fp16, then one multiply by the fp16 scale: a single rounding per element.
-// negz2 = -(1024 + z) in both halves, s2 = scale in both halves.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t negz2, half2_t s2) {
-  half8_t v = unpack_1024(w);
-  half2_t p0 = {v[0], v[1]}, p1 = {v[2], v[3]}, p2 = {v[4], v[5]}, p3 = {v[6], v[7]};
-  p0 = (p0 + negz2) * s2;
-  p1 = (p1 + negz2) * s2;
-  p2 = (p2 + negz2) * s2;
-  p3 = (p3 + negz2) * s2;
-  half8_t o = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  return o;
+// Exact dequantization of one word: ((1024 + q) - (1024 + z)) and ((64 + q) - (64 + z))
+// are the exact integer q - z in fp16, then one multiply by the fp16 scale: a single
+// rounding per element.  c1024 = -(1024 + z) and c64 = -(64 + z) in both halves (bit
+// patterns 0xE400 | z and 0xD400 | 16 z), s2 = scale in both halves.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, const Magic& c, half2_t c1024, half2_t c64, half2_t s2) {
+  const u32x4 r = expand_word(w, c);
+  half2_t p0 = __builtin_bit_cast(half2_t, (uint32_t)r[0]);
+  half2_t p1 = __builtin_bit_cast(half2_t, (uint32_t)r[1]);
+  half2_t p2 = __builtin_bit_cast(half2_t, (uint32_t)r[2]);
+  half2_t p3 = __builtin_bit_cast(half2_t, (uint32_t)r[3]);
+  p0 = (p0 + c1024) * s2;
+  p1 = (p1 + c64) * s2;
+  p2 = (p2 + c1024) * s2;
+  p3 = (p3 + c64) * s2;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+// -(1024 + z) and -(64 + z) in both halves of a register, and s twice, as bit patterns.
+__device__ __forceinline__ half2_t neg1024z2(uint32_t z) {
+  return __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
+}
+__device__ __forceinline__ half2_t neg64z2(uint32_t z) {
+  return __builtin_bit_cast(half2_t, (0xD400u | (z << 4)) * 0x00010001u);
+}
+__device__ __forceinline__ half2_t scale2(uint32_t sbits) {
+  return __builtin_bit_cast(half2_t, sbits * 0x00010001u);
 }
 
 __device__ __forceinline__ half2_t splat2(half_t h) { return half2_t{h, h}; }

@@ -7,11 +7,11 @@
 // GEMM runs dequantized fp16 weights through the tensor cores; dequantization is the
 // tricky part and the rest is normal FP16 work.  On gfx950 the same split holds: the
 // MFMA does the FP16 work; the dequantization is amortized over the 128 rows of a wave
-// tile.  A word is expanded in 5 VALU ops to fp16 (1024 + q) at even k (code in the low
-// mantissa bits under exponent 2^10) and (64 + q) at odd k (code in mantissa bits 4..7
-// under exponent 2^6), in the k order 0,4,1,5,2,6,3,7; subtracting 1024 + z or 64 + z is
-// exact, and the multiply by s is the element's single fp16 rounding (4 packed adds, 4
-// packed multiplies).  X chunks are permuted to the same k order when staged in LDS.
+// tile.  A parity-split word is expanded in natural k order in 5 VALU ops to fp16
+// (1024 + q) at k = 0, 1 mod 4 (code in the low mantissa bits under exponent 2^10) and
+// (64 + q) at k = 2, 3 mod 4 (code in mantissa bits 4..7 under exponent 2^6);
+// subtracting 1024 + z or 64 + z is exact, and the multiply by s is the element's single
+// fp16 rounding (4 packed adds, 4 packed multiplies).  X stays in natural order.
 //
 // Tile: BM x BN x BK = (32 MI) x (128 NF) x 64, 256 threads, (MI, NF) in {4, 2} x {2, 1}.
 // The 4 waves split N: wave w owns 32 NF columns as NF 32-column MFMA fragments, and
@@ -31,9 +31,6 @@
 // that are still too small, with partials summed by the last arriving workgroup in
 // split order (deterministic).
 #include "kernels.hpp"
-#ifndef SFX
-#define SFX true
-#endif
 
 namespace w4 {
 
@@ -142,11 +139,6 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   // loads into that freed slot and set, then the MFMAs of step t.  Loads past the last step
   // are clamped to it (they refill slots no later step reads), so the counts stay uniform.
   //
-  // With X in LDS in its natural k order, each code word is expanded in natural order too:
-  // byte p of the word holds k = 2p (low nibble) and 2p + 1 (high nibble); v_perm_b32 puts
-  // it under fp16 1024 in the low half and under fp16 64 in the high half, and one AND keeps
-  // the low nibble and the high nibble respectively: (1024 + q_2p, 64 + q_2p+1).  Then the
-  // exact subtraction of (1024 + z, 64 + z) and the multiply by s (one rounding).
     // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5, registers)
     constexpr int R = (PD == 5 || PD == 7) ? 3 : kRing;
     constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
@@ -204,15 +196,13 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
                                          (__attribute__((address_space(3))) void*)(ring(slot) + (4 * i + wave) * 64), 16, 0,
                                          0);
     };
-    const uint32_t magic = vreg(0x00005464u);  // bytes 0x64 (fp16 1024 high byte), 0x54 (fp16 64)
-    const uint32_t keep = vreg(0xfff0ff0fu);
-    constexpr bool kSchedFence = SFX && !(MI == 2 && NF == 1 && PD == 0);
+    const Magic mc = magic_regs();
     auto step = [&](int t, int j) {
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_s_barrier();
       // nothing that reads this step's registers may be scheduled above the wait (the
       // compiler's own wait for such a read drains every load in flight)
-      if (kSchedFence) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
       issue(min(t + R - 1, kend - 1), (j + R - 1) % R, bs[(j + R - 1) % R]);
       const BSet& S = bs[j];
       u32x4 bw[NF];
@@ -221,12 +211,13 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         if constexpr (kBLds) bw[f] = bring(j)[(4 * f + wave) * 64 + lane];
         else bw[f] = S.b[f];
       }
-      half2_t cz[NF], s2[NF];
+      half2_t c1024[NF], c64[NF], s2[NF];
   #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const uint32_t z = (S.z[f] >> (4 * (nclamp[f] & 7))) & 15u;
-        cz[f] = __builtin_bit_cast(half2_t, (0xE400u | z) | ((0xD400u | (z << 4)) << 16));
-        s2[f] = __builtin_bit_cast(half2_t, S.s[f] * 0x00010001u);
+        c1024[f] = neg1024z2(z);
+        c64[f] = neg64z2(z);
+        s2[f] = scale2(S.s[f]);
       }
       const u32x4* xa = ring(j);
       // A fragments of k16 steps s (in use) and s + 1 (in flight) with one wave per SIMD;
@@ -250,22 +241,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         }
         half8_t bf[NF];
   #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint32_t w = bw[f][s];
-          u32x4 pr;
-  #pragma unroll
-          for (int p = 0; p < 4; ++p)
-            pr[p] = __builtin_amdgcn_perm(magic, w, (5u << 24) | ((uint32_t)p << 16) | (4u << 8) | (uint32_t)p) & keep;
-          half2_t p0 = __builtin_bit_cast(half2_t, (uint32_t)pr[0]);
-          half2_t p1 = __builtin_bit_cast(half2_t, (uint32_t)pr[1]);
-          half2_t p2 = __builtin_bit_cast(half2_t, (uint32_t)pr[2]);
-          half2_t p3 = __builtin_bit_cast(half2_t, (uint32_t)pr[3]);
-          p0 = (p0 + cz[f]) * s2[f];
-          p1 = (p1 + cz[f]) * s2[f];
-          p2 = (p2 + cz[f]) * s2[f];
-          p3 = (p3 + cz[f]) * s2[f];
-          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
+        for (int f = 0; f < NF; ++f) bf[f] = dequant8(bw[f][s], mc, c1024[f], c64[f], s2[f]);
   #pragma unroll
         for (int i = 0; i < MI; ++i)
   #pragma unroll
@@ -307,13 +283,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   #pragma unroll
       for (int i = 0; i < kAPer; ++i) {
         const int cid = threadIdx.x + i * kThreads;
-        const u32x4 v = areg[i];
-        u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching dequant_mixed
-        o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-        o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-        o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-        o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-        lds[buf][swz(cid >> 3, cid & 7)] = o;
+        lds[buf][swz(cid >> 3, cid & 7)] = areg[i];
       }
     };
     u32x4 breg[NF];
@@ -349,7 +319,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         s2[f] = __builtin_bit_cast(half2_t, sraw[f] * 0x00010001u);
       }
     };
-    const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+    const Magic mc = magic_regs();
 
     if (kbeg < kend) {
       load_a(kbeg);
@@ -377,19 +347,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
       for (int s = 0; s < 4; ++s) {
         half8_t bf[NF];
   #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint32_t w = breg[f][s];
-          const uint32_t w8 = w >> 8;
-          half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
-          half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
-          half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
-          half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
-          p0 = (p0 + c1024[f]) * s2[f];
-          p1 = (p1 + c64[f]) * s2[f];
-          p2 = (p2 + c1024[f]) * s2[f];
-          p3 = (p3 + c64[f]) * s2[f];
-          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
+        for (int f = 0; f < NF; ++f) bf[f] = dequant8(breg[f][s], mc, c1024[f], c64[f], s2[f]);
   #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
@@ -441,16 +399,10 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   #pragma unroll
       for (int i = 0; i < kAPer; ++i) {
         const int cid = threadIdx.x + i * kThreads;
-        const u32x4 v = S.a[i];
-        u32x4 o;  // k order 0,4,1,5,2,6,3,7 within the chunk, matching the dequantization
-        o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-        o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-        o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-        o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-        lds[buf][swz(cid >> 3, cid & 7)] = o;
+        lds[buf][swz(cid >> 3, cid & 7)] = S.a[i];
       }
     };
-    const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+    const Magic mc = magic_regs();
     // One BK step t on register set `cur` (B, scales, zero points) and LDS buffer
     // (t - kbeg) & 1 (its X tile); then the X tile of step t + 1 (set `nxt`) goes to the
     // other buffer, and after the barrier set `cur` is refilled with step t + PD's loads
@@ -473,19 +425,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
       for (int s = 0; s < 4; ++s) {
         half8_t bf[NF];
   #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint32_t w = S.b[f][s];
-          const uint32_t w8 = w >> 8;
-          half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, mlo, e1024));   // 1024 + q0, q4
-          half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, mhi, e64));     //   64 + q1, q5
-          half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, mlo, e1024));  // 1024 + q2, q6
-          half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, mhi, e64));    //   64 + q3, q7
-          p0 = (p0 + c1024[f]) * s2[f];
-          p1 = (p1 + c64[f]) * s2[f];
-          p2 = (p2 + c1024[f]) * s2[f];
-          p3 = (p3 + c64[f]) * s2[f];
-          bf[f] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
+        for (int f = 0; f < NF; ++f) bf[f] = dequant8(S.b[f][s], mc, c1024[f], c64[f], s2[f]);
   #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const u32x4 av = lds[buf][swz(i * 32 + col, h * 4 + s)];
@@ -601,7 +541,7 @@ GemmPlan gemm_plan(int M, int N, int K) {
   if (forced >= 1 && forced <= 4) {
     pick = forced - 1;
   } else if (mid) {
-    // 64 x 128 tiles with 4 register sets in flight up to M = 256 (K = 5120, N = 13824:
+    // 64 x 128 tiles up to M = 256 (K = 5120, N = 13824, with register sets in flight:
     // M = 64 30.2 -> 26.9 us, M = 128 45.2 -> 37.5, M = 256 62.7 -> 54.2 against the
     // one-step-ahead 128 x 128 / 64 x 128 plans); 128 x 128 above
     pick = (M > 256 && (N >= 8192 || M >= 384)) ? 1 : 3;
@@ -618,18 +558,20 @@ GemmPlan gemm_plan(int M, int N, int K) {
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
   // register sets in flight (BK steps of loads ahead of the MFMAs)
-  // Loop: depth 7 streams both the X tiles and the packed weights into a three-step LDS
-  // ring (two workgroups per CU, nothing held in registers while in flight): the 128-row
-  // tiles at large M, 1.01-1.11 PFLOP/s at M = 4096 with the clocks warm against
-  // 0.96-1.06 for depth 1 (the next step's X tile in registers); M = 1024, N = 5120 on
-  // 128 x 128 tiles 85.4 -> 73.4 us.  Depth 0 is the
-  // direct-to-LDS pipeline with X tiles four steps ahead (one workgroup of 4 waves per CU
-  // for 128-row tiles), which wins at mid M where each workgroup is latency-bound:
-  // K = 5120, N = 13824 at M = 64 / 128 / 256 / 512 26.9 -> 23.3, 37.7 -> 31.2,
-  // 57.4 -> 52.0, 95.2 -> 88.1 us (register-staged, 3-4 sets ahead before).  Depths 3, 4,
-  // 6 (register sets in flight, 64 x 128 tiles) and 5 (X direct-to-LDS, weights in
-  // registers, two workgroups per CU) stay compiled for sweeps.
-  p.depth = env_int("W4_GEMM_DEPTH", mid ? 0 : (pick <= 1 ? 7 : 1));
+  // Loop (K = 5120, N = 13824 unless stated, clocks warm, weights streamed from HBM):
+  //  * depth 7 streams both the X tiles and the packed weights into a three-step LDS ring
+  //    (two workgroups per CU, nothing held in registers while in flight): the 128-row
+  //    tiles at large M, 1.00-1.09 PFLOP/s at M = 4096 (N in {27648, 5120}, and
+  //    K = 13824) against 0.96-1.06 for depth 1 (the next step's X tile in registers);
+  //    M = 1024, N = 5120 on 128 x 128 tiles 85.4 -> 73.3 us;
+  //  * depth 5, X tiles direct-to-LDS three steps ahead and the weights in registers, two
+  //    or more workgroups per CU: the 64 x 128 tiles at mid M, M = 64 / 128 / 256
+  //    25.8 / 35.1 / 50.4 us (27.4 / 36.4 / 52.3 with depth 0);
+  //  * depth 0, X tiles direct-to-LDS four steps ahead, one workgroup of 4 waves per CU
+  //    for 128-row tiles: the 128 x 128 tiles at 256 < M <= 512 (M = 384 / 512 70.9 /
+  //    79.6 us; 95.2 us at M = 512 with register-staged X, 3-4 sets ahead).
+  // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 5 : 0) : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipeline addresses X with 32-bit element offsets
   if ((p.depth == 0 || p.depth == 5 || p.depth == 7) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;

@@ -11,10 +11,10 @@
 //   cols (the printed Triton orientation): qweight int32 [K/8, N], scales fp16 [K/G, N],
 //                              qzeros int32 [ceil(K/G / 8), N].
 // In both, element k = 8j + i of a row's codes sits in bits 4i..4i+3 of word j and the
-// zero point of group g in bits 4 (g % 8).. of word g / 8.  The library keeps the same
-// words tiled in 1 KB blocks of 16 rows x 128 k, the scales group-major [K/G, N] and the
-// zero points packed along N [K/G, ceil(N/8)]; every conversion is a rearrangement of
-// bits (exact).  "[Feature] support qqq(w4a8) for lmdeploy" ("Modification") converts
+// zero point of group g in bits 4 (g % 8).. of word g / 8.  The library keeps the W4A16
+// words split by parity (element i in nibble i / 2 + 4 (i % 2)) and tiled in 1 KB
+// blocks of 16 rows x 128 k, the scales group-major [K/G, N] and the zero points packed
+// along N [K/G, ceil(N/8)]; every conversion is a rearrangement of bits (exact).  "[Feature] support qqq(w4a8) for lmdeploy" ("Modification") converts
 // exported QQQ weights before its GEMM can load them; here the W4A8 words (biased
 // nibbles q + 8) are tiled like the W4A16 ones and the int8 group scales go to [K/G, N].
 #include "kernels.hpp"
@@ -29,13 +29,21 @@ struct Strides {
   int64_t sn, si;
 };
 
+// Plain word -> parity-split word: element i (nibble i) to nibble i / 2 + 4 (i % 2).
+__device__ __forceinline__ uint32_t split_parity(uint32_t w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= ((w >> (4 * i)) & 15u) << (4 * ((i >> 1) + 4 * (i & 1)));
+  return o;
+}
+
 // One thread per 16-byte chunk of the tiled array, in its order (contiguous stores):
 // chunk ((n / 16 * ng + g) * 4 + slot) * 16 + n % 16 holds words 16 g + 4 slot .. + 3 of
 // row n.  Rows past N (up to a multiple of 16) hold the pad word.  In the rows
 // orientation (si == 1) the four words are one aligned 16-byte load.
 __global__ __launch_bounds__(256) void tile_words_kernel(const uint32_t* __restrict__ plain,
                                                          u32x4* __restrict__ tiled, int N, int ng, Strides st,
-                                                         uint32_t pad, int64_t total) {
+                                                         uint32_t pad, int split, int64_t total) {
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(c & 15);
     const int64_t blk = c >> 4;  // (n / 16 * ng + g) * 4 + slot
@@ -52,6 +60,10 @@ __global__ __launch_bounds__(256) void tile_words_kernel(const uint32_t* __restr
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = src[i * st.si];
+      }
+      if (split) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = split_parity(v[i]);
       }
     }
     tiled[c] = v;
@@ -97,11 +109,12 @@ inline unsigned grid_for(int64_t total) {
 
 hipError_t launch_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
                                const int8_t* gscale_plain, int32_t* qweight, void* scales, int32_t* qzeros,
-                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, hipStream_t stream) {
+                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, bool split,
+                               hipStream_t stream) {
   const int64_t chunks = (int64_t)((N + 15) / 16) * (K / 128) * 64;
   const Strides sw = cols ? Strides{1, N} : Strides{K / 8, 1};
   hipLaunchKernelGGL(tile_words_kernel, dim3(grid_for(chunks)), dim3(256), 0, stream, (const uint32_t*)qweight_plain,
-                     (u32x4*)qweight, N, K / 128, sw, pad, chunks);
+                     (u32x4*)qweight, N, K / 128, sw, pad, (int)split, chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t vals = (int64_t)N * ng;

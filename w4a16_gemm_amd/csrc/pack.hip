@@ -2,9 +2,12 @@
 //
 //  * awq_pack: asymmetric 4-bit group quantization ("Some fixes for AWQ",
 //    neuralmagic/compressed-tensors PR 269, opening comment: the asymmetric rule of
-//    AutoAWQ's pseudo-quantize) and packing into the plain nibble order (packed
-//    weight format of the Triton AWQ kernels in "Implement AWQ quantization support
-//    for LLaMA", vllm-project/vllm PR 1032: pack_num = 8 codes per 32-bit word).
+//    AutoAWQ's pseudo-quantize) and packing 8 codes per 32-bit word (packed weight
+//    format of the Triton AWQ kernels in "Implement AWQ quantization support for
+//    LLaMA", vllm-project/vllm PR 1032: pack_num = 8), each word split by parity
+//    (elements 0, 2, 4, 6 in nibbles 0..3, elements 1, 3, 5, 7 in nibbles 4..7: the
+//    order the GEMMs expand in one shift and four v_and_or_b32), in the tiled layout.
+//    The zero points keep the plain nibble order (element i in nibble i).
 //    Per-channel weights (group_size -1: one group over K, a reading of the
 //    per-channel variant named on "[Feature] support qqq(w4a8) for lmdeploy") take
 //    their row statistics from awq_rowstats first.  Symmetric weights (the W4A16
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const half_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q = fminf(fmaxf(rintf((float)h[8 * j + i] / s) + z[u], 0.0f), 15.0f);
-        word |= ((uint32_t)q) << (4 * i);
+        word |= ((uint32_t)q) << (4 * ((i >> 1) + 4 * (i & 1)));  // parity-split word
       }
       ow[j] = word;
     }
@@ -180,10 +183,9 @@ __global__ __launch_bounds__(256) void awq_unpack_dequant_kernel(const uint32_t*
   const int nzw = (N + 7) / 8;
   const int64_t row = (8 * j) >> glog;
   const uint32_t z = (qzeros[row * nzw + n / 8] >> (4 * (n & 7))) & 15u;
-  const half_t s = scales[row * N + n];
-  const half2_t negz2 = splat2(-(half_t)(1024 + z));
+  const uint16_t sb = reinterpret_cast<const uint16_t*>(scales)[row * N + n];
   const uint32_t word = qweight[tiled_chunk(n, g, (j & 15) >> 2, K / 128) + (j & 3)];
-  const half8_t v = dequant8(word, negz2, splat2(s));
+  const half8_t v = dequant8(word, magic_regs(), neg1024z2(z), neg64z2(z), scale2(sb));
   *reinterpret_cast<half8_t*>(out + (int64_t)n * K + (int64_t)j * 8) = v;
 }
 

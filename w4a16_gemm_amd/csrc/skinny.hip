@@ -8,12 +8,12 @@
 //
 //   Y[m,n] = sum_g s[n,g] * ( T_g[m,n] - P_g[m] - z[n,g] * S_g[m] ),
 //   T_g[m,n] = sum_{k in g} X[m,k] * (c_k + q[n,k]),   S_g[m] = sum_{k in g} X[m,k],
-//   P_g[m] = sum_{k in g} c_k X[m,k],   c_k = 1024 for even k, 64 for odd k,
+//   P_g[m] = sum_{k in g} c_k X[m,k],   c_k = 1024 for k = 0, 1 mod 4, 64 for k = 2, 3 mod 4,
 //
 // which equals sum_k X[m,k] * (q - z) * s exactly in real arithmetic.  The MFMA
-// consumes the raw fp16 values c_k + q (five VALU ops per 8 codes, X taken in the
-// matching k order; no per-element subtract or multiply); fp16 x (c_k + q) products
-// are exact in fp32, only the fp32 sums round.
+// consumes the raw fp16 values c_k + q (five VALU ops per 8 codes of a parity-split
+// word, in natural k order like X; no per-element subtract or multiply); fp16
+// x (c_k + q) products are exact in fp32, only the fp32 sums round.
 //
 // Work split (register-X kernel, M <= 32; the kernel further below stages X in LDS and
 // is the default only at M = 1 on wide, short matrices): a workgroup (4 or 8 waves) owns 16 T output columns n (T = 1, 2, 4 or 8 tiles
@@ -96,39 +96,24 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
   }
 }
 
-__device__ __forceinline__ half8_t unpack_mixed(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t e1024,
-                                                uint32_t e64) {
-  const uint32_t w8 = w >> 8;
-  u32x4 r;
-  r[0] = and_or(w, mlo, e1024);   // 1024 + q0, 1024 + q4
-  r[1] = and_or(w, mhi, e64);     //   64 + q1,   64 + q5
-  r[2] = and_or(w8, mlo, e1024);  // 1024 + q2, 1024 + q6
-  r[3] = and_or(w8, mhi, e64);    //   64 + q3,   64 + q7
-  return __builtin_bit_cast(half8_t, r);
+// The 8 codes of a (parity-split) word as the fp16 B fragment (1024 + q0, 1024 + q1,
+// 64 + q2, 64 + q3, 1024 + q4, 1024 + q5, 64 + q6, 64 + q7): natural k order, one shift
+// and four v_and_or_b32.
+__device__ __forceinline__ half8_t unpack_mixed(uint32_t w, const Magic& c) {
+  return __builtin_bit_cast(half8_t, expand_word(w, c));
 }
 
-// Eight halves of X in the k order 0,4,1,5,2,6,3,7 (the order unpack_mixed produces).
-__device__ __forceinline__ half8_t permute_x(half8_t a) {
-  const u32x4 v = __builtin_bit_cast(u32x4, a);
-  u32x4 o;
-  o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // x0, x4
-  o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // x1, x5
-  o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // x2, x6
-  o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // x3, x7
-  return __builtin_bit_cast(half8_t, o);
-}
-
-// One group.  The X fragments are permuted to the k order of unpack_mixed (four
-// v_perm_b32 per fragment, shared by the T n-tiles), so each code word costs five VALU
-// operations.  Two MFMA chains against constant B operands give, per row, S_g (ones)
-// and -P_g (-1024 on even k, -64 on odd k); -P_g seeds every n-tile's chain, which then
-// holds T_g - P_g = sum_k X (q + 0) and the fold is y += s (T_g - P_g - z S_g).
+// One group.  Each code word costs five VALU operations and X enters the MFMAs as
+// loaded (both in natural k order).  Two MFMA chains against constant B operands give,
+// per row, S_g (ones) and -P_g (-1024 at k = 0, 1 mod 4, -64 at k = 2, 3 mod 4); -P_g
+// seeds every n-tile's chain, which then holds T_g - P_g = sum_k X q and the fold is
+// y += s (T_g - P_g - z S_g).
 template <int MT, int T, bool XS = false>
 __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T],
                                               const int (&zsh)[kChunks<T>], half_t* xb = nullptr, int lane = 0) {
   const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
   const half8_t negmagic = {-1024, -1024, -64, -64, -1024, -1024, -64, -64};
-  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+  const Magic mc = magic_regs();
   half8_t a[MT][4];
   float4_t ssum[MT], negp[MT];
   if (XS) {
@@ -150,7 +135,7 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
     negp[mt] = float4_t{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[mt][j] = permute_x(XS ? a[mt][j] : r.a[mt][j]);
+      if (!XS) a[mt][j] = r.a[mt][j];
       ssum[mt] = mfma16(a[mt][j], ones, ssum[mt]);
       negp[mt] = mfma16(a[mt][j], negmagic, negp[mt]);
     }
@@ -164,7 +149,7 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
   for (int t = 0; t < T; ++t) {
     half8_t bv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mlo, mhi, e1024, e64);
+    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mc);
     const float z = (float)((sz[t] >> 16) & 0xffu);
     const float sc = (float)__builtin_bit_cast(half2_t, sz[t])[0];
 #pragma unroll
@@ -188,18 +173,17 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
 template <int MT, int T>
 __device__ __forceinline__ void compute_group_dq(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T], int n0,
                                                  int lane, int N) {
+  const Magic mc = magic_regs();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
-    // fp16 bit patterns built with integer ops: -(1024 + z) is 0xE400 | z; the scale's
-    // 16 bits in both halves
+    // fp16 bit patterns built with integer ops: -(1024 + z), -(64 + z), the scale twice
     const uint32_t z = (r.zw[t] >> (4 * (nc & 7))) & 15u;
-    const half2_t negz2 = __builtin_bit_cast(half2_t, (0xE400u | z) * 0x00010001u);
-    const uint32_t sb = __builtin_bit_cast(uint16_t, r.s[t]);
-    const half2_t s2 = __builtin_bit_cast(half2_t, sb * 0x00010001u);
+    const half2_t c1024 = neg1024z2(z), c64 = neg64z2(z);
+    const half2_t s2 = scale2(__builtin_bit_cast(uint16_t, r.s[t]));
     half8_t bv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = dequant8(r.b[t][j], negz2, s2);
+    for (int j = 0; j < 4; ++j) bv[j] = dequant8(r.b[t][j], mc, c1024, c64, s2);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -211,8 +195,18 @@ __device__ __forceinline__ void compute_group_dq(const GroupRegs<MT, T>& r, floa
 // D register sets rotate (loop unrolled by D, no register copies), so while a wave
 // computes one group the loads of its next D groups are in flight (D * T KB per wave).
 // A workgroup owns 16 T output columns (T 16-row tiles; all its waves share them).
+//
+// Workgroups resident per CU that the register allocation must allow, for the plans
+// that pick these variants: three 4-wave workgroups (<= 168 VGPRs) or two 8-wave ones
+// (<= 128 VGPRs); the others take what they need.
+constexpr int skinny_min_blocks(int mt, int t, int d, int waves, bool dq, bool xs) {
+  if (mt != 1 || dq || xs) return 1;
+  if (waves == 4 && ((t == 4 && d <= 3) || (t == 2 && d == 2) || (t == 1 && d == 4))) return 3;
+  if (waves == 8 && ((t == 2 && d <= 3) || (t == 4 && d == 2) || (t == 1 && d == 4))) return 2;
+  return 1;
+}
 template <int MT, int T, int D, int WAVES, bool DQ, bool XS = false>
-__global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __restrict__ x,
+__global__ __launch_bounds__(WAVES * kWave, skinny_min_blocks(MT, T, D, WAVES, DQ, XS)) void skinny_kernel(const half_t* __restrict__ x,
                                                                const uint32_t* __restrict__ qweight,
                                                                const half_t* __restrict__ scales,
                                                                const uint32_t* __restrict__ qzeros,
@@ -351,14 +345,15 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(const half_t* __r
 // per-group register sets that are prefetched D deep then carry only what comes from
 // HBM: T x 16 bytes of codes, T scales and T zero-point words per lane.
 //
-// B operand: for the 8 codes of a word, v_and_or_b32 with mask 0x000f000f and fp16
-// 1024 in both halves gives (1024 + q_0, 1024 + q_4) -- a code in the low mantissa bits
-// under exponent 2^10 -- and with mask 0x00f000f0 and fp16 64 gives (64 + q_1, 64 + q_5)
-// -- a code in mantissa bits 4..7 under exponent 2^6 is worth q exactly.  The same on
-// the word shifted right by 8 gives k = 2, 6 and 3, 7: four v_and_or_b32 and one shift
-// per word, the k order within every 8 being 0,4,1,5,2,6,3,7.  X is stored in LDS in
-// that order, so one MFMA chain forms, exactly up to its fp32 sums,
-//   T_g[m,n] = sum_k X[m,k] q[n,k] + P_g[m],   P_g[m] = 1024 sum_{k even} X[m,k] + 64 sum_{k odd} X[m,k],
+// B operand: for the 8 codes of a parity-split word, v_and_or_b32 with mask 0x000f000f
+// and fp16 1024 in both halves gives (1024 + q_0, 1024 + q_1) -- a code in the low
+// mantissa bits under exponent 2^10 -- and with mask 0x00f000f0 and fp16 64 gives
+// (64 + q_2, 64 + q_3) -- a code in mantissa bits 4..7 under exponent 2^6 is worth q
+// exactly.  The same on the word shifted right by 8 gives k = 4, 5 and 6, 7: four
+// v_and_or_b32 and one shift per word, in natural k order, as X is stored in LDS.  One
+// MFMA chain forms, exactly up to its fp32 sums,
+//   T_g[m,n] = sum_k X[m,k] q[n,k] + P_g[m],
+//   P_g[m] = 1024 sum_{k = 0,1 mod 4} X[m,k] + 64 sum_{k = 2,3 mod 4} X[m,k],
 // and the group's contribution to Y is s (T_g - P_g - z S_g), S_g[m] = sum_{k in g} X[m,k].
 // P_g and S_g depend on X only: they are summed in fp32 while X is staged, reduced over
 // the 16 chunks of a group with DPP moves (fixed order, deterministic) and kept in LDS.
@@ -415,20 +410,15 @@ __device__ __forceinline__ int chunk_row(int cc, int cpr) {
 }
 
 // Stage one 16-byte chunk (8 halves of X) of chunk index cc (clamped into the slice) to
-// LDS in the k order 0,4,1,5,2,6,3,7, and add its even / odd sums to the group's S, P
-// (written by the first lane of the 16 lanes that hold the group's 16 chunks; `live`
-// is false for the clamped copies past the slice, which are rewritten, not summed).
+// LDS, and add its sums over k = 0, 1 mod 4 (e) and k = 2, 3 mod 4 (od) to the group's
+// S, P (written by the first lane of the 16 lanes that hold the group's 16 chunks;
+// `live` is false for the clamped copies past the slice, which are rewritten, not summed).
 __device__ __forceinline__ void stage_chunk(u32x4 v, int cc, bool live, int cpr, int rs, half_t* xs, float* sp) {
   const int row = chunk_row(cc, cpr), col = cc - row * cpr;
-  u32x4 o;
-  o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // x0, x4
-  o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // x1, x5
-  o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // x2, x6
-  o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // x3, x7
-  *reinterpret_cast<u32x4*>(xs + row * rs + col * 8) = o;
+  *reinterpret_cast<u32x4*>(xs + row * rs + col * 8) = v;
   // (vector elements are copied to scalars before __builtin_bit_cast: applied directly
   // to an element of an ext_vector this hipcc reads element 0)
-  const uint32_t o0 = o[0], o1 = o[1], o2 = o[2], o3 = o[3];
+  const uint32_t o0 = v[0], o1 = v[1], o2 = v[2], o3 = v[3];  // (x0, x1), (x2, x3), (x4, x5), (x6, x7)
   const half2_t one2 = {1, 1};
   float e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o0), one2, 0.0f, false);
   e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o2), one2, e, false);
@@ -453,12 +443,12 @@ __device__ __forceinline__ void compute_wstage(const WStage<T>& r, const half_t*
   for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const half8_t*>(xrow + 8 * j);
   const float4_t S = *reinterpret_cast<const float4_t*>(spg + 4 * (lane >> 4));
   const float4_t P = *reinterpret_cast<const float4_t*>(spg + 16 + 4 * (lane >> 4));
-  const uint32_t mlo = vreg(0x000f000fu), mhi = vreg(0x00f000f0u), e1024 = vreg(0x64006400u), e64 = vreg(0x54005400u);
+  const Magic mc = magic_regs();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     half8_t bv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mlo, mhi, e1024, e64);
+    for (int j = 0; j < 4; ++j) bv[j] = unpack_mixed(r.b[t][j], mc);
     float4_t tacc = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) tacc = mfma16(a[j], bv[j], tacc);
@@ -620,7 +610,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
   V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
-  V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 8, 3, 8, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
+  V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
   V(1, 1, 8, 8, 1) V(1, 1, 4, 16, 0) V(1, 2, 4, 8, 1)
 static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 100 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
