@@ -683,7 +683,19 @@ __global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_
         for (int r = 0; r < 16; ++r) acc[i][f][r] >>= 4;
   }
 
-  // element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 h + (r % 4), column nrow[f]
+  // The epilogue's lane indices are formed again from the thread id (hidden from the
+  // compiler, which would otherwise keep the first ones live across the main loop: one
+  // register too many for the three-slot ring of the two-level weights).
+  int tid_e = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int he = (tid_e >> 5) & 1;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    nrow[f] = n0 + wave * 64 + f * 32 + (tid_e & 31);
+    nok[f] = nrow[f] < N;
+    nclamp[f] = min(nrow[f], N - 1);
+  }
+  // element (i, f, r): row m0 + 32 i + 8 (r / 4) + 4 he + (r % 4), column nrow[f]
   if (nsplit > 1) {
     // Split K: every part writes its int32 partial sums, the last arriving workgroup
     // adds the others' to its own (exact in any order).  Uniform mode keeps the partials
@@ -700,7 +712,7 @@ __global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_
         if (!nok[f]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * he + (r & 3);
           if (m < M) st_coherent(pbase + split * sstride + (m - m0) * ld + (nrow[f] - n0), acc[i][f][r]);
         }
       }
@@ -714,7 +726,7 @@ __global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_
           if (sp_ == split) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), M - 1);
+            const int m = min(m0 + i * 32 + 8 * (r >> 2) + 4 * he + (r & 3), M - 1);
             acc[i][f][r] += ld_coherent(pbase + sp_ * sstride + (m - m0) * ld + (nclamp[f] - n0));
           }
         }
@@ -729,7 +741,7 @@ __global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_
       const float cs = f == 0 ? cs0 : cs1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * he + (r & 3);
         if (m < M) {
           if (acc_out) acc_out[(int64_t)m * N + nrow[f]] = acc[i][f][r];
           else y[(int64_t)m * N + nrow[f]] = (half_t)(((float)acc[i][f][r] * s_a[m]) * cs);
@@ -963,19 +975,19 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // one ahead); 64-row tiles up to 512 with the four-tile direct-to-LDS ring (depth 0:
   // per-channel / two-level / int8 weights at M = 256 33.9 / 48.0 / 41.9 us with four
   // register sets -> 30.5 / 41.0 / 40.0, at M = 512 58.0 / 72.7 / 65.0 one group ahead
-  // -> 46.1 / 62.0 / 61.4); 128-row tiles above 512, per-channel weights with the
-  // three-tile ring at two workgroups per CU (depth 5: M = 4096 321.9 -> 270.5 us), the
-  // others one group ahead.
+  // -> 46.1 / 62.0 / 61.4); 128-row tiles above 512, int4 weights with the three-tile
+  // ring at two workgroups per CU (depth 5, M = 4096: per-channel 321.9 -> 270.5 us,
+  // two-level 382.2 -> 328.6), int8 weights one group ahead.
   p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
-  const int dflt = p.bm == 32 ? 4 : p.bm == 64 ? 0 : (group_size == -1 ? 5 : 1);
+  const int dflt = p.bm == 32 ? 4 : p.bm == 64 ? 0 : (group_size != 0 ? 5 : 1);
   p.depth = env_int("W4_W4A8_DEPTH", dflt);
   // depth 0: the direct-to-LDS pipeline (64- and 128-row tiles; 32-bit xq offsets)
   if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4)) ||
         (p.depth == 0 && p.bm >= 64 && (int64_t)M * K < (int64_t(1) << 31)) ||
         // depth 5: three-tile direct-to-LDS ring, two workgroups per CU (128-row tiles only
-        // with per-channel weights: the other formats' register sets do not fit)
-        (p.depth == 5 && (p.bm == 64 || (p.bm == 128 && group_size == -1)) &&
+        // with int4 weights: the int8 weights' register sets do not fit three deep)
+        (p.depth == 5 && (p.bm == 64 || (p.bm == 128 && group_size != 0)) &&
          (int64_t)M * K < (int64_t(1) << 31))))
     p.depth = 1;
   p.tiles_m = (M + p.bm - 1) / p.bm;
@@ -1054,7 +1066,7 @@ hipError_t launch_int8_gemm(const W4A8Plan& p, int mode, const int8_t* xq, const
   W4A8_LAUNCH(2, MODE, 3) W4A8_LAUNCH(2, MODE, 4) W4A8_LAUNCH(4, MODE, 0) W4A8_LAUNCH(2, MODE, 0)    \
   W4A8_LAUNCH(2, MODE, 5)
   const int mi = p.bm / 32;
-  if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); }
+  if (mode == kI4TwoLevel) { W4A8_LAUNCH_MI(kI4TwoLevel); W4A8_LAUNCH(4, kI4TwoLevel, 5); }
   else if (mode == kI8) { W4A8_LAUNCH_MI(kI8); }
   else { W4A8_LAUNCH_MI(kI4PerChannel); W4A8_LAUNCH(4, kI4PerChannel, 5); }
 #undef W4A8_LAUNCH_MI
