@@ -541,10 +541,11 @@ GemmPlan gemm_plan(int M, int N, int K) {
   if (forced >= 1 && forced <= 4) {
     pick = forced - 1;
   } else if (mid) {
-    // 64 x 128 tiles up to M = 256 (K = 5120, N = 13824, with register sets in flight:
-    // M = 64 30.2 -> 26.9 us, M = 128 45.2 -> 37.5, M = 256 62.7 -> 54.2 against the
-    // one-step-ahead 128 x 128 / 64 x 128 plans); 128 x 128 above
-    pick = (M > 256 && (N >= 8192 || M >= 384)) ? 1 : 3;
+    // 64 x 128 tiles up to M = 128 (K = 5120, N = 13824, with register sets in flight:
+    // M = 64 30.2 -> 26.9 us, M = 128 45.2 -> 37.5 against the one-step-ahead 128 x 128 /
+    // 64 x 128 plans); 128 x 128 above on wide matrices (M = 256: 52.1 -> 48.8 us, whole
+    // K per workgroup) and from M = 384 on
+    pick = ((M > 128 && N >= 8192) || M >= 384) ? 1 : 3;
   } else {
     for (int i = 0; i < 4; ++i) {
       const int tm = (M + 32 * kShapes[i][0] - 1) / (32 * kShapes[i][0]);
@@ -569,9 +570,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
   //    25.8 / 35.1 / 50.4 us (27.4 / 36.4 / 52.3 with depth 0);
   //  * depth 0, X tiles direct-to-LDS four steps ahead, one workgroup of 4 waves per CU
   //    for 128-row tiles: the 128 x 128 tiles at 256 < M <= 512 (M = 384 / 512 70.9 /
-  //    79.6 us; 95.2 us at M = 512 with register-staged X, 3-4 sets ahead).
+  //    79.6 us; 95.2 us at M = 512 with register-staged X, 3-4 sets ahead); at
+  //    128 < M <= 256 those tiles take depth 7 (M = 256 48.8 us).
   // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
-  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 5 : 0) : (pick <= 1 ? 7 : 1));
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 5 : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipeline addresses X with 32-bit element offsets
   if ((p.depth == 0 || p.depth == 5 || p.depth == 7) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;
@@ -581,7 +583,8 @@ GemmPlan gemm_plan(int M, int N, int K) {
   const int tiles = p.tiles_m * p.tiles_n;
   int splits = 1;
   // fill the CUs when there are few tiles; keep >= 8 BK steps per split
-  const int want = mid ? 320 : min_tiles / 2;
+  // (mid M: 64 x 128 tiles split towards 320 workgroups; 128 x 128 tiles from 192 on)
+  const int want = mid ? (pick == 1 ? 192 : 320) : min_tiles / 2;
   while (tiles * splits < want && ktiles / (splits * 2) >= 8) splits *= 2;
   const int forced_splits = env_int("W4_GEMM_SPLITS", 0);
   if (forced_splits > 0) splits = min(forced_splits, ktiles);
