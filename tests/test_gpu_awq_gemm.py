@@ -237,7 +237,7 @@ def test_gemm_every_tile_shape(shape, depth, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("depth", ["3", "4", "6", "0", "5", "7"])
+@pytest.mark.parametrize("depth", ["3", "4", "6", "0", "5", "7", "8"])
 @pytest.mark.parametrize("M,N,K,splits", [(65, 300, 640, "1"), (130, 520, 1024, "2"), (257, 1030, 2048, "4"),
                                           (40, 129, 128, "1"), (100, 260, 1408, "3")])
 def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):

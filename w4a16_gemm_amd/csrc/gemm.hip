@@ -62,8 +62,8 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   constexpr int kAPer = BM * 8 / kThreads;  // 16-byte X chunks per thread per BK step
   // PD == 0: X goes global -> LDS directly into a ring of kRing tiles (separate arrays,
   // see below); otherwise two register-staged buffers
-  constexpr bool kDma = PD == 0 || PD == 5 || PD == 7;
-  constexpr bool kBLds = PD == 7;  // the packed weights too go through LDS
+  constexpr bool kDma = PD == 0 || PD == 5 || PD == 7 || PD == 8;
+  constexpr bool kBLds = PD == 7 || PD == 8;  // the packed weights too go through LDS
   __shared__ u32x4 lds[kDma ? 1 : 2][kDma ? 1 : BM * 8];
 
   const int ktiles = K / BK;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   // are clamped to it (they refill slots no later step reads), so the counts stay uniform.
   //
     // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5, registers)
-    constexpr int R = (PD == 5 || PD == 7) ? 3 : kRing;
+    constexpr int R = (PD == 5 || PD == 7) ? 3 : PD == 8 ? 6 : kRing;
     constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
     constexpr int kWaitImm = vmcnt_imm((R - 2) * kPerStage);
     // thread's chunk i of a tile lands at LDS position (4 i + wave) * 64 + lane (each wave
@@ -157,14 +157,20 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     // One LDS array per ring slot: the compiler's wait insertion tells direct-to-LDS loads
     // into distinct arrays apart, so reading slot t does not wait for the loads in flight
     // into the other slots (with one array it waited for all of them).
-    __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8];
-    auto ring = [&](int j) -> u32x4* { return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3; };
+    constexpr int kA45 = R > 4 ? BM * 8 : 1;
+    __shared__ u32x4 ring0[BM * 8], ring1[BM * 8], ring2[BM * 8], ring3[BM * 8], ring4[kA45], ring5[kA45];
+    auto ring = [&](int j) -> u32x4* {
+      return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : j == 3 ? ring3 : j == 4 ? ring4 : ring5;
+    };
     // PD 7: this lane's weight chunks of step t land in LDS slot t % R at position
     // (4 f + wave) * 64 + lane (each wave instruction writes 1 KB contiguously) and are read
     // back by the same lane: no registers held for them while in flight
     constexpr int kBSlot = kBLds ? NF * 4 * 64 : 1;
-    __shared__ u32x4 bring0[kBSlot], bring1[kBSlot], bring2[kBSlot];
-    auto bring = [&](int j) -> u32x4* { return j == 0 ? bring0 : j == 1 ? bring1 : bring2; };
+    constexpr int kB35 = R > 3 ? kBSlot : 1;
+    __shared__ u32x4 bring0[kBSlot], bring1[kBSlot], bring2[kBSlot], bring3[kB35], bring4[kB35], bring5[kB35];
+    auto bring = [&](int j) -> u32x4* {
+      return j == 0 ? bring0 : j == 1 ? bring1 : j == 2 ? bring2 : j == 3 ? bring3 : j == 4 ? bring4 : bring5;
+    };
     struct BSet {
       u32x4 b[kBLds ? 1 : NF];
       uint32_t z[NF], s[NF];
@@ -522,7 +528,7 @@ constexpr int kCUs = 256;
 // Compiled (MI, NF, prefetch depth) variants.
 #define GEMM_VARIANTS(V) \
   V(4, 2, 1) V(4, 1, 1) V(2, 2, 1) V(2, 1, 1) V(2, 1, 3) V(2, 1, 4) V(2, 1, 6) V(4, 2, 0) V(4, 1, 0) V(2, 2, 0) \
-  V(2, 1, 0) V(4, 1, 5) V(2, 2, 5) V(2, 1, 5) V(4, 2, 7) V(4, 1, 7) V(2, 2, 7) V(2, 1, 7)
+  V(2, 1, 0) V(4, 1, 5) V(2, 2, 5) V(2, 1, 5) V(4, 2, 7) V(4, 1, 7) V(2, 2, 7) V(2, 1, 7) V(2, 1, 8)
 static bool gemm_variant_compiled(int mi, int nf, int pd) {
 #define V(MI, NF, PD) if (mi == MI && nf == NF && pd == PD) return true;
   GEMM_VARIANTS(V)
@@ -565,26 +571,33 @@ GemmPlan gemm_plan(int M, int N, int K) {
   //    tiles at large M, 1.00-1.09 PFLOP/s at M = 4096 (N in {27648, 5120}, and
   //    K = 13824) against 0.96-1.06 for depth 1 (the next step's X tile in registers);
   //    M = 1024, N = 5120 on 128 x 128 tiles 85.4 -> 73.3 us;
+  //  * depth 8, X tiles and weights in a six-slot LDS ring (five steps ahead, two
+  //    workgroups per CU): the 64 x 128 tiles at 32 < M <= 128, split towards only 160
+  //    workgroups (M = 64 / 96 / 128: 23.1 / 29.7 / 30.0 us against 26.1 / 33.6 / 34.5
+  //    with depth 5 and 320 workgroups; N = 5120: M = 48 / 64 / 128 17.6 / 18.2 / 22.5
+  //    against 20.6 / 18.5 / 23.4);
   //  * depth 5, X tiles direct-to-LDS three steps ahead and the weights in registers, two
-  //    or more workgroups per CU: the 64 x 128 tiles at mid M, M = 64 / 128 / 256
-  //    25.8 / 35.1 / 50.4 us (27.4 / 36.4 / 52.3 with depth 0);
+  //    or more workgroups per CU (M = 64 / 128 / 256 25.8 / 35.1 / 50.4 us; 27.4 / 36.4 /
+  //    52.3 with depth 0);
   //  * depth 0, X tiles direct-to-LDS four steps ahead, one workgroup of 4 waves per CU
   //    for 128-row tiles: the 128 x 128 tiles at 256 < M <= 512 (M = 384 / 512 70.9 /
   //    79.6 us; 95.2 us at M = 512 with register-staged X, 3-4 sets ahead); at
   //    128 < M <= 256 those tiles take depth 7 (M = 256 48.8 us).
   // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
-  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 5 : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 8 : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipeline addresses X with 32-bit element offsets
-  if ((p.depth == 0 || p.depth == 5 || p.depth == 7) && (int64_t)M * K >= (int64_t(1) << 31)) p.depth = 1;
+  if ((p.depth == 0 || p.depth == 5 || p.depth == 7 || p.depth == 8) && (int64_t)M * K >= (int64_t(1) << 31))
+    p.depth = 1;
   p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
   p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
   const int ktiles = K / BK;
   const int tiles = p.tiles_m * p.tiles_n;
   int splits = 1;
   // fill the CUs when there are few tiles; keep >= 8 BK steps per split
-  // (mid M: 64 x 128 tiles split towards 320 workgroups; 128 x 128 tiles from 192 on)
-  const int want = mid ? (pick == 1 ? 192 : 320) : min_tiles / 2;
+  // (mid M: 64 x 128 tiles split towards 160 workgroups -- two resident per CU with the
+  // six-slot ring, fewer split-K partials; 128 x 128 tiles from 192 on)
+  const int want = mid ? (pick == 1 ? 192 : 160) : min_tiles / 2;
   while (tiles * splits < want && ktiles / (splits * 2) >= 8) splits *= 2;
   const int forced_splits = env_int("W4_GEMM_SPLITS", 0);
   if (forced_splits > 0) splits = min(forced_splits, ktiles);
