@@ -215,7 +215,7 @@ def test_skinny_lds_variants(variant, M, N, K, monkeypatch):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("depth", ["1", "0", "5", "7"])
+@pytest.mark.parametrize("depth", ["1", "0", "5", "7", "8"])
 @pytest.mark.parametrize("shape", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K", [(65, 300, 640), (130, 520, 1024), (257, 1030, 2048), (33, 128, 128),
                                    (200, 520, 384)])
