@@ -1,7 +1,9 @@
-// Large-M W4A16 GEMM (prefill): fp16 X tiles staged through LDS, packed int4 weights
-// streamed from global memory straight into registers, dequantized exactly in
-// registers (one fp16 rounding per element), fed to v_mfma_f32_32x32x16_f16 with fp32
-// accumulation.
+// Large-M W4A16 GEMM (prefill and mid M): fp16 X tiles staged through LDS, packed int4
+// weights streamed from global memory into registers (or through an LDS ring, each lane
+// reading back its own chunk), dequantized exactly in registers (one fp16 rounding per
+// element), fed to v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The loop variants
+// (register-staged, or direct-to-LDS rings of 3, 4 or 6 steps) are described at each
+// branch below and chosen per shape in gemm_plan.
 //
 // "Implement AWQ quantization support for LLaMA" (vllm-project/vllm PR 1032): the AWQ
 // GEMM runs dequantized fp16 weights through the tensor cores; dequantization is the
@@ -16,10 +18,11 @@
 // Tile: BM x BN x BK = (32 MI) x (128 NF) x 64, 256 threads, (MI, NF) in {4, 2} x {2, 1}.
 // The 4 waves split N: wave w owns 32 NF columns as NF 32-column MFMA fragments, and
 // all BM rows as MI 32-row fragments (acc = MI x NF x 16 fp32 per lane).  Each weight
-// code is therefore dequantized exactly once per workgroup.  Per BK step a lane loads one 16-byte chunk
-// (4 words = 32 codes) per fragment: lane l (column l % 32, K-slot h = l / 32) takes
-// words 4h..4h+3 of the 8 words of its row in this BK step (slot 2 (kt % 2) + h of the
-// tiled layout: 16 lanes read 256 contiguous bytes), and k16-step s uses word s.  The X fragment for k16-step s is read from LDS with the same K-slot assignment
+// code is therefore dequantized exactly once per workgroup.  Per BK step a lane loads
+// one 16-byte chunk (4 words = 32 codes) per fragment: lane l (column l % 32, K-slot
+// h = l / 32) takes words 4h..4h+3 of the 8 words of its row in this BK step (slot
+// 2 (kt % 2) + h of the tiled layout: 16 lanes read 256 contiguous bytes), and k16-step
+// s uses word s.  The X fragment for k16-step s is read from LDS with the same K-slot assignment
 // (row l % 32, elements k = 8 (4h + s) .. + 7).  X rows live in LDS as 128-byte rows
 // of 8 16-byte chunks, chunk c of row r stored at position c ^ ((r / 2) % 8): two
 // consecutive rows fill one 256-byte bank window, so any 16 consecutive rows read at
@@ -131,15 +134,17 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
   if constexpr (kDma) {
   // Direct-to-LDS pipeline.  The X tile of BK step t lands in LDS slot t % R straight
   // from global memory (global_load_lds_dwordx4: no registers, no VALU), issued R - 1
-  // steps ahead; this lane's weight chunks and raw scale / zero-point words of step t sit
-  // in register set t % R, issued as far ahead.  Each step: wait until the loads of
-  // step t are complete (every step issues the same kPerStage loads per thread, so that is
-  // "at most 2 kPerStage loads outstanding"), barrier (every wave's part of the tile is in
-  // LDS, and every wave is done with the slot and set of step t - 1), issue step t + 3's
-  // loads into that freed slot and set, then the MFMAs of step t.  Loads past the last step
-  // are clamped to it (they refill slots no later step reads), so the counts stay uniform.
+  // steps ahead; this lane's weight chunks (in register set t % R, or with PD 7 / 8 in
+  // LDS slot t % R of a second ring) and raw scale / zero-point words of step t are
+  // issued as far ahead.  Each step: wait until the loads of step t are complete (every
+  // step issues the same kPerStage loads per thread, so that is "at most (R - 2)
+  // kPerStage loads outstanding"), barrier (every wave's part of the tile is in LDS, and
+  // every wave is done with the slot and set of step t - 1), issue step t + R - 1's loads
+  // into that freed slot and set, then the MFMAs of step t.  Loads past the last step are
+  // clamped to it (they refill slots no later step reads), so the counts stay uniform.
   //
-    // ring of R tiles: 4 with one workgroup per CU (PD 0), 3 with two (PD 5, registers)
+    // ring of R tiles: 4 with one workgroup per CU (PD 0); 3 with two (PD 5: weights in
+    // registers; PD 7: weights in LDS); 6 with two for 64-row tiles (PD 8, weights in LDS)
     constexpr int R = (PD == 5 || PD == 7) ? 3 : PD == 8 ? 6 : kRing;
     constexpr int kPerStage = kAPer + 3 * NF;  // vector-memory instructions per thread per step
     constexpr int kWaitImm = vmcnt_imm((R - 2) * kPerStage);
