@@ -44,6 +44,10 @@ Readings where the pages are silent:
   (one 1 KB block holds 16 rows x 128 k; rows past N are padding with code 0,
   or q = 0 for W4A8).  ``scales`` fp16 [K/G, N]; ``qzeros`` int32
   [K/G, ceil(N/8)] (zero points packed along N).
+* R5b The W4A8 ``qweight`` holds each word of biased nibbles split by halves: element
+  ``i`` of the word in nibble ``2 * (i % 4) + i // 4`` (elements 0..3 in the even
+  nibbles, 4..7 in the odd ones), tiled as the W4A16 words; a layout choice of the
+  library (its int8 expansion then needs no byte permutation).
 * R5 W4A8 weights (the pages print no constants): per-channel (group -1)
   ``s_c = fp16(max(max|w| / 7, 1e-5))``, ``q = clamp(rint(w / s_c), -8, 7)``;
   two-level g128: ``s_c = fp16(max(max|w| / 127, 1e-5))``,
@@ -103,7 +107,8 @@ F32 = np.float32
 F64 = np.float64
 
 __all__ = [
-    "pack_nibbles", "unpack_nibbles", "split_parity", "merge_parity", "tile_words", "untile_words",
+    "pack_nibbles", "unpack_nibbles", "split_parity", "merge_parity", "split_halves", "merge_halves",
+    "tile_words", "untile_words",
     "quantize_asym", "quantize_sym", "pack_awq", "unpack_awq", "dequant_awq", "awq_reference",
     "linear_ref",
     "quantize_w4a8", "pack_w4a8", "unpack_w4a8", "w4a8_quant_act_ref", "quantize_w8a8",
@@ -175,6 +180,32 @@ def merge_parity(words: np.ndarray) -> np.ndarray:
     out = np.zeros_like(u)
     for i in range(8):
         out |= ((u >> (4 * (i // 2 + 4 * (i % 2)))) & 0xF) << (4 * i)
+    return out.astype(np.uint32).view(np.int32)
+
+
+def split_halves(words: np.ndarray) -> np.ndarray:
+    """Plain words -> the W4A8 qweight's word format (R5b): element ``i`` of each word
+    (plain nibble i) moves to nibble ``2 * (i % 4) + i // 4``: elements 0..3 fill the
+    even nibbles and elements 4..7 the odd ones, each in element order."""
+    words = np.asarray(words)
+    if words.dtype != np.int32:
+        raise ValueError("words must be int32")
+    u = words.view(np.uint32).astype(np.int64)
+    out = np.zeros_like(u)
+    for i in range(8):
+        out |= ((u >> (4 * i)) & 0xF) << (4 * (2 * (i % 4) + i // 4))
+    return out.astype(np.uint32).view(np.int32)
+
+
+def merge_halves(words: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`split_halves`."""
+    words = np.asarray(words)
+    if words.dtype != np.int32:
+        raise ValueError("words must be int32")
+    u = words.view(np.uint32).astype(np.int64)
+    out = np.zeros_like(u)
+    for i in range(8):
+        out |= ((u >> (4 * (2 * (i % 4) + i // 4))) & 0xF) << (4 * i)
     return out.astype(np.uint32).view(np.int32)
 
 
@@ -396,16 +427,16 @@ def untile_w8a8(tiled: np.ndarray, N: int) -> np.ndarray:
 
 
 def pack_w4a8(q: np.ndarray, cscale: np.ndarray, gscale):
-    """-> ``(qweight int32 [ceil(N/16), K/128, 4, 16, 4] of biased nibbles q+8 (pad
-    rows q = 0), cscale fp16 [N], gscale int8 [K/G, N] or None)``."""
-    qweight = tile_words(pack_nibbles(np.asarray(q, dtype=np.int64) + 8), pad_word=0x88888888)
+    """-> ``(qweight int32 [ceil(N/16), K/128, 4, 16, 4] of biased nibbles q+8 in words
+    split by halves (R5b; pad rows q = 0), cscale fp16 [N], gscale int8 [K/G, N] or None)``."""
+    qweight = tile_words(split_halves(pack_nibbles(np.asarray(q, dtype=np.int64) + 8)), pad_word=0x88888888)
     gs = None if gscale is None else np.ascontiguousarray(np.asarray(gscale, dtype=np.int8).T)
     return qweight, np.asarray(cscale, dtype=F16), gs
 
 
 def unpack_w4a8(qweight: np.ndarray, N: int, K: int) -> np.ndarray:
     """Tiled biased-nibble words -> signed int4 values [N, K] (int64)."""
-    return unpack_nibbles(untile_words(qweight, N), K).astype(np.int64) - 8
+    return unpack_nibbles(merge_halves(untile_words(qweight, N)), K).astype(np.int64) - 8
 
 
 def w4a8_quant_act_ref(x16: np.ndarray, gamma16=None, eps: float = 1e-5):

@@ -87,6 +87,36 @@ def pin_parity_words(ora):
     assert np.array_equal(ora.split_parity(ora.merge_parity(words)), words)
 
 
+def pin_halves_words(ora):
+    """Worked words of the W4A8 qweight's split-halves word format
+    (tests/golden/halves_words.txt): the plain word of the codes, split, gives the
+    listed word; merging it gives the plain word back; and a single nonzero q at element
+    i of a word lands, after pack_w4a8, as the biased nibble q + 8 in nibble
+    2 (i % 4) + i // 4 of the only word that is not 0x88888888."""
+    for codes, word in read_pack_words("halves_words.txt"):
+        plain = ora.pack_nibbles(np.array([codes], dtype=np.uint8))
+        got = ora.split_halves(plain)
+        assert int(got.view(np.uint32)[0, 0]) == word, (codes, hex(int(got.view(np.uint32)[0, 0])), hex(word))
+        back = ora.merge_halves(np.array([[np.uint32(word)]], dtype=np.uint32).view(np.int32))
+        assert np.array_equal(back, plain)
+    nib = {0: 0, 1: 2, 2: 4, 3: 6, 4: 1, 5: 3, 6: 5, 7: 7}  # element -> nibble, by hand
+    N, K = 3, 128
+    for k in range(16):
+        q = np.zeros((N, K), np.int64)
+        q[2, k] = -5
+        qw, _, _ = ora.pack_w4a8(q, np.ones(N, F16), None)
+        flat = qw.reshape(-1).view(np.uint32)
+        off = ((k % 128) // 32) * 64 + 2 * 4 + (k % 32) // 8
+        others = np.delete(flat, off)
+        assert np.all(others == 0x88888888), k
+        expect = (0x88888888 & ~(0xF << (4 * nib[k % 8]))) | (3 << (4 * nib[k % 8]))
+        assert int(flat[off]) == expect, (k, hex(int(flat[off])))
+    rng = _rng(10)
+    words = rng.integers(0, 2**32, size=(64, 5), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    assert np.array_equal(ora.merge_halves(ora.split_halves(words)), words)
+    assert np.array_equal(ora.split_halves(ora.merge_halves(words)), words)
+
+
 def pin_tile_layout(ora):
     """Tiled word order: a single code placed at (n, k) lands in exactly one word of
     the flat qweight, at the offset computed by hand from the layout rule
@@ -547,7 +577,7 @@ def pin_w4a8_acc_bruteforce(ora):
 
 
 ALL_PINS = [
-    pin_pack_words, pin_pack_bijection, pin_parity_words, pin_tile_layout,
+    pin_pack_words, pin_pack_bijection, pin_parity_words, pin_halves_words, pin_tile_layout,
     pin_asym_worked, pin_asym_constructed, pin_asym_roundtrip_bound,
     pin_fraction_bruteforce, pin_identity_probe, pin_per_channel_special_case,
     pin_constructed_exact_gemm,

@@ -24,6 +24,9 @@ MUTANTS = [
     ("parity split reversed", "out |= ((u >> (4 * i)) & 0xF) << (4 * (i // 2 + 4 * (i % 2)))", "out |= ((u >> (4 * i)) & 0xF) << (4 * (4 * (i % 2) + 3 - i // 2))"),
     ("parity merge identity", "out |= ((u >> (4 * (i // 2 + 4 * (i % 2)))) & 0xF) << (4 * i)", "out |= ((u >> (4 * i)) & 0xF) << (4 * i)"),
     ("awq qweight without the parity split", "qweight = tile_words(split_parity(pack_nibbles(codes)))", "qweight = tile_words(pack_nibbles(codes))"),
+    ("halves split reversed", "out |= ((u >> (4 * i)) & 0xF) << (4 * (2 * (i % 4) + i // 4))", "out |= ((u >> (4 * i)) & 0xF) << (4 * (2 * (i // 4) + i % 4))"),
+    ("halves merge identity", "out |= ((u >> (4 * (2 * (i % 4) + i // 4))) & 0xF) << (4 * i)", "out |= ((u >> (4 * i)) & 0xF) << (4 * i)"),
+    ("w4a8 qweight without the halves split", "qweight = tile_words(split_halves(pack_nibbles(np.asarray(q, dtype=np.int64) + 8)), pad_word=0x88888888)", "qweight = tile_words(pack_nibbles(np.asarray(q, dtype=np.int64) + 8), pad_word=0x88888888)"),
     ("tile rows and slots swapped", "out[:, :, slot, n, w] = full[n::16, slot * 4 + w::16]", "out[:, :, slot, n, w] = full[n::16, (w * 4 + slot)::16]"),
     ("untile rows and slots swapped", "full[n::16, slot * 4 + w::16] = tiled[:, :, slot, n, w]", "full[n::16, (w * 4 + slot)::16] = tiled[:, :, slot, n, w]"),
     ("scales not transposed", "scales = np.ascontiguousarray(scales_gn.T)", "scales = np.ascontiguousarray(scales_gn).reshape(scales_gn.shape[::-1])"),
