@@ -41,7 +41,8 @@
  *   qzeros   int32 [K/G, ceil(N/8)]  4-bit zero points packed along N, plain nibble
  *                                    order, pad nibbles 0 ([1, ceil(N/8)] per-channel)
  *   (W4A8)   qweight int32 [ceil(N/16), K/128, 4, 16, 4] (same tiling) of biased nibbles
- *            q + 8 in plain nibble order (element 8j+i in bits 4i..4i+3 of word j; q in
+ *            q + 8, each word split by halves (element 8j+i in nibble 2(i%4) + i/4 of
+ *            word j: elements 0..3 in the even nibbles, 4..7 in the odd ones; q in
  *            [-8, 7]; padding rows q = 0),
  *            cscale fp16 [N] per-channel scale, gscale int8 [K/G, N] group scales
  *            (two-level variant only), xq int8 [M, K], s_a fp32 [M].
@@ -139,8 +140,9 @@ int awq_import_plain(const int32_t* qweight_plain, const void* scales_plain, con
 /*
  * w4a8_import_plain -- as awq_import_plain for W4A8 weights: qweight_plain holds biased
  * nibbles q + 8 ("[Feature] support qqq(w4a8) for lmdeploy", "Modification": exported
- * QQQ weights are converted to the serving format before the GEMM loads them); the tiled
- * output's padding rows hold q = 0 (nibble 8).  group_size 128 (two-level: gscale_plain
+ * QQQ weights are converted to the serving format before the GEMM loads them) in the
+ * plain nibble order; each word is split by halves on the way (the W4A8 qweight layout,
+ * top of this file), and the tiled output's padding rows hold q = 0 (nibble 8).  group_size 128 (two-level: gscale_plain
  * int8 in the orientation of `layout` -> gscale [K/G, N]) or -1 (per-channel:
  * gscale_plain and gscale must be NULL).  cscale [N] is the same in every layout and is
  * not an argument.

@@ -219,7 +219,7 @@ int awq_import_plain(const int32_t* qweight_plain, const void* scales_plain, con
   W4_TRY(check_device(fn));
   const int ng = group_size == -1 ? 1 : (int)(K / group_size);
   return launched(fn, w4::launch_import_plain(qweight_plain, scales_plain, qzeros_plain, nullptr, qweight, scales,
-                                              qzeros, nullptr, (int)N, (int)K, ng, layout, 0u, true,
+                                              qzeros, nullptr, (int)N, (int)K, ng, layout, 0u, 1,
                                               (hipStream_t)stream));
 }
 
@@ -239,7 +239,7 @@ int w4a8_import_plain(const int32_t* qweight_plain, const int8_t* gscale_plain, 
   }
   W4_TRY(check_device(fn));
   return launched(fn, w4::launch_import_plain(qweight_plain, nullptr, nullptr, gscale_plain, qweight, nullptr, nullptr,
-                                              gscale, (int)N, (int)K, (int)(K / 128), layout, 0x88888888u, false,
+                                              gscale, (int)N, (int)K, (int)(K / 128), layout, 0x88888888u, 2,
                                               (hipStream_t)stream));
 }
 

@@ -124,36 +124,37 @@ __device__ __forceinline__ half2_t scale2(uint32_t sbits) {
 
 __device__ __forceinline__ half2_t splat2(half_t h) { return half2_t{h, h}; }
 
-// Biased int4 (stored nibble b = q + 8) -> 16 * q as int8 bytes, natural order.
-// b ^ 8 is the 4-bit two's complement of q; placing it in the high nibble of a byte
-// gives the int8 value 16 * q exactly.  Returns the 8 elements as two words
-// (elements 0..3, 4..7).
+// W4A8 code words hold 8 biased nibbles b = q + 8 split by halves: elements e_0..e_3 in
+// nibbles 0, 2, 4, 6 and e_4..e_7 in nibbles 1, 3, 5, 7.
+//
+// Biased int4 -> 16 * q as int8 bytes, natural order: b ^ 8 is the 4-bit two's
+// complement of q, and placed in the high nibble of a byte it is the int8 value 16 q
+// exactly.  Shifting the even nibbles up (and masking) gives e_0..e_3 as bytes, masking
+// the odd ones in place gives e_4..e_7: four VALU operations, no byte permutation.
 __device__ __forceinline__ void unpack_i4x16(uint32_t w, uint32_t& lo, uint32_t& hi) {
   const uint32_t t = w ^ 0x88888888u;
-  const uint32_t ev = (t << 4) & 0xf0f0f0f0u;  // bytes: 16*q0, 16*q2, 16*q4, 16*q6
-  const uint32_t od = t & 0xf0f0f0f0u;         // bytes: 16*q1, 16*q3, 16*q5, 16*q7
-  lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // q0 q1 q2 q3
-  hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // q4 q5 q6 q7
+  lo = (t << 4) & 0xf0f0f0f0u;  // bytes 16 q0, 16 q1, 16 q2, 16 q3
+  hi = t & 0xf0f0f0f0u;         // bytes 16 q4, 16 q5, 16 q6, 16 q7
 }
 
-// Biased int4 (b = q + 8) times a per-group int8 scale s -> int8 bytes q * s (|q s| <= 127
-// is guaranteed by the weight rule), natural order, as two words (elements 0..3, 4..7).
+// Biased int4 times a per-group int8 scale s -> int8 bytes q * s (|q s| <= 127 is
+// guaranteed by the weight rule), natural order, as two words (elements 0..3, 4..7).
 // The products are formed in 16-bit lanes: (b * s + (-8 s)) mod 2^16 is q * s as int16,
-// whose low byte is the int8 value.  sp = (s, s), cp = (-8 s, -8 s) as u16 pairs.
+// whose low byte is the int8 value; the nibble pairs (0, 4), (1, 5), (2, 6), (3, 7) of
+// the word hold elements (0, 2), (4, 6), (1, 3), (5, 7), so one v_perm_b32 gathers the
+// low bytes of each half.  sp = (s, s), cp = (-8 s, -8 s) as u16 pairs.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void unpack_i4_scaled(uint32_t w, u16x2 sp, u16x2 cp, uint32_t& lo, uint32_t& hi) {
-  const u16x2 e0 = __builtin_bit_cast(u16x2, w & 0x000f000fu);          // b0, b4
-  const u16x2 e1 = __builtin_bit_cast(u16x2, (w >> 4) & 0x000f000fu);   // b1, b5
-  const u16x2 e2 = __builtin_bit_cast(u16x2, (w >> 8) & 0x000f000fu);   // b2, b6
-  const u16x2 e3 = __builtin_bit_cast(u16x2, (w >> 12) & 0x000f000fu);  // b3, b7
+  const u16x2 e0 = __builtin_bit_cast(u16x2, w & 0x000f000fu);          // b0, b2
+  const u16x2 e1 = __builtin_bit_cast(u16x2, (w >> 4) & 0x000f000fu);   // b4, b6
+  const u16x2 e2 = __builtin_bit_cast(u16x2, (w >> 8) & 0x000f000fu);   // b1, b3
+  const u16x2 e3 = __builtin_bit_cast(u16x2, (w >> 12) & 0x000f000fu);  // b5, b7
   const uint32_t r0 = __builtin_bit_cast(uint32_t, (u16x2)(e0 * sp + cp));
   const uint32_t r1 = __builtin_bit_cast(uint32_t, (u16x2)(e1 * sp + cp));
   const uint32_t r2 = __builtin_bit_cast(uint32_t, (u16x2)(e2 * sp + cp));
   const uint32_t r3 = __builtin_bit_cast(uint32_t, (u16x2)(e3 * sp + cp));
-  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x06020400u);  // p0 p1 p4 p5
-  const uint32_t t1 = __builtin_amdgcn_perm(r3, r2, 0x06020400u);  // p2 p3 p6 p7
-  lo = __builtin_amdgcn_perm(t1, t0, 0x05040100u);                 // p0 p1 p2 p3
-  hi = __builtin_amdgcn_perm(t1, t0, 0x07060302u);                 // p4 p5 p6 p7
+  lo = __builtin_amdgcn_perm(r2, r0, 0x06020400u);  // p0 p1 p2 p3
+  hi = __builtin_amdgcn_perm(r3, r1, 0x06020400u);  // p4 p5 p6 p7
 }
 
 // ------------------------------------------------------------ reductions

@@ -111,12 +111,12 @@ hipError_t launch_ceiling_read(const void* buf, int64_t bytes, uint32_t* sink, i
 hipError_t launch_ceiling_mfma(const void* operands, int64_t operand_bytes, int kind, int iters, float* out,
                                int blocks, hipStream_t stream);
 // Plain (untiled) weights -> the library's layout; NULL sources skip that array.
-// cols: the K-major orientation (qweight [K/8, N], per-group arrays [., N]); split: each
-// code word is split by parity on the way (the W4A16 word format; W4A8 words keep the
-// plain nibble order).
+// cols: the K-major orientation (qweight [K/8, N], per-group arrays [., N]); split: the
+// word format each plain code word is converted to (1: split by parity, the W4A16 words;
+// 2: split by halves, the W4A8 words).
 hipError_t launch_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
                                const int8_t* gscale_plain, int32_t* qweight, void* scales, int32_t* qzeros,
-                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, bool split,
+                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, int split,
                                hipStream_t stream);
 
 // Every GEMM entry point plans once per call: the plan sizes the workspace and is then

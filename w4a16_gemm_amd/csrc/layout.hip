@@ -12,8 +12,9 @@
 //                              qzeros int32 [ceil(K/G / 8), N].
 // In both, element k = 8j + i of a row's codes sits in bits 4i..4i+3 of word j and the
 // zero point of group g in bits 4 (g % 8).. of word g / 8.  The library keeps the W4A16
-// words split by parity (element i in nibble i / 2 + 4 (i % 2)) and tiled in 1 KB
-// blocks of 16 rows x 128 k, the scales group-major [K/G, N] and the zero points packed
+// words split by parity (element i in nibble i / 2 + 4 (i % 2)), the W4A8 words split by
+// halves (element i in nibble 2 (i % 4) + i / 4), both tiled in 1 KB blocks of 16 rows x
+// 128 k, the scales group-major [K/G, N] and the zero points packed
 // along N [K/G, ceil(N/8)]; every conversion is a rearrangement of bits (exact).  "[Feature] support qqq(w4a8) for lmdeploy" ("Modification") converts
 // exported QQQ weights before its GEMM can load them; here the W4A8 words (biased
 // nibbles q + 8) are tiled like the W4A16 ones and the int8 group scales go to [K/G, N].
@@ -29,11 +30,15 @@ struct Strides {
   int64_t sn, si;
 };
 
-// Plain word -> parity-split word: element i (nibble i) to nibble i / 2 + 4 (i % 2).
-__device__ __forceinline__ uint32_t split_parity(uint32_t w) {
+// Plain word -> the library's word formats: split by parity (W4A16; element i to nibble
+// i / 2 + 4 (i % 2)) or by halves (W4A8; element i to nibble 2 (i % 4) + i / 4).
+__device__ __forceinline__ uint32_t split_word(uint32_t w, int split) {
   uint32_t o = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o |= ((w >> (4 * i)) & 15u) << (4 * ((i >> 1) + 4 * (i & 1)));
+  for (int i = 0; i < 8; ++i) {
+    const int to = split == 1 ? (i >> 1) + 4 * (i & 1) : 2 * (i & 3) + (i >> 2);
+    o |= ((w >> (4 * i)) & 15u) << (4 * to);
+  }
   return o;
 }
 
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(256) void tile_words_kernel(const uint32_t* __restr
       }
       if (split) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = split_parity(v[i]);
+        for (int i = 0; i < 4; ++i) v[i] = split_word(v[i], split);
       }
     }
     tiled[c] = v;
@@ -109,12 +114,12 @@ inline unsigned grid_for(int64_t total) {
 
 hipError_t launch_import_plain(const int32_t* qweight_plain, const void* scales_plain, const int32_t* qzeros_plain,
                                const int8_t* gscale_plain, int32_t* qweight, void* scales, int32_t* qzeros,
-                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, bool split,
+                               int8_t* gscale, int N, int K, int ng, int cols, uint32_t pad, int split,
                                hipStream_t stream) {
   const int64_t chunks = (int64_t)((N + 15) / 16) * (K / 128) * 64;
   const Strides sw = cols ? Strides{1, N} : Strides{K / 8, 1};
   hipLaunchKernelGGL(tile_words_kernel, dim3(grid_for(chunks)), dim3(256), 0, stream, (const uint32_t*)qweight_plain,
-                     (u32x4*)qweight, N, K / 128, sw, pad, (int)split, chunks);
+                     (u32x4*)qweight, N, K / 128, sw, pad, split, chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t vals = (int64_t)N * ng;

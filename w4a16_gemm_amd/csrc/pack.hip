@@ -18,7 +18,9 @@
 //  * awq_unpack_dequant: fp16((q - z) * s), the GEMM's dequantization, exported.
 //  * w4a8_pack: symmetric int4 weights for the W4A8 GEMM, per-channel or two-level
 //    with int8 group scales ("[Feature] support qqq(w4a8) for lmdeploy", section
-//    "Benchmark": QQQ per-channel and QQQ-g128 variants).
+//    "Benchmark": QQQ per-channel and QQQ-g128 variants), as biased nibbles q + 8 in
+//    words split by halves (elements 0..3 in the even nibbles, 4..7 in the odd ones: the
+//    order the int8 expansion takes without byte permutations).
 //  * w8a8_pack: per-channel symmetric int8 weights for W8A8 (the 8-bit-weight method
 //    mentioned on the vLLM AWQ page, and W8A8 as named on the compressed-tensors
 //    page; constants as the first level of the two-level W4A8 rule):
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q = fminf(fmaxf(rintf(e[i] / s), -8.0f), 7.0f);
-        word |= ((uint32_t)((int)q + 8)) << (4 * i);
+        word |= ((uint32_t)((int)q + 8)) << (4 * (2 * (i & 3) + (i >> 2)));  // split by halves
       }
     } else {
       float w8[8];
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256) void w4a8_pack_kernel(const half_t* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q = fminf(fmaxf(rintf(w8[i] / sg), -7.0f), 7.0f);
-        word |= ((uint32_t)((int)q + 8)) << (4 * i);
+        word |= ((uint32_t)((int)q + 8)) << (4 * (2 * (i & 3) + (i >> 2)));
       }
       if (ok && (j & 15) == 0) gscale[(int64_t)(j / 16) * N + n] = (int8_t)(int)sg;
     }

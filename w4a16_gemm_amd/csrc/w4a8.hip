@@ -8,7 +8,9 @@
 // 8-bit matmuls: the int8 product accumulates to int32 and is rescaled by the weight
 // and activation scales; activations are quantized dynamically per token.
 //
-// Weight codes are stored as biased nibbles b = q + 8.
+// Weight codes are stored as biased nibbles b = q + 8, each word split by halves
+// (elements 0..3 in the even nibbles, 4..7 in the odd ones), so that the int8 bytes of
+// a word come out in natural k order without byte permutations.
 //   per-channel:  b ^ 8 is the 4-bit two's complement of q; shifted into the high
 //                 nibble of a byte it is the int8 value 16 q, so the MFMA accumulates
 //                 16 * sum(xq * q) exactly and an exact arithmetic shift by 4 (every
