@@ -182,11 +182,26 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
     };
     BSet bs[R];
     const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
+    // Every address of step kt is a wave-uniform base (scalar registers) plus a per-lane
+    // 32-bit offset fixed for the whole loop, so no per-lane 64-bit address arithmetic is
+    // left in the loop (the plan takes these pipelines only while the offsets fit):
+    //  * codes: the chunk of (row n, group kt / 2, slot 2 (kt % 2) + h) is word
+    //    tiled_chunk(n, 0, h) + 128 kt;
+    //  * scale / zero point: row (64 kt + 32 h) >> glog of [K/G, .] = (64 kt) >> glog, plus
+    //    h for G = 32 (this lane's 32 k of a BK step lie in one group for G >= 32).
+    uint32_t boff[NF], zoff[NF], soff[NF];
+    const int hrow = glog == 5 ? h : 0;
+  #pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      boff[f] = (uint32_t)tiled_chunk(nclamp[f], 0, h, ng);
+      zoff[f] = (uint32_t)(hrow * nzw + (nclamp[f] >> 3));
+      soff[f] = (uint32_t)(hrow * N + nclamp[f]);
+    }
     auto issue = [&](int kt, int slot, BSet& S) {
-      // BK step kt is half of group kt / 2: slot 2 (kt % 2) + h of the tiled layout
+      const uint32_t* qw_kt = qweight + (int64_t)kt * 128;
   #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const uint32_t* src = qweight + tiled_chunk(nclamp[f], kt >> 1, (kt & 1) * 2 + h, ng);
+        const uint32_t* src = qw_kt + boff[f];
         if constexpr (kBLds)
           __builtin_amdgcn_global_load_lds((void*)src,
                                            (__attribute__((address_space(3))) void*)(bring(slot) + (4 * f + wave) * 64),
@@ -194,16 +209,18 @@ __global__ __launch_bounds__(kThreads, PD == 0 ? 1 : 2) void gemm_kernel(const h
         else
           S.b[f] = *reinterpret_cast<const u32x4*>(src);
       }
-      // this lane's k range in BK step kt is kt * 64 + 32 h .. + 31: one group for G >= 32
-      const int64_t row = (int64_t)((kt * BK + 32 * h) >> glog);
+      const int64_t row = (int64_t)((kt * BK) >> glog);
+      const uint32_t* qz_kt = qzeros + row * nzw;
+      const uint16_t* sc_kt = sbits + row * N;
   #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        S.z[f] = qzeros[row * nzw + (nclamp[f] >> 3)];
-        S.s[f] = sbits[row * N + nclamp[f]];
+        S.z[f] = qz_kt[zoff[f]];
+        S.s[f] = sc_kt[soff[f]];
       }
+      const half_t* x_kt = x + kt * BK;
   #pragma unroll
       for (int i = 0; i < kAPer; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(x + xoff[i] + kt * BK),
+        __builtin_amdgcn_global_load_lds((void*)(x_kt + xoff[i]),
                                          (__attribute__((address_space(3))) void*)(ring(slot) + (4 * i + wave) * 64), 16, 0,
                                          0);
     };
@@ -591,8 +608,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
   // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
   p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 8 : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
-  // the direct-to-LDS pipeline addresses X with 32-bit element offsets
-  if ((p.depth == 0 || p.depth == 5 || p.depth == 7 || p.depth == 8) && (int64_t)M * K >= (int64_t(1) << 31))
+  // the direct-to-LDS pipelines address X, the codes, scales and zero points with 32-bit
+  // per-lane offsets
+  if ((p.depth == 0 || p.depth == 5 || p.depth == 7 || p.depth == 8) &&
+      ((int64_t)M * K >= (int64_t(1) << 31) || (int64_t)N * K >= (int64_t(1) << 33)))
     p.depth = 1;
   p.tiles_m = (M + 32 * p.mi - 1) / (32 * p.mi);
   p.tiles_n = (N + 128 * p.nf - 1) / (128 * p.nf);
