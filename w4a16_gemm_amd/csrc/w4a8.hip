@@ -1005,7 +1005,8 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // Tail split (128-row tiles, two resident per CU: 512 slots on 256 CUs): a last round
   // under half full split in two over its groups.  Off by default: at M = 4096,
   // N = 13824 (1728 tiles = 3 rounds + 192) it measured 431 -> 464 us (per-channel),
-  // 490 -> 533 (two-level), 448 -> 440 (W8A8), unlike the fp16 GEMM.
+  // 490 -> 533 (two-level), 448 -> 440 (W8A8) with the register pipeline, and still
+  // 270 -> 301, 326 -> 356, 376 -> 373 with the direct-to-LDS rings, unlike the fp16 GEMM.
   p.n_full = 0;
   p.tail_splits = 0;
   const int slots = 512 * env_int("W4_W4A8_SLOTS_SCALE", 1) / env_int("W4_W4A8_SLOTS_DIV", 1);
