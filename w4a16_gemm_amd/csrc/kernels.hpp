@@ -71,7 +71,7 @@ struct SkinnyPlan {
   int smem;        // LDS kernel: dynamic LDS bytes per workgroup
   int drain;       // 1: wait for all loads in flight once per D groups
   int waves;       // register-X kernel: waves per workgroup (4 or 8)
-  int xs;          // register-X kernel, M <= 4: one X load per group, fragments formed in LDS
+  int xs;          // register-X kernel, mt == 1: X loaded as whole rows (ceil(M / 4) loads per group), fragments formed in LDS
 };
 SkinnyPlan skinny_plan(int M, int N, int K, int group_size);
 

@@ -48,7 +48,7 @@ struct GroupRegs {
 // row depends only on its own A row and an output column only on its own B column
 // (and scale / zero point), so clamped data only reaches outputs that are never
 // stored.
-template <int MT, int T, bool DQ, bool XS = false>
+template <int MT, int T, bool DQ, int XS = 0>
 __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __restrict__ x,
                                            const uint32_t* __restrict__ qweight,
                                            const half_t* __restrict__ scales,
@@ -66,7 +66,7 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     // tiled layout: lane l reads chunk l of the 1 KB block (16 rows x 128 k) -- row
     // l % 16 of the tile, words 4 (l / 16) .. + 3 of the group
     const int tile = min((n0 >> 4) + t, last_tile);
-    r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+    r.b[t] = ld_stream(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
     if (DQ) {
       const int nc = min(n0 + 16 * t + (lane & 15), N - 1);
       r.s[t] = scales[row * N + nc];
@@ -82,9 +82,13 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     }
   }
   if (XS) {
-    // M <= 4: one load brings the group's X for all rows -- lane l takes 16-byte chunk
-    // l % 16 of row l / 16 (rows past M clamped); compute_group forms the fragments in LDS
-    r.a[0][0] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(lane >> 4, M - 1) * K + g * 128 + (lane & 15) * 8);
+    // M <= 4 XS: XS loads bring the group's X for all rows -- load i of lane l takes
+    // 16-byte chunk l % 16 of row 4 i + l / 16 (rows past M clamped; each load reads four
+    // whole 256-byte rows); compute_group forms the fragments in LDS
+#pragma unroll
+    for (int i = 0; i < XS; ++i)
+      r.a[0][i] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(4 * i + (lane >> 4), M - 1) * K + g * 128 +
+                                                    (lane & 15) * 8);
     return;
   }
 #pragma unroll
@@ -108,7 +112,7 @@ __device__ __forceinline__ half8_t unpack_mixed(uint32_t w, const Magic& c) {
 // per row, S_g (ones) and -P_g (-1024 at k = 0, 1 mod 4, -64 at k = 2, 3 mod 4); -P_g
 // seeds every n-tile's chain, which then holds T_g - P_g = sum_k X q and the fold is
 // y += s (T_g - P_g - z S_g).
-template <int MT, int T, bool XS = false>
+template <int MT, int T, int XS = 0>
 __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_t (&yacc)[MT][T],
                                               const int (&zsh)[kChunks<T>], half_t* xb = nullptr, int lane = 0) {
   const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
@@ -117,14 +121,19 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
   half8_t a[MT][4];
   float4_t ssum[MT], negp[MT];
   if (XS) {
-    // The group's 4 rows x 256 bytes through this wave's 1 KB of LDS: chunk c of row q at
-    // chunk c ^ q (the 4 rows of one fragment read fall in distinct banks).  Fragment j
-    // of lane l is chunk 4 (l / 16) + j of row (l % 16) % 4 (rows 4..15 of the MFMA only
-    // reach outputs that are never stored when M <= 4).  LDS operations of one wave
-    // execute in order, so the reads see the whole wave's writes.
+    // The group's 4 XS rows x 256 bytes through this wave's XS KB of LDS: chunk c of row
+    // q at chunk c ^ q (the rows of one fragment read, and the chunks of one row written,
+    // fall in distinct banks).  Fragment j of lane l is chunk 4 (l / 16) + j of row
+    // (l % 16) mod 4 XS (MFMA rows past 4 XS only reach outputs that are never stored:
+    // M <= 4 XS).  LDS operations of one wave execute in order, so the reads see the
+    // whole wave's writes.
     const int q = lane >> 4, c = lane & 15;
-    *reinterpret_cast<half8_t*>(xb + q * 128 + (c ^ q) * 8) = r.a[0][0];
-    const int rr = lane & 3;
+#pragma unroll
+    for (int i = 0; i < XS; ++i) {
+      const int row = 4 * i + q;
+      *reinterpret_cast<half8_t*>(xb + row * 128 + (c ^ row) * 8) = r.a[0][i];
+    }
+    const int rr = lane & (4 * XS - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       a[0][j] = *reinterpret_cast<const half8_t*>(xb + rr * 128 + ((4 * q + j) ^ rr) * 8);
@@ -199,13 +208,13 @@ __device__ __forceinline__ void compute_group_dq(const GroupRegs<MT, T>& r, floa
 // Workgroups resident per CU that the register allocation must allow, for the plans
 // that pick these variants: three 4-wave workgroups (<= 168 VGPRs) or two 8-wave ones
 // (<= 128 VGPRs); the others take what they need.
-constexpr int skinny_min_blocks(int mt, int t, int d, int waves, bool dq, bool xs) {
+constexpr int skinny_min_blocks(int mt, int t, int d, int waves, bool dq, int xs) {
   if (mt != 1 || dq || xs) return 1;
   if (waves == 4 && ((t == 4 && d <= 3) || (t == 2 && d == 2) || (t == 1 && d == 4))) return 3;
   if (waves == 8 && ((t == 2 && d <= 3) || (t == 4 && d == 2) || (t == 1 && d == 4))) return 2;
   return 1;
 }
-template <int MT, int T, int D, int WAVES, bool DQ, bool XS = false>
+template <int MT, int T, int D, int WAVES, bool DQ, int XS = 0>
 __global__ __launch_bounds__(WAVES * kWave, skinny_min_blocks(MT, T, D, WAVES, DQ, XS)) void skinny_kernel(const half_t* __restrict__ x,
                                                                const uint32_t* __restrict__ qweight,
                                                                const half_t* __restrict__ scales,
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(WAVES * kWave, skinny_min_blocks(MT, T, D, WAVES, D
   // outputs: threads past the last output only read a clamped entry and store nothing)
   constexpr int kPer = (kOut + kT - 1) / kT;
   __shared__ float red[WAVES][MT * T * 4 * kWave];
-  __shared__ __align__(16) half_t xbuf[XS ? WAVES : 1][XS ? 512 : 8];  // M <= 4: X rows of a group
+  __shared__ __align__(16) half_t xbuf[XS ? WAVES : 1][XS ? 512 * XS : 8];  // M <= 4 XS: X rows of a group
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int rb = blockIdx.x;
@@ -259,8 +268,12 @@ __global__ __launch_bounds__(WAVES * kWave, skinny_min_blocks(MT, T, D, WAVES, D
     for (int d = 0; d < D; ++d) {
       if (DQ) compute_group_dq<MT, T>(r[d], yacc, n0, lane, N);
       else compute_group<MT, T, XS>(r[d], yacc, zsh, xbuf[wave], lane);
+      // (scheduling fences: without them the compiler starts the next set's MFMAs before
+      // this set's loads are issued, and its waits then drain nearly every load in flight)
+      __builtin_amdgcn_sched_barrier(0);
       load_group<MT, T, DQ, XS>(r[d], x, qweight, scales, qzeros, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N,
                             K, glog);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -383,7 +396,7 @@ __device__ __forceinline__ void load_wstage(WStage<T>& r, const uint32_t* __rest
   for (int t = 0; t < T; ++t) {
     const int tile = min(tile0 + t, last_tile);
     const int nc = min(16 * (tile0 + t) + (lane & 15), N - 1);
-    r.b[t] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+    r.b[t] = ld_stream(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
     r.s[t] = srow[nc];
     r.zw[t] = zrow[nc >> 3];
   }
@@ -554,8 +567,10 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
     for (int d = 0; d < D; ++d) {
       const int gl = g + (it + d) * WK - gbeg;
       compute_wstage<T, ONE_ROW>(r[d], xrow + gl * 128, sp + gl * 32, yacc, zsh, lane);
+      __builtin_amdgcn_sched_barrier(0);  // (as in the register-X kernel)
       load_wstage<T>(r[d], qweight, scales, qzeros, min(gbeg + gl + D * WK, glast), tile0, lane, N, ng, nzw,
                      glog);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
   V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
-  V(1, 1, 8, 8, 1) V(1, 1, 4, 16, 0) V(1, 2, 4, 8, 1)
+  V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1)
 static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 100 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
   const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
@@ -715,6 +730,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     if (rb >= 256 || rb >= kMaxCounters) sp = 1;
     return sp;
   };
+  const bool narrow = p.mt == 1 && N <= 8192;
   t = env_int("W4_SKINNY_TILES", 0);
   if (t != 1 && t != 2 && t != 4 && t != 8) {
     // (4 < M <= 8 with long K: 4 tiles, 8 waves, split K -- down 13824 x 5120 at M = 8:
@@ -734,6 +750,10 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // 4 < M <= 16 on wide matrices: 8 tiles halve the X loads per weight byte and still
     // leave > 160 column blocks (gate+up 5120 x 27648 at M = 16: 20.8 -> 17.7 us)
     if (M > 4 && M <= 16 && N > 16384) t = 8;
+    // narrow matrices (N <= 8192) at 4 < M <= 16: 2 tiles, or 4 on long K past M = 8, with
+    // X loaded as whole rows (below; O 5120 x 5120 at M = 8 / 16 7.2 -> 6.6 / 9.1 -> 8.0 us,
+    // down 13824 x 5120 13.2 -> 12.1 / 15.2 -> 14.3, single 4096 x 4096 at M = 8 7.7 -> 6.8)
+    if (narrow && M > 4) t = (M > 8 && K > 8192) ? 4 : 2;
   }
   if (t == 8 && (group_size == 64 || group_size == 32)) t = 4;  // (no 8-tile dequantizing kernel)
   p.tiles = t;
@@ -741,21 +761,27 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   // 8 waves for narrow workgroups at M <= 8 (more groups in flight per column block:
   // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
   // and for the 8-tile ones
-  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8)) ? 8 : 4;
+  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8 || narrow)) ? 8 : 4;
   p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
     // 4-tile, 4-wave workgroups below 16384 columns keep a third group of loads in
     // flight (weights streamed from HBM: QKV 5120 x 15360 at M = 1-8 ~11.0 -> ~9.9 us,
     // O 5120 x 5120 at M = 16 9.7 -> 9.2 us, down 13824 x 5120 at M = 16 15.9 -> 15.5 us)
-    if (p.mt == 1 && p.tiles == 4 && p.waves == 4 && N <= 16384) p.depth = 3;
+    // (at 8 < M <= 16 two deep with X loaded as whole rows: QKV 5120 x 15360 at M = 16
+    // 11.9 -> 11.3 us)
+    if (p.mt == 1 && p.tiles == 4 && p.waves == 4 && N <= 16384 && M <= 8) p.depth = 3;
     // variants (sweeps): prefetch depth, 8-wave workgroups
     SkinnyPlan q = p;
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
     q.waves = env_int("W4_SKINNY_WAVES", p.waves);
-    // one X load per group (fragments formed in LDS) at 1 < M <= 4 on wide matrices:
-    // gate+up 5120 x 27648 at M = 4 15.8 -> 14.7 us; 2-5 % slower on QKV, O and down
-    q.xs = (M <= 4 && p.mt == 1) ? env_int("W4_SKINNY_XS", M > 1 && N > 16384) : 0;
+    // X loaded as whole rows, ceil(M / 4) 16-byte loads per lane and group (fragments
+    // formed in LDS) instead of four fragment loads: at 1 < M <= 4 on wide matrices
+    // (gate+up 5120 x 27648 at M = 4 15.8 -> 14.7 us), at 8 < M <= 16 up to 16384
+    // columns, and on narrow matrices with two or more tiles (down 13824 x 5120 at
+    // M = 1 / 4 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8
+    const bool xs_dflt = (M > 1 && M <= 4 && N > 16384) || (M > 8 && N <= 16384) || (narrow && q.tiles >= 2);
+    q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
     if (skinny_variant_compiled(q)) p = q;
   }
   int splits = plan_splits(t, p.row_blocks);
@@ -814,8 +840,24 @@ hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const int32_t* qwei
   }
 #define V(MT, T, D, W, XS)                                                                                   \
   if (key == variant_key(MT, T, D, W, XS)) {                                                                 \
-    hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, XS != 0>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, \
-                       qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                 \
+    if constexpr (XS == 0) {                                                                                 \
+      hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 0>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, qz, \
+                         yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                   \
+    } else if (M > 4) { /* (the plan takes XS at M > 4 only with two-deep, multi-tile variants) */           \
+      if constexpr (T > 1 && D <= 2) {                                                                       \
+        if (M > 8)                                                                                           \
+          hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 4>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, \
+                             qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);           \
+        else                                                                                                 \
+          hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 2>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, \
+                             qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);           \
+      } else {                                                                                               \
+        return hipErrorInvalidValue;                                                                         \
+      }                                                                                                      \
+    } else {                                                                                                 \
+      hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 1>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, qz, \
+                         yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                   \
+    }                                                                                                        \
     return hipGetLastError();                                                                                \
   }
   SKINNY_VARIANTS(V)

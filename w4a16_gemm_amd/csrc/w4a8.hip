@@ -783,11 +783,11 @@ __device__ __forceinline__ void w8_load(W8Regs<T, MODE>& r, const int8_t* __rest
       const int8_t* w8 = reinterpret_cast<const int8_t*>(qweight);
       const int nc = min(n0 + 16 * t + (lane & 15), 16 * last_tile + 15);
       const int slot = lane >> 4;
-      r.b[t][0] = *reinterpret_cast<const u32x4*>(w8 + tiled8_offset(nc, g, 2 * slot, ng));
-      r.b[t][1] = *reinterpret_cast<const u32x4*>(w8 + tiled8_offset(nc, g, 2 * slot + 1, ng));
+      r.b[t][0] = ld_stream(w8 + tiled8_offset(nc, g, 2 * slot, ng));
+      r.b[t][1] = ld_stream(w8 + tiled8_offset(nc, g, 2 * slot + 1, ng));
     } else {
       const int tile = min((n0 >> 4) + t, last_tile);
-      r.b[t][0] = *reinterpret_cast<const u32x4*>(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
+      r.b[t][0] = ld_stream(qweight + ((int64_t)tile * ng + g) * 256 + lane * 4);
     }
   }
   if (MODE == kI4TwoLevel) {
@@ -875,7 +875,11 @@ __global__ __launch_bounds__(256) void w4a8_skinny_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       w8_compute<T, MODE>(r[d], acc);
+      // (scheduling fences: the next set's MFMAs must not start before this set's loads
+      // are issued, or the waits drain nearly every load in flight)
+      __builtin_amdgcn_sched_barrier(0);
       w8_load<T, MODE>(r[d], xq, qweight, gscale, min(g + (it + d + D) * WAVES, glast), n0, lane, M, N, K);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
