@@ -185,10 +185,11 @@ template <int T>
 constexpr int kChunks = (T + 3) / 4;
 
 // Column (within the workgroup's 16 T) whose scale and zero point lane `lane` loads in
-// chunk c: 64 c + lane for T >= 4; for T < 4 the 16 T columns repeat over the lanes.
+// chunk c: 64 c + lane for T >= 3 (past column 16 T - 1 the values are never used); for
+// T = 1, 2 the 16 T columns repeat over the lanes.
 template <int T>
 __device__ __forceinline__ int chunk_col(int c, int lane) {
-  return 64 * c + (lane & (16 * (T < 4 ? T : 4) - 1));
+  return 64 * c + (lane & (T == 1 ? 15 : T == 2 ? 31 : 63));
 }
 
 // v holds, in 16-lane row r of chunk c, the value of n-tile 4 c + r (rows repeat for
@@ -209,10 +210,11 @@ __device__ __forceinline__ void rows_to_tiles(const uint32_t (&v)[kChunks<T>], u
       const auto h = __builtin_amdgcn_permlane32_swap(v[c], v[c], false, false);
       const auto p = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
       const auto q = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+      // (T not a multiple of 4: the last chunk's rows past tile T - 1 are dropped)
       w[4 * c] = p[0];
-      w[4 * c + 1] = p[1];
-      w[4 * c + 2] = q[0];
-      w[4 * c + 3] = q[1];
+      if (4 * c + 1 < T) w[4 * c + 1] = p[1];
+      if (4 * c + 2 < T) w[4 * c + 2] = q[0];
+      if (4 * c + 3 < T) w[4 * c + 3] = q[1];
     }
   }
 }

@@ -16,8 +16,8 @@
 // x (c_k + q) products are exact in fp32, only the fp32 sums round.
 //
 // Work split (register-X kernel, M <= 32; the kernel further below stages X in LDS and
-// is the default only at M = 1 on wide, short matrices): a workgroup (4 or 8 waves) owns 16 T output columns n (T = 1, 2, 4 or 8 tiles
-// of 16) and a contiguous range of K groups (split-K across workgroups only for narrow
+// is kept behind a tuning variable): a workgroup (4 or 8 waves) owns 16 T output columns
+// n (T = 1 .. 8 tiles of 16) and a contiguous range of K groups (split-K across workgroups only for narrow
 // N); its waves take the groups of that range round robin.  Per group, lane l of a wave
 // loads one 16-byte chunk (32 codes) of row n0 + 16t + (l % 16) for each tile t -- with
 // the tiled weight layout the 64 lanes read one contiguous 1 KB block -- the 64 bytes of
@@ -350,9 +350,9 @@ __global__ __launch_bounds__(WAVES * kWave, skinny_min_blocks(MT, T, D, WAVES, D
 
 
 // ---------------------------------------------------------------------------------
-// M <= 16: X staged in LDS, codes unpacked in five VALU operations per word (the plan
-// takes this kernel by default for one row against a wide, short matrix only; it is
-// kept for every M <= 16 behind its tuning variable and tested that way).
+// M <= 16: X staged in LDS, codes unpacked in five VALU operations per word (no default
+// plan takes this kernel; it is kept for every M <= 16 behind its tuning variable and
+// tested that way).
 //
 // The workgroup copies its slice of X (M rows x its K range) into LDS once; the
 // per-group register sets that are prefetched D deep then carry only what comes from
@@ -623,7 +623,9 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 #define SKINNY_VARIANTS(V)                                                                                   \
   V(1, 4, 2, 4, 0) V(1, 2, 2, 4, 0) V(1, 1, 4, 4, 0) V(2, 4, 2, 4, 0) V(2, 2, 2, 4, 0) V(2, 1, 4, 4, 0)          \
   V(1, 8, 2, 4, 0) V(1, 4, 3, 4, 0) V(1, 2, 4, 4, 0) V(1, 1, 8, 4, 0) V(1, 4, 2, 8, 0) V(1, 2, 2, 8, 0)          \
-  V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
+  V(1, 8, 2, 8, 0) V(2, 8, 2, 4, 0) V(1, 7, 2, 4, 0) V(1, 7, 2, 8, 0) V(1, 7, 2, 4, 1)       \
+  V(1, 6, 2, 4, 0) V(1, 6, 2, 8, 0) V(1, 5, 2, 4, 0) V(1, 5, 2, 8, 0)  \
+  V(1, 3, 2, 8, 0) V(1, 3, 2, 8, 1) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
   V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
   V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1)
@@ -664,9 +666,9 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
                       (group_size == 128 || group_size == -1);
   // Default kernel and shape, from sweeps on the MI355X over the Llama-2-13B projection
   // shapes at M = 1, 4, 8, 16: the register-X kernel (one scale and one zero-point load
-  // per 64 columns, five-op unpack) wins everywhere except one row against a wide, short
-  // matrix (gate+up 5120 x 27648 at M = 1: 14.8 us against 15.0-15.4).
-  int use_lds = lds_ok && M == 1 && N > 16384 && K <= 8192;
+  // per 64 columns, five-op unpack) wins everywhere (the last case the LDS kernel held,
+  // gate+up 5120 x 27648 at M = 1, went to 7-tile register-X workgroups: 15.7 -> 14.9 us).
+  int use_lds = 0;
   int t = 1, d = 4, wn = 1, wk = 4, target = 256;
   if (N > 16384) { t = 4; d = 2; }
   else if (N > 8192) { wn = 2; }
@@ -732,7 +734,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   };
   const bool narrow = p.mt == 1 && N <= 8192;
   t = env_int("W4_SKINNY_TILES", 0);
-  if (t != 1 && t != 2 && t != 4 && t != 8) {
+  if (t < 1 || t > 8) {
     // (4 < M <= 8 with long K: 4 tiles, 8 waves, split K -- down 13824 x 5120 at M = 8:
     // 13.1 -> 11.9 us)
     const bool longk = M > 4 && M <= 8 && K > 8192;
@@ -747,21 +749,24 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     while (M <= 8 && !longk && t > 1 && (N + 16 * t - 1) / (16 * t) < 160 && (N + 8 * t - 1) / (8 * t) >= 160) t /= 2;
     // 8 < M <= 16: 4 tiles share each X fragment, unless that leaves under 128 workgroups
     if (M > 8 && M <= 16 && t == 4 && plan_splits(4, rb1) * rb1 < 128 && plan_splits(2, rb2) * rb2 >= 128) t = 2;
-    // 4 < M <= 16 on wide matrices: 8 tiles halve the X loads per weight byte and still
-    // leave > 160 column blocks (gate+up 5120 x 27648 at M = 16: 20.8 -> 17.7 us)
-    if (M > 4 && M <= 16 && N > 16384) t = 8;
+    // wide matrices at M <= 16: the fewest tiles (at most 8) that still give one column
+    // block per CU, so that every CU streams the same share (gate+up 5120 x 27648: 7
+    // tiles, 247 workgroups; at M = 1 / 8 / 16 15.1-15.7 -> 14.9, 16.5 -> 15.9, 18.1 ->
+    // 17.7 us against 4 tiles on 432 workgroups or 8 tiles on 216)
+    if (M <= 16 && N > 16384) t = min(8, (N + 4095) / 4096);
     // narrow matrices (N <= 8192) at 4 < M <= 16: 2 tiles, or 4 on long K past M = 8, with
     // X loaded as whole rows (below; O 5120 x 5120 at M = 8 / 16 7.2 -> 6.6 / 9.1 -> 8.0 us,
     // down 13824 x 5120 13.2 -> 12.1 / 15.2 -> 14.3, single 4096 x 4096 at M = 8 7.7 -> 6.8)
     if (narrow && M > 4) t = (M > 8 && K > 8192) ? 4 : 2;
   }
-  if (t == 8 && (group_size == 64 || group_size == 32)) t = 4;  // (no 8-tile dequantizing kernel)
+  // (the dequantizing kernel exists for 1, 2 and 4 tiles)
+  if ((group_size == 64 || group_size == 32) && t != 1 && t != 2 && t != 4) t = t > 4 ? 4 : 2;
   p.tiles = t;
   p.depth = t == 1 ? 4 : 2;
   // 8 waves for narrow workgroups at M <= 8 (more groups in flight per column block:
   // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
   // and for the 8-tile ones
-  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8 || narrow)) ? 8 : 4;
+  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8 || narrow || (N > 16384 && M > 8))) ? 8 : 4;
   p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
@@ -776,13 +781,22 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
     q.waves = env_int("W4_SKINNY_WAVES", p.waves);
     // X loaded as whole rows, ceil(M / 4) 16-byte loads per lane and group (fragments
-    // formed in LDS) instead of four fragment loads: at 1 < M <= 4 on wide matrices
-    // (gate+up 5120 x 27648 at M = 4 15.8 -> 14.7 us), at 8 < M <= 16 up to 16384
-    // columns, and on narrow matrices with two or more tiles (down 13824 x 5120 at
-    // M = 1 / 4 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8
-    const bool xs_dflt = (M > 1 && M <= 4 && N > 16384) || (M > 8 && N <= 16384) || (narrow && q.tiles >= 2);
+    // formed in LDS) instead of four fragment loads: at 8 < M <= 16 up to 16384 columns,
+    // and on narrow matrices with two or more tiles (down 13824 x 5120 at M = 1 / 4
+    // 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8 and with 7 tiles on wide
+    // matrices (gate+up at M = 4: 14.9 against 16.4 us)
+    const bool xs_dflt = (M > 8 && N <= 16384) || (narrow && q.tiles >= 2);
     q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
     if (skinny_variant_compiled(q)) p = q;
+    // (a tile width forced by a tuning variable without a compiled variant for its m-tiles
+    // falls back to the widest power of two below it, 4 waves)
+    if (!skinny_variant_compiled(p)) {
+      t = t >= 4 ? 4 : t >= 2 ? 2 : 1;
+      p.tiles = t;
+      p.depth = t == 1 ? 4 : 2;
+      p.waves = 4;
+      p.xs = 0;
+    }
   }
   int splits = plan_splits(t, p.row_blocks);
   p.gps = (ng + splits - 1) / splits;
