@@ -332,7 +332,7 @@ def single_workload(args, dev, torch, np, synth, w4):
     return res
 
 
-READ_CONFIGS = ((512, 4), (1024, 4), (2048, 4), (1024, 8), (2048, 8), (4096, 4))
+READ_CONFIGS = ((256, 8), (512, 4), (512, 8), (1024, 4), (2048, 4), (1024, 8), (2048, 8), (4096, 4))
 
 
 def _read_ceiling(torch, w4, dev, sizes, steps, pool_bytes=1 << 30):

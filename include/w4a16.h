@@ -314,8 +314,8 @@ int w4_pack_codes(const uint8_t* codes, int32_t* out, int64_t R, int64_t C, void
  * for lmdeploy", "Throughput").  Neither computes anything of the method.
  *
  * w4_ceiling_read -- read every byte of buf[0, bytes) once from device memory (16-byte
- * vector loads, grid-stride over `blocks` workgroups of 256 threads, `unroll` (4 or 8)
- * loads in flight per thread) and store one xor-fold word per wave to sink (blocks * 4
+ * non-temporal vector loads, grid-stride over `blocks` workgroups of 256 threads, `unroll`
+ * (4 or 8) loads in flight per thread) and store one xor-fold word per wave to sink (blocks * 4
  * uint32, device).  bytes a positive multiple of 16; 1 <= blocks <= 65536.
  *
  * w4_ceiling_mfma -- `blocks` workgroups of 4 waves, each wave running `iters` rounds of

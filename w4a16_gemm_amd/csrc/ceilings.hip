@@ -5,9 +5,10 @@
 // serving throughput of FP16, W4A16 and W4A8 side by side), and a roofline fraction is
 // only as meaningful as its denominator.
 //
-//  * read_stream_kernel: every 16-byte chunk of a buffer read once (grid-stride, U loads
-//    in flight per thread), the data folded with xor and one word per wave stored, so
-//    no load is dead.  Timed by the caller at the byte counts of the GEMMs' weights.
+//  * read_stream_kernel: every 16-byte chunk of a buffer read once (grid-stride, U
+//    non-temporal loads in flight per thread, as the decode kernels read their weights),
+//    the data folded with xor and one word per wave stored, so no load is dead.  Timed by
+//    the caller at the byte counts of the GEMMs' weights.
 //  * mfma_loop_kernel: C independent accumulator chains of v_mfma_f32_32x32x16_f16 or
 //    v_mfma_i32_32x32x32_i8 per wave, no memory traffic in the loop; the operands come
 //    from a caller buffer (constant or random values: the sustained rate depends on the
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = buf[i + u * stride];
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&buf[i + u * stride]);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
