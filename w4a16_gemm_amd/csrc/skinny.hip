@@ -766,7 +766,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
   // 8 waves for narrow workgroups at M <= 8 (more groups in flight per column block:
   // O 5120 x 5120 at M = 1 6.4 -> 5.5 us, down 13824 x 5120 at M = 4 12.2 -> 10.1 us)
   // and for the 8-tile ones
-  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8 || narrow || (N > 16384 && M > 8))) ? 8 : 4;
+  p.waves = (p.mt == 1 && ((M <= 8 && (t <= 2 || K > 8192)) || t == 8 || narrow)) ? 8 : 4;
   p.xs = 0;
   if (!skinny_variant_compiled(p) || group_size == 64 || group_size == 32) p.waves = 4;
   if (group_size != 64 && group_size != 32) {
@@ -781,11 +781,12 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
     q.waves = env_int("W4_SKINNY_WAVES", p.waves);
     // X loaded as whole rows, ceil(M / 4) 16-byte loads per lane and group (fragments
-    // formed in LDS) instead of four fragment loads: at 8 < M <= 16 up to 16384 columns,
-    // and on narrow matrices with two or more tiles (down 13824 x 5120 at M = 1 / 4
-    // 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8 and with 7 tiles on wide
-    // matrices (gate+up at M = 4: 14.9 against 16.4 us)
-    const bool xs_dflt = (M > 8 && N <= 16384) || (narrow && q.tiles >= 2);
+    // formed in LDS) instead of four fragment loads: at 8 < M <= 16 (QKV 5120 x 15360 at
+    // M = 16 11.9 -> 11.3 us; gate+up 5120 x 27648 with 7 tiles and 4 waves 17.4 -> 16.8
+    // against 8 waves without), and on narrow matrices with two or more tiles (down
+    // 13824 x 5120 at M = 1 / 4 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8
+    // and with 7 tiles on wide matrices at M <= 8 (gate+up at M = 4: 14.9 against 16.4 us)
+    const bool xs_dflt = M > 8 || (narrow && q.tiles >= 2);
     q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
     if (skinny_variant_compiled(q)) p = q;
     // (a tile width forced by a tuning variable without a compiled variant for its m-tiles
