@@ -157,6 +157,29 @@ def test_awq_gemm_full_size_sampled(M, N, K, kw):
     assert err <= TIGHT, err
 
 
+@pytest.mark.parametrize("N", [17000, 22000, 27648, 30000])
+@pytest.mark.parametrize("M", [1, 4, 9, 16])
+def test_skinny_wide_default_plans(M, N):
+    """The default plans on wide matrices (N > 16384: 5, 6, 7 or 8 tiles per workgroup so
+    that the column blocks number at most one per CU; 4 or 8 waves; whole-row X at
+    M > 8), ragged last column blocks included, against the oracle on every column."""
+    dev = device()
+    K = 256
+    announce(f"skinny wide default M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N, outliers=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+    # (at K = 256 one output's fp16 rounding alone reaches up to 2^-11 |y| <= 2^-11 |x| |w|:
+    # the regression bar is that unit roundoff, not the K = 5120 bar)
+    assert err <= 2.0 ** -11, err
+
+
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",
                                    "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs", "2,3,8", "2,4,8",
                                    "2,6,8", "4,3,8", "4,4,4", "1,4,8", "1,8,8", "1,4,8,xs", "1,8,8,xs",
