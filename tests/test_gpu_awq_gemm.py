@@ -183,7 +183,7 @@ def test_skinny_wide_default_plans(M, N):
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",
                                    "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs", "2,3,8", "2,4,8",
                                    "2,6,8", "4,3,8", "4,4,4", "1,4,8", "1,8,8", "1,4,8,xs", "1,8,8,xs",
-                                   "2,4,8,xs", "7,2,4", "7,2,8", "7,2,4,xs", "6,2,4", "6,2,8", "5,2,4", "5,2,8",
+                                   "2,4,8,xs", "7,2,4", "7,2,8", "7,2,4,xs", "2,2,12,xs", "6,2,4", "6,2,8", "5,2,4", "5,2,8",
                                    "3,2,8", "3,2,8,xs"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (4, 1000, 2048), (7, 333, 1152), (16, 520, 1280), (17, 96, 768),
                                    (32, 300, 640)])

@@ -628,7 +628,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 3, 2, 8, 0) V(1, 3, 2, 8, 1) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
   V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
-  V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1)
+  V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1) V(1, 2, 2, 12, 1)
 static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 100 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
   const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
@@ -779,7 +779,9 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // variants (sweeps): prefetch depth, 8-wave workgroups
     SkinnyPlan q = p;
     q.depth = env_int("W4_SKINNY_RDEPTH", p.depth);
-    q.waves = env_int("W4_SKINNY_WAVES", p.waves);
+    // one row on narrow matrices: 12 waves (three per SIMD) with X as whole rows (down
+    // 13824 x 5120 10.5 -> 9.9 us, O 5120 x 5120 5.9 -> 5.8; at M = 4 no better)
+    q.waves = env_int("W4_SKINNY_WAVES", narrow && M == 1 && p.tiles == 2 && p.depth == 2 ? 12 : p.waves);
     // X loaded as whole rows, ceil(M / 4) 16-byte loads per lane and group (fragments
     // formed in LDS) instead of four fragment loads: at 8 < M <= 16 (QKV 5120 x 15360 at
     // M = 16 11.9 -> 11.3 us; gate+up 5120 x 27648 with 7 tiles and 4 waves 17.4 -> 16.8
@@ -787,7 +789,7 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // 13824 x 5120 at M = 1 / 4 11.5 -> 10.5 / 12.1 -> 10.6 us); slower on QKV at M <= 8
     // and with 7 tiles on wide matrices at M <= 8 (gate+up at M = 4: 14.9 against 16.4 us)
     const bool xs_dflt = M > 8 || (narrow && q.tiles >= 2);
-    q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
+    q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2 && q.waves <= 8) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
     if (skinny_variant_compiled(q)) p = q;
     // (a tile width forced by a tuning variable without a compiled variant for its m-tiles
     // falls back to the widest power of two below it, 4 waves)
@@ -858,8 +860,8 @@ hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const int32_t* qwei
     if constexpr (XS == 0) {                                                                                 \
       hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 0>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, qz, \
                          yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                   \
-    } else if (M > 4) { /* (the plan takes XS at M > 4 only with two-deep, multi-tile variants) */           \
-      if constexpr (T > 1 && D <= 2) {                                                                       \
+    } else if (M > 4) { /* (the plan takes XS at M > 4 only with two-deep, multi-tile variants of at most 8 waves) */ \
+      if constexpr (T > 1 && D <= 2 && W <= 8) {                                                             \
         if (M > 8)                                                                                           \
           hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 4>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, \
                              qz, yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);           \
