@@ -198,7 +198,7 @@ def test_skinny_every_tile_width(tiles, M, N, K, monkeypatch):
     if rest:
         monkeypatch.setenv("W4_SKINNY_RDEPTH", rest[0])
         monkeypatch.setenv("W4_SKINNY_WAVES", rest[1])
-    if rest[2:] == ["xs"]:  # M <= 4: one X load per group, fragments formed in LDS
+    if rest[2:] == ["xs"]:  # X loaded as whole rows (ceil(M / 4) loads per group), fragments formed in LDS
         monkeypatch.setenv("W4_SKINNY_XS", "1")
     monkeypatch.setenv("W4_SKINNY_LDS", "0")
     announce(f"skinny tiles={tiles} M={M} N={N} K={K}")

@@ -617,7 +617,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
 
 }  // namespace
 
-// Compiled register-X variants (m-tiles, n-tiles, depth, waves, one X load per group);
+// Compiled register-X variants (m-tiles, n-tiles, depth, waves, X loaded as whole rows);
 // the dequantizing kernels (group sizes 64, 32) are compiled for the default depth and
 // 4 waves only.
 #define SKINNY_VARIANTS(V)                                                                                   \
