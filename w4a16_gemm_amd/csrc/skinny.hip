@@ -16,9 +16,9 @@
 // x (c_k + q) products are exact in fp32, only the fp32 sums round.
 //
 // Work split (register-X kernel, M <= 32; the kernel further below stages X in LDS and
-// is kept behind a tuning variable): a workgroup (4 or 8 waves) owns 16 T output columns
-// n (T = 1 .. 8 tiles of 16) and a contiguous range of K groups (split-K across workgroups only for narrow
-// N); its waves take the groups of that range round robin.  Per group, lane l of a wave
+// is kept behind a tuning variable): a workgroup (4, 8 or 12 waves) owns 16 T output
+// columns n (T = 1 .. 8 tiles of 16) and a contiguous range of K groups (split-K across
+// workgroups only for narrow N); its waves take the groups of that range round robin.  Per group, lane l of a wave
 // loads one 16-byte chunk (32 codes) of row n0 + 16t + (l % 16) for each tile t -- with
 // the tiled weight layout the 64 lanes read one contiguous 1 KB block -- the 64 bytes of
 // X it needs, and one scale and one zero-point word per 64 columns; the four MFMAs of a
@@ -82,9 +82,9 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     }
   }
   if (XS) {
-    // M <= 4 XS: XS loads bring the group's X for all rows -- load i of lane l takes
-    // 16-byte chunk l % 16 of row 4 i + l / 16 (rows past M clamped; each load reads four
-    // whole 256-byte rows); compute_group forms the fragments in LDS
+    // M <= 4 XS: XS loads bring the group's X, all rows -- load i of lane l takes 16-byte
+    // chunk l % 16 of row 4 i + l / 16 (rows past M clamped; each load reads four whole
+    // 256-byte rows); compute_group forms the fragments in LDS
 #pragma unroll
     for (int i = 0; i < XS; ++i)
       r.a[0][i] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(4 * i + (lane >> 4), M - 1) * K + g * 128 +
