@@ -180,6 +180,29 @@ def test_skinny_wide_default_plans(M, N):
     assert err <= 2.0 ** -11, err
 
 
+@pytest.mark.parametrize("M,N,K", [(21, 1280, 1024), (27, 1280, 1024), (32, 1280, 1024), (24, 9000, 1024),
+                                   (27, 9000, 1024), (31, 9000, 1024), (27, 640, 9216), (29, 640, 9216)])
+def test_skinny_two_mtile_default_plans(M, N, K):
+    """The default plans at 16 < M <= 32 (two m-tiles per workgroup) on both sides of the
+    row count above which X is loaded as whole rows (eight loads per lane and group, rows
+    past M repeat the last one): above 20 rows on narrow matrices, above 26 on wide ones,
+    above 28 on long K (where M = 27 also splits K and M = 29 does not), against the oracle
+    on every output."""
+    dev = device()
+    announce(f"skinny two m-tile default M={M} N={N} K={K}")
+    inp = synth.make_linear(M, N, K, seed=M + N + K, outliers=True)
+    ref, (qw, sc, qz) = _oracle_packed(inp.w.numpy(), dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y = to_np(w4.awq_gemm(inp.x.to(dev), qw, sc, qz, out=out)).astype(np.float64)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    yr = ora.linear_ref(inp.x.numpy(), ref["w_deq"])
+    err = normalized_error(y, yr, np.linalg.norm(inp.x.numpy().astype(np.float64), axis=1),
+                           np.linalg.norm(ref["w_deq"], axis=1))
+    assert err <= TOL, err
+    # (short K: the regression bar is the fp16 output's unit roundoff, as on wide matrices)
+    assert err <= 2.0 ** -11, err
+
+
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "8", "4,3,4", "2,4,4", "1,8,4", "4,2,8", "2,2,8", "8,2,8",
                                    "4,2,4,xs", "2,2,4,xs", "1,4,4,xs", "2,2,8,xs", "4,2,8,xs", "2,3,8", "2,4,8",
                                    "2,6,8", "4,3,8", "4,4,4", "1,4,8", "1,8,8", "1,4,8,xs", "1,8,8,xs",

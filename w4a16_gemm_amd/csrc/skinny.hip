@@ -87,8 +87,8 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
     // 256-byte rows); compute_group forms the fragments in LDS
 #pragma unroll
     for (int i = 0; i < XS; ++i)
-      r.a[0][i] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(4 * i + (lane >> 4), M - 1) * K + g * 128 +
-                                                    (lane & 15) * 8);
+      r.a[i >> 2][i & 3] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(4 * i + (lane >> 4), M - 1) * K +
+                                                             g * 128 + (lane & 15) * 8);
     return;
   }
 #pragma unroll
@@ -131,12 +131,16 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
 #pragma unroll
     for (int i = 0; i < XS; ++i) {
       const int row = 4 * i + q;
-      *reinterpret_cast<half8_t*>(xb + row * 128 + (c ^ row) * 8) = r.a[0][i];
+      *reinterpret_cast<half8_t*>(xb + row * 128 + (c ^ (row & 15)) * 8) = r.a[i >> 2][i & 3];
     }
-    const int rr = lane & (4 * XS - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      a[0][j] = *reinterpret_cast<const half8_t*>(xb + rr * 128 + ((4 * q + j) ^ rr) * 8);
+    for (int mt = 0; mt < MT; ++mt) {
+      // (two m-tiles, XS = 8: rows 16 mt + l % 16)
+      const int rr = MT == 1 ? lane & (4 * XS - 1) : 16 * mt + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[mt][j] = *reinterpret_cast<const half8_t*>(xb + rr * 128 + ((4 * q + j) ^ (rr & 15)) * 8);
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -628,7 +632,7 @@ __global__ __launch_bounds__(512) void skinny_lds_kernel(const half_t* __restric
   V(1, 3, 2, 8, 0) V(1, 3, 2, 8, 1) V(1, 4, 2, 4, 1) V(1, 2, 2, 4, 1) V(1, 1, 4, 4, 1) V(1, 2, 2, 8, 1)          \
   V(1, 4, 2, 8, 1) V(1, 2, 3, 8, 0) V(1, 2, 4, 8, 0) V(1, 2, 6, 8, 0)          \
   V(1, 4, 3, 8, 0) V(1, 4, 4, 4, 0) V(1, 1, 4, 8, 0) V(1, 1, 8, 8, 0) V(1, 1, 4, 8, 1)   \
-  V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1) V(1, 2, 2, 12, 1)
+  V(1, 1, 8, 8, 1) V(1, 2, 4, 8, 1) V(1, 2, 2, 12, 1) V(2, 2, 2, 4, 1) V(2, 4, 2, 4, 1)
 static int variant_key(int mt, int t, int d, int w, int xs) { return (((mt * 10 + t) * 10 + d) * 100 + w) * 2 + xs; }
 static bool skinny_variant_compiled(const SkinnyPlan& p) {
   const int key = variant_key(p.mt, p.tiles, p.depth, p.waves, p.xs);
@@ -790,6 +794,12 @@ SkinnyPlan skinny_plan(int M, int N, int K, int group_size) {
     // and with 7 tiles on wide matrices at M <= 8 (gate+up at M = 4: 14.9 against 16.4 us)
     const bool xs_dflt = M > 8 || (narrow && q.tiles >= 2);
     q.xs = p.mt == 1 && ((q.tiles > 1 && q.depth <= 2 && q.waves <= 8) || M <= 4) ? env_int("W4_SKINNY_XS", xs_dflt) : 0;
+    // (two m-tiles: all 32 rows in eight loads per lane and group, whatever M, so it pays
+    // only near 32 rows: at M = 32 O 5120 x 5120 14.5 -> 11.6 us, QKV 5120 x 15360 16.9 ->
+    // 15.7, down 13824 x 5120 21.1 -> 20.4; it pays from M = 21 on O, 27 on QKV, 29 on down,
+    // and is slower below)
+    if (p.mt == 2 && q.tiles > 1 && q.depth <= 2 && q.waves <= 8)
+      q.xs = env_int("W4_SKINNY_XS", M > (K > 8192 ? 28 : N <= 8192 ? 20 : 26));
     if (skinny_variant_compiled(q)) p = q;
     // (a tile width forced by a tuning variable without a compiled variant for its m-tiles
     // falls back to the widest power of two below it, 4 waves)
@@ -860,6 +870,12 @@ hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const int32_t* qwei
     if constexpr (XS == 0) {                                                                                 \
       hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 0>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, qz, \
                          yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                   \
+    } else if constexpr (MT == 2) { /* two m-tiles: the 32 rows in 8 loads */                              \
+      if constexpr (T > 1 && D <= 2 && W <= 8)                                                               \
+        hipLaunchKernelGGL((skinny_kernel<MT, T, D, W, false, 8>), grid, dim3(W * kWave), 0, stream, xh, qw, sc, qz, \
+                           yh, counters, partials, M, N, K, p.splits, p.gps, p.drain, glog);                 \
+      else                                                                                                   \
+        return hipErrorInvalidValue;                                                                         \
     } else if (M > 4) { /* (the plan takes XS at M > 4 only with two-deep, multi-tile variants of at most 8 waves) */ \
       if constexpr (T > 1 && D <= 2 && W <= 8) {                                                             \
         if (M > 8)                                                                                           \
