@@ -149,20 +149,26 @@ __device__ __forceinline__ void unpack_i4x16(uint32_t w, uint32_t& lo, uint32_t&
 // guaranteed by the weight rule), natural order, as two words (elements 0..3, 4..7).
 // The products are formed in 16-bit lanes: (b * s + (-8 s)) mod 2^16 is q * s as int16,
 // whose low byte is the int8 value; the nibble pairs (0, 4), (1, 5), (2, 6), (3, 7) of
-// the word hold elements (0, 2), (4, 6), (1, 3), (5, 7), so one v_perm_b32 gathers the
-// low bytes of each half.  sp = (s, s), cp = (-8 s, -8 s) as u16 pairs.
+// the word hold elements (0, 2), (4, 6), (1, 3), (5, 7).  Pairs (2, 6) and (3, 7) are
+// masked in place at bits 8..11 of each half (256 b): (256 b s + 256 (-8 s)) mod 2^16 is
+// 256 ((q s) mod 256), so their products land in the high byte of each 16-bit lane with
+// no shift.  One v_perm_b32 per half then gathers the low bytes of one product word and
+// the high bytes of the other (11 VALU operations per word).  sp = (s, s),
+// cp = (-8 s, -8 s) as u16 pairs.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void unpack_i4_scaled(uint32_t w, u16x2 sp, u16x2 cp, uint32_t& lo, uint32_t& hi) {
-  const u16x2 e0 = __builtin_bit_cast(u16x2, w & 0x000f000fu);          // b0, b2
-  const u16x2 e1 = __builtin_bit_cast(u16x2, (w >> 4) & 0x000f000fu);   // b4, b6
-  const u16x2 e2 = __builtin_bit_cast(u16x2, (w >> 8) & 0x000f000fu);   // b1, b3
-  const u16x2 e3 = __builtin_bit_cast(u16x2, (w >> 12) & 0x000f000fu);  // b5, b7
+  const uint32_t ws = w >> 4;
+  const u16x2 cp8 = cp << (unsigned short)8;                       // 256 (-8 s) mod 2^16
+  const u16x2 e0 = __builtin_bit_cast(u16x2, w & 0x000f000fu);     // b0, b2
+  const u16x2 e1 = __builtin_bit_cast(u16x2, ws & 0x000f000fu);    // b4, b6
+  const u16x2 e2 = __builtin_bit_cast(u16x2, w & 0x0f000f00u);     // 256 b1, 256 b3
+  const u16x2 e3 = __builtin_bit_cast(u16x2, ws & 0x0f000f00u);    // 256 b5, 256 b7
   const uint32_t r0 = __builtin_bit_cast(uint32_t, (u16x2)(e0 * sp + cp));
   const uint32_t r1 = __builtin_bit_cast(uint32_t, (u16x2)(e1 * sp + cp));
-  const uint32_t r2 = __builtin_bit_cast(uint32_t, (u16x2)(e2 * sp + cp));
-  const uint32_t r3 = __builtin_bit_cast(uint32_t, (u16x2)(e3 * sp + cp));
-  lo = __builtin_amdgcn_perm(r2, r0, 0x06020400u);  // p0 p1 p2 p3
-  hi = __builtin_amdgcn_perm(r3, r1, 0x06020400u);  // p4 p5 p6 p7
+  const uint32_t r2 = __builtin_bit_cast(uint32_t, (u16x2)(e2 * sp + cp8));
+  const uint32_t r3 = __builtin_bit_cast(uint32_t, (u16x2)(e3 * sp + cp8));
+  lo = __builtin_amdgcn_perm(r2, r0, 0x07020500u);  // p0 p1 p2 p3
+  hi = __builtin_amdgcn_perm(r3, r1, 0x07020500u);  // p4 p5 p6 p7
 }
 
 // ------------------------------------------------------------ reductions
