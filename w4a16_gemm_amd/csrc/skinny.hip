@@ -83,8 +83,8 @@ __device__ __forceinline__ void load_group(GroupRegs<MT, T>& r, const half_t* __
   }
   if (XS) {
     // M <= 4 XS: XS loads bring the group's X, all rows -- load i of lane l takes 16-byte
-    // chunk l % 16 of row 4 i + l / 16 (rows past M clamped; each load reads four whole
-    // 256-byte rows); compute_group forms the fragments in LDS
+    // chunk l % 16 of row 4 i + l / 16 into a[i / 4][i % 4] (rows past M clamped; each
+    // load reads four whole 256-byte rows); compute_group forms the fragments in LDS
 #pragma unroll
     for (int i = 0; i < XS; ++i)
       r.a[i >> 2][i & 3] = *reinterpret_cast<const half8_t*>(x + (int64_t)min(4 * i + (lane >> 4), M - 1) * K +
@@ -122,11 +122,12 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
   float4_t ssum[MT], negp[MT];
   if (XS) {
     // The group's 4 XS rows x 256 bytes through this wave's XS KB of LDS: chunk c of row
-    // q at chunk c ^ q (the rows of one fragment read, and the chunks of one row written,
-    // fall in distinct banks).  Fragment j of lane l is chunk 4 (l / 16) + j of row
-    // (l % 16) mod 4 XS (MFMA rows past 4 XS only reach outputs that are never stored:
-    // M <= 4 XS).  LDS operations of one wave execute in order, so the reads see the
-    // whole wave's writes.
+    // q at chunk c ^ (q mod 16) (the rows of one fragment read, and the chunks of one row
+    // written, fall in distinct banks).  Fragment j of lane l in m-tile mt is chunk
+    // 4 (l / 16) + j of row (l % 16) mod 4 XS with one m-tile (MFMA rows past 4 XS only
+    // reach outputs that are never stored: M <= 4 XS), of row 16 mt + l % 16 with two
+    // (XS = 8).  LDS operations of one wave execute in order, so the reads see the whole
+    // wave's writes.
     const int q = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int i = 0; i < XS; ++i) {
@@ -135,7 +136,6 @@ __device__ __forceinline__ void compute_group(const GroupRegs<MT, T>& r, float4_
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      // (two m-tiles, XS = 8: rows 16 mt + l % 16)
       const int rr = MT == 1 ? lane & (4 * XS - 1) : 16 * mt + (lane & 15);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
