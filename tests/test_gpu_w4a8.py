@@ -266,6 +266,36 @@ def test_w4a8_full_size_sampled(group, M):
 
 
 @pytest.mark.parametrize("group", [-1, 128])
+def test_w4a8_down_shape_default_tail(group):
+    """The down projection at prefill (M = 4096, K = 13824, N = 5120): 640 128 x 256 tiles
+    on 512 resident workgroups, so the default plan splits the 128 tiles of the last round
+    over their groups; int32 accumulators bit-exact on sampled outputs that include rows
+    and columns of those tiles (the last row block group: rows 3072.., columns 1024..)."""
+    dev = device()
+    M, N, K = 4096, 5120, 13824
+    assert w4.w4a8_gemm_workspace_bytes(M, N, K, group) == 16384 + 128 * 2 * 128 * 256 * 4
+    announce(f"w4a8 down shape default tail M={M} group={group}")
+    inp = synth.make_linear(M, N, K, seed=3, outliers=True, rms_spread=True, with_gamma=True)
+    qw, gs, cs = w4.w4a8_pack(inp.w.to(dev), group)
+    rxq, rsa, _ = ora.w4a8_quant_act_ref(inp.x.numpy(), inp.gamma.numpy())
+    xqd, sad = torch.from_numpy(rxq).to(dev), torch.from_numpy(rsa).to(dev)
+    acc = w4.w4a8_gemm_i32(xqd, qw, gs, group, N=N)
+    y = w4.w4a8_gemm(xqd, sad, qw, gs, cs, group)
+    torch.cuda.synchronize()
+    ms = sample_idx(M, 48, seed=11, must=list(range(0, 8)) + list(range(4088, 4096)))
+    ns = sample_idx(N, 256, seed=12, must=list(range(0, 16)) + list(range(5104, 5120)))
+    q, rcs, rgs = ora.quantize_w4a8(inp.w.numpy()[ns], group)
+    racc = ora.w4a8_acc_ref(rxq[ms], q, rgs, 128)
+    assert np.array_equal(to_np(acc)[np.ix_(ms, ns)].astype(np.int64), racc)
+    yr = ora.w4a8_linear_ref(racc, rsa[ms], rcs)
+    qs = q.astype(np.float64) * (1 if rgs is None else np.repeat(rgs.astype(np.float64), 128, axis=1))
+    wn = np.linalg.norm(qs, axis=1) * rcs.astype(np.float64)
+    xn = np.linalg.norm(rxq[ms].astype(np.float64), axis=1) * rsa[ms].astype(np.float64)
+    err = normalized_error(to_np(y)[np.ix_(ms, ns)].astype(np.float64), yr, xn, wn)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("group", [-1, 128])
 @pytest.mark.parametrize("tiles", ["1", "2", "4", "off"])
 @pytest.mark.parametrize("M,N,K", [(1, 200, 1024), (7, 1000, 2048), (16, 130, 13824), (3, 64, 128)])
 def test_w4a8_skinny_variants(group, tiles, M, N, K, monkeypatch):

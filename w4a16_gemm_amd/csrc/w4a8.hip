@@ -1017,17 +1017,22 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   if (tiles >= kMaxCounters) splits = 1;
   p.kt_per_split = (ng + splits - 1) / splits;
   p.splits = (ng + p.kt_per_split - 1) / p.kt_per_split;
-  // Tail split (128-row tiles, two resident per CU: 512 slots on 256 CUs): a last round
-  // under half full split in two over its groups.  Off by default: at M = 4096,
-  // N = 13824 (1728 tiles = 3 rounds + 192) it measured 431 -> 464 us (per-channel),
-  // 490 -> 533 (two-level), 448 -> 440 (W8A8) with the register pipeline, and still
-  // 270 -> 301, 326 -> 356, 376 -> 373 with the direct-to-LDS rings, unlike the fp16 GEMM.
+  // Tail split (128-row tiles, two resident per CU: 512 slots on 256 CUs): the last
+  // round's tiles split in two over their groups.  Taken by default only when that round
+  // holds at most a quarter of the slots and K is long (at least 64 groups), where the
+  // uneven round costs more than the int32 partials: M = 4096 on 13824 x 5120 (640 tiles,
+  // 128 in the last round) per-channel / two-level / W8A8 250.6 / 315.6 / 396.9 ->
+  // 234.9 / 292.2 / 356.1 us, K = 8192 165.7 -> 161.0; slower with 192 or 208 tiles in
+  // the last round (M = 4096 on 5120 x 13824 253.1 -> 279.6, M = 4608 on 13824 x 5120
+  // 257.9 -> 273.5), no faster at K = 5120, and four parts slower than two.
+  // W4_W4A8_TAIL = 1 takes it whenever the last round is at most half full, 0 never.
   p.n_full = 0;
   p.tail_splits = 0;
   const int slots = 512 * env_int("W4_W4A8_SLOTS_SCALE", 1) / env_int("W4_W4A8_SLOTS_DIV", 1);
   const int rem = tiles % slots;
-  if (p.bm == 128 && p.splits == 1 && env_int("W4_W4A8_TAIL", 0) && tiles > slots && rem > 0 && 2 * rem <= slots &&
-      ng >= 8) {
+  const int tail_env = env_int("W4_W4A8_TAIL", -1);
+  const bool tail_ok = tail_env < 0 ? (4 * rem <= slots && ng >= 64) : (tail_env > 0 && 2 * rem <= slots);
+  if (p.bm == 128 && p.splits == 1 && tail_ok && tiles > slots && rem > 0 && ng >= 8) {
     p.n_full = tiles - rem;
     p.tail_splits = max(2, min(8, env_int("W4_W4A8_TAIL_PARTS", 2)));
   }
