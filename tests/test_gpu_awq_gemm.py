@@ -308,6 +308,24 @@ def test_gemm_prefetch_depths(depth, M, N, K, splits, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("M,N,K,div,split", [
+    (640, 1000, 2048, 32, True),    # 20 tiles on 16 slots: 4 in the last round, a quarter
+    (1400, 500, 2048, 32, False),   # 22 tiles on 16 slots: 6 in the last round
+    (1100, 300, 4096, 64, True),    # 18 tiles on 8 slots: 2 in the last round
+    (1500, 300, 4096, 64, False),   # 24 tiles on 8 slots: none left over
+])
+def test_gemm_tail_split_default_rule(M, N, K, div, split, monkeypatch):
+    """The plan's own choice (no forcing variable): the last round's tiles are split in two
+    only when it holds at most a quarter of the slots; seen through the workspace size."""
+    monkeypatch.setenv("W4_GEMM_SHAPE", "1")
+    monkeypatch.setenv("W4_GEMM_MIN_TILES", "2")
+    monkeypatch.setenv("W4_GEMM_SLOTS_DIV", str(div))
+    tiles = -(-M // 128) * -(-N // 256)
+    rem = tiles % (512 // div)
+    want = 16384 + rem * 2 * 128 * 256 * 4 if split else 0
+    assert w4.awq_gemm_workspace_bytes(M, N, K) == want
+
+
 @pytest.mark.parametrize("M,N,K,scale,div,expect", [
     (640, 1000, 2048, 1, 32, 2),   # 20 tiles on 16 slots: the last 4 tiles split in two
     (600, 520, 2048, 3, 128, 4),   # 15 tiles on 12 slots: the last 3 split 4 ways (forced); ragged M, N
@@ -323,6 +341,7 @@ def test_gemm_tail_split(M, N, K, scale, div, expect, depth, monkeypatch):
     dev = device()
     monkeypatch.setenv("W4_GEMM_SHAPE", "1")
     monkeypatch.setenv("W4_GEMM_MIN_TILES", "2")
+    monkeypatch.setenv("W4_GEMM_TAIL", "1")  # whenever the last round is at most half full
     monkeypatch.setenv("W4_GEMM_SLOTS_SCALE", str(scale))
     monkeypatch.setenv("W4_GEMM_SLOTS_DIV", str(div))
     monkeypatch.setenv("W4_GEMM_TAIL_PARTS", str(expect))

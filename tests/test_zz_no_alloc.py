@@ -36,8 +36,11 @@ def test_noalloc_matches_awq_gemm_on_consecutive_calls():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
-def test_noalloc_refuses_workspace_above_the_static_array():
+def test_noalloc_refuses_workspace_above_the_static_array(monkeypatch):
     dev = device()
+    # 768 tiles on 512 slots: the last 256 split in two (forced; the default plan splits a
+    # last round only up to a quarter of the slots) need 64 MiB + 16 KiB of partials
+    monkeypatch.setenv("W4_GEMM_TAIL", "1")
     M, N, K = 4096, 6144, 5120
     announce(f"awq_gemm_noalloc refusal M={M} N={N} K={K}")
     assert w4.load().awq_gemm_workspace_bytes(M, N, K, 128) > SCRATCH

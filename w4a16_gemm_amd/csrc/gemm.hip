@@ -654,9 +654,14 @@ GemmPlan gemm_plan(int M, int N, int K) {
   p.tail_splits = 0;
   const int slots = kCUs * kResidentPerCU[pick] * env_int("W4_GEMM_SLOTS_SCALE", 1) /
                     env_int("W4_GEMM_SLOTS_DIV", 1);
+  // Taken when the last round holds at most a quarter of the slots: with 192 or 208 of
+  // 512 it was slower (M = 4096 on 5120 x 13824 524.3 -> 547.8 us, M = 4608 on
+  // 13824 x 5120 586.3 -> 605.9), with 128 faster (O above; K = 8192 335.8 -> 321.4).
+  // W4_GEMM_TAIL = 1 takes it whenever the last round is at most half full, 0 never.
   const int rem = tiles % slots;
-  if (p.splits == 1 && !mid && env_int("W4_GEMM_TAIL", 1) && tiles > slots && rem > 0 && 2 * rem <= slots &&
-      ktiles >= 16) {
+  const int tail_env = env_int("W4_GEMM_TAIL", -1);
+  const bool tail_ok = tail_env < 0 ? 4 * rem <= slots : (tail_env > 0 && 2 * rem <= slots);
+  if (p.splits == 1 && !mid && tail_ok && tiles > slots && rem > 0 && ktiles >= 16) {
     const int ts = max(2, min(8, env_int("W4_GEMM_TAIL_PARTS", 2)));
     p.n_full = tiles - rem;
     p.tail_splits = ts;
