@@ -997,7 +997,14 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // two-level 382.2 -> 328.6), int8 weights one group ahead.
   p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
-  const int dflt = p.bm == 32 ? 4 : p.bm == 64 ? 0 : (group_size != 0 ? 5 : 1);
+  // int8 weights on 128-row tiles: the four-tile ring at one workgroup per CU (depth 0)
+  // beats the one-ahead loop at two per CU on narrow matrices (N <= 8192) with more tiles
+  // than one round of two per CU (M = 4096: 5120 x 5120 172.2 -> 163.8 us, K = 8192
+  // 226.7 -> 216.9, K = 13824 341.8 -> 319.8; M = 8192 625.0 -> 610.9), not with fewer
+  // (M = 2048, 320 tiles: 217.7 -> 231.1) or on N = 13824 (even at K = 13824, slower at
+  // K = 5120: 366.1 -> 406.5)
+  const bool i8_ring = group_size == 0 && N <= 8192 && (int64_t)((M + 127) / 128) * ((N + 255) / 256) > 512;
+  const int dflt = p.bm == 32 ? 4 : p.bm == 64 ? 0 : (group_size != 0 ? 5 : (i8_ring ? 0 : 1));
   p.depth = env_int("W4_W4A8_DEPTH", dflt);
   // depth 0: the direct-to-LDS pipeline (64- and 128-row tiles; 32-bit xq offsets)
   if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4)) ||
