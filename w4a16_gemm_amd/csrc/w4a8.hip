@@ -114,7 +114,7 @@ __global__ __launch_bounds__(T) void quant_act_kernel(const half_t* __restrict__
     if constexpr (R > 0) {
       half8_t xv[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) xv[r] = xr[min((int)threadIdx.x + r * T, nv - 1)];
+      for (int r = 0; r < R; ++r) xv[r] = __builtin_nontemporal_load(xr + min((int)threadIdx.x + r * T, nv - 1));
       float y[R][8];
       if (gamma) {
         half8_t gv[R];
@@ -257,8 +257,9 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int j = min((int)threadIdx.x + r * T, nv - 1);
-        gv[r] = g8[j];
-        uv[r] = u8[j];
+        // (non-temporal: every input byte is read once; 4096 x 13824 51.1 -> 49.9 us)
+        gv[r] = __builtin_nontemporal_load(g8 + j);
+        uv[r] = __builtin_nontemporal_load(u8 + j);
       }
       float y[R][8];
 #pragma unroll
