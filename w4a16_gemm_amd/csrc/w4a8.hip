@@ -310,7 +310,7 @@ __global__ __launch_bounds__(T) void silu_mul_quant_kernel(const half_t* __restr
 // weights enter as q * s_g, expanded per group in registers (|q s_g| <= 126 fits int8),
 // so both variants accumulate the exact integer sum in one int32 accumulator set.
 constexpr int WBN = 256, WBK = 128;
-constexpr int kGroupM8 = 8;  // row tiles per group in the large-M tile order
+constexpr int kRowTilesPerGroup = 4;  // row tiles per group in the large-M tile order
 // Weight formats of the int8 MFMA kernels: int4 per-channel (entering as 16 q), int4
 // two-level (entering as q s_g), and plain row-major int8 [N, K] (W8A8).
 constexpr int kI4PerChannel = 0, kI4TwoLevel = 1, kI8 = 2;
@@ -363,15 +363,17 @@ __global__ __launch_bounds__(kWThreads, (PD == 1 || PD == 5) ? 2 : 1) void w4a8_
     nsplit = tail_splits;
     gpl = (ng + tail_splits - 1) / tail_splits;
   }
-  // grouped ordering: walk kGroupM8 row tiles for each column tile, so the tiles one XCD
-  // runs at a time (consecutive ids after xcd_remap: 64 at two workgroups per CU) cover
-  // 8 x 8 tiles and share 8 row blocks of xq and 8 column blocks of weights in its L2,
+  // grouped ordering: walk kRowTilesPerGroup row tiles for each column tile, so the
+  // tiles one XCD runs at a time (consecutive ids after xcd_remap: 64 at two workgroups
+  // per CU) cover 4 row blocks of xq and 16 column blocks of weights that its L2 shares,
   // instead of every row block against two column blocks (M = 4096, K = 5120,
-  // N = 13824: 1161 MB fetched per call with the plain column-major order)
-  const int per_group = kGroupM8 * tiles_n;
+  // N = 13824: 1161 MB fetched per call with the plain column-major order, ~430 MB
+  // grouped; groups of 4 against 8: equal at M = 4096, M = 384 / 8192 44.8 -> 43.4 /
+  // 496.6 -> 482.2 us; 16 slower)
+  const int per_group = kRowTilesPerGroup * tiles_n;
   const int grp = tile / per_group;
-  const int first_m = grp * kGroupM8;
-  const int gsize = min(tiles_m - first_m, kGroupM8);
+  const int first_m = grp * kRowTilesPerGroup;
+  const int gsize = min(tiles_m - first_m, kRowTilesPerGroup);
   const int in_grp = tile % per_group;
   // (wave-uniform: kept in scalar registers)
   const int m0 = __builtin_amdgcn_readfirstlane((first_m + in_grp % gsize) * BM);
