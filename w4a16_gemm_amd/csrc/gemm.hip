@@ -621,8 +621,14 @@ GemmPlan gemm_plan(int M, int N, int K) {
   //    for 128-row tiles: the 128 x 128 tiles at 256 < M <= 512 (M = 384 / 512 70.9 /
   //    79.6 us; 95.2 us at M = 512 with register-staged X, 3-4 sets ahead); at
   //    128 < M <= 256 those tiles take depth 7 (M = 256 48.8 us).
+  //  * on narrow matrices (N < 8192) the 64 x 128 tiles at mid M take depth 0 instead of
+  //    8: one workgroup per CU with X four steps ahead (K = 5120, N = 5120 at
+  //    M = 48 / 96 / 128 / 256: 17.0 / 21.5 / 21.6 / 28.4 -> 16.7 / 20.6 / 20.5 / 26.0 us;
+  //    K = 13824 at M = 64 / 128 / 256: 27.3 / 41.3 / 68.3 -> 26.4 / 38.7 / 62.8; no gain
+  //    at N = 8192).
   // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
-  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? 8 : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
+  p.depth = env_int("W4_GEMM_DEPTH",
+                    mid ? (pick == 3 ? (N < 8192 ? 0 : 8) : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipelines address X, the codes, scales and zero points with 32-bit
   // per-lane offsets
