@@ -589,7 +589,9 @@ GemmPlan gemm_plan(int M, int N, int K) {
     // M = 64 30.2 -> 26.9 us, M = 128 45.2 -> 37.5 against the one-step-ahead 128 x 128 /
     // 64 x 128 plans); 128 x 128 above on wide matrices (M = 256: 52.1 -> 48.8 us, whole
     // K per workgroup) and from M = 384 on
-    pick = ((M > 128 && N >= 8192) || M >= 384) ? 1 : 3;
+    // (narrow matrices, N < 8192, keep the 64 x 128 tiles up to M = 512: M = 512, K = 5120,
+    // N = 5120 52.7 -> 43.6 us against 128 x 128 tiles)
+    pick = (M > 128 && N >= 8192) ? 1 : 3;
   } else {
     for (int i = 0; i < 4; ++i) {
       const int tm = (M + 32 * kShapes[i][0] - 1) / (32 * kShapes[i][0]);
@@ -599,6 +601,10 @@ GemmPlan gemm_plan(int M, int N, int K) {
         break;
       }
     }
+    // narrow matrices up to M = 1024: 64 x 128 tiles with the X ring at one workgroup per
+    // CU (K = 5120, N = 5120 at M = 768 / 1024: 63.3 / 73.0 -> 51.1 / 70.4 us; K = 13824 at
+    // M = 1024 181.9 -> 179.2; at M = 2048 the 128 x 256 tiles stay faster)
+    if (N < 8192 && M <= 1024) pick = 3;
   }
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
@@ -627,8 +633,8 @@ GemmPlan gemm_plan(int M, int N, int K) {
   //    K = 13824 at M = 64 / 128 / 256: 27.3 / 41.3 / 68.3 -> 26.4 / 38.7 / 62.8; no gain
   //    at N = 8192).
   // Depths 1, 3, 4, 6 (register sets in flight) stay compiled for sweeps and other shapes.
-  p.depth = env_int("W4_GEMM_DEPTH",
-                    mid ? (pick == 3 ? (N < 8192 ? 0 : 8) : (M <= 256 ? 7 : 0)) : (pick <= 1 ? 7 : 1));
+  p.depth = env_int("W4_GEMM_DEPTH", mid ? (pick == 3 ? (N < 8192 ? 0 : 8) : (M <= 256 ? 7 : 0))
+                                         : (pick <= 1 ? 7 : (pick == 3 && N < 8192 && M <= 1024 ? 0 : 1)));
   if (!gemm_variant_compiled(p.mi, p.nf, p.depth)) p.depth = 1;
   // the direct-to-LDS pipelines address X, the codes, scales and zero points with 32-bit
   // per-lane offsets
