@@ -998,7 +998,12 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // -> 46.1 / 62.0 / 61.4); 128-row tiles above 512, int4 weights with the three-tile
   // ring at two workgroups per CU (depth 5, M = 4096: per-channel 321.9 -> 270.5 us,
   // two-level 382.2 -> 328.6), int8 weights one group ahead.
-  p.bm = env_int("W4_W4A8_BM", M <= 128 ? 32 : (M <= 512 ? 64 : 128));
+  // (narrow, short-K matrices keep the 32-row tiles up to M = 384: K = 5120, N = 5120
+  // per-channel at M = 192 / 256 / 384 26.6 / 25.8 / 26.0 -> 18.3 / 19.9 / 20.1 us, W8A8 at
+  // M = 256 28.2 -> 23.2, N = 8192 at M = 256 27.7 -> 21.4; slower at M = 512, at
+  // K = 13824 and on N = 13824)
+  const bool short_narrow = N <= 8192 && K <= 8192 && M <= 384;
+  p.bm = env_int("W4_W4A8_BM", (M <= 128 || short_narrow) ? 32 : (M <= 512 ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
   // int8 weights on 128-row tiles: the four-tile ring at one workgroup per CU (depth 0)
   // beats the one-ahead loop at two per CU on narrow matrices (N <= 8192) with more tiles
