@@ -1003,13 +1003,14 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // M = 256 28.2 -> 23.2, N = 8192 at M = 256 27.7 -> 21.4; slower at M = 512, at
   // K = 13824 and on N = 13824)
   const bool short_narrow = N <= 8192 && K <= 8192 && M <= 384;
-  // (int4 weights at 512 < M <= 768: 64-row tiles, on the three-slot ring at two
-  // workgroups per CU for wide matrices and the four-slot ring at one for narrow ones --
+  // (512 < M <= 768: 64-row tiles, for int4 weights on the three-slot ring at two
+  // workgroups per CU on wide matrices, otherwise the four-slot ring at one --
   // per-channel on 5120 x 13824 at M = 640 / 768 72.0 / 73.7 -> 58.5 / 60.6 us (two-level
-  // 85.7 -> 84.2), on 5120 x 5120 at M = 768 48.8 -> 27.3; 128-row tiles stay faster at
-  // M = 1024)
-  const bool mid_i4 = group_size != 0 && M > 512 && M <= 768;
-  p.bm = env_int("W4_W4A8_BM", (M <= 128 || short_narrow) ? 32 : ((M <= 512 || mid_i4) ? 64 : 128));
+  // 85.7 -> 84.2), on 5120 x 5120 at M = 768 48.8 -> 27.3; W8A8 96.6 / 98.3 -> 82.1 /
+  // 84.8, 62.4 -> 33.1, 13824 x 5120 at M = 600 105.8 -> 77.7; 128-row tiles stay faster
+  // at M = 1024)
+  const bool mid_rows = M > 512 && M <= 768;
+  p.bm = env_int("W4_W4A8_BM", (M <= 128 || short_narrow) ? 32 : ((M <= 512 || mid_rows) ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
   // int8 weights on 128-row tiles: the four-tile ring at one workgroup per CU (depth 0)
   // beats the one-ahead loop at two per CU on narrow matrices (N <= 8192) with more tiles
@@ -1019,7 +1020,7 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // K = 5120: 366.1 -> 406.5)
   const bool i8_ring = group_size == 0 && N <= 8192 && (int64_t)((M + 127) / 128) * ((N + 255) / 256) > 512;
   const int dflt =
-      p.bm == 32 ? 4 : p.bm == 64 ? (mid_i4 && N > 8192 ? 5 : 0) : (group_size != 0 ? 5 : (i8_ring ? 0 : 1));
+      p.bm == 32 ? 4 : p.bm == 64 ? (mid_rows && group_size != 0 && N > 8192 ? 5 : 0) : (group_size != 0 ? 5 : (i8_ring ? 0 : 1));
   p.depth = env_int("W4_W4A8_DEPTH", dflt);
   // depth 0: the direct-to-LDS pipeline (64- and 128-row tiles; 32-bit xq offsets)
   if (!((p.depth == 1) || (p.bm == 32 && p.depth == 4) || (p.bm == 64 && (p.depth == 3 || p.depth == 4)) ||
