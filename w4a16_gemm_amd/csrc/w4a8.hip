@@ -1008,8 +1008,13 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // per-channel on 5120 x 13824 at M = 640 / 768 72.0 / 73.7 -> 58.5 / 60.6 us (two-level
   // 85.7 -> 84.2), on 5120 x 5120 at M = 768 48.8 -> 27.3; W8A8 96.6 / 98.3 -> 82.1 /
   // 84.8, 62.4 -> 33.1, 13824 x 5120 at M = 600 105.8 -> 77.7; 128-row tiles stay faster
-  // at M = 1024)
-  const bool mid_rows = M > 512 && M <= 768;
+  // at M = 1024 on wide matrices; extended for per-channel and W8A8 weights where
+  // measured: narrow matrices up to M = 1024 -- 5120 x 5120 48.5 / 69.8 -> 39.8 / 49.1 us,
+  // per-channel on 13824 x 5120 at M = 896 95.6 -> 81.3 -- and per-channel on wide ones up
+  // to M = 896 -- 75.5 -> 61.8; not for two-level weights, 3-8 % slower past M = 768)
+  const bool two_level = group_size > 0;
+  const int rows64_max = two_level ? 768 : N <= 8192 ? 1024 : (group_size < 0 ? 896 : 768);
+  const bool mid_rows = M > 512 && M <= rows64_max;
   p.bm = env_int("W4_W4A8_BM", (M <= 128 || short_narrow) ? 32 : ((M <= 512 || mid_rows) ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
   // int8 weights on 128-row tiles: the four-tile ring at one workgroup per CU (depth 0)
