@@ -605,10 +605,11 @@ GemmPlan gemm_plan(int M, int N, int K) {
     // CU (K = 5120, N = 5120 at M = 768 / 1024: 63.3 / 73.0 -> 51.1 / 70.4 us; K = 13824 at
     // M = 1024 181.9 -> 179.2; at M = 2048 the 128 x 256 tiles stay faster)
     if (N < 8192 && M <= 1024) pick = 3;
-    // wide matrices where 128 x 256 tiles fill under 384 of the 512 slots: 128 x 128 tiles
-    // (M = 640 / 768 on N = 13824 and M = 768 on N = 15360: 123.8 / 128.3 / 132.6 ->
-    // 119.1 / 123.7 / 128.0 us)
-    if (pick == 0 && N >= 8192 && ((M + 127) / 128) * ((N + 255) / 256) < 384) pick = 1;
+    // where 128 x 256 tiles fill under 384 of the 512 slots: 128 x 128 tiles (M = 640 /
+    // 768 on N = 13824 and M = 768 on N = 15360: 123.8 / 128.3 / 132.6 -> 119.1 / 123.7 /
+    // 128.0 us; M = 2048 on N = 5120, K = 5120 / 13824: 128.3 / 328.1 -> 123.5 / 319.0;
+    // not on N = 4096: 4096 x 4096 at M = 2048 69.9 against 70.8)
+    if (pick == 0 && N > 4096 && ((M + 127) / 128) * ((N + 255) / 256) < 384) pick = 1;
   }
   p.mi = kShapes[pick][0];
   p.nf = kShapes[pick][1];
