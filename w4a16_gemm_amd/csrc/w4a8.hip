@@ -1009,11 +1009,13 @@ W4A8Plan w4a8_plan(int M, int N, int K, int group_size) {
   // 85.7 -> 84.2), on 5120 x 5120 at M = 768 48.8 -> 27.3; W8A8 96.6 / 98.3 -> 82.1 /
   // 84.8, 62.4 -> 33.1, 13824 x 5120 at M = 600 105.8 -> 77.7; 128-row tiles stay faster
   // at M = 1024 on wide matrices; extended for per-channel and W8A8 weights where
-  // measured: narrow matrices up to M = 1024 -- 5120 x 5120 48.5 / 69.8 -> 39.8 / 49.1 us,
-  // per-channel on 13824 x 5120 at M = 896 95.6 -> 81.3 -- and per-channel on wide ones up
-  // to M = 896 -- 75.5 -> 61.8; not for two-level weights, 3-8 % slower past M = 768)
+  // measured: narrow matrices up to M = 2048 -- 5120 x 5120 at M = 1024 48.5 / 69.8 ->
+  // 39.8 / 49.1 us, at M = 1536 / 2048 per-channel 49.2 / 70.1 -> 42.1 / 61.9 and W8A8 at
+  // 2048 86.5 -> 77.2, per-channel on 13824 x 5120 at M = 896 / 2048 95.6 / 148.2 ->
+  // 81.3 / 135.4 -- and per-channel on wide ones up to M = 896 -- 75.5 -> 61.8; not for
+  // two-level weights, 3-8 % slower past M = 768)
   const bool two_level = group_size > 0;
-  const int rows64_max = two_level ? 768 : N <= 8192 ? 1024 : (group_size < 0 ? 896 : 768);
+  const int rows64_max = two_level ? 768 : N <= 8192 ? 2048 : (group_size < 0 ? 896 : 768);
   const bool mid_rows = M > 512 && M <= rows64_max;
   p.bm = env_int("W4_W4A8_BM", (M <= 128 || short_narrow) ? 32 : ((M <= 512 || mid_rows) ? 64 : 128));
   if (p.bm != 32 && p.bm != 64) p.bm = 128;
